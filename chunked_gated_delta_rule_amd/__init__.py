@@ -1,0 +1,197 @@
+"""Python binding of libgdn.so, the MI355X (gfx950) chunked gated-delta-rule
+prefill forward.
+
+The functions below carry the names of the C ABI in ``include/gdn.h`` and
+only marshal arguments: torch tensors become device pointers, the current
+torch stream becomes the hipStream_t, and a non-OK status becomes a
+``GDNError``. Every step of the computation runs in the library's HIP
+kernels; there is no fallback of any kind. If the library has not been built
+(``python -m chunked_gated_delta_rule_amd.build``), importing the binding
+still works but the first call raises.
+
+Layouts (packed varlen, batch 1): q, k [t_max, h, 128]; v, o [t_max, hv, 128];
+g, beta [t_max, hv] fp32; states [n_max, hv, 128 (v), 128 (k)] fp32;
+cu_seqlens int32 [n_max + 1].
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "GDNError", "gdn_config", "GDN_BF16", "GDN_F32", "load_library", "library_path",
+    "gdn_nt_max", "gdn_workspace_size", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
+    "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
+    "make_config", "chunk_gated_delta_rule", "EXPORTED_SYMBOLS",
+]
+
+GDN_BF16 = 0
+GDN_F32 = 1
+_STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
+           3: "GDN_ERR_CAPACITY", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
+EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_size", "gdn_build_chunk_indices",
+                    "gdn_front_conv_silu_l2", "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter",
+                    "gdn_chunk_fwd", "gdn_status_str")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libgdn.so")
+
+
+class gdn_config(ctypes.Structure):
+    _fields_ = [("t_max", ctypes.c_int32), ("n_max", ctypes.c_int32), ("h", ctypes.c_int32),
+                ("hv", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int), ("o_dtype", ctypes.c_int),
+                ("scale", ctypes.c_float)]
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libgdn.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is missing: build it with "
+                           "`python -m chunked_gated_delta_rule_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(gdn_config)
+    lib.gdn_nt_max.argtypes = [i32, i32, i32]
+    lib.gdn_nt_max.restype = ctypes.c_int64
+    lib.gdn_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
+    lib.gdn_build_chunk_indices.argtypes = [cfgp, vp, vp, vp]
+    lib.gdn_front_conv_silu_l2.argtypes = [cfgp, vp, vp, i32, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_intra.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_inter.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for name in ("gdn_workspace_size", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
+                 "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.gdn_status_str.argtypes = [ctypes.c_int]
+    lib.gdn_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def make_config(t_max, n_max, h, hv, qkv_dtype=GDN_BF16, scale=0.0, o_dtype=GDN_F32,
+                dk=128, dv=128, chunk=64) -> gdn_config:
+    if isinstance(qkv_dtype, torch.dtype):
+        qkv_dtype = GDN_F32 if qkv_dtype == torch.float32 else GDN_BF16
+    return gdn_config(int(t_max), int(n_max), int(h), int(hv), int(dk), int(dv), int(chunk),
+                      int(qkv_dtype), int(o_dtype), float(scale))
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, torch.Tensor):
+        if not x.is_cuda:
+            raise ValueError("device tensor expected")
+        if not x.is_contiguous():
+            raise ValueError("contiguous tensor expected")
+        return x.data_ptr()
+    raise TypeError(type(x))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise GDNError(st, where)
+
+
+def gdn_status_str(status: int) -> str:
+    return load_library().gdn_status_str(int(status)).decode()
+
+
+def gdn_nt_max(t_max: int, n_max: int, chunk: int = 64) -> int:
+    return int(load_library().gdn_nt_max(int(t_max), int(n_max), int(chunk)))
+
+
+def gdn_workspace_size(cfg: gdn_config) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().gdn_workspace_size(ctypes.byref(cfg), ctypes.byref(out)),
+           "gdn_workspace_size")
+    return int(out.value)
+
+
+def gdn_build_chunk_indices(cfg, cu_seqlens, chunk_indices, stream=None):
+    _check(load_library().gdn_build_chunk_indices(ctypes.byref(cfg), _ptr(cu_seqlens),
+                                                  _ptr(chunk_indices), _stream(stream)),
+           "gdn_build_chunk_indices")
+
+
+def gdn_front_conv_silu_l2(cfg, qkv, conv_w, d_conv, cu_seqlens, q, k, v, stream=None):
+    _check(load_library().gdn_front_conv_silu_l2(ctypes.byref(cfg), _ptr(qkv), _ptr(conv_w),
+                                                 int(d_conv), _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                                                 _ptr(v), _stream(stream)),
+           "gdn_front_conv_silu_l2")
+
+
+def gdn_chunk_fwd_intra(cfg, k, v, g, beta, cu_seqlens, chunk_indices, w, u, stream=None):
+    _check(load_library().gdn_chunk_fwd_intra(ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(g),
+                                              _ptr(beta), _ptr(cu_seqlens), _ptr(chunk_indices),
+                                              _ptr(w), _ptr(u), _stream(stream)),
+           "gdn_chunk_fwd_intra")
+
+
+def gdn_chunk_fwd_inter(cfg, q, k, w, u, g, h0, cu_seqlens, o, hT, stream=None):
+    _check(load_library().gdn_chunk_fwd_inter(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(w),
+                                              _ptr(u), _ptr(g), _ptr(h0), _ptr(cu_seqlens),
+                                              _ptr(o), _ptr(hT), _stream(stream)),
+           "gdn_chunk_fwd_inter")
+
+
+def gdn_chunk_fwd(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT, workspace,
+                  ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().gdn_chunk_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                        _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+                                        _ptr(chunk_indices), _ptr(o), _ptr(hT), _ptr(workspace),
+                                        int(ws_bytes), _stream(stream)),
+           "gdn_chunk_fwd")
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, cu_seqlens, initial_state=None,
+                           output_final_state=True, scale=None, chunk_indices=None,
+                           workspace=None, n_max=None):
+    """Allocate outputs with torch and run gdn_chunk_fwd on the current stream.
+
+    q, k [T, H, 128] and v [T, Hv, 128] (bf16 or fp32, same dtype); g, beta
+    [T, Hv] fp32; cu_seqlens int32 [N + 1] on the device; initial_state
+    [N, Hv, 128, 128] fp32 or None. Returns (o [T, Hv, 128] fp32, final state
+    or None).
+    """
+    T, H, _ = q.shape
+    Hv = v.shape[1]
+    n = cu_seqlens.numel() - 1 if n_max is None else n_max
+    cfg = make_config(T, n, H, Hv, q.dtype, scale or 0.0)
+    if workspace is None:
+        workspace = torch.empty(gdn_workspace_size(cfg), dtype=torch.uint8, device=q.device)
+    o = torch.empty((T, Hv, 128), dtype=torch.float32, device=q.device)
+    hT = torch.empty((n, Hv, 128, 128), dtype=torch.float32, device=q.device) \
+        if output_final_state else None
+    gdn_chunk_fwd(cfg, q, k, v, g, beta, initial_state, cu_seqlens, chunk_indices, o, hT,
+                  workspace)
+    return o, hT

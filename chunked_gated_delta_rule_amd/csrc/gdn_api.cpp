@@ -1,0 +1,180 @@
+// C ABI of the gfx950 GDN chunk-prefill library (declared in include/gdn.h).
+//
+// Every entry point validates all of its arguments on the host first and
+// returns a status without touching the GPU when a check fails; only then does
+// it enqueue kernels on the caller's stream. Nothing here allocates, frees or
+// synchronises, so a call can be captured into a HIP graph.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "gdn_launch.hpp"
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kChunk = 64;
+constexpr int kMaxHeads = 4096;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+gdn_status check_config(const gdn_config *cfg) {
+  if (!cfg) return GDN_ERR_INVALID_ARG;
+  if (cfg->t_max < 0 || cfg->n_max < 1 || cfg->h < 1 || cfg->hv < 1) return GDN_ERR_INVALID_ARG;
+  if (cfg->qkv_dtype != GDN_BF16 && cfg->qkv_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
+  if (cfg->o_dtype != GDN_BF16 && cfg->o_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
+  if (std::isnan(cfg->scale) || std::isinf(cfg->scale)) return GDN_ERR_INVALID_ARG;
+  if (cfg->dk != kD || cfg->dv != kD || cfg->chunk != kChunk) return GDN_ERR_UNSUPPORTED;
+  if (cfg->hv % cfg->h != 0) return GDN_ERR_UNSUPPORTED;
+  if (cfg->o_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (cfg->t_max > GDN_T_MAX_LIMIT || cfg->n_max > GDN_N_MAX_LIMIT || cfg->hv > kMaxHeads)
+    return GDN_ERR_CAPACITY;
+  return GDN_OK;
+}
+
+int32_t nt_max_of(const gdn_config *cfg) {
+  return static_cast<int32_t>((static_cast<int64_t>(cfg->t_max) + kChunk - 1) / kChunk +
+                              cfg->n_max - 1);
+}
+
+size_t w_bytes(const gdn_config *cfg) { return static_cast<size_t>(cfg->hv) * cfg->t_max * kD * 2; }
+size_t u_bytes(const gdn_config *cfg) { return static_cast<size_t>(cfg->hv) * cfg->t_max * kD * 4; }
+size_t table_bytes(const gdn_config *cfg) { return static_cast<size_t>(nt_max_of(cfg)) * 2 * 4; }
+
+float scale_of(const gdn_config *cfg) {
+  return cfg->scale > 0.f ? cfg->scale : 1.0f / std::sqrt(static_cast<float>(cfg->dk));
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk) {
+  if (t_max < 0 || n_max < 1 || chunk < 1) return -1;
+  return (static_cast<int64_t>(t_max) + chunk - 1) / chunk + n_max - 1;
+}
+
+gdn_status gdn_workspace_size(const gdn_config *cfg, size_t *bytes) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!bytes) return GDN_ERR_INVALID_ARG;
+  *bytes = align_up(w_bytes(cfg)) + align_up(u_bytes(cfg)) + align_up(table_bytes(cfg));
+  return GDN_OK;
+}
+
+gdn_status gdn_build_chunk_indices(const gdn_config *cfg, const int32_t *cu_seqlens,
+                                   int32_t *chunk_indices, void *stream) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!cu_seqlens || !chunk_indices || !aligned16(chunk_indices) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return GDN_ERR_INVALID_ARG;
+  return from_hip(gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), chunk_indices,
+                                          as_stream(stream)));
+}
+
+gdn_status gdn_front_conv_silu_l2(const gdn_config *cfg, const void *qkv, const void *conv_w,
+                                  int32_t d_conv, const int32_t *cu_seqlens, float *q, float *k,
+                                  float *v, void *stream) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!qkv || !conv_w || !cu_seqlens || !q || !k || !v) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(qkv) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      (reinterpret_cast<uintptr_t>(conv_w) & 1u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return GDN_ERR_INVALID_ARG;
+  if (d_conv < 1 || d_conv > 8) return GDN_ERR_UNSUPPORTED;
+  return from_hip(gdn::launch_front(qkv, conv_w, d_conv, cu_seqlens, cfg->n_max, cfg->t_max,
+                                    cfg->h, cfg->hv, q, k, v, as_stream(stream)));
+}
+
+gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *k, const void *v,
+                               const float *g, const float *beta, const int32_t *cu_seqlens,
+                               const int32_t *chunk_indices, void *w, float *u, void *stream) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!k || !v || !g || !beta || !cu_seqlens || !chunk_indices || !w || !u)
+    return GDN_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
+      !aligned16(chunk_indices) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return GDN_ERR_INVALID_ARG;
+  if (cfg->t_max == 0) return GDN_OK;
+  return from_hip(gdn::launch_intra(cfg->qkv_dtype == GDN_F32, k, v, g, beta, cu_seqlens,
+                                    chunk_indices, nt_max_of(cfg), cfg->h, cfg->hv, cfg->t_max,
+                                    w, u, as_stream(stream)));
+}
+
+gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const void *q, const void *k,
+                               const void *w, const float *u, const float *g, const float *h0,
+                               const int32_t *cu_seqlens, void *o, float *hT, void *stream) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !w || !u || !g || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(u) || !aligned16(o) ||
+      (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) ||
+      (reinterpret_cast<uintptr_t>(g) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return GDN_ERR_INVALID_ARG;
+  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, q, k, w, u, g, h0, cu_seqlens,
+                                    cfg->n_max, cfg->h, cfg->hv, cfg->t_max, scale_of(cfg),
+                                    static_cast<float *>(o), hT, as_stream(stream)));
+}
+
+gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *h0,
+                         const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
+                         float *hT, void *workspace, size_t ws_bytes, void *stream) {
+  size_t need = 0;
+  const gdn_status st = gdn_workspace_size(cfg, &need);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return GDN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) ||
+      (chunk_indices && !aligned16(chunk_indices)) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return GDN_ERR_INVALID_ARG;
+  char *ws = static_cast<char *>(workspace);
+  void *w = ws;
+  float *u = reinterpret_cast<float *>(ws + align_up(w_bytes(cfg)));
+  int32_t *table = reinterpret_cast<int32_t *>(ws + align_up(w_bytes(cfg)) + align_up(u_bytes(cfg)));
+  hipStream_t s = as_stream(stream);
+  if (!chunk_indices) {
+    const hipError_t e = gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), table, s);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    chunk_indices = table;
+  }
+  if (cfg->t_max > 0) {
+    const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, k, v, g, beta, cu_seqlens,
+                                           chunk_indices, nt_max_of(cfg), cfg->h, cfg->hv,
+                                           cfg->t_max, w, u, s);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+  }
+  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, q, k, w, u, g, h0, cu_seqlens,
+                                    cfg->n_max, cfg->h, cfg->hv, cfg->t_max, scale_of(cfg),
+                                    static_cast<float *>(o), hT, s));
+}
+
+const char *gdn_status_str(gdn_status status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_CAPACITY: return "GDN_ERR_CAPACITY";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Device-side building blocks shared by the gfx950 GDN kernels: vector types,
+// bf16 rounding and hi/lo splitting, the 16x16x32 bf16 MFMA, and fragment
+// loads from LDS.
+//
+// MFMA fragment convention (v_mfma_f32_16x16x32_bf16, one wave64):
+//   A (16 x 32): lane l holds row (l & 15), eight consecutive k starting at
+//                8 * (l >> 4);
+//   B (32 x 16): lane l holds column (l & 15), the same eight k;
+//   C (16 x 16): lane l holds column (l & 15), rows 4 * (l >> 4) + i, i < 4.
+// Which physical k each lane slot feeds does not change the result as long as
+// A and B use the same assignment, which the loaders below guarantee. So an
+// operand whose contraction index is contiguous in LDS is read with one
+// 16-byte load per fragment.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;       // Dk = Dv
+constexpr int kC = 64;        // chunk length
+constexpr int kThreads = 256; // four wave64s per work-group
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
+__device__ __forceinline__ float from_bf16(__bf16 x) { return static_cast<float>(x); }
+
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): 16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
+  hi = to_bf16(x);
+  lo = to_bf16(x - from_bf16(hi));
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const __bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// A fragment of a row-major LDS matrix (row stride ld elements), rows
+// [r0, r0 + 16), contraction columns [k0, k0 + 32).
+__device__ __forceinline__ bf16x8 frag_rows(const __bf16 *base, int ld, int r0, int k0, int lane) {
+  return lds_frag(base + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Unpack 8 bf16 held in a 16-byte word into floats.
+__device__ __forceinline__ void unpack8(const u32x4 &w, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+}  // namespace gdn

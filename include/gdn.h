@@ -1,0 +1,145 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunked gated-delta-rule prefill forward.
+ *
+ * The operation (gated delta rule, per sequence s and value head hv, state S of
+ * Dk x Dv = 128 x 128 fp32; Alloy page "Chunking Qwen3.5's gated DeltaNet ...",
+ * section "What is the gated delta rule in Qwen3.5?"): for each token t the
+ * state is decayed by exp(g[t,hv]), corrected by beta[t,hv] * (v_t - S^T k_t),
+ * written back as S += k_t d^T, and the output is o_t = scale * S^T q_t, read
+ * after the write. It is evaluated in chunks of 64 tokens in two stages whose
+ * parallel domains differ ("Optimizing GDN Chunk Prefill on Intel AMX CPU",
+ * sections 1 and 3): an intra-chunk stage over [chunks, key heads] producing
+ * w and u, and an inter-chunk stage over [sequences, value heads] carrying S.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked (device) are device memory owned by the caller. The
+ *    library never allocates, never frees, never synchronises, and launches
+ *    only on `stream` (a hipStream_t passed as void*, NULL = null stream), so
+ *    every call can be captured into a HIP graph.
+ *  - Inputs are read-only. Layouts are row-major, packed varlen with batch 1
+ *    (AMX page, section 9): token rows [t_max, ...].
+ *  - cu_seqlens (device, int32, n_max + 1 entries): cu[0] = 0, non-decreasing,
+ *    cu[n_max] <= t_max; unused tail sequences are zero-length (FLA issue 1155,
+ *    "Core design"). It is a precondition: it is never read on the host.
+ *  - GQA: value head hv reads key/query head hv / (hv_count / h_count) (AMX
+ *    page, section 4).
+ *  - States h0 / hT: [n_max, hv, dv, dk] fp32, value-major (AMX page, s. 9).
+ *  - Errors: every argument and capacity is checked on the host before any
+ *    HIP call; a failed check returns a status and touches nothing. A launch
+ *    failure returns GDN_ERR_HIP. No call ever aborts the process.
+ *  - Thread safety: the functions keep no state; concurrent calls on different
+ *    streams are safe when their output and workspace buffers are disjoint.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum */
+  GDN_ERR_UNSUPPORTED = 2, /* dk/dv != 128, chunk != 64, hv % h != 0, dtype */
+  GDN_ERR_CAPACITY = 3,    /* t_max / n_max beyond what the kernels index */
+  GDN_ERR_WORKSPACE = 4,   /* workspace too small or misaligned */
+  GDN_ERR_HIP = 5          /* a kernel launch failed */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+typedef struct {
+  int32_t t_max;       /* token capacity (rows of q, k, v, g, beta, o) */
+  int32_t n_max;       /* sequence capacity (cu_seqlens has n_max + 1 entries) */
+  int32_t h;           /* key / query heads */
+  int32_t hv;          /* value heads, a multiple of h */
+  int32_t dk, dv;      /* head dims; must both be 128 */
+  int32_t chunk;       /* chunk length; must be 64 */
+  gdn_dtype qkv_dtype; /* dtype of q, k, v: GDN_BF16 or GDN_F32 */
+  gdn_dtype o_dtype;   /* dtype of o: GDN_F32 (the only one supported) */
+  float scale;         /* output scale; <= 0 selects 1 / sqrt(dk) */
+} gdn_config;
+
+/* Largest valid gdn_config.t_max / n_max. */
+#define GDN_T_MAX_LIMIT (1 << 24)
+#define GDN_N_MAX_LIMIT 16384
+
+/* Static bound on the number of chunks of any batch of at most t_max tokens in
+ * at most n_max sequences: cdiv(t_max, chunk) + n_max - 1 (FLA issue 1155,
+ * "Core design"). Returns -1 if an argument is not positive (t_max may be 0). */
+int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
+
+/* Bytes of workspace gdn_chunk_fwd needs for `cfg`: w [hv, t_max, dk] bf16,
+ * u [hv, t_max, dv] fp32 and a [nt_max, 2] int32 chunk table, each 256-byte
+ * aligned. Writes *bytes; returns a validation status. */
+gdn_status gdn_workspace_size(const gdn_config *cfg, size_t *bytes);
+
+/* Chunk-index table built on the device (FLA issue 1155, "Core design": a
+ * searchsorted fill of a fixed [NT_max, 2] buffer, sentinel in unused slots).
+ *   cu_seqlens    (device) int32 [n_max + 1]
+ *   chunk_indices (device) int32 [nt_max, 2], written: slot j < total chunks
+ *                 holds (sequence id, chunk number within the sequence), in
+ *                 (sequence, chunk) order; every other slot holds (-1, -1).
+ * One work-group; reads cu_seqlens on the device only. */
+gdn_status gdn_build_chunk_indices(const gdn_config *cfg, const int32_t *cu_seqlens,
+                                   int32_t *chunk_indices, void *stream);
+
+/* Causal depthwise conv + SiLU + per-head L2 norm of q and k, producing the
+ * fp32 q, k, v that the chunk forward consumes (llama.cpp PR 399, "How
+ * (exactness)": sum over d_conv taps with the current token last, no bias;
+ * AMX page, section 7: x / sqrt(sum x^2 + eps), eps = 1e-6).
+ *   qkv    (device) bf16 [t_max, 2*h*dk + hv*dv], channels q | k | v, head-major
+ *   conv_w (device) bf16 [2*h*dk + hv*dv, d_conv], 1 <= d_conv <= 8
+ *   q, k   (device) fp32 [t_max, h, dk]   v (device) fp32 [t_max, hv, dv]
+ * History before each sequence start is zero. Rows past cu[n_max] are not
+ * written. cfg->qkv_dtype is ignored (the front always reads bf16). */
+gdn_status gdn_front_conv_silu_l2(const gdn_config *cfg, const void *qkv, const void *conv_w,
+                                  int32_t d_conv, const int32_t *cu_seqlens, float *q, float *k,
+                                  float *v, void *stream);
+
+/* Intra-chunk stage over [nt_max, h] (AMX page, section 4): per chunk and key
+ * head, K K^T once; per value head of the group the beta/decay-masked strictly
+ * lower A, T = (I + A)^-1 kept on chip, w = T diag(beta e^gamma) K and
+ * u = T diag(beta) V, gamma the chunk-local cumulative g.
+ *   k (device) [t_max, h, dk]; v (device) [t_max, hv, dv]; dtype cfg->qkv_dtype
+ *   g, beta (device) fp32 [t_max, hv]
+ *   chunk_indices (device) int32 [nt_max, 2] as built by gdn_build_chunk_indices
+ *   w (device) bf16 [hv, t_max, dk], u (device) fp32 [hv, t_max, dv]: rows of
+ *     valid tokens are written, every other row is left untouched. */
+gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *k, const void *v,
+                               const float *g, const float *beta, const int32_t *cu_seqlens,
+                               const int32_t *chunk_indices, void *w, float *u, void *stream);
+
+/* Inter-chunk stage over [n_max, hv, dv / 16] (AMX page, section 5): chunks in
+ * order with S on chip: v' = u - w S; o = scale (diag(e^gamma) q S +
+ * tril(q k^T * Gamma) v'); S = e^{gamma_last} S + (diag(e^{gamma_last-gamma}) k)^T v'.
+ *   q, k (device) [t_max, h, dk], dtype cfg->qkv_dtype; w, u as written by
+ *   gdn_chunk_fwd_intra; g (device) fp32 [t_max, hv];
+ *   h0 (device, nullable = zero state) fp32 [n_max, hv, dv, dk];
+ *   o  (device) fp32 [t_max, hv, dv]: valid rows written, others untouched;
+ *   hT (device, nullable) fp32 [n_max, hv, dv, dk]; hT may alias h0 exactly.
+ * A zero-length sequence writes hT = h0 (or zeros when h0 is null). */
+gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const void *q, const void *k,
+                               const void *w, const float *u, const float *g, const float *h0,
+                               const int32_t *cu_seqlens, void *o, float *hT, void *stream);
+
+/* Whole forward: [chunk table if chunk_indices is NULL] -> intra -> inter, all
+ * on `stream`, no host synchronisation. Arguments as above; workspace (device)
+ * of at least gdn_workspace_size bytes, 256-byte aligned, holds w, u and the
+ * table between the stages and may be reused once the stream passes the call. */
+gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *h0,
+                         const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
+                         float *hT, void *workspace, size_t ws_bytes, void *stream);
+
+/* Static string for a status code (never NULL). */
+const char *gdn_status_str(gdn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+declared in include/gdn.h, and rejects bad arguments on the host with the
+documented status before any HIP call. No test here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_gated_delta_rule_amd as gdn
+from oracle import index_table
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.library_path):
+        pytest.fail("libgdn.so is not built (run python -m chunked_gated_delta_rule_amd.build)")
+    return gdn.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert set(_declared_functions()) == set(gdn.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "GDN_OK"), (1, "GDN_ERR_INVALID_ARG"), (2, "GDN_ERR_UNSUPPORTED"),
+                       (3, "GDN_ERR_CAPACITY"), (4, "GDN_ERR_WORKSPACE"), (5, "GDN_ERR_HIP")]:
+        assert gdn.gdn_status_str(code) == name
+    assert gdn.gdn_status_str(99) == "GDN_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("t_max,n_max", [(0, 1), (1, 1), (64, 1), (65, 1), (4096, 32),
+                                         (32768, 32), (32768, 1), (100, 7)])
+def test_nt_max_matches_oracle_bound(lib, t_max, n_max):
+    assert gdn.gdn_nt_max(t_max, n_max) == index_table.nt_max(t_max, n_max)
+
+
+def test_nt_max_rejects_bad_arguments(lib):
+    assert gdn.gdn_nt_max(-1, 1) == -1
+    assert gdn.gdn_nt_max(10, 0) == -1
+    assert gdn.gdn_nt_max(10, 1, 0) == -1
+
+
+def test_workspace_size_layout(lib):
+    cfg = gdn.make_config(4096, 1, 16, 32)
+    al = lambda x: (x + 255) // 256 * 256
+    nt = index_table.nt_max(4096, 1)
+    assert gdn.gdn_workspace_size(cfg) == al(32 * 4096 * 128 * 2) + al(32 * 4096 * 128 * 4) + al(nt * 8)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dk", 64, UNSUPPORTED), ("dv", 256, UNSUPPORTED), ("chunk", 32, UNSUPPORTED),
+    ("hv", 24, UNSUPPORTED), ("o_dtype", gdn.GDN_BF16, UNSUPPORTED),
+    ("t_max", -1, INVALID), ("n_max", 0, INVALID), ("h", 0, INVALID), ("qkv_dtype", 7, INVALID),
+    ("scale", float("nan"), INVALID), ("t_max", (1 << 24) + 1, CAPACITY), ("n_max", 16385, CAPACITY),
+])
+def test_config_validation(lib, field, value, status):
+    cfg = gdn.make_config(256, 2, 16, 32)
+    setattr(cfg, field, value)
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_workspace_size(ctypes.byref(cfg), ctypes.byref(out)) == status
+
+
+def test_null_config_and_output(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_workspace_size(None, ctypes.byref(out)) == INVALID
+    cfg = gdn.make_config(256, 2, 16, 32)
+    assert lib.gdn_workspace_size(ctypes.byref(cfg), None) == INVALID
+
+
+FAKE = 1 << 20  # 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def _fwd(lib, cfg, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=FAKE, ci=None, o=FAKE,
+                hT=None, ws=FAKE, ws_bytes=1 << 40)
+    args.update(over)
+    return lib.gdn_chunk_fwd(ctypes.byref(cfg), args["q"], args["k"], args["v"], args["g"],
+                             args["beta"], args["h0"], args["cu"], args["ci"], args["o"],
+                             args["hT"], args["ws"], args["ws_bytes"], None)
+
+
+def test_chunk_fwd_host_errors(lib):
+    cfg = gdn.make_config(256, 2, 16, 32)
+    need = gdn.gdn_workspace_size(cfg)
+    assert _fwd(lib, cfg, q=None) == INVALID
+    assert _fwd(lib, cfg, o=None) == INVALID
+    assert _fwd(lib, cfg, ws=None) == WORKSPACE
+    assert _fwd(lib, cfg, ws_bytes=need - 1) == WORKSPACE
+    assert _fwd(lib, cfg, ws=FAKE + 16) == WORKSPACE          # not 256-byte aligned
+    assert _fwd(lib, cfg, q=FAKE + 2) == INVALID               # not 16-byte aligned
+    assert _fwd(lib, cfg, g=FAKE + 2) == INVALID
+    bad = gdn.make_config(256, 2, 16, 24)
+    assert _fwd(lib, bad) == UNSUPPORTED
+
+
+def test_stage_entry_points_host_errors(lib):
+    cfg = gdn.make_config(256, 2, 16, 32)
+    c = ctypes.byref(cfg)
+    assert lib.gdn_chunk_fwd_intra(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == INVALID
+    assert lib.gdn_chunk_fwd_intra(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, None) == INVALID
+    assert lib.gdn_chunk_fwd_inter(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None) == INVALID
+    assert lib.gdn_chunk_fwd_inter(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, None, None) == INVALID
+    assert lib.gdn_build_chunk_indices(c, FAKE, None, None) == INVALID
+    assert lib.gdn_front_conv_silu_l2(c, FAKE, FAKE, 9, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.gdn_front_conv_silu_l2(c, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.gdn_front_conv_silu_l2(c, None, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == INVALID

@@ -1,0 +1,289 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar (from the method's tolerance): max |o_gpu - o_ref| / max |o_ref| <= 2e-3
+and relative Frobenius error of the final states <= 1e-3 over every checked
+lane; the chunk-index table is bit-exact. Small cases are checked on every
+lane; the five full-size workloads are run whole on the GPU, in the launch
+configuration the benchmark times, and checked on sampled lanes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_rule_amd as gdn
+import workloads
+from oracle import chunked, index_table, recurrent
+
+from gpu_helpers import (O_TOL, S_TOL, config_of, device_inputs, lane_errors, log,
+                         oracle_inputs_f64, oracle_lanes, run_forward, run_front)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    gdn.load_library()  # raises if the HIP library is missing
+
+
+def _all_lanes(wl):
+    n = len(wl.cu_seqlens) - 1
+    return [(s, hv) for s in range(n) for hv in range(wl.Hv)]
+
+
+# --------------------------------------------------------------------------- #
+# chunk-index table: bit-exact against the oracle's loops
+# --------------------------------------------------------------------------- #
+
+def _cu_cases():
+    rng = np.random.Generator(np.random.PCG64(3))
+    cases = [([256], 256, 1), ([4096], 4096, 1), ([32768], 32768, 1),
+             ([1, 63, 64, 65, 0, 128, 129], 600, 9), ([0, 0, 5], 5, 3)]
+    w2 = workloads.make(2)
+    cases.append((list(np.diff(w2.cu_seqlens)), w2.t_max, w2.n_max))
+    lengths = rng.integers(0, 2000, size=700)
+    cases.append((list(lengths), int(lengths.sum()) + 77, 1000))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(7))
+def test_chunk_index_table_bit_exact(case):
+    lengths, t_max, n_max = _cu_cases()[case]
+    cu = np.zeros(n_max + 1, np.int32)
+    cu[1:len(lengths) + 1] = np.cumsum(lengths)
+    cu[len(lengths) + 1:] = cu[len(lengths)]
+    cfg = gdn.make_config(t_max, n_max, 1, 1)
+    nt = gdn.gdn_nt_max(t_max, n_max)
+    log(f"index case {case}: n={len(lengths)} t_max={t_max} n_max={n_max} nt_max={nt}")
+    table = torch.full((nt, 2), 12345, dtype=torch.int32, device=DEV)
+    gdn.gdn_build_chunk_indices(cfg, torch.from_numpy(cu).to(DEV), table)
+    torch.cuda.synchronize()
+    ref = np.array(index_table.chunk_index_table(list(cu), nt), dtype=np.int32)
+    assert np.array_equal(table.cpu().numpy(), ref)
+
+
+# --------------------------------------------------------------------------- #
+# front: conv + SiLU + L2 norm (fp32) against the fp64 front
+# --------------------------------------------------------------------------- #
+
+def test_front_small_varlen():
+    wl = workloads.make_custom([5, 0, 130, 1, 64], 2, 4, seed=11, front=True, t_max=230, n_max=6)
+    log("front small varlen")
+    d = device_inputs(wl)
+    q, k, v = run_front(wl, d)
+    torch.cuda.synchronize()
+    rq, rk, rv = recurrent.gdn_front(wl.f64("qkv"), wl.f64("conv_w"), wl.cu_seqlens, 2, 4, 128, 128)
+    T = int(wl.cu_seqlens[-1])
+    for got, ref in ((q, rq), (k, rk), (v, rv)):
+        g64 = got[:T].cpu().double().numpy()
+        assert np.max(np.abs(g64 - ref[:T])) / np.max(np.abs(ref[:T])) < 1e-5
+
+
+# --------------------------------------------------------------------------- #
+# stage 1 alone: w (bf16) and u (fp32) against the chunked-form oracle
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_intra_stage_w_u(dtype):
+    wl = workloads.make_custom([130, 70, 64, 1], 2, 4, seed=5, dtype=dtype, t_max=300, n_max=5)
+    log(f"intra stage {dtype}")
+    d = device_inputs(wl)
+    cfg = config_of(wl)
+    nt = gdn.gdn_nt_max(wl.t_max, wl.n_max)
+    table = torch.empty((nt, 2), dtype=torch.int32, device=DEV)
+    gdn.gdn_build_chunk_indices(cfg, d["cu"], table)
+    w = torch.zeros((wl.Hv, wl.t_max, 128), dtype=torch.bfloat16, device=DEV)
+    u = torch.zeros((wl.Hv, wl.t_max, 128), dtype=torch.float32, device=DEV)
+    gdn.gdn_chunk_fwd_intra(cfg, d["k"], d["v"], d["g"], d["beta"], d["cu"], table, w, u)
+    torch.cuda.synchronize()
+    _, _, W, U = chunked.gdn_chunked(wl.f64("q"), wl.f64("k"), wl.f64("v"), wl.f64("g"),
+                                     wl.f64("beta"), wl.cu_seqlens, chunk=64, return_wu=True)
+    T = int(wl.cu_seqlens[-1])
+    wg = w[:, :T].cpu().double().numpy()
+    ug = u[:, :T].cpu().double().numpy()
+    ew = np.max(np.abs(wg - W[:, :T])) / np.max(np.abs(W[:, :T]))
+    eu = np.max(np.abs(ug - U[:, :T])) / np.max(np.abs(U[:, :T]))
+    log(f"  w err {ew:.3e}  u err {eu:.3e}")
+    assert ew < 4e-3   # bf16 storage of w: half an ulp is 2^-9 of the value
+    assert eu < 1e-4
+
+
+# --------------------------------------------------------------------------- #
+# whole forward, small cases, every lane
+# --------------------------------------------------------------------------- #
+
+SMALL = {
+    "dense-256-fp32": dict(lengths=[256], H=2, Hv=2, dtype=torch.float32),
+    "ragged-bf16-gqa-h0": dict(lengths=[1, 63, 64, 65, 200, 0, 129], H=2, Hv=4,
+                               dtype=torch.bfloat16, h0_sigma=0.02, n_max=8, t_max=600),
+    "ragged-fp32-h0": dict(lengths=[70, 3, 190], H=1, Hv=2, dtype=torch.float32, h0_sigma=0.05),
+    "strong-decay": dict(lengths=[300], H=1, Hv=1, dtype=torch.bfloat16, g_mu=2.0, h0_sigma=0.02),
+    "weak-decay": dict(lengths=[400, 150], H=1, Hv=2, dtype=torch.bfloat16, g_mu=-5.0,
+                       h0_sigma=0.02),
+    "gqa4": dict(lengths=[100, 60], H=1, Hv=4, dtype=torch.bfloat16),
+    "beta-one": dict(lengths=[128], H=2, Hv=2, dtype=torch.bfloat16, beta_mode=1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small_every_lane(name):
+    p = dict(SMALL[name])
+    lengths = p.pop("lengths")
+    H, Hv = p.pop("H"), p.pop("Hv")
+    wl = workloads.make_custom(lengths, H, Hv, seed=17, name=name, **p)
+    log(f"forward small {name}")
+    o, hT, _ = run_forward(wl)
+    ref = oracle_lanes(wl, _all_lanes(wl))
+    eo, es = lane_errors(wl, o, hT, ref)
+    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+
+
+def test_forward_front_small_every_lane():
+    wl = workloads.make_custom([100, 37, 0, 64], 2, 4, seed=23, front=True, n_max=5, t_max=220)
+    log("forward front small")
+    o, hT, _ = run_forward(wl)
+    qkv64 = oracle_inputs_f64(wl)
+    ref = oracle_lanes(wl, _all_lanes(wl), qkv64=qkv64)
+    eo, es = lane_errors(wl, o, hT, ref)
+    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+
+
+# --------------------------------------------------------------------------- #
+# bitwise self-consistency of the HIP path
+# --------------------------------------------------------------------------- #
+
+def _wl_props():
+    return workloads.make_custom([200, 64, 77], 2, 4, seed=31, h0_sigma=0.02, t_max=400, n_max=4)
+
+
+def test_replay_is_bitwise_deterministic():
+    wl = _wl_props()
+    d = device_inputs(wl)
+    o1, s1, _ = run_forward(wl, d)
+    o2, s2, _ = run_forward(wl, d)
+    T = int(wl.cu_seqlens[-1])
+    assert torch.equal(o1[:T], o2[:T]) and torch.equal(s1, s2)
+
+
+def test_packing_invariance_bitwise():
+    wl = _wl_props()
+    o, hT, _ = run_forward(wl)
+    cu = wl.cu_seqlens
+    for s in range(3):
+        a, e = int(cu[s]), int(cu[s + 1])
+        one = workloads.Workload(
+            name="alone", cu_seqlens=np.array([0, e - a], np.int32), t_max=e - a, n_max=1,
+            H=wl.H, Hv=wl.Hv, qkv_dtype=wl.qkv_dtype, q=wl.q[a:e].clone(), k=wl.k[a:e].clone(),
+            v=wl.v[a:e].clone(), g=wl.g[a:e].clone(), beta=wl.beta[a:e].clone(),
+            h0=wl.h0[s:s + 1].clone())
+        o1, h1, _ = run_forward(one)
+        assert torch.equal(o1, o[a:e]) and torch.equal(h1[0], hT[s])
+
+
+def test_chunk_aligned_continuation_bitwise():
+    wl = workloads.make_custom([320], 2, 4, seed=41, h0_sigma=0.02)
+    o, hT, _ = run_forward(wl)
+    split = 128
+    parts = []
+    state = wl.h0.clone()
+    for a, e in ((0, split), (split, 320)):
+        part = workloads.Workload(
+            name="part", cu_seqlens=np.array([0, e - a], np.int32), t_max=e - a, n_max=1,
+            H=wl.H, Hv=wl.Hv, qkv_dtype=wl.qkv_dtype, q=wl.q[a:e].clone(), k=wl.k[a:e].clone(),
+            v=wl.v[a:e].clone(), g=wl.g[a:e].clone(), beta=wl.beta[a:e].clone(), h0=state)
+        op, hp, _ = run_forward(part)
+        parts.append(op)
+        state = hp.cpu()
+    assert torch.equal(torch.cat(parts), o) and torch.equal(state.to(DEV), hT)
+
+
+def test_external_table_and_in_place_state():
+    wl = _wl_props()
+    d = device_inputs(wl)
+    o1, s1, _ = run_forward(wl, d)
+    cfg = config_of(wl)
+    table = torch.empty((gdn.gdn_nt_max(wl.t_max, wl.n_max), 2), dtype=torch.int32, device=DEV)
+    gdn.gdn_build_chunk_indices(cfg, d["cu"], table)
+    state = d["h0"].clone()
+    o2, s2, _ = run_forward(wl, d, h0=state, hT=state, chunk_indices=table)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and s2.data_ptr() == state.data_ptr()
+
+
+def test_zero_length_sequences_keep_state():
+    wl = workloads.make_custom([0, 50, 0], 1, 2, seed=43, h0_sigma=0.1, n_max=5, t_max=64)
+    o, hT, _ = run_forward(wl)
+    for s in (0, 2, 3, 4):
+        assert torch.equal(hT[s].cpu(), wl.h0[s])
+    wl.h0 = None
+    o, hT, _ = run_forward(wl)
+    assert torch.count_nonzero(hT[[0, 2, 3, 4]]) == 0
+
+
+def test_untouched_rows_past_the_batch():
+    wl = workloads.make_custom([70, 10], 1, 2, seed=47, t_max=200, n_max=2)
+    o, _, _ = run_forward(wl)
+    assert torch.isnan(o[80:]).all() and torch.isfinite(o[:80]).all()
+
+
+def test_no_decay_no_write_keeps_state_bitwise():
+    wl = workloads.make_custom([150], 1, 2, seed=53, h0_sigma=0.1)
+    wl.g.zero_()
+    wl.beta.zero_()
+    o, hT, _ = run_forward(wl)
+    assert torch.equal(hT.cpu(), wl.h0)
+
+
+# --------------------------------------------------------------------------- #
+# the five named workloads at full size (sampled lanes)
+# --------------------------------------------------------------------------- #
+
+SAMPLED = {
+    0: None,  # every lane
+    1: [(0, 0), (0, 1), (0, 13), (0, 31)],
+    2: "pick",
+    3: [(0, 0), (0, 15)],
+    4: [(0, 0), (3, 31)],
+}
+
+
+@pytest.mark.parametrize("cfg_id", [0, 1, 2, 3, 4])
+def test_named_workload_full_size(cfg_id):
+    wl = workloads.make(cfg_id)
+    log(f"workload {cfg_id} ({wl.name}) tokens={wl.n_tokens}")
+    o, hT, _ = run_forward(wl)
+    lanes = SAMPLED[cfg_id]
+    if lanes is None:
+        lanes = _all_lanes(wl)
+    elif lanes == "pick":
+        lens = np.diff(wl.cu_seqlens)
+        order = np.argsort(lens)
+        lanes = [(int(order[-1]), 5), (int(order[0]), 30), (int(order[len(order) // 2]), 17)]
+    qkv64 = None
+    if wl.qkv is not None:
+        # the fp64 front of only the sampled sequences
+        qkv64 = _front_for(wl, sorted({s for s, _ in lanes}))
+    ref = oracle_lanes(wl, lanes, qkv64=qkv64)
+    eo, es = lane_errors(wl, o, hT, ref)
+    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+    T = wl.n_tokens
+    assert torch.isfinite(o[:T]).all()
+
+
+def _front_for(wl, seqs):
+    cu = wl.cu_seqlens
+    T = wl.t_max
+    q = np.zeros((T, wl.H, 128)); k = np.zeros((T, wl.H, 128)); v = np.zeros((T, wl.Hv, 128))
+    w64 = wl.f64("conv_w")
+    for s in seqs:
+        a, e = int(cu[s]), int(cu[s + 1])
+        x = wl.qkv[a:e].to(torch.float64).numpy()
+        qs, ks, vs = recurrent.gdn_front(x, w64, np.array([0, e - a], np.int32), wl.H, wl.Hv,
+                                         128, 128)
+        q[a:e], k[a:e], v[a:e] = qs, ks, vs
+    return q, k, v
