@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked gated-delta-rule prefill forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: device chunk-index table -> intra-chunk stage ->
+inter-chunk stage (plus the conv/SiLU/L2 front for workloads that have one),
+each launched through the C ABI on torch's current stream. W untimed warm-up
+steps, then exactly K timed steps bracketed by device synchronisation. HIP
+events recorded on the same stream between the launches give each kernel's
+average duration over the timed region; the dominant kernel's algorithmic
+bytes per launch divided by that duration is the roofline figure.
+
+Prints ONE JSON line. Default workload: single sequence, T = 4096, H = 16,
+Hv = 32, D = 128, bf16 q/k/v (the configuration the metric is quoted on).
+The CPU baseline is the fp64 oracle timed on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN chunk-prefill tokens/s at 1 GPU; % MFMA peak (intra), % HBM BW (inter)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+SOLVE_FLOP = 83328           # 64x64 unit-lower inverse: 41,664 multiply-adds
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def algorithmic_work(wl, nt, qkv_bytes):
+    """Bytes and flops each stage must move / perform (counted once; partial
+    chunks counted as whole 64-token chunks for flops)."""
+    T, H, Hv, D = wl.n_tokens, wl.H, wl.Hv, 128
+    HG = Hv // H
+    n_state = len(wl.cu_seqlens) - 1
+    stage1_bytes = T * (H * D * qkv_bytes + Hv * D * qkv_bytes + Hv * 4 + Hv * 4
+                        + Hv * D * 2 + Hv * D * 4)
+    stage2_bytes = T * (2 * H * D * qkv_bytes + Hv * D * 2 + Hv * D * 4 + Hv * 4 + Hv * D * 4)
+    stage2_bytes += n_state * Hv * D * D * 4 * (2 if wl.h0 is not None else 1)
+    stage1_flop = nt * H * (2 * 64 * 64 * D + HG * (2 * 2 * 64 * 64 * D + SOLVE_FLOP))
+    stage2_flop = nt * Hv * (3 * 2 * 64 * D * D + 2 * 2 * 64 * 64 * D)
+    front_bytes = 0
+    if wl.qkv is not None:
+        C = (2 * H + Hv) * D
+        front_bytes = T * C * 2 + T * C * 4
+    return dict(intra=(stage1_bytes, stage1_flop), inter=(stage2_bytes, stage2_flop),
+                front=(front_bytes, 0), index=(0, 0))
+
+
+def kernel_source_digest(name):
+    csrc = os.path.join(ROOT, "chunked_gated_delta_rule_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (name + ".hip", "gdn_common.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel, workload_name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current source of that kernel; else None."""
+    try:
+        with open(COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel, {}).get(workload_name)
+    if not ent or ent.get("source_digest") != kernel_source_digest(kernel):
+        return None
+    return ent.get("traffic_bytes")
+
+
+def cpu_baseline(wl, max_seconds=20.0):
+    """The fp64 oracle on this host's cores: whole workload if it fits the
+    budget, else the first key-head groups' lanes, scaled to tokens/s."""
+    from oracle import recurrent
+
+    threads = recurrent.threads()
+    q, k, v = wl.f64("q"), wl.f64("k"), wl.f64("v")
+    g, b, h0 = wl.f64("g"), wl.f64("beta"), wl.f64("h0")
+    HG = wl.Hv // wl.H
+
+    def run(n_groups):  # the first n_groups key heads and their value heads
+        hv_hi = n_groups * HG
+        t0 = time.perf_counter()
+        recurrent.gdn_recurrent(q[:, :n_groups], k[:, :n_groups], v[:, :hv_hi], g[:, :hv_hi],
+                                b[:, :hv_hi], wl.cu_seqlens,
+                                h0=None if h0 is None else h0[:, :hv_hi])
+        return time.perf_counter() - t0
+
+    lane_s = run(1)  # HG lanes side by side: about one lane's time
+    groups_per_round = max(1, threads // HG)
+    fit = int(max_seconds / 3 / max(lane_s, 1e-3)) * groups_per_round
+    n_groups = max(1, min(wl.H, fit))
+    times = [run(n_groups) for _ in range(3)]
+    med = statistics.median(times)
+    lanes = n_groups * HG
+    full = med * (wl.Hv / lanes)
+    sample = (f"{'all' if lanes == wl.Hv else lanes} of {wl.Hv} value-head lanes x "
+              f"{wl.n_tokens} tokens, median of 3 runs ({med:.2f} s each)"
+              + ("" if lanes == wl.Hv else ", scaled to all lanes"))
+    return {"value": wl.n_tokens / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, help="named workload 0..4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import chunked_gated_delta_rule_amd as gdn
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = "cuda:0"
+    wl = workloads.make(args.workload)
+    d = {n: (getattr(wl, n).to(dev).contiguous() if getattr(wl, n) is not None else None)
+         for n in ("q", "k", "v", "g", "beta", "h0", "qkv", "conv_w")}
+    cu = torch.from_numpy(wl.cu_seqlens).to(dev)
+    has_front = wl.qkv is not None
+    qkv_dtype = torch.float32 if has_front else wl.qkv_dtype
+    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype)
+    nt = gdn.gdn_nt_max(wl.t_max, wl.n_max)
+    table = torch.empty((nt, 2), dtype=torch.int32, device=dev)
+    w = torch.empty((wl.Hv, wl.t_max, 128), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((wl.Hv, wl.t_max, 128), dtype=torch.float32, device=dev)
+    o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
+    hT = torch.empty((wl.n_max, wl.Hv, 128, 128), dtype=torch.float32, device=dev)
+    if has_front:
+        q = torch.empty((wl.t_max, wl.H, 128), dtype=torch.float32, device=dev)
+        k = torch.empty_like(q)
+        v = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
+    else:
+        q, k, v = d["q"], d["k"], d["v"]
+
+    stages = (["front"] if has_front else []) + ["index", "intra", "inter"]
+
+    def step(evs=None):
+        i = 0
+        if evs is not None:
+            evs[0].record()
+        if has_front:
+            gdn.gdn_front_conv_silu_l2(cfg, d["qkv"], d["conv_w"], wl.d_conv, cu, q, k, v)
+            i += 1
+            if evs is not None:
+                evs[i].record()
+        gdn.gdn_build_chunk_indices(cfg, cu, table)
+        i += 1
+        if evs is not None:
+            evs[i].record()
+        gdn.gdn_chunk_fwd_intra(cfg, k, v, d["g"], d["beta"], cu, table, w, u)
+        i += 1
+        if evs is not None:
+            evs[i].record()
+        gdn.gdn_chunk_fwd_inter(cfg, q, k, w, u, d["g"], d["h0"], cu, o, hT)
+        i += 1
+        if evs is not None:
+            evs[i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_stage_ms = {name: statistics.fmean(ev[i].elapsed_time(ev[i + 1]) for ev in events)
+                    for i, name in enumerate(stages)}
+    chunks = int(sum(-(-int(x) // 64) for x in np.diff(wl.cu_seqlens)))
+    work = algorithmic_work(wl, chunks, 4 if qkv_dtype == torch.float32 else 2)
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = wl.n_tokens
+    detail = {}
+    for name in stages:
+        t_s = per_stage_ms[name] * 1e-3
+        b, f = work[name]
+        detail[name] = {"us": round(per_stage_ms[name] * 1e3, 2),
+                        "alg_bytes": b, "alg_flop": f,
+                        "hbm_frac": round(b / t_s / (HBM_PEAK_GBS * 1e9), 4) if b else None,
+                        "mfma_frac": round(f / t_s / (BF16_PEAK_TFLOPS * 1e12), 4) if f else None}
+    dom = max(("intra", "inter"), key=lambda n: per_stage_ms[n])
+    b_dom = work[dom][0]
+    t_dom = per_stage_ms[dom] * 1e-3
+    ach = b_dom / t_dom / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(dom, wl.name)}
+
+    cpu = None
+    if not args.no_cpu_baseline and not has_front:
+        cpu = cpu_baseline(wl)
+
+    line = {
+        "metric": METRIC,
+        "value": round(args.steps * tokens / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if qkv_dtype == torch.bfloat16 else "f32-split-bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": tokens, "sequences": wl.n_seqs, "H": wl.H,
+                   "Hv": wl.Hv, "Dk": 128, "Dv": 128, "chunk": 64,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,9 +37,13 @@
  * bias) and the AMX page, section 7 (1 / sqrt(sum of squares + eps)).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int gdn_oracle_threads(void) { return omp_get_max_threads(); }
 
 /* Token recurrence over every (sequence, value head) lane. h0 may be NULL
  * (zero initial state); hT may be NULL. Lanes are independent, so they run in

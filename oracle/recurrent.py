@@ -44,8 +44,15 @@ def _load():
     lib.gdn_oracle_front.argtypes = [dp, dp, i32, ip, i32, i32, i32, i32, i32,
                                      ctypes.c_double, dp]
     lib.gdn_oracle_front.restype = None
+    lib.gdn_oracle_threads.argtypes = []
+    lib.gdn_oracle_threads.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's lane loop runs on."""
+    return int(_load().gdn_oracle_threads())
 
 
 def _dptr(a):

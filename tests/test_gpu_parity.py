@@ -211,7 +211,9 @@ def test_external_table_and_in_place_state():
     gdn.gdn_build_chunk_indices(cfg, d["cu"], table)
     state = d["h0"].clone()
     o2, s2, _ = run_forward(wl, d, h0=state, hT=state, chunk_indices=table)
-    assert torch.equal(o1, o2) and torch.equal(s1, s2) and s2.data_ptr() == state.data_ptr()
+    T = wl.n_tokens
+    assert torch.equal(o1[:T], o2[:T]) and torch.equal(s1, s2)
+    assert s2.data_ptr() == state.data_ptr()
 
 
 def test_zero_length_sequences_keep_state():
