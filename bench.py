@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1, help="named workload 0..4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -132,6 +134,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     dev = "cuda:0"
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": args.steps}))
+        return
     wl = workloads.make(args.workload)
     d = {n: (getattr(wl, n).to(dev).contiguous() if getattr(wl, n) is not None else None)
          for n in ("q", "k", "v", "g", "beta", "h0", "qkv", "conv_w")}

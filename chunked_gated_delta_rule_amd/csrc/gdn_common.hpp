@@ -72,6 +72,53 @@ __device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
+// Raw buffer access: a descriptor over [base, base + bytes) whose out-of-range
+// reads return zero, which masks the rows past a sequence's end without
+// branches (gfx9 buffer resource, word 3 = 0x00020000).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 2^x on the hardware transcendental unit (v_exp_f32); used with exponents
+// that are differences of log2-scaled cumulative gates, always <= 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 hi pair and packed bf16 lo pair (x = hi + lo), using
+// one packed conversion per pair.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float r0 = x0 - __uint_as_float(hi << 16);
+  const float r1 = x1 - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+}
+
+// Split four fp32 values into hi/lo bf16, packed as {01, 23} pairs.
+__device__ __forceinline__ void split_pack4(const float (&x)[4], u32x2 &hi, u32x2 &lo) {
+  uint32_t h0, l0, h1, l1;
+  split2(x[0], x[1], h0, l0);
+  split2(x[2], x[3], h1, l1);
+  hi = u32x2{h0, h1};
+  lo = u32x2{l0, l1};
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 #pragma unroll
