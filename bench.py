@@ -152,8 +152,7 @@ def main():
     cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype)
     nt = gdn.gdn_nt_max(wl.t_max, wl.n_max)
     table = torch.empty((nt, 2), dtype=torch.int32, device=dev)
-    w = torch.empty((wl.Hv, wl.t_max, 128), dtype=torch.bfloat16, device=dev)
-    u = torch.empty((wl.Hv, wl.t_max, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=dev)
     o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
     hT = torch.empty((wl.n_max, wl.Hv, 128, 128), dtype=torch.float32, device=dev)
     if has_front:
@@ -178,11 +177,11 @@ def main():
         i += 1
         if evs is not None:
             evs[i].record()
-        gdn.gdn_chunk_fwd_intra(cfg, k, v, d["g"], d["beta"], cu, table, w, u)
+        gdn.gdn_chunk_fwd_intra(cfg, q, k, v, d["g"], d["beta"], cu, table, ws)
         i += 1
         if evs is not None:
             evs[i].record()
-        gdn.gdn_chunk_fwd_inter(cfg, q, k, w, u, d["g"], d["h0"], cu, o, hT)
+        gdn.gdn_chunk_fwd_inter(cfg, d["h0"], cu, ws, o, hT)
         i += 1
         if evs is not None:
             evs[i].record()

@@ -26,16 +26,16 @@ __all__ = [
     "GDNError", "gdn_config", "GDN_BF16", "GDN_F32", "load_library", "library_path",
     "gdn_nt_max", "gdn_workspace_size", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
     "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
-    "make_config", "chunk_gated_delta_rule", "EXPORTED_SYMBOLS",
+    "gdn_workspace_layout", "make_config", "chunk_gated_delta_rule", "EXPORTED_SYMBOLS",
 ]
 
 GDN_BF16 = 0
 GDN_F32 = 1
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
            3: "GDN_ERR_CAPACITY", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
-EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_size", "gdn_build_chunk_indices",
-                    "gdn_front_conv_silu_l2", "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter",
-                    "gdn_chunk_fwd", "gdn_status_str")
+EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_layout", "gdn_workspace_size",
+                    "gdn_build_chunk_indices", "gdn_front_conv_silu_l2", "gdn_chunk_fwd_intra",
+                    "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libgdn.so")
@@ -46,6 +46,11 @@ class gdn_config(ctypes.Structure):
                 ("hv", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int), ("o_dtype", ctypes.c_int),
                 ("scale", ctypes.c_float)]
+
+
+class gdn_workspace_layout_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("w16", "q16", "kimg", "uimg", "pimg", "gimg", "table", "total")]
 
 
 class GDNError(RuntimeError):
@@ -71,12 +76,13 @@ def load_library():
     lib.gdn_nt_max.argtypes = [i32, i32, i32]
     lib.gdn_nt_max.restype = ctypes.c_int64
     lib.gdn_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
+    lib.gdn_workspace_layout.argtypes = [cfgp, ctypes.POINTER(gdn_workspace_layout_t)]
     lib.gdn_build_chunk_indices.argtypes = [cfgp, vp, vp, vp]
     lib.gdn_front_conv_silu_l2.argtypes = [cfgp, vp, vp, i32, vp, vp, vp, vp, vp]
-    lib.gdn_chunk_fwd_intra.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.gdn_chunk_fwd_inter.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_intra.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_chunk_fwd_inter.argtypes = [cfgp, vp, vp, vp, sz, vp, vp, vp]
     lib.gdn_chunk_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for name in ("gdn_workspace_size", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
+    for name in ("gdn_workspace_size", "gdn_workspace_layout", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
                  "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gdn_status_str.argtypes = [ctypes.c_int]
@@ -148,24 +154,39 @@ def gdn_front_conv_silu_l2(cfg, qkv, conv_w, d_conv, cu_seqlens, q, k, v, stream
            "gdn_front_conv_silu_l2")
 
 
-def gdn_chunk_fwd_intra(cfg, k, v, g, beta, cu_seqlens, chunk_indices, w, u, stream=None):
-    _check(load_library().gdn_chunk_fwd_intra(ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(g),
-                                              _ptr(beta), _ptr(cu_seqlens), _ptr(chunk_indices),
-                                              _ptr(w), _ptr(u), _stream(stream)),
+def gdn_workspace_layout(cfg: gdn_config) -> dict:
+    """Byte offsets of the intermediates inside a workspace (and its total size)."""
+    out = gdn_workspace_layout_t()
+    _check(load_library().gdn_workspace_layout(ctypes.byref(cfg), ctypes.byref(out)),
+           "gdn_workspace_layout")
+    return {name: int(getattr(out, name)) for name, _ in gdn_workspace_layout_t._fields_}
+
+
+def _ws_bytes(workspace, ws_bytes):
+    if ws_bytes is not None:
+        return int(ws_bytes)
+    return workspace.numel() * workspace.element_size()
+
+
+def gdn_chunk_fwd_intra(cfg, q, k, v, g, beta, cu_seqlens, chunk_indices, workspace,
+                        ws_bytes=None, stream=None):
+    _check(load_library().gdn_chunk_fwd_intra(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                              _ptr(chunk_indices), _ptr(workspace),
+                                              _ws_bytes(workspace, ws_bytes), _stream(stream)),
            "gdn_chunk_fwd_intra")
 
 
-def gdn_chunk_fwd_inter(cfg, q, k, w, u, g, h0, cu_seqlens, o, hT, stream=None):
-    _check(load_library().gdn_chunk_fwd_inter(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(w),
-                                              _ptr(u), _ptr(g), _ptr(h0), _ptr(cu_seqlens),
+def gdn_chunk_fwd_inter(cfg, h0, cu_seqlens, workspace, o, hT, ws_bytes=None, stream=None):
+    _check(load_library().gdn_chunk_fwd_inter(ctypes.byref(cfg), _ptr(h0), _ptr(cu_seqlens),
+                                              _ptr(workspace), _ws_bytes(workspace, ws_bytes),
                                               _ptr(o), _ptr(hT), _stream(stream)),
            "gdn_chunk_fwd_inter")
 
 
 def gdn_chunk_fwd(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT, workspace,
                   ws_bytes=None, stream=None):
-    if ws_bytes is None:
-        ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace, ws_bytes)
     _check(load_library().gdn_chunk_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                         _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
                                         _ptr(chunk_indices), _ptr(o), _ptr(hT), _ptr(workspace),

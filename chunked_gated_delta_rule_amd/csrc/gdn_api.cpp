@@ -43,9 +43,42 @@ int32_t nt_max_of(const gdn_config *cfg) {
                               cfg->n_max - 1);
 }
 
-size_t w_bytes(const gdn_config *cfg) { return static_cast<size_t>(cfg->hv) * cfg->t_max * kD * 2; }
-size_t u_bytes(const gdn_config *cfg) { return static_cast<size_t>(cfg->hv) * cfg->t_max * kD * 4; }
-size_t table_bytes(const gdn_config *cfg) { return static_cast<size_t>(nt_max_of(cfg)) * 2 * 4; }
+gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
+  const size_t t = static_cast<size_t>(cfg->t_max), nt = static_cast<size_t>(nt_max_of(cfg));
+  const size_t h = static_cast<size_t>(cfg->h), hv = static_cast<size_t>(cfg->hv);
+  const size_t nk = cfg->qkv_dtype == GDN_F32 ? 32 : 16;
+  gdn_workspace_layout_t l;
+  size_t at = 0;
+  auto take = [&](size_t bytes) { const size_t here = at; at += align_up(bytes); return here; };
+  l.w16 = take(hv * t * kD * 2);
+  l.q16 = take(t * h * kD * 2);
+  l.kimg = take(h * nt * nk * 1024);
+  l.uimg = take(hv * nt * kD * kChunk * 4);
+  l.pimg = take(hv * nt * 12 * 1024);
+  l.gimg = take(hv * nt * 192 * 4);
+  l.table = take(nt * 2 * 4);
+  l.total = at;
+  return l;
+}
+
+gdn::StageBuffers stage_buffers(const gdn_workspace_layout_t &l, const void *workspace) {
+  char *ws = static_cast<char *>(const_cast<void *>(workspace));
+  gdn::StageBuffers b;
+  b.w16 = reinterpret_cast<_Float16 *>(ws + l.w16);
+  b.q16 = reinterpret_cast<_Float16 *>(ws + l.q16);
+  b.kimg = reinterpret_cast<__bf16 *>(ws + l.kimg);
+  b.uimg = reinterpret_cast<float *>(ws + l.uimg);
+  b.pimg = reinterpret_cast<__bf16 *>(ws + l.pimg);
+  b.gimg = reinterpret_cast<float *>(ws + l.gimg);
+  return b;
+}
+
+// Workspace present, large enough and 256-byte aligned.
+gdn_status check_workspace(const gdn_workspace_layout_t &l, const void *ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < l.total) return GDN_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return GDN_ERR_WORKSPACE;
+  return GDN_OK;
+}
 
 float scale_of(const gdn_config *cfg) {
   return cfg->scale > 0.f ? cfg->scale : 1.0f / std::sqrt(static_cast<float>(cfg->dk));
@@ -64,11 +97,19 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk) {
   return (static_cast<int64_t>(t_max) + chunk - 1) / chunk + n_max - 1;
 }
 
+gdn_status gdn_workspace_layout(const gdn_config *cfg, gdn_workspace_layout_t *layout) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!layout) return GDN_ERR_INVALID_ARG;
+  *layout = layout_of(cfg);
+  return GDN_OK;
+}
+
 gdn_status gdn_workspace_size(const gdn_config *cfg, size_t *bytes) {
   const gdn_status st = check_config(cfg);
   if (st != GDN_OK) return st;
   if (!bytes) return GDN_ERR_INVALID_ARG;
-  *bytes = align_up(w_bytes(cfg)) + align_up(u_bytes(cfg)) + align_up(table_bytes(cfg));
+  *bytes = layout_of(cfg).total;
   return GDN_OK;
 }
 
@@ -97,71 +138,74 @@ gdn_status gdn_front_conv_silu_l2(const gdn_config *cfg, const void *qkv, const 
                                     cfg->h, cfg->hv, q, k, v, as_stream(stream)));
 }
 
-gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *k, const void *v,
+gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *q, const void *k, const void *v,
                                const float *g, const float *beta, const int32_t *cu_seqlens,
-                               const int32_t *chunk_indices, void *w, float *u, void *stream) {
+                               const int32_t *chunk_indices, void *workspace, size_t ws_bytes,
+                               void *stream) {
   const gdn_status st = check_config(cfg);
   if (st != GDN_OK) return st;
-  if (!k || !v || !g || !beta || !cu_seqlens || !chunk_indices || !w || !u)
+  if (!q || !k || !v || !g || !beta || !cu_seqlens || !chunk_indices) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(chunk_indices) ||
+      (reinterpret_cast<uintptr_t>(g) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return GDN_ERR_INVALID_ARG;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
-      !aligned16(chunk_indices) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
-      (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
-    return GDN_ERR_INVALID_ARG;
+  const gdn_workspace_layout_t l = layout_of(cfg);
+  const gdn_status ws = check_workspace(l, workspace, ws_bytes);
+  if (ws != GDN_OK) return ws;
   if (cfg->t_max == 0) return GDN_OK;
-  return from_hip(gdn::launch_intra(cfg->qkv_dtype == GDN_F32, k, v, g, beta, cu_seqlens,
+  return from_hip(gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
                                     chunk_indices, nt_max_of(cfg), cfg->h, cfg->hv, cfg->t_max,
-                                    w, u, as_stream(stream)));
+                                    scale_of(cfg), stage_buffers(l, workspace), as_stream(stream)));
 }
 
-gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const void *q, const void *k,
-                               const void *w, const float *u, const float *g, const float *h0,
-                               const int32_t *cu_seqlens, void *o, float *hT, void *stream) {
+gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int32_t *cu_seqlens,
+                               const void *workspace, size_t ws_bytes, void *o, float *hT,
+                               void *stream) {
   const gdn_status st = check_config(cfg);
   if (st != GDN_OK) return st;
-  if (!q || !k || !w || !u || !g || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(u) || !aligned16(o) ||
-      (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) ||
-      (reinterpret_cast<uintptr_t>(g) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+  if (!cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(o) || (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return GDN_ERR_INVALID_ARG;
-  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, q, k, w, u, g, h0, cu_seqlens,
-                                    cfg->n_max, cfg->h, cfg->hv, cfg->t_max, scale_of(cfg),
-                                    static_cast<float *>(o), hT, as_stream(stream)));
+  const gdn_workspace_layout_t l = layout_of(cfg);
+  const gdn_status ws = check_workspace(l, workspace, ws_bytes);
+  if (ws != GDN_OK) return ws;
+  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, stage_buffers(l, workspace), h0,
+                                    cu_seqlens, cfg->n_max, cfg->h, cfg->hv, cfg->t_max,
+                                    nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream)));
 }
 
 gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,
                          const float *g, const float *beta, const float *h0,
                          const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
                          float *hT, void *workspace, size_t ws_bytes, void *stream) {
-  size_t need = 0;
-  const gdn_status st = gdn_workspace_size(cfg, &need);
+  const gdn_status st = check_config(cfg);
   if (st != GDN_OK) return st;
   if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
-  if (!workspace || ws_bytes < need) return GDN_ERR_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return GDN_ERR_WORKSPACE;
+  const gdn_workspace_layout_t l = layout_of(cfg);
+  const gdn_status ws = check_workspace(l, workspace, ws_bytes);
+  if (ws != GDN_OK) return ws;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) ||
       (chunk_indices && !aligned16(chunk_indices)) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
       (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return GDN_ERR_INVALID_ARG;
-  char *ws = static_cast<char *>(workspace);
-  void *w = ws;
-  float *u = reinterpret_cast<float *>(ws + align_up(w_bytes(cfg)));
-  int32_t *table = reinterpret_cast<int32_t *>(ws + align_up(w_bytes(cfg)) + align_up(u_bytes(cfg)));
   hipStream_t s = as_stream(stream);
   if (!chunk_indices) {
+    int32_t *table = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + l.table);
     const hipError_t e = gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), table, s);
     if (e != hipSuccess) return GDN_ERR_HIP;
     chunk_indices = table;
   }
+  const gdn::StageBuffers b = stage_buffers(l, workspace);
   if (cfg->t_max > 0) {
-    const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, k, v, g, beta, cu_seqlens,
+    const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
                                            chunk_indices, nt_max_of(cfg), cfg->h, cfg->hv,
-                                           cfg->t_max, w, u, s);
+                                           cfg->t_max, scale_of(cfg), b, s);
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
-  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, q, k, w, u, g, h0, cu_seqlens,
-                                    cfg->n_max, cfg->h, cfg->hv, cfg->t_max, scale_of(cfg),
+  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, b, h0, cu_seqlens, cfg->n_max,
+                                    cfg->h, cfg->hv, cfg->t_max, nt_max_of(cfg),
                                     static_cast<float *>(o), hT, s));
 }
 

@@ -32,7 +32,23 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// fp16 operands: the state S enters w S and q S as a single fp16 term (11
+// significant bits; its products carry the fp32 state to well below the
+// method's tolerance), with w stored in fp16 and q converted exactly.
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Two fp32 -> packed fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  typedef float f32x2_ __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_{a, b}, f16x2));
+}
 
 // Round to nearest even (hardware conversion on gfx950).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
@@ -110,6 +126,15 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
 
+// Split eight fp32 values into packed bf16 hi and lo words (x = hi + lo).
+__device__ __forceinline__ void split8_words(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], l[i]);
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // Split four fp32 values into hi/lo bf16, packed as {01, 23} pairs.
 __device__ __forceinline__ void split_pack4(const float (&x)[4], u32x2 &hi, u32x2 &lo) {
   uint32_t h0, l0, h1, l1;
@@ -118,6 +143,16 @@ __device__ __forceinline__ void split_pack4(const float (&x)[4], u32x2 &hi, u32x
   hi = u32x2{h0, h1};
   lo = u32x2{l0, l1};
 }
+
+// Column order inside each 32-column block of the fp16 w and q copies: the
+// four-column group m (columns 4m .. 4m + 3) starts at position perm4(m), so
+// MFMA lane group g reads columns {4g .. 4g + 3, 16 + 4g .. 16 + 4g + 3} as one
+// 16-byte word -- the rows a 16x16 accumulator pair hands to a lane.
+__host__ __device__ constexpr int perm4(int m) { return m < 4 ? 8 * m : 8 * (m - 4) + 4; }
+
+// Floats per (value head, chunk) in the gate block: e^{gamma_last - gamma_t}
+// [64], scale * e^{gamma_t} [64], e^{gamma_last} and zero padding [64].
+constexpr int kGateStride = 192;
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {

@@ -8,6 +8,17 @@
 
 namespace gdn {
 
+// Intermediates written by the intra stage and read by the inter stage (all
+// device memory inside the caller's workspace; layouts in intra.hip).
+struct StageBuffers {
+  _Float16 *w16;  // [hv, t_max, 128]
+  _Float16 *q16;  // [t_max, h, 128]
+  __bf16 *kimg;   // [h, nt_max, 16 or 32 fragments, 64 lanes, 8]
+  float *uimg;    // [hv, nt_max, 8, 4, 64 lanes, 4]
+  __bf16 *pimg;   // [hv, nt_max, 6 pairs, 2 terms, 64 lanes, 8]
+  float *gimg;    // [hv, nt_max, 192]
+};
+
 hipError_t launch_chunk_index(const int32_t *cu_seqlens, int32_t n_max, int32_t nt_max,
                               int32_t *table, hipStream_t stream);
 
@@ -15,14 +26,13 @@ hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t t_max, int32_t h,
                         int32_t hv, float *q, float *k, float *v, hipStream_t stream);
 
-hipError_t launch_intra(bool f32_in, const void *k, const void *v, const float *g,
+hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const int32_t *cu_seqlens, const int32_t *table,
-                        int32_t nt_max, int32_t h, int32_t hv, int32_t t_max, void *w, float *u,
-                        hipStream_t stream);
+                        int32_t nt_max, int32_t h, int32_t hv, int32_t t_max, float scale,
+                        const StageBuffers &out, hipStream_t stream);
 
-hipError_t launch_inter(bool f32_in, const void *q, const void *k, const void *w, const float *u,
-                        const float *g, const float *h0, const int32_t *cu_seqlens,
-                        int32_t n_max, int32_t h, int32_t hv, int32_t t_max, float scale,
-                        float *o, float *hT, hipStream_t stream);
+hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
+                        const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
+                        int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream);
 
 }  // namespace gdn

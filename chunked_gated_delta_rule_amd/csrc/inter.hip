@@ -7,39 +7,38 @@
 //
 //   v'  = u - w S
 //   o   = scale * ( diag(e^gamma) q S + tril(q k^T * Gamma) v' )   (diagonal kept)
-//   S   = e^{gamma_last} S + (diag(e^{gamma_last - gamma}) k)^T v'
+//   S   = e^{gamma_last} S + k^T diag(e^{gamma_last - gamma}) v'
 //
 // The value columns of S are independent, so the state is blocked over Dv
 // (Alloy page, "How do you parallelize a recurrence for prefill?": the state
-// tile is blocked along the value dimension to fit on chip). One 256-thread
-// work-group owns a 128 x 16 column block of S for one (sequence, value head)
-// for the whole sequence; wave wv owns token rows 16 wv .. 16 wv + 15 of the
-// chunk and state rows 32 wv .. 32 wv + 31.
+// tile is blocked along the value dimension to fit on chip). Here one wave64
+// owns a 128 x 16 column slice of S for the whole sequence and keeps it in
+// registers, as eight 16 x 16 MFMA accumulators. Every product of the chunk
+// step is arranged so that its operands come either from those accumulators
+// directly or from fragments the intra stage stored in MFMA order:
 //
-// Per chunk there are two phases separated by a barrier, and a barrier ends
-// the chunk:
-//   phase 1: X = w S and Y = q S (w, q fragments straight from HBM/L2 into
-//            registers, S as hi/lo bf16 from LDS); this wave's row block of
-//            P = tril(q k^T * Gamma), kept in registers; v' = u - X and the
-//            decayed v' go to LDS as hi/lo bf16.
-//   phase 2: o = scale (e^gamma Y + P v') and S = e^{gamma_last} S + k^T v'_dec
-//            (k transposed from LDS); S goes back to LDS as hi/lo bf16; the
-//            next chunk's k tile and gates are staged.
-// The next chunk's inputs are loaded at the start of phase 1 (buffer loads;
-// rows past the sequence end read as zero) so their latency hides behind a
-// whole chunk of work. Every product runs on v_mfma_f32_16x16x32_bf16; the
-// fp32 operands S, P, v' and the decayed v' enter as hi + lo bf16 pairs.
+//   v'      = u + w (-S)          A = w fragment, B = -S (fp16)      C = v' tiles
+//   o^T     = -(-S)^T q^T         A = -S (fp16),  B = q16 fragment   C = o^T tiles
+//   o^T    += v'^T P^T            A = v' (hi+lo), B = P fragment (hi+lo)
+//   S       = e^{gamma_last} S + K^T v'_dec    A = K^T fragment, B = v'_dec (hi+lo)
 //
-// P stays in registers: the MFMA result layout of a P^T block gives each lane
-// one row t and four consecutive columns j, so two P^T blocks form the lane's
-// eight contraction slots of a P v' product. v' is stored with the matching
-// permutation of j, so its fragment is still one 16-byte LDS read.
+// A 16x16 accumulator gives lane (g, c) = (l >> 4, l & 15) rows 4g .. 4g + 3 of
+// column c; two accumulators stacked along the contraction give a lane exactly
+// the eight contraction values of an A (row c) or B (column c) fragment, with
+// the contraction order {4g + i, 16 + 4g + i}. The intra stage writes w, q16,
+// K^T and P in that order, so no value ever moves between lanes or through
+// LDS inside the recurrence, and the chunk step itself has no barrier.
 //
-// Work-group numbering is XCD-aware: all value-column blocks of all value
-// heads that share a key head (16 work-groups at Hv = 2 H) get the same
-// blockIdx modulo 8, so they run on one XCD and share q, k, w through its L2.
-// Gates enter the exponentials as log2-scaled cumulative sums, and every
-// exponent is a difference that is <= 0 (masked before the exponential).
+// Every operand fragment is one coalesced 16-byte-per-lane load straight into
+// registers (rows past the sequence end read as zero); nothing goes through
+// LDS. Each fragment array is refilled with the next chunk's fragments as soon
+// as the current chunk's product has consumed it, so every load has about one
+// chunk step of latency to land, and the wave never blocks on issue. A
+// work-group is a single wave: waves never wait for each other.
+//
+// Work-group numbering is XCD-aware: all work-groups of the value heads that
+// share a key head get the same blockIdx modulo 8, so they run on one XCD and
+// share q16 and K^T through its L2.
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -47,405 +46,280 @@ namespace gdn {
 
 namespace {
 
-constexpr int kBV = 16;          // value columns per work-group
-constexpr int kNVT = kD / kBV;   // value-column blocks per head
-constexpr int kLdRow = kD + 8;   // k row-major [64][136] bf16
-constexpr int kLdCol = kC + 8;   // k transposed [128][72] bf16, 16-byte groups swizzled
-constexpr int kLdS = kD + 8;     // S^T hi/lo [16][136]
-constexpr int kLdV = kC + 8;     // v'^T hi/lo [16][72]
 constexpr int kXcds = 8;
+constexpr int kSlices = kD / 16;  // 16-column value slices per head
 
+// Fragments of one chunk (16 bytes per lane each):
+//   w    (token tile R, d block p)   [4 R + p]   A of w S
+//   q16  (token tile R, d block p)   [4 R + p]   B of S^T q^T
+//   P    pair pi, term t (hi, lo)    [2 pi + t]  B of v'^T P^T
+//   K^T  (d tile tau, token block q) [2 tau + q] (+16: lo term)  A of K^T v'
 template <bool kF32In>
-struct InterSmem {
-  static constexpr int kT = kF32In ? 2 : 1;
-  static constexpr int kKr = kT * 64 * kLdRow * 2;
-  static constexpr int kKc = kT * 128 * kLdCol * 2;
-  static constexpr int kS = 2 * kBV * kLdS * 2;
-  static constexpr int kDl = 2 * kBV * kLdV * 2;
-  static constexpr int kBytes = kKr + kKc + kS + 2 * kDl + 2 * 64 * 4;
-  static_assert(kBytes <= 160 * 1024, "LDS budget");
+struct Chunk {
+  static constexpr int kNK = kF32In ? 32 : 16;
+  f16x8 w[16];
+  f16x8 q[16];
+  bf16x8 p[12];
+  bf16x8 k[kNK];
+  f32x4 u[4];     // u tile R: rows 16 R + 4 g + i, value column v0 + c
+  f32x4 dec[4];   // e^{gamma_last - gamma} of those rows
+  float exs[4];   // scale * e^{gamma_r}, r = 16 R + c
+  float el;       // e^{gamma_last}
 };
 
-// Element (d, j) of the transposed k tile. The eight 16-byte groups of a row
-// are XOR-swizzled by d / 16 so that the transposing stores (one d per lane,
-// four consecutive j) and the fragment reads (16 consecutive d, eight j) are
-// both free of bank conflicts.
-__device__ __forceinline__ int kcol_at(int d, int j) {
-  return d * kLdCol + ((((j >> 3) ^ (d >> 4)) & 7) << 3) + (j & 7);
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
-__device__ __forceinline__ uint16_t half_of(const u32x4 &w, int i) {
-  return static_cast<uint16_t>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+// Two stacked accumulators -> bf16 hi + lo fragments.
+__device__ __forceinline__ void split8(const f32x4 &a, const f32x4 &b, bf16x8 &hi, bf16x8 &lo) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 h, l;
+  split8_words(x, h, l);
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 
-// Eight fp32 (two 16-byte words) -> eight bf16 hi and eight bf16 lo.
-__device__ __forceinline__ void split8(const u32x4 &a, const u32x4 &b, u32x4 &hi, u32x4 &lo) {
-  uint32_t h[4], l[4];
-  split2(__uint_as_float(a[0]), __uint_as_float(a[1]), h[0], l[0]);
-  split2(__uint_as_float(a[2]), __uint_as_float(a[3]), h[1], l[1]);
-  split2(__uint_as_float(b[0]), __uint_as_float(b[1]), h[2], l[2]);
-  split2(__uint_as_float(b[2]), __uint_as_float(b[3]), h[3], l[3]);
-  hi = u32x4{h[0], h[1], h[2], h[3]};
-  lo = u32x4{l[0], l[1], l[2], l[3]};
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words (same fields as make_rsrc) for the store below.
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int32_t>(a & 0xffffffffu), static_cast<int32_t>((a >> 32) & 0xffffu),
+               static_cast<int32_t>(bytes), 0x00020000};
 }
 
-// One chunk's per-wave MFMA operands, as loaded from memory.
-template <bool kF32In>
-struct ChunkFrags {
-  static constexpr int kN = kF32In ? 8 : 4;
-  u32x4 q[kN];  // q rows 16 wv + (lane & 15); k-step kk in q[kk] (fp32: q[2kk], q[2kk+1])
-  u32x4 w[4];   // w rows 16 wv + (lane & 15), bf16
-  float u[4];   // u rows 16 wv + quad + i, column vcol
-};
+// 16-byte buffer store issued as inline assembly. The compiler then never
+// sees a store among the outstanding vector-memory operations, so its waits
+// for the prefetched fragments stay counts of loads (loads return in order)
+// instead of draining every load at each store. Out-of-range lanes are
+// dropped like any buffer store; the leading s_nop covers a scalar operand
+// written just before.
+__device__ __forceinline__ void store16(const i32x4 &r, uint32_t voff, uint32_t soff, const f32x4 &v) {
+  asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %0, %1, %2, %3 offen"
+               :
+               : "v"(v), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
 
-// This thread's 4 x 8 block of the chunk's k tile, and (wave 0) its gate.
-template <bool kF32In>
-struct ChunkK {
-  static constexpr int kN = kF32In ? 8 : 4;
-  u32x4 v[kN];
-  float g;
-};
+// -S of two stacked accumulators as one fp16 fragment (round to nearest even).
+__device__ __forceinline__ f16x8 neg_f16(const f32x4 &a, const f32x4 &b) {
+  const u32x4 w{pack_f16(-a[0], -a[1]), pack_f16(-a[2], -a[3]), pack_f16(-b[0], -b[1]),
+                pack_f16(-b[2], -b[3])};
+  return __builtin_bit_cast(f16x8, w);
+}
 
 template <bool kF32In>
-__global__ __launch_bounds__(kThreads, 1) void inter_kernel(
-    const void *__restrict__ qin, const void *__restrict__ kin, const __bf16 *__restrict__ win,
-    const float *__restrict__ uin, const float *__restrict__ g, const float *__restrict__ h0,
-    const int32_t *__restrict__ cu, float *__restrict__ o, float *__restrict__ hT, int n_max,
-    int H, int Hv, int t_max, float scale) {
-  using Smem = InterSmem<kF32In>;
-  constexpr int kElt = kF32In ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[Smem::kBytes];
-  unsigned char *p = smem;
-  __bf16 *krow = reinterpret_cast<__bf16 *>(p); p += Smem::kKr;
-  __bf16 *kcol = reinterpret_cast<__bf16 *>(p); p += Smem::kKc;
-  __bf16 *s_hi = reinterpret_cast<__bf16 *>(p);
-  __bf16 *s_lo = s_hi + kBV * kLdS; p += Smem::kS;
-  __bf16 *dl_hi = reinterpret_cast<__bf16 *>(p);
-  __bf16 *dl_lo = dl_hi + kBV * kLdV; p += Smem::kDl;
-  __bf16 *dp_hi = reinterpret_cast<__bf16 *>(p);
-  __bf16 *dp_lo = dp_hi + kBV * kLdV; p += Smem::kDl;
-  float *gam2 = reinterpret_cast<float *>(p);  // [2][64], log2-scaled cumulative gates
+__global__ __launch_bounds__(64) void inter_kernel(StageBuffers in, const float *__restrict__ h0,
+                                                  const int32_t *__restrict__ cu,
+                                                  float *__restrict__ o, float *__restrict__ hT,
+                                                  int n_max, int H, int Hv, int t_max, int nt) {
+  using CK = Chunk<kF32In>;
+  constexpr int kNK = CK::kNK;
 
-  // ---- XCD-aware work-group -> (sequence, value head, column block) -------
+  // ---- XCD-aware work-group -> (sequence, value head, slice) --------------
   const int HG = Hv / H;
-  const int members = HG * kNVT;
+  const int members = HG * kSlices;
   const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int group = (slot / members) * kXcds + xcd;  // (sequence, key head)
-  const int member = slot % members;
+  const int wslot = blockIdx.x / kXcds;
+  const int group = (wslot / members) * kXcds + xcd;  // (sequence, key head)
+  const int member = wslot % members;
   if (group >= n_max * H) return;
   const int s = group / H;
   const int h = group % H;
-  const int hv = h * HG + member / kNVT;
-  const int vt = member % kNVT;
+  const int hv = h * HG + member / kSlices;
+  const int slice = member % kSlices;
+  const int v0 = 16 * slice;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int l16 = lane & 15;
-  const int quad = 4 * (lane >> 4);
-  const int lrow = 4 * (tid >> 4);  // k staging: rows lrow .. lrow + 3
-  const int lcol = 8 * (tid & 15);  //            columns lcol .. lcol + 7
-  const int vcol = kBV * vt + l16;  // this lane's value column in result layouts
+  const int lane = threadIdx.x & 63;
+  const int c16 = lane & 15;
+  const int g4 = 4 * (lane >> 4);
 
   const int bos = cu[s];
   const int eos = cu[s + 1];
-  const int nchunks = (eos - bos + kC - 1) / kC;
-  const uint32_t rs_qk = static_cast<uint32_t>(H) * kD * kElt;  // bytes per q/k token row
-  const uint32_t rs_o = static_cast<uint32_t>(Hv) * kD * 4;     // bytes per o token row
-  float *hT_lane = hT ? hT + (((int64_t)s * Hv + hv) * kD + vcol) * kD : nullptr;
+  const int nc = (eos - bos + kC - 1) / kC;
 
-  // ---- initial state: S[d][v] for d = 32 wv + 16 b + quad + i ---------------
-  f32x4 sacc[2];
+  // lane parts of the buffer offsets (chunk parts go into the descriptors)
+  const uint32_t vo_w = static_cast<uint32_t>(c16 * kD + 2 * g4) * 2;      // w16 rows
+  const uint32_t vo_q = static_cast<uint32_t>(c16 * H * kD + 2 * g4) * 2;  // q16 rows
+  const uint32_t vo_f = static_cast<uint32_t>(lane) * 16;                  // 1 KB blocks
+  const uint32_t vo_o = static_cast<uint32_t>(c16 * Hv * kD + g4) * 4;     // o rows
+  const uint32_t row_q = static_cast<uint32_t>(16 * H * kD * 2);           // 16 q16 rows
+  const uint32_t row_o = static_cast<uint32_t>(16 * Hv * kD * 4);          // 16 o rows
+
+  // descriptors of chunk c (zero-length past the last chunk: loads read 0)
+  struct Rsrc { rsrc_t w, q, p, k, u, g; };
+  auto rsrc_of = [&](int c) __attribute__((always_inline)) {
+    const int t0 = bos + kC * c;
+    const int slot = (t0 >> 6) + s;
+    const bool ok = c < nc;
+    const uint32_t lc = ok ? static_cast<uint32_t>(min(kC, eos - t0)) : 0u;
+    Rsrc r;
+    r.w = make_rsrc(in.w16 + ((int64_t)hv * t_max + t0) * kD, lc * kD * 2);
+    r.q = make_rsrc(in.q16 + ((int64_t)t0 * H + h) * kD, lc * H * kD * 2);
+    r.p = make_rsrc(in.pimg + ((int64_t)hv * nt + slot) * 12 * 512, ok ? 12 * 1024 : 0);
+    r.k = make_rsrc(in.kimg + ((int64_t)h * nt + slot) * kNK * 512, ok ? kNK * 1024 : 0);
+    r.u = make_rsrc(in.uimg + (((int64_t)hv * nt + slot) * kSlices + slice) * 4 * 256, ok ? 4096 : 0);
+    r.g = make_rsrc(in.gimg + ((int64_t)hv * nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
+    return r;
+  };
+  auto load_w = [&](CK &x, const Rsrc &r) __attribute__((always_inline)) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int d = 32 * wv + 16 * b + quad;
-    sacc[b] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + (((int64_t)s * Hv + hv) * kD + vcol) * kD + d)
-                 : zero4();
+    for (int f = 0; f < 16; ++f)
+      x.w[f] = __builtin_bit_cast(f16x8, ld16(r.w, vo_w, (f >> 2) * 16 * kD * 2 + (f & 3) * 64));
+  };
+  auto load_q = [&](CK &x, const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 16; ++f)
+      x.q[f] = __builtin_bit_cast(f16x8, ld16(r.q, vo_q, (f >> 2) * row_q + (f & 3) * 64));
+  };
+  auto load_p = [&](CK &x, const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 12; ++f) x.p[f] = __builtin_bit_cast(bf16x8, ld16(r.p, vo_f, f * 1024));
+  };
+  auto load_k = [&](CK &x, const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < kNK; ++f) x.k[f] = __builtin_bit_cast(bf16x8, ld16(r.k, vo_f, f * 1024));
+  };
+  auto load_gates = [&](CK &x, const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      x.u[R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, R * 1024));
+      x.dec[R] = __builtin_bit_cast(f32x4, ld16(r.g, 4 * g4, R * 64));
+      x.exs[R] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 4 * c16, 256 + R * 64, 0));
+    }
+    x.el = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
+  };
+
+  // ---- state slice: S[tau] holds S[d = 16 tau + 4g + i][v0 + c] ---------------
+  f32x4 S[8];
+  {
+    const int64_t base = (((int64_t)s * Hv + hv) * kD + v0 + c16) * kD + g4;
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau)
+      S[tau] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + base + 16 * tau) : zero4();
   }
-  if (nchunks == 0) {
-    if (hT_lane) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        *reinterpret_cast<f32x4 *>(hT_lane + 32 * wv + 16 * b + quad) = sacc[b];
-    }
-    return;
+
+  // Chunk 0's fragments, issued in the loop's order (the compiler's waits at
+  // the loop head assume the same order on entry and on the back edge).
+  CK x;
+  {
+    const Rsrc r = rsrc_of(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(x, r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(x, r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_gates(x, r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_p(x, r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(x, r);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  for (int c = 0; c < nc; ++c) {
+    const Rsrc rn = rsrc_of(c + 1);
 
-  auto store_state = [&]() {
+    // v' = u + w (-S); then the next chunk's w
+    f16x8 sn[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const float x[4] = {sacc[b][0], sacc[b][1], sacc[b][2], sacc[b][3]};
-      u32x2 hi, lo;
-      split_pack4(x, hi, lo);
-      const int d = 32 * wv + 16 * b + quad;
-      *reinterpret_cast<u32x2 *>(s_hi + l16 * kLdS + d) = hi;
-      *reinterpret_cast<u32x2 *>(s_lo + l16 * kLdS + d) = lo;
-    }
-  };
+    for (int p = 0; p < 4; ++p) sn[p] = neg_f16(S[2 * p], S[2 * p + 1]);
+    f32x4 v[4] = {x.u[0], x.u[1], x.u[2], x.u[3]};
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) v[R] = mfma(x.w[4 * R + p], sn[p], v[R]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(x, rn);
+    __builtin_amdgcn_sched_barrier(0);
 
-  auto load_chunk = [&](int c, ChunkFrags<kF32In> &f, ChunkK<kF32In> &kr) {
-    const int t0 = bos + c * kC;
-    const uint32_t L = static_cast<uint32_t>(min(kC, eos - t0));
-    const char *qb = static_cast<const char *>(qin) + ((int64_t)t0 * H + h) * kD * kElt;
-    const char *kb = static_cast<const char *>(kin) + ((int64_t)t0 * H + h) * kD * kElt;
-    const rsrc_t rq = make_rsrc(qb, L * rs_qk);
-    const rsrc_t rk = make_rsrc(kb, L * rs_qk);
-    const rsrc_t rw = make_rsrc(win + ((int64_t)hv * t_max + t0) * kD, L * kD * 2);
-    const rsrc_t ru = make_rsrc(uin + ((int64_t)hv * t_max + t0) * kD, L * kD * 4);
-    const rsrc_t rg = make_rsrc(g + (int64_t)t0 * Hv + hv, L * Hv * 4);
+    // y^T = (-S)^T q^T; then the next chunk's q16
+    f32x4 ya[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const uint32_t off = (lrow + rr) * rs_qk + lcol * kElt;
-      if constexpr (kF32In) {
-        kr.v[2 * rr] = buf_load16(rk, off);
-        kr.v[2 * rr + 1] = buf_load16(rk, off + 16);
-      } else {
-        kr.v[rr] = buf_load16(rk, off);
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) ya[R] = mfma(sn[p], x.q[4 * R + p], ya[R]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(x, rn);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // v' and the decayed v' as hi + lo; pa^T = v'^T P^T
+    bf16x8 dh[2], dl[2], eh[2], elo[2];
+    split8(v[0], v[1], dh[0], dl[0]);
+    split8(v[2], v[3], dh[1], dl[1]);
+    split8(v[0] * x.dec[0], v[1] * x.dec[1], eh[0], elo[0]);
+    split8(v[2] * x.dec[2], v[3] * x.dec[3], eh[1], elo[1]);
+    float exs[4] = {x.exs[0], x.exs[1], x.exs[2], x.exs[3]};
+    const float el = x.el;
+    __builtin_amdgcn_sched_barrier(0);
+    load_gates(x, rn);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 pa[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+#pragma unroll
+      for (int q = 0; q <= (R >> 1); ++q) {
+        const int pi = R < 2 ? R : 2 * R - 2 + q;
+        pa[R] = mfma(dh[q], x.p[2 * pi], pa[R]);
+        pa[R] = mfma(dl[q], x.p[2 * pi], pa[R]);
+        pa[R] = mfma(dh[q], x.p[2 * pi + 1], pa[R]);
       }
     }
-    kr.g = wv == 0 ? buf_load_f32(rg, lane * Hv * 4) : 0.f;
-    const uint32_t qrow = (16 * wv + l16) * rs_qk;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int col = 32 * kk + 8 * (lane >> 4);
-      if constexpr (kF32In) {
-        f.q[2 * kk] = buf_load16(rq, qrow + col * 4);
-        f.q[2 * kk + 1] = buf_load16(rq, qrow + col * 4 + 16);
-      } else {
-        f.q[kk] = buf_load16(rq, qrow + col * 2);
-      }
-      f.w[kk] = buf_load16(rw, (16 * wv + l16) * kD * 2 + col * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.u[i] = buf_load_f32(ru, ((16 * wv + quad + i) * kD + vcol) * 4);
-  };
-
-  auto k_rows = [&](const ChunkK<kF32In> &kr, u32x4 (&hi)[4], u32x4 (&lo)[4]) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      if constexpr (kF32In) {
-        split8(kr.v[2 * rr], kr.v[2 * rr + 1], hi[rr], lo[rr]);
-      } else {
-        hi[rr] = kr.v[rr];
-        lo[rr] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-
-  auto stage_krow = [&](const ChunkK<kF32In> &kr) {
-    u32x4 hi[4], lo[4];
-    k_rows(kr, hi, lo);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      *reinterpret_cast<u32x4 *>(krow + (lrow + rr) * kLdRow + lcol) = hi[rr];
-      if constexpr (kF32In)
-        *reinterpret_cast<u32x4 *>(krow + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = lo[rr];
-    }
-  };
-
-  auto stage_kcol = [&](const ChunkK<kF32In> &kr) {
-    u32x4 hi[4], lo[4];
-    k_rows(kr, hi, lo);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int at = kcol_at(lcol + i, lrow);
-      const uint32_t a = half_of(hi[0], i) | (static_cast<uint32_t>(half_of(hi[1], i)) << 16);
-      const uint32_t b = half_of(hi[2], i) | (static_cast<uint32_t>(half_of(hi[3], i)) << 16);
-      *reinterpret_cast<u32x2 *>(kcol + at) = u32x2{a, b};
-      if constexpr (kF32In) {
-        const uint32_t c2 = half_of(lo[0], i) | (static_cast<uint32_t>(half_of(lo[1], i)) << 16);
-        const uint32_t d2 = half_of(lo[2], i) | (static_cast<uint32_t>(half_of(lo[3], i)) << 16);
-        *reinterpret_cast<u32x2 *>(kcol + 128 * kLdCol + at) = u32x2{c2, d2};
-      }
-    }
-  };
-
-  auto stage_gates = [&](const ChunkK<kF32In> &kr, int buf) {
-    if (wv == 0) gam2[buf * 64 + lane] = wave_inclusive_scan(kr.g, lane) * kLog2e;
-  };
-
-  // One chunk: `cur` holds its fragments, the next chunk is loaded into `nxt`.
-  ChunkK<kF32In> kr;
-  auto chunk = [&](int c, ChunkFrags<kF32In> &cur, ChunkFrags<kF32In> &nxt) {
-    const int t0 = bos + c * kC;
-    const int L = min(kC, eos - t0);
-    const float *gm = gam2 + (c & 1) * 64;
-    stage_kcol(kr);
-    const bool more = c + 1 < nchunks;
-    if (more) load_chunk(c + 1, nxt, kr);
-
-    // ---- phase 1: X = w S, Y = q S ------------------------------------------
-    bf16x8 qh[4], ql[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if constexpr (kF32In) {
-        u32x4 hi, lo;
-        split8(cur.q[2 * kk], cur.q[2 * kk + 1], hi, lo);
-        qh[kk] = as_bf16x8(hi);
-        ql[kk] = as_bf16x8(lo);
-      } else {
-        qh[kk] = as_bf16x8(cur.q[kk]);
-      }
-    }
-    f32x4 xh = zero4(), xl = zero4(), yh = zero4(), yl = zero4();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 sh = frag_rows(s_hi, kLdS, 0, 32 * kk, lane);
-      const bf16x8 sl = frag_rows(s_lo, kLdS, 0, 32 * kk, lane);
-      const bf16x8 aw = as_bf16x8(cur.w[kk]);
-      xh = mfma(aw, sh, xh);
-      xl = mfma(aw, sl, xl);
-      yh = mfma(qh[kk], sh, yh);
-      yl = mfma(qh[kk], sl, yl);
-      if constexpr (kF32In) yl = mfma(ql[kk], sh, yl);
-    }
-    // ---- this wave's row block of P, as P^T blocks (jb, wv) in registers ------
-    // lane holds P[t = 16 wv + l16][j = 16 jb + quad + i]
-    u32x2 ph[4], pl[4];
-    const int t = 16 * wv + l16;
-    const float gt = gm[t];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      ph[jb] = u32x2{0u, 0u};
-      pl[jb] = u32x2{0u, 0u};
-      if (jb <= wv) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 ak = frag_rows(krow, kLdRow, 16 * jb, 32 * kk, lane);
-          acc = mfma(ak, qh[kk], acc);
-          if constexpr (kF32In) {
-            acc = mfma(frag_rows(krow + 64 * kLdRow, kLdRow, 16 * jb, 32 * kk, lane), qh[kk], acc);
-            acc = mfma(ak, ql[kk], acc);
-          }
-        }
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 16 * jb + quad + i;
-          const float e = fast_exp2(gt - gm[j]);  // only used where j <= t
-          pv[i] = j <= t ? acc[i] * e : 0.f;
-        }
-        split_pack4(pv, ph[jb], pl[jb]);
-      }
-    }
-    // ---- v' and decayed v' ---------------------------------------------------
-    const float gl = gm[63];
-    f32x4 X = xh + xl;
+    __builtin_amdgcn_sched_barrier(0);
+    load_p(x, rn);
     {
-      float dl[4], dp[4];
+      // o^T = scale e^gamma S^T q^T + v'^T P^T
+      const int t0 = bos + kC * c;
+      const uint32_t lc = static_cast<uint32_t>(min(kC, eos - t0));
+      const i32x4 ro = rsrc_words(o + ((int64_t)t0 * Hv + hv) * kD + v0, lc * Hv * kD * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wv + quad + i;
-        dl[i] = cur.u[i] - X[i];
-        dp[i] = dl[i] * fast_exp2(gl - gm[r]);
-      }
-      u32x2 hi, lo;
-      split_pack4(dl, hi, lo);
-      const int perm = 32 * (wv >> 1) + 2 * quad + 4 * (wv & 1);  // see the P v' product
-      *reinterpret_cast<u32x2 *>(dl_hi + l16 * kLdV + perm) = hi;
-      *reinterpret_cast<u32x2 *>(dl_lo + l16 * kLdV + perm) = lo;
-      split_pack4(dp, hi, lo);
-      *reinterpret_cast<u32x2 *>(dp_hi + l16 * kLdV + 16 * wv + quad) = hi;
-      *reinterpret_cast<u32x2 *>(dp_lo + l16 * kLdV + 16 * wv + quad) = lo;
+      for (int R = 0; R < 4; ++R) store16(ro, vo_o, R * row_o, pa[R] - exs[R] * ya[R]);
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- phase 2: o = scale (e^gamma Y + P v') --------------------------------
-    {
-      f32x4 oacc = zero4();
+    // S = e^{gamma_last} S + K^T (e^{gamma_last - gamma} v'); then the next K^T
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk <= (wv >> 1)) {
-          const bf16x8 pa = __builtin_bit_cast(
-              bf16x8, u32x4{ph[2 * kk][0], ph[2 * kk][1], ph[2 * kk + 1][0], ph[2 * kk + 1][1]});
-          const bf16x8 pb = __builtin_bit_cast(
-              bf16x8, u32x4{pl[2 * kk][0], pl[2 * kk][1], pl[2 * kk + 1][0], pl[2 * kk + 1][1]});
-          const bf16x8 dh = frag_rows(dl_hi, kLdV, 0, 32 * kk, lane);
-          const bf16x8 dlo = frag_rows(dl_lo, kLdV, 0, 32 * kk, lane);
-          oacc = mfma(pa, dh, oacc);
-          oacc = mfma(pa, dlo, oacc);
-          oacc = mfma(pb, dh, oacc);
-        }
+    for (int tau = 0; tau < 8; ++tau) S[tau] = S[tau] * el;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau) {
+        S[tau] = mfma(x.k[2 * tau + q], eh[q], S[tau]);
+        S[tau] = mfma(x.k[2 * tau + q], elo[q], S[tau]);
+        if constexpr (kF32In) S[tau] = mfma(x.k[16 + 2 * tau + q], eh[q], S[tau]);
       }
-      const f32x4 Y = yh + yl;
-      const rsrc_t ro = make_rsrc(o + ((int64_t)t0 * Hv + hv) * kD, L * rs_o);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wv + quad + i;
-        const float val = scale * (fast_exp2(gm[r]) * Y[i] + oacc[i]);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, r * rs_o + vcol * 4, 0, 0);
-      }
-    }
-    // ---- S = e^{gamma_last} S + k^T v'_dec -------------------------------------
-    {
-      const float decay = fast_exp2(gl);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int d = 32 * wv + 16 * b + l16;
-        f32x4 ah = sacc[b] * decay, al = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int at = kcol_at(d, 32 * kk + 8 * (lane >> 4));
-          const bf16x8 ak = lds_frag(kcol + at);
-          const bf16x8 bh = frag_rows(dp_hi, kLdV, 0, 32 * kk, lane);
-          const bf16x8 bl = frag_rows(dp_lo, kLdV, 0, 32 * kk, lane);
-          ah = mfma(ak, bh, ah);
-          al = mfma(ak, bl, al);
-          if constexpr (kF32In) al = mfma(lds_frag(kcol + 128 * kLdCol + at), bh, al);
-        }
-        sacc[b] = ah + al;
-      }
-    }
-    store_state();
-    if (more) {
-      stage_krow(kr);
-      stage_gates(kr, (c + 1) & 1);
-    }
-    __syncthreads();
-  };
-
-  ChunkFrags<kF32In> fa, fb;
-  load_chunk(0, fa, kr);
-  stage_krow(kr);
-  stage_gates(kr, 0);
-  store_state();
-  __syncthreads();
-  for (int c = 0;;) {
-    chunk(c, fa, fb);
-    if (++c >= nchunks) break;
-    chunk(c, fb, fa);
-    if (++c >= nchunks) break;
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(x, rn);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  if (hT_lane) {
+  if (hT) {
+    const int64_t base = (((int64_t)s * Hv + hv) * kD + v0 + c16) * kD + g4;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-      *reinterpret_cast<f32x4 *>(hT_lane + 32 * wv + 16 * b + quad) = sacc[b];
+    for (int tau = 0; tau < 8; ++tau) *reinterpret_cast<f32x4 *>(hT + base + 16 * tau) = S[tau];
   }
+}
+
+template <bool kF32In>
+hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
+                        int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
+                        hipStream_t stream) {
+  const int members = (hv / h) * kSlices;
+  const int groups = n_max * h;
+  const int rounds = (groups + kXcds - 1) / kXcds;
+  const dim3 grid(rounds * kXcds * members);
+  hipLaunchKernelGGL((inter_kernel<kF32In>), grid, dim3(64), 0, stream, in, h0, cu, o, hT, n_max,
+                     h, hv, t_max, nt);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_inter(bool f32_in, const void *q, const void *k, const void *w, const float *u,
-                        const float *g, const float *h0, const int32_t *cu_seqlens,
-                        int32_t n_max, int32_t h, int32_t hv, int32_t t_max, float scale,
-                        float *o, float *hT, hipStream_t stream) {
-  const int members = (hv / h) * kNVT;
-  const int groups = n_max * h;
-  const int rounds = (groups + kXcds - 1) / kXcds;
-  const dim3 grid(rounds * kXcds * members);
-  if (f32_in) {
-    hipLaunchKernelGGL(inter_kernel<true>, grid, dim3(kThreads), 0, stream, q, k,
-                       static_cast<const __bf16 *>(w), u, g, h0, cu_seqlens, o, hT, n_max, h,
-                       hv, t_max, scale);
-  } else {
-    hipLaunchKernelGGL(inter_kernel<false>, grid, dim3(kThreads), 0, stream, q, k,
-                       static_cast<const __bf16 *>(w), u, g, h0, cu_seqlens, o, hT, n_max, h,
-                       hv, t_max, scale);
-  }
-  return hipGetLastError();
+hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
+                        const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
+                        int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream) {
+  return f32_in ? launch_waves<true>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream)
+                : launch_waves<false>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream);
 }
 
 }  // namespace gdn

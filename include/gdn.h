@@ -72,9 +72,32 @@ typedef struct {
  * "Core design"). Returns -1 if an argument is not positive (t_max may be 0). */
 int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
 
-/* Bytes of workspace gdn_chunk_fwd needs for `cfg`: w [hv, t_max, dk] bf16,
- * u [hv, t_max, dv] fp32 and a [nt_max, 2] int32 chunk table, each 256-byte
- * aligned. Writes *bytes; returns a validation status. */
+/* Byte offsets of the intermediates inside a workspace, each 256-byte aligned.
+ * The intra stage writes them and the inter stage reads them; their layouts
+ * are an internal contract between the two stages (MFMA fragment order), but
+ * they are documented so that they can be inspected:
+ *   w16   fp16 [hv, t_max, dk]: w (AMX page, section 4) with the columns of
+ *         each 32-column block in the order 0-3,16-19,4-7,20-23,..,12-15,28-31
+ *   q16   fp16 [t_max, h, dk]: q rounded to fp16, same column order
+ *   kimg  bf16 [h, nt_max, 16 (32 for fp32 input), 64, 8]: K^T fragments
+ *   uimg  fp32 [hv, nt_max, dv / 16, 4, 64, 4]: u (AMX page, section 4), one
+ *         16 x 16 tile per 1 KB block
+ *   pimg  bf16 [hv, nt_max, 6, 2, 64, 8]: scale * tril(q k^T * Gamma) as hi + lo
+ *   gimg  fp32 [hv, nt_max, 192]: per token e^{gamma_last - gamma},
+ *         scale * e^gamma, then e^{gamma_last}
+ *   table int32 [nt_max, 2]: the chunk-index table
+ * Per-chunk blocks are indexed by slot floor(t0 / 64) + n for a chunk starting
+ * at token t0 of sequence n (distinct per chunk, < nt_max). */
+typedef struct {
+  size_t w16, q16, kimg, uimg, pimg, gimg, table;
+  size_t total; /* bytes of workspace gdn_chunk_fwd needs */
+} gdn_workspace_layout_t;
+
+/* Fills *layout for `cfg`; returns a validation status. */
+gdn_status gdn_workspace_layout(const gdn_config *cfg, gdn_workspace_layout_t *layout);
+
+/* Bytes of workspace gdn_chunk_fwd needs for `cfg` (layout.total). Writes
+ * *bytes; returns a validation status. */
 gdn_status gdn_workspace_size(const gdn_config *cfg, size_t *bytes);
 
 /* Chunk-index table built on the device (FLA issue 1155, "Core design": a
@@ -101,35 +124,41 @@ gdn_status gdn_front_conv_silu_l2(const gdn_config *cfg, const void *qkv, const 
                                   float *v, void *stream);
 
 /* Intra-chunk stage over [nt_max, h] (AMX page, section 4): per chunk and key
- * head, K K^T once; per value head of the group the beta/decay-masked strictly
- * lower A, T = (I + A)^-1 kept on chip, w = T diag(beta e^gamma) K and
- * u = T diag(beta) V, gamma the chunk-local cumulative g.
- *   k (device) [t_max, h, dk]; v (device) [t_max, hv, dv]; dtype cfg->qkv_dtype
+ * head, K K^T and K q^T once; per value head of the group the beta/decay-masked
+ * strictly lower A, T = (I + A)^-1 kept on chip, w = T diag(beta e^gamma) K and
+ * u = T diag(beta) V, gamma the chunk-local cumulative g (section 3), and the
+ * masked intra-chunk attention P = scale * tril(q k^T * Gamma) of section 5.
+ *   q, k (device) [t_max, h, dk]; v (device) [t_max, hv, dv]; dtype qkv_dtype
  *   g, beta (device) fp32 [t_max, hv]
  *   chunk_indices (device) int32 [nt_max, 2] as built by gdn_build_chunk_indices
- *   w (device) bf16 [hv, t_max, dk], u (device) fp32 [hv, t_max, dv]: rows of
- *     valid tokens are written, every other row is left untouched. */
-gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *k, const void *v,
+ *   workspace (device) >= gdn_workspace_size bytes, 256-byte aligned: all the
+ *     intermediates of gdn_workspace_layout except the table are written
+ *     (token rows of w16 / q16 for valid tokens only).
+ * q16 is q rounded to fp16 (exact for bf16 inputs of magnitude >= 2^-14). */
+gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *q, const void *k, const void *v,
                                const float *g, const float *beta, const int32_t *cu_seqlens,
-                               const int32_t *chunk_indices, void *w, float *u, void *stream);
+                               const int32_t *chunk_indices, void *workspace, size_t ws_bytes,
+                               void *stream);
 
 /* Inter-chunk stage over [n_max, hv, dv / 16] (AMX page, section 5): chunks in
  * order with S on chip: v' = u - w S; o = scale (diag(e^gamma) q S +
- * tril(q k^T * Gamma) v'); S = e^{gamma_last} S + (diag(e^{gamma_last-gamma}) k)^T v'.
- *   q, k (device) [t_max, h, dk], dtype cfg->qkv_dtype; w, u as written by
- *   gdn_chunk_fwd_intra; g (device) fp32 [t_max, hv];
+ * tril(q k^T * Gamma) v'); S = e^{gamma_last} S + (diag(e^{gamma_last - gamma}) k)^T v',
+ * Gamma[r, i] = exp(gamma_r - gamma_i) for i <= r (diagonal kept). Reads only
+ * the intermediates gdn_chunk_fwd_intra wrote into `workspace` for the same
+ * cfg and cu_seqlens.
  *   h0 (device, nullable = zero state) fp32 [n_max, hv, dv, dk];
  *   o  (device) fp32 [t_max, hv, dv]: valid rows written, others untouched;
  *   hT (device, nullable) fp32 [n_max, hv, dv, dk]; hT may alias h0 exactly.
  * A zero-length sequence writes hT = h0 (or zeros when h0 is null). */
-gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const void *q, const void *k,
-                               const void *w, const float *u, const float *g, const float *h0,
-                               const int32_t *cu_seqlens, void *o, float *hT, void *stream);
+gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int32_t *cu_seqlens,
+                               const void *workspace, size_t ws_bytes, void *o, float *hT,
+                               void *stream);
 
 /* Whole forward: [chunk table if chunk_indices is NULL] -> intra -> inter, all
  * on `stream`, no host synchronisation. Arguments as above; workspace (device)
- * of at least gdn_workspace_size bytes, 256-byte aligned, holds w, u and the
- * table between the stages and may be reused once the stream passes the call. */
+ * of at least gdn_workspace_size bytes, 256-byte aligned, holds the
+ * intermediates and the table between the stages and may be reused once the
+ * stream passes the call. */
 gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,
                          const float *g, const float *beta, const float *h0,
                          const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,

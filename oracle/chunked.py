@@ -77,11 +77,17 @@ def intra_chunk(Kc, Vc, gc, bc):
     return w, u, gamma, Gam
 
 
+def local_attention(Qc, Kc, Gam):
+    """tril(Q K^T * Gamma), diagonal kept: the intra-chunk attention of the
+    output (AMX page, section 5), before the output scale."""
+    return np.tril(Qc @ Kc.T * Gam)
+
+
 def inter_chunk(Qc, Kc, w, u, gamma, Gam, S, scale):
     """Inter stage step for one chunk (AMX page, section 5). S is [Dk, Dv]."""
     v_prime = u - w @ S
     attn_inter = (Qc * np.exp(gamma)[:, None]) @ S
-    local_attn = np.tril(Qc @ Kc.T * Gam)
+    local_attn = local_attention(Qc, Kc, Gam)
     o = scale * (local_attn @ v_prime + attn_inter)
     g_last = gamma[-1]
     S_new = S * np.exp(g_last) + (Kc * np.exp(g_last - gamma)[:, None]).T @ v_prime
@@ -89,14 +95,15 @@ def inter_chunk(Qc, Kc, w, u, gamma, Gam, S, scale):
 
 
 def gdn_chunked(q, k, v, g, beta, cu_seqlens, h0=None, scale=None, chunk=64,
-                return_wu=False):
+                return_wu=False, stages=None):
     """Chunked-form forward over a packed varlen batch, every (seq, value head).
 
     Same array conventions as ``oracle.recurrent.gdn_recurrent``. A sequence's
     last chunk may be partial; it is evaluated at its real length (which is
     what zero-padding g and beta past the end would also give).
     With return_wu, also returns w, u as [Hv, T, D] arrays (the intra stage's
-    outputs, indexed by token).
+    outputs, indexed by token). A dict passed as `stages` receives, per
+    (value head, chunk start token), the chunk's gamma and local attention.
     """
     q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
     T, H, Dk = q.shape
@@ -122,6 +129,8 @@ def gdn_chunked(q, k, v, g, beta, cu_seqlens, h0=None, scale=None, chunk=64,
                 if return_wu:
                     W[hv, t0:t1] = w
                     U[hv, t0:t1] = u
+                if stages is not None:
+                    stages[(hv, t0)] = (gamma, local_attention(Qc, Kc, Gam))
                 o[t0:t1, hv], S = inter_chunk(Qc, Kc, w, u, gamma, Gam, S, scale)
             hT[s, hv] = S.T
     if return_wu:

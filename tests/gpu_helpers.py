@@ -125,3 +125,82 @@ def lane_errors(wl, o_gpu, hT_gpu, ref):
     eo = num_o / den_o if den_o > 0 else num_o
     es = np.sqrt(num_s / den_s) if den_s > 0 else np.sqrt(num_s)
     return eo, es
+
+
+# --------------------------------------------------------------------------- #
+# decoders of the intermediates the intra stage writes (layouts in include/gdn.h)
+# --------------------------------------------------------------------------- #
+
+def _perm4(m):
+    return 8 * m if m < 4 else 8 * (m - 4) + 4
+
+
+# column d of a permuted 128-wide row sits at position POS[d]
+POS = np.array([32 * (d // 32) + _perm4((d % 32) // 4) + d % 4 for d in range(128)])
+
+# P pairs: (token block q, output tile R)
+PAIRS = [(0, 0), (0, 1), (0, 2), (1, 2), (0, 3), (1, 3)]
+
+
+def frag_token(q, g, j):
+    """Token (within the chunk) of contraction slot j of lane group g in token block q."""
+    return 32 * q + (16 if j >= 4 else 0) + 4 * g + (j & 3)
+
+
+def workspace_views(cfg, ws):
+    lay = gdn.gdn_workspace_layout(cfg)
+    nt = gdn.gdn_nt_max(cfg.t_max, cfg.n_max)
+    nk = 32 if cfg.qkv_dtype == gdn.GDN_F32 else 16
+
+    def view(name, dtype, shape):
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        return ws[lay[name]:lay[name] + n].view(dtype).view(*shape)
+
+    return dict(
+        w16=view("w16", torch.float16, (cfg.hv, cfg.t_max, 128)),
+        q16=view("q16", torch.float16, (cfg.t_max, cfg.h, 128)),
+        kimg=view("kimg", torch.bfloat16, (cfg.h, nt, nk, 64, 8)),
+        uimg=view("uimg", torch.float32, (cfg.hv, nt, 8, 4, 64, 4)),
+        pimg=view("pimg", torch.bfloat16, (cfg.hv, nt, 6, 2, 64, 8)),
+        gimg=view("gimg", torch.float32, (cfg.hv, nt, 192)),
+        nt=nt, nk=nk)
+
+
+def decode_kimg(kimg_slot):
+    """[nk, 64, 8] fragments -> K [64 tokens, 128] (hi, and lo when nk == 32)."""
+    x = kimg_slot.float().numpy()
+    out = []
+    for term in range(x.shape[0] // 16):
+        K = np.zeros((64, 128), np.float64)
+        for f in range(16):
+            tau, q = f // 2, f % 2
+            for lane in range(64):
+                g, c = lane // 16, lane % 16
+                for j in range(8):
+                    K[frag_token(q, g, j), 16 * tau + c] = x[16 * term + f, lane, j]
+        out.append(K)
+    return out
+
+
+def decode_uimg(uimg_slot):
+    """[8, 4, 64, 4] -> u [64 tokens, 128]."""
+    x = uimg_slot.numpy().astype(np.float64)
+    U = np.zeros((64, 128))
+    for sl in range(8):
+        for R in range(4):
+            for lane in range(64):
+                g, c = lane // 16, lane % 16
+                U[16 * R + 4 * g:16 * R + 4 * g + 4, 16 * sl + c] = x[sl, R, lane]
+    return U
+
+
+def decode_pimg(pimg_slot):
+    """[6, 2, 64, 8] hi/lo -> P [64 r, 64 j] (hi + lo), zero outside the pairs."""
+    x = pimg_slot.float().numpy().astype(np.float64)
+    P = np.zeros((64, 64))
+    for pi, (q, R) in enumerate(PAIRS):
+        for lane in range(64):
+            g, c = lane // 16, lane % 16
+            for j in range(8):
+                P[16 * R + c, frag_token(q, g, j)] = x[pi, 0, lane, j] + x[pi, 1, lane, j]
+    return P

@@ -58,11 +58,21 @@ def test_nt_max_rejects_bad_arguments(lib):
     assert gdn.gdn_nt_max(10, 1, 0) == -1
 
 
-def test_workspace_size_layout(lib):
-    cfg = gdn.make_config(4096, 1, 16, 32)
+@pytest.mark.parametrize("dtype,nk", [(gdn.GDN_BF16, 16), (gdn.GDN_F32, 32)])
+def test_workspace_layout(lib, dtype, nk):
+    T, N, H, Hv = 4100, 3, 16, 32
+    cfg = gdn.make_config(T, N, H, Hv, dtype)
     al = lambda x: (x + 255) // 256 * 256
-    nt = index_table.nt_max(4096, 1)
-    assert gdn.gdn_workspace_size(cfg) == al(32 * 4096 * 128 * 2) + al(32 * 4096 * 128 * 4) + al(nt * 8)
+    nt = index_table.nt_max(T, N)
+    sizes = [("w16", Hv * T * 128 * 2), ("q16", T * H * 128 * 2), ("kimg", H * nt * nk * 1024),
+             ("uimg", Hv * nt * 64 * 128 * 4), ("pimg", Hv * nt * 12 * 1024),
+             ("gimg", Hv * nt * 192 * 4), ("table", nt * 8)]
+    lay = gdn.gdn_workspace_layout(cfg)
+    at = 0
+    for name, size in sizes:
+        assert lay[name] == at, name
+        at += al(size)
+    assert lay["total"] == at == gdn.gdn_workspace_size(cfg)
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -114,11 +124,22 @@ def test_chunk_fwd_host_errors(lib):
 def test_stage_entry_points_host_errors(lib):
     cfg = gdn.make_config(256, 2, 16, 32)
     c = ctypes.byref(cfg)
-    assert lib.gdn_chunk_fwd_intra(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == INVALID
-    assert lib.gdn_chunk_fwd_intra(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, None) == INVALID
-    assert lib.gdn_chunk_fwd_inter(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None) == INVALID
-    assert lib.gdn_chunk_fwd_inter(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, None, None) == INVALID
-    assert lib.gdn_build_chunk_indices(c, FAKE, None, None) == INVALID
-    assert lib.gdn_front_conv_silu_l2(c, FAKE, FAKE, 9, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
-    assert lib.gdn_front_conv_silu_l2(c, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
-    assert lib.gdn_front_conv_silu_l2(c, None, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    F = FAKE
+    need = gdn.gdn_workspace_size(cfg)
+    # intra: (cfg, q, k, v, g, beta, cu, table, workspace, ws_bytes, stream)
+    assert lib.gdn_chunk_fwd_intra(c, F, F, F, F, F, F, None, F, need, None) == INVALID
+    assert lib.gdn_chunk_fwd_intra(c, None, F, F, F, F, F, F, F, need, None) == INVALID
+    assert lib.gdn_chunk_fwd_intra(c, F, F, F, F, F, F, F + 8, F, need, None) == INVALID
+    assert lib.gdn_chunk_fwd_intra(c, F, F, F, F, F, F, F, None, need, None) == WORKSPACE
+    assert lib.gdn_chunk_fwd_intra(c, F, F, F, F, F, F, F, F, need - 1, None) == WORKSPACE
+    assert lib.gdn_chunk_fwd_intra(c, F, F, F, F, F, F, F, F + 16, need, None) == WORKSPACE
+    # inter: (cfg, h0, cu, workspace, ws_bytes, o, hT, stream)
+    assert lib.gdn_chunk_fwd_inter(c, None, F, F, need, None, None, None) == INVALID
+    assert lib.gdn_chunk_fwd_inter(c, None, None, F, need, F, None, None) == INVALID
+    assert lib.gdn_chunk_fwd_inter(c, F + 4, F, F, need, F, None, None) == INVALID
+    assert lib.gdn_chunk_fwd_inter(c, None, F, None, need, F, None, None) == WORKSPACE
+    assert lib.gdn_chunk_fwd_inter(c, None, F, F, need - 1, F, None, None) == WORKSPACE
+    assert lib.gdn_build_chunk_indices(c, F, None, None) == INVALID
+    assert lib.gdn_front_conv_silu_l2(c, F, F, 9, F, F, F, F, None) == UNSUPPORTED
+    assert lib.gdn_front_conv_silu_l2(c, F, F, 0, F, F, F, F, None) == UNSUPPORTED
+    assert lib.gdn_front_conv_silu_l2(c, None, F, 4, F, F, F, F, None) == INVALID

@@ -15,8 +15,9 @@ import chunked_gated_delta_rule_amd as gdn
 import workloads
 from oracle import chunked, index_table, recurrent
 
-from gpu_helpers import (O_TOL, S_TOL, config_of, device_inputs, lane_errors, log,
-                         oracle_inputs_f64, oracle_lanes, run_forward, run_front)
+from gpu_helpers import (O_TOL, POS, S_TOL, config_of, decode_kimg, decode_pimg, decode_uimg,
+                         device_inputs, lane_errors, log, oracle_inputs_f64, oracle_lanes,
+                         run_forward, run_front, workspace_views)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -83,32 +84,74 @@ def test_front_small_varlen():
 
 
 # --------------------------------------------------------------------------- #
-# stage 1 alone: w (bf16) and u (fp32) against the chunked-form oracle
+# stage 1 alone: every intermediate against the chunked-form oracle
 # --------------------------------------------------------------------------- #
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_intra_stage_w_u(dtype):
+def test_intra_stage_intermediates(dtype):
     wl = workloads.make_custom([130, 70, 64, 1], 2, 4, seed=5, dtype=dtype, t_max=300, n_max=5)
     log(f"intra stage {dtype}")
     d = device_inputs(wl)
     cfg = config_of(wl)
+    scale = 1.0 / np.sqrt(128.0)
     nt = gdn.gdn_nt_max(wl.t_max, wl.n_max)
     table = torch.empty((nt, 2), dtype=torch.int32, device=DEV)
     gdn.gdn_build_chunk_indices(cfg, d["cu"], table)
-    w = torch.zeros((wl.Hv, wl.t_max, 128), dtype=torch.bfloat16, device=DEV)
-    u = torch.zeros((wl.Hv, wl.t_max, 128), dtype=torch.float32, device=DEV)
-    gdn.gdn_chunk_fwd_intra(cfg, d["k"], d["v"], d["g"], d["beta"], d["cu"], table, w, u)
+    ws = torch.zeros(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    gdn.gdn_chunk_fwd_intra(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], table, ws)
     torch.cuda.synchronize()
+    V = {k_: (v_.cpu() if isinstance(v_, torch.Tensor) else v_)
+         for k_, v_ in workspace_views(cfg, ws).items()}
+    stages = {}
     _, _, W, U = chunked.gdn_chunked(wl.f64("q"), wl.f64("k"), wl.f64("v"), wl.f64("g"),
-                                     wl.f64("beta"), wl.cu_seqlens, chunk=64, return_wu=True)
+                                     wl.f64("beta"), wl.cu_seqlens, chunk=64, return_wu=True,
+                                     stages=stages)
     T = int(wl.cu_seqlens[-1])
-    wg = w[:, :T].cpu().double().numpy()
-    ug = u[:, :T].cpu().double().numpy()
+    # w (fp16, permuted columns) and q16 (q rounded to fp16, permuted columns)
+    wg = V["w16"][:, :T][..., POS].double().numpy()
     ew = np.max(np.abs(wg - W[:, :T])) / np.max(np.abs(W[:, :T]))
-    eu = np.max(np.abs(ug - U[:, :T])) / np.max(np.abs(U[:, :T]))
-    log(f"  w err {ew:.3e}  u err {eu:.3e}")
-    assert ew < 4e-3   # bf16 storage of w: half an ulp is 2^-9 of the value
+    q16 = V["q16"][:T][..., POS]
+    if dtype == torch.bfloat16:  # bf16 -> fp16 is exact here: one rounding, bit for bit
+        assert torch.equal(q16, wl.q[:T].float().half()), "q16 is not q rounded to fp16"
+    else:  # fp32 input passes through hi + lo bf16 first: within one fp16 ulp
+        qf = wl.q[:T].double()
+        assert torch.all((q16.double() - qf).abs() <= qf.abs() * 2.0 ** -10 + 2.0 ** -24)
+    cu = wl.cu_seqlens
+    eu = ep = eg = 0.0
+    pmax = max(np.max(np.abs(la)) for _, la in stages.values()) * scale
+    k64 = wl.f64("k")
+    for s_ in range(len(cu) - 1):
+        for t0 in range(int(cu[s_]), int(cu[s_ + 1]), 64):
+            L = min(64, int(cu[s_ + 1]) - t0)
+            slot = (t0 >> 6) + s_
+            # K^T fragments: exact copy of k (hi[+lo] for fp32 input), zero past the end
+            for h in range(wl.H):
+                terms = decode_kimg(V["kimg"][h, slot])
+                Kd = sum(terms)
+                ref = np.zeros((64, 128))
+                ref[:L] = k64[t0:t0 + L, h]
+                tol = 0.0 if dtype == torch.bfloat16 else 2e-5 * np.max(np.abs(k64))
+                assert np.max(np.abs(Kd - ref)) <= tol
+            for hv in range(wl.Hv):
+                gamma, la = stages[(hv, t0)]
+                Ud = decode_uimg(V["uimg"][hv, slot])
+                assert np.all(Ud[L:] == 0.0)
+                eu = max(eu, np.max(np.abs(Ud[:L] - U[hv, t0:t0 + L])) / np.max(np.abs(U[hv, :T])))
+                Pd = decode_pimg(V["pimg"][hv, slot])
+                Pref = np.zeros((64, 64))
+                Pref[:L, :L] = scale * la
+                ep = max(ep, np.max(np.abs(Pd - Pref)) / pmax)
+                gd = V["gimg"][hv, slot].double().numpy()
+                gl = gamma[L - 1]
+                for got, want in ((gd[:L], np.exp(gl - gamma)), (gd[64:64 + L], scale * np.exp(gamma)),
+                                  (gd[128:129], np.exp([gl]))):
+                    eg = max(eg, np.max(np.abs(got - want) / np.maximum(np.abs(want), 1e-30)))
+                assert np.all(gd[L:64] == 0) and np.all(gd[64 + L:128] == 0)
+    log(f"  w err {ew:.3e}  u err {eu:.3e}  P err {ep:.3e}  gate err {eg:.3e}")
+    assert ew < 1e-3   # fp16 storage of w: half an ulp is 2^-12 of the value
     assert eu < 1e-4
+    assert ep < 2e-5   # hi + lo bf16 carries ~16 significant bits
+    assert eg < 1e-5
 
 
 # --------------------------------------------------------------------------- #
