@@ -14,7 +14,7 @@
 // produced here, where the work is parallel over chunks, and written in the
 // exact MFMA fragment order the inter stage reads (each fragment one 1 KB
 // block, 16 bytes per lane), so that stage only streams blocks:
-//   w16   fp16 [hv, t, 128]     w, d permuted inside each 32-column block
+//   w16   fp16 [hv, t, 128]     -w, d permuted inside each 32-column block
 //   q16   fp16 [t, h, 128]      q rounded to fp16, same d permutation
 //   kimg  bf16 per (h, chunk)   K^T fragments for the state update (hi[, lo])
 //   uimg  fp32 per (hv, chunk)  u fragments, one 1 KB block per 16 x 16 tile
@@ -447,7 +447,8 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
             if (r < L) {
               _Float16 *dst = out.w16 + ((int64_t)hv * t_max + t0 + r) * kD + 32 * (db >> 1) +
                               perm4(4 * (db & 1) + (lane >> 4));
-              *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_f16(acc[0], acc[1]), pack_f16(acc[2], acc[3])};
+              *reinterpret_cast<u32x2 *>(dst) =
+                  u32x2{pack_f16(-acc[0], -acc[1]), pack_f16(-acc[2], -acc[3])};
             }
           } else {
             // lane holds u[r = 16 rb + 4 (lane >> 4) + i][d = 16 db + (lane & 15)]

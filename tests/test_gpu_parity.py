@@ -107,8 +107,8 @@ def test_intra_stage_intermediates(dtype):
                                      wl.f64("beta"), wl.cu_seqlens, chunk=64, return_wu=True,
                                      stages=stages)
     T = int(wl.cu_seqlens[-1])
-    # w (fp16, permuted columns) and q16 (q rounded to fp16, permuted columns)
-    wg = V["w16"][:, :T][..., POS].double().numpy()
+    # -w (fp16, permuted columns) and q16 (q rounded to fp16, permuted columns)
+    wg = -V["w16"][:, :T][..., POS].double().numpy()  # stored negated
     ew = np.max(np.abs(wg - W[:, :T])) / np.max(np.abs(W[:, :T]))
     q16 = V["q16"][:T][..., POS]
     if dtype == torch.bfloat16:  # bf16 -> fp16 is exact here: one rounding, bit for bit
