@@ -4,11 +4,14 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: device chunk-index table -> intra-chunk stage ->
 inter-chunk stage (plus the conv/SiLU/L2 front for workloads that have one),
-each launched through the C ABI on torch's current stream. W untimed warm-up
-steps, then exactly K timed steps bracketed by device synchronisation. HIP
-events recorded on the same stream between the launches give each kernel's
-average duration over the timed region; the dominant kernel's algorithmic
-bytes per launch divided by that duration is the roofline figure.
+launched through the C ABI's whole-forward call on torch's current stream.
+W untimed warm-up steps, then exactly K timed steps bracketed by device
+synchronisation; value = tokens x K / wall time of the timed region. Each
+kernel records a pair of HIP events at its own start and end (the timed
+variants of the entry points launch with hipExtLaunchKernel), so no packet
+sits between the launches and each kernel's average duration over the timed
+region is its execution time; the dominant kernel's algorithmic bytes per
+launch divided by that duration is the roofline figure.
 
 Prints ONE JSON line. Default workload: single sequence, T = 4096, H = 16,
 Hv = 32, D = 128, bf16 q/k/v (the configuration the metric is quoted on).
@@ -76,6 +79,41 @@ def counter_traffic(kernel, workload_name):
     if not ent or ent.get("source_digest") != kernel_source_digest(kernel):
         return None
     return ent.get("traffic_bytes")
+
+
+class HipEvents:
+    """Raw HIP events from the runtime torch has loaded (same soname)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = self.ct.c_void_p()
+            if self.rt.hipEventCreate(self.ct.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        self.made += out
+        return out
+
+    def ms(self, a, b):
+        t = self.ct.c_float()
+        if self.rt.hipEventElapsedTime(self.ct.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self):
+        for e in self.made:
+            self.rt.hipEventDestroy(e)
+        self.made = []
 
 
 def cpu_baseline(wl, max_seconds=20.0):
@@ -150,8 +188,6 @@ def main():
     has_front = wl.qkv is not None
     qkv_dtype = torch.float32 if has_front else wl.qkv_dtype
     cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype)
-    nt = gdn.gdn_nt_max(wl.t_max, wl.n_max)
-    table = torch.empty((nt, 2), dtype=torch.int32, device=dev)
     ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=dev)
     o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
     hT = torch.empty((wl.n_max, wl.Hv, 128, 128), dtype=torch.float32, device=dev)
@@ -163,43 +199,37 @@ def main():
         q, k, v = d["q"], d["k"], d["v"]
 
     stages = (["front"] if has_front else []) + ["index", "intra", "inter"]
+    hip = HipEvents()
 
     def step(evs=None):
-        i = 0
-        if evs is not None:
-            evs[0].record()
         if has_front:
-            gdn.gdn_front_conv_silu_l2(cfg, d["qkv"], d["conv_w"], wl.d_conv, cu, q, k, v)
-            i += 1
-            if evs is not None:
-                evs[i].record()
-        gdn.gdn_build_chunk_indices(cfg, cu, table)
-        i += 1
-        if evs is not None:
-            evs[i].record()
-        gdn.gdn_chunk_fwd_intra(cfg, q, k, v, d["g"], d["beta"], cu, table, ws)
-        i += 1
-        if evs is not None:
-            evs[i].record()
-        gdn.gdn_chunk_fwd_inter(cfg, d["h0"], cu, ws, o, hT)
-        i += 1
-        if evs is not None:
-            evs[i].record()
+            if evs is None:
+                gdn.gdn_front_conv_silu_l2(cfg, d["qkv"], d["conv_w"], wl.d_conv, cu, q, k, v)
+            else:
+                gdn.gdn_front_conv_silu_l2_timed(cfg, d["qkv"], d["conv_w"], wl.d_conv, cu, q, k,
+                                                 v, evs[6], evs[7])
+        if evs is None:
+            gdn.gdn_chunk_fwd(cfg, q, k, v, d["g"], d["beta"], d["h0"], cu, None, o, hT, ws)
+        else:
+            gdn.gdn_chunk_fwd_timed(cfg, q, k, v, d["g"], d["beta"], d["h0"], cu, None, o, hT, ws,
+                                    evs[:6])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-              for _ in range(args.steps)]
+    events = [hip.create(8 if has_front else 6) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
+    for s_ in range(args.steps):
+        step(events[s_])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    per_stage_ms = {name: statistics.fmean(ev[i].elapsed_time(ev[i + 1]) for ev in events)
-                    for i, name in enumerate(stages)}
+    pair = {"index": (0, 1), "intra": (2, 3), "inter": (4, 5), "front": (6, 7)}
+    per_stage_ms = {name: statistics.fmean(hip.ms(ev[pair[name][0]], ev[pair[name][1]])
+                                           for ev in events)
+                    for name in stages}
+    hip.close()
     chunks = int(sum(-(-int(x) // 64) for x in np.diff(wl.cu_seqlens)))
     work = algorithmic_work(wl, chunks, 4 if qkv_dtype == torch.float32 else 2)
     ms_per_step = elapsed * 1e3 / args.steps

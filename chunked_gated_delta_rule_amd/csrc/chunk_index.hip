@@ -62,10 +62,10 @@ __global__ __launch_bounds__(kIndexThreads) void chunk_index_kernel(const int32_
 }  // namespace
 
 hipError_t launch_chunk_index(const int32_t *cu_seqlens, int32_t n_max, int32_t nt_max,
-                              int32_t *table, hipStream_t stream) {
+                              int32_t *table, hipStream_t stream, KernelEvents ev) {
   if (n_max > kMaxSeqs) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(kIndexThreads), 0, stream, cu_seqlens,
-                     n_max, nt_max, table);
+  hipExtLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(kIndexThreads), 0, stream, ev.start,
+                        ev.stop, 0, cu_seqlens, n_max, nt_max, table);
   return hipGetLastError();
 }
 

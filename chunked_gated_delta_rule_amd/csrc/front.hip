@@ -99,14 +99,15 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
 
 hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t t_max, int32_t h,
-                        int32_t hv, float *q, float *k, float *v, hipStream_t stream) {
+                        int32_t hv, float *q, float *k, float *v, hipStream_t stream,
+                        KernelEvents ev) {
   if (d_conv < 1 || d_conv > kMaxTaps) return hipErrorInvalidValue;
   const int channels = (2 * h + hv) * kD;
   const dim3 grid((channels / 8 + kThreads - 1) / kThreads, (t_max + kTokens - 1) / kTokens);
   if (grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL(front_kernel, grid, dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t *>(qkv), static_cast<const uint16_t *>(conv_w),
-                     d_conv, cu_seqlens, n_max, t_max, h, hv, q, k, v);
+  hipExtLaunchKernelGGL(front_kernel, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
+                        static_cast<const uint16_t *>(qkv), static_cast<const uint16_t *>(conv_w),
+                        d_conv, cu_seqlens, n_max, t_max, h, hv, q, k, v);
   return hipGetLastError();
 }
 

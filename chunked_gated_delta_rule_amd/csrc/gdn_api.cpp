@@ -88,6 +88,57 @@ gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HI
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Shared bodies of the plain and the timed entry points.
+gdn_status front_impl(const gdn_config *cfg, const void *qkv, const void *conv_w, int32_t d_conv,
+                      const int32_t *cu_seqlens, float *q, float *k, float *v, void *stream,
+                      gdn::KernelEvents ev) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!qkv || !conv_w || !cu_seqlens || !q || !k || !v) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(qkv) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      (reinterpret_cast<uintptr_t>(conv_w) & 1u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return GDN_ERR_INVALID_ARG;
+  if (d_conv < 1 || d_conv > 8) return GDN_ERR_UNSUPPORTED;
+  return from_hip(gdn::launch_front(qkv, conv_w, d_conv, cu_seqlens, cfg->n_max, cfg->t_max,
+                                    cfg->h, cfg->hv, q, k, v, as_stream(stream), ev));
+}
+
+gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, const void *v,
+                          const float *g, const float *beta, const float *h0,
+                          const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
+                          float *hT, void *workspace, size_t ws_bytes, void *stream,
+                          const gdn::KernelEvents (&ev)[3]) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+  const gdn_workspace_layout_t l = layout_of(cfg);
+  const gdn_status ws = check_workspace(l, workspace, ws_bytes);
+  if (ws != GDN_OK) return ws;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) ||
+      (chunk_indices && !aligned16(chunk_indices)) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return GDN_ERR_INVALID_ARG;
+  hipStream_t s = as_stream(stream);
+  if (!chunk_indices) {
+    int32_t *table = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + l.table);
+    const hipError_t e =
+        gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), table, s, ev[0]);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    chunk_indices = table;
+  }
+  const gdn::StageBuffers b = stage_buffers(l, workspace);
+  if (cfg->t_max > 0) {
+    const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
+                                           chunk_indices, nt_max_of(cfg), cfg->h, cfg->hv,
+                                           cfg->t_max, scale_of(cfg), b, s, ev[1]);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+  }
+  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, b, h0, cu_seqlens, cfg->n_max,
+                                    cfg->h, cfg->hv, cfg->t_max, nt_max_of(cfg),
+                                    static_cast<float *>(o), hT, s, ev[2]));
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,15 +178,16 @@ gdn_status gdn_build_chunk_indices(const gdn_config *cfg, const int32_t *cu_seql
 gdn_status gdn_front_conv_silu_l2(const gdn_config *cfg, const void *qkv, const void *conv_w,
                                   int32_t d_conv, const int32_t *cu_seqlens, float *q, float *k,
                                   float *v, void *stream) {
-  const gdn_status st = check_config(cfg);
-  if (st != GDN_OK) return st;
-  if (!qkv || !conv_w || !cu_seqlens || !q || !k || !v) return GDN_ERR_INVALID_ARG;
-  if (!aligned16(qkv) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
-      (reinterpret_cast<uintptr_t>(conv_w) & 1u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
-    return GDN_ERR_INVALID_ARG;
-  if (d_conv < 1 || d_conv > 8) return GDN_ERR_UNSUPPORTED;
-  return from_hip(gdn::launch_front(qkv, conv_w, d_conv, cu_seqlens, cfg->n_max, cfg->t_max,
-                                    cfg->h, cfg->hv, q, k, v, as_stream(stream)));
+  return front_impl(cfg, qkv, conv_w, d_conv, cu_seqlens, q, k, v, stream, {});
+}
+
+gdn_status gdn_front_conv_silu_l2_timed(const gdn_config *cfg, const void *qkv,
+                                        const void *conv_w, int32_t d_conv,
+                                        const int32_t *cu_seqlens, float *q, float *k, float *v,
+                                        void *stream, void *ev_start, void *ev_stop) {
+  if (!ev_start || !ev_stop) return GDN_ERR_INVALID_ARG;
+  return front_impl(cfg, qkv, conv_w, d_conv, cu_seqlens, q, k, v, stream,
+                    {static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)});
 }
 
 gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *q, const void *k, const void *v,
@@ -179,34 +231,24 @@ gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, co
                          const float *g, const float *beta, const float *h0,
                          const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
                          float *hT, void *workspace, size_t ws_bytes, void *stream) {
-  const gdn_status st = check_config(cfg);
-  if (st != GDN_OK) return st;
-  if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
-  const gdn_workspace_layout_t l = layout_of(cfg);
-  const gdn_status ws = check_workspace(l, workspace, ws_bytes);
-  if (ws != GDN_OK) return ws;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) ||
-      (chunk_indices && !aligned16(chunk_indices)) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
-      (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
-    return GDN_ERR_INVALID_ARG;
-  hipStream_t s = as_stream(stream);
-  if (!chunk_indices) {
-    int32_t *table = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + l.table);
-    const hipError_t e = gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), table, s);
-    if (e != hipSuccess) return GDN_ERR_HIP;
-    chunk_indices = table;
-  }
-  const gdn::StageBuffers b = stage_buffers(l, workspace);
-  if (cfg->t_max > 0) {
-    const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
-                                           chunk_indices, nt_max_of(cfg), cfg->h, cfg->hv,
-                                           cfg->t_max, scale_of(cfg), b, s);
-    if (e != hipSuccess) return GDN_ERR_HIP;
-  }
-  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, b, h0, cu_seqlens, cfg->n_max,
-                                    cfg->h, cfg->hv, cfg->t_max, nt_max_of(cfg),
-                                    static_cast<float *>(o), hT, s));
+  const gdn::KernelEvents none[3] = {};
+  return chunk_fwd_impl(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT, workspace,
+                        ws_bytes, stream, none);
+}
+
+gdn_status gdn_chunk_fwd_timed(const gdn_config *cfg, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *h0,
+                               const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
+                               float *hT, void *workspace, size_t ws_bytes, void *stream,
+                               void *const *events) {
+  if (!events) return GDN_ERR_INVALID_ARG;
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return GDN_ERR_INVALID_ARG;
+  gdn::KernelEvents ev[3];
+  for (int i = 0; i < 3; ++i)
+    ev[i] = {static_cast<hipEvent_t>(events[2 * i]), static_cast<hipEvent_t>(events[2 * i + 1])};
+  return chunk_fwd_impl(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT, workspace,
+                        ws_bytes, stream, ev);
 }
 
 const char *gdn_status_str(gdn_status status) {

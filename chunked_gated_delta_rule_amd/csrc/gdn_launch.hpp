@@ -1,8 +1,12 @@
 // Host-side launchers of the gfx950 GDN kernels (internal to the library).
 // Each enqueues work on `stream` and returns the launch status; none
 // allocates or synchronises. Shapes have already been validated by the C ABI.
+// Every launcher takes an optional pair of caller-created HIP events that the
+// dispatch itself records at its start and end (hipExtLaunchKernel), for
+// kernel timing without extra packets between launches.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,20 +23,28 @@ struct StageBuffers {
   float *gimg;    // [hv, nt_max, 192]
 };
 
+// Start / end events recorded by one dispatch (both may be null).
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_chunk_index(const int32_t *cu_seqlens, int32_t n_max, int32_t nt_max,
-                              int32_t *table, hipStream_t stream);
+                              int32_t *table, hipStream_t stream, KernelEvents ev = {});
 
 hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t t_max, int32_t h,
-                        int32_t hv, float *q, float *k, float *v, hipStream_t stream);
+                        int32_t hv, float *q, float *k, float *v, hipStream_t stream,
+                        KernelEvents ev = {});
 
 hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const int32_t *cu_seqlens, const int32_t *table,
                         int32_t nt_max, int32_t h, int32_t hv, int32_t t_max, float scale,
-                        const StageBuffers &out, hipStream_t stream);
+                        const StageBuffers &out, hipStream_t stream, KernelEvents ev = {});
 
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
-                        int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream);
+                        int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,
+                        KernelEvents ev = {});
 
 }  // namespace gdn

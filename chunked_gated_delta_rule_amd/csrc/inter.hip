@@ -348,13 +348,13 @@ __global__ __launch_bounds__(128) void inter_kernel(StageBuffers in, const float
 template <bool kF32In>
 hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
                         int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
-                        hipStream_t stream) {
+                        hipStream_t stream, KernelEvents ev) {
   const int members = (hv / h) * kSlices;
   const int groups = n_max * h;
   const int rounds = (groups + kXcds - 1) / kXcds;
   const dim3 grid(rounds * kXcds * members);
-  hipLaunchKernelGGL((inter_kernel<kF32In>), grid, dim3(128), 0, stream, in, h0, cu, o, hT, n_max,
-                     h, hv, t_max, nt);
+  hipExtLaunchKernelGGL((inter_kernel<kF32In>), grid, dim3(128), 0, stream, ev.start, ev.stop, 0,
+                        in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
   return hipGetLastError();
 }
 
@@ -362,9 +362,11 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
 
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
-                        int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream) {
-  return f32_in ? launch_waves<true>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream)
-                : launch_waves<false>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream);
+                        int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,
+                        KernelEvents ev) {
+  return f32_in
+             ? launch_waves<true>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream, ev)
+             : launch_waves<false>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream, ev);
 }
 
 }  // namespace gdn

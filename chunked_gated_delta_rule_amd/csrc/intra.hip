@@ -26,21 +26,26 @@
 // distinct for every chunk of a batch and below cdiv(t_max, 64) + n_max - 1.
 //
 // The exponent is always a masked difference gamma_r - gamma_i <= 0, never
-// e^gamma_r * e^-gamma_i, which would overflow under strong decay. Only lower
-// 16x16 blocks are computed (AMX page, section 8: triangular work stays
-// triangular).
+// e^gamma_r * e^-gamma_i, which would overflow under strong decay; it is taken
+// as exp2 of log2-scaled cumulative gates. Only lower 16x16 blocks are
+// computed (AMX page, section 8: triangular work stays triangular).
 //
 // gfx950 mapping: one 256-thread work-group per (chunk, h), four wave64s.
+//  * Every global operand of the work-group (K, q, and V, g, beta of the
+//    first value head) is requested at entry; V, g, beta of the next value
+//    head are requested while the current one is processed.
 //  * K K^T and K q^T on v_mfma_f32_16x16x32_bf16 (lower 16x16 blocks, kept in
 //    registers across the value heads). fp32 inputs are split x = hi + lo into
 //    two bf16 terms and the products take three MFMA terms.
-//  * The solve runs in fp32 in LDS: the four diagonal 16x16 blocks by column
-//    forward substitution, then the off-diagonal blocks in three wavefront
-//    steps T_ij = -T_ii (sum_k A_ik T_kj).
+//  * Each wave scans the chunk's gates itself (one token per lane) and keeps
+//    its own copy in LDS, so the gates need no work-group barrier.
+//  * The solve runs in fp32: the four diagonal 16x16 blocks by column forward
+//    substitution, then the off-diagonal blocks in two doubling levels on
+//    v_mfma_f32_16x16x4_f32 (T_10 = -T_11 A_10 T_00 and T_32 likewise, then
+//    the lower-left 32x32 block = -T_BB A_BA T_AA).
 //  * w and u are MFMA products of the transposed K (V) tile with the scaled
-//    T; the scaled T is split into hi + lo bf16 so w/u carry ~16 bits of T.
-//  * A tile of K (V) is read once from HBM and written to LDS both row-major
-//    (for K K^T) and transposed (for the products that contract over tokens).
+//    T; each lane scales and splits its own T fragment into hi + lo bf16 in
+//    registers, so w and u are formed in one pass with no staging buffer.
 // Rows of a partial last chunk are zero-filled, so they add nothing; w and q16
 // are written for valid rows only, the per-chunk blocks in full (zeros past
 // the end).
@@ -53,7 +58,7 @@ namespace {
 
 constexpr int kLdRow = kD + 8;   // bf16 row-major tile [64][136]
 constexpr int kLdCol = kC + 8;   // bf16 transposed tile [128][72]
-constexpr int kLdA = kC + 8;     // fp32 A [64][72] (also hosts the split T)
+constexpr int kLdA = kC + 8;     // fp32 A [64][72]
 constexpr int kLdT = kC + 4;     // fp32 T [64][68]
 constexpr int kLdX = 16 + 4;     // fp32 per-wave 16x16 scratch
 
@@ -64,12 +69,15 @@ struct IntraSmem {
   static constexpr int kR1 = kTerms * 128 * kLdCol * 2;
   // region 2: K transposed (hi[, lo])
   static constexpr int kR2 = kTerms * 128 * kLdCol * 2;
-  // region 3: A (fp32) during the solve, then T-scaled hi/lo (bf16)
+  // regions 3 + 4: A (fp32) and T (fp32); q row-major (hi[, lo]) during set-up
   static constexpr int kR3 = 64 * kLdA * 4;
   static constexpr int kR4 = 64 * kLdT * 4;
   static constexpr int kR5 = 4 * 16 * kLdX * 4;
-  static constexpr int kBytes = kR1 + kR2 + kR3 + kR4 + kR5 + 3 * 64 * 4;
+  // per wave: log2-scaled gamma, beta, beta e^gamma (64 floats each)
+  static constexpr int kGates = 4 * 3 * 64 * 4;
+  static constexpr int kBytes = kR1 + kR2 + kR3 + kR4 + kR5 + kGates;
   static_assert(kTerms * 64 * kLdRow * 2 <= kR1, "row tile must fit region 1");
+  static_assert(kTerms * 64 * kLdRow * 2 <= kR3 + kR4, "q tile must fit regions 3-4");
 };
 
 // Load 4 rows x 8 columns of a [rows, heads, 128] tile starting at token row
@@ -86,14 +94,7 @@ __device__ __forceinline__ void load_rows4x8(const void *base, int64_t row_strid
         const f32x4 a = reinterpret_cast<const f32x4 *>(p)[0];
         const f32x4 b = reinterpret_cast<const f32x4 *>(p)[1];
         const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __bf16 h0, l0, h1, l1;
-          split_bf16(x[2 * i], h0, l0);
-          split_bf16(x[2 * i + 1], h1, l1);
-          hi[rr][i] = pack2(h0, h1);
-          lo[rr][i] = pack2(l0, l1);
-        }
+        split8_words(x, hi[rr], lo[rr]);
       } else {
         const uint16_t *p = static_cast<const uint16_t *>(base) + (int64_t)r * row_stride + col;
         hi[rr] = *reinterpret_cast<const u32x4 *>(p);
@@ -125,6 +126,35 @@ __device__ __forceinline__ void store_col4x8(__bf16 *dst, int row0, int col, con
 __device__ __forceinline__ int pair_q(int pi) { return pi == 3 || pi == 5 ? 1 : 0; }
 __device__ __forceinline__ int pair_r(int pi) { return pi < 2 ? pi : 2 + ((pi - 2) >> 1); }
 
+// acc += X Y for 16 x 16 fp32 blocks in LDS (row strides ldx, ldy) on the
+// fp32 MFMA. Step s contracts k = 4 (lane >> 4) + s: lane l holds X row
+// (l & 15) and Y column (l & 15), so one 16-byte read gives its X values for
+// all four steps. Result: lane (g, c) holds rows 4 g .. 4 g + 3 of column c.
+__device__ __forceinline__ f32x4 mm16(const float *x, int ldx, const float *y, int ldy, int lane,
+                                      f32x4 acc) {
+  const int r = lane & 15, g = lane >> 4;
+  const f32x4 xa = *reinterpret_cast<const f32x4 *>(x + r * ldx + 4 * g);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], y[(4 * g + s) * ldy + r], acc, 0, 0, 0);
+  return acc;
+}
+
+// Store an accumulator (lane (g, c): rows 4 g + i of column c) to a 16 x 16
+// fp32 block in LDS, multiplied by `sign`.
+__device__ __forceinline__ void put16(float *dst, int ld, const f32x4 &acc, float sign, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[(4 * g + i) * ld + c] = sign * acc[i];
+}
+
+// Orders this wave's LDS writes before its own later LDS reads by other lanes
+// (a wave's LDS operations complete in order; this keeps the compiler from
+// moving the reads up).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 template <bool kF32In>
 __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     const void *__restrict__ qin, const void *__restrict__ kin, const void *__restrict__ vin,
@@ -136,18 +166,16 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   __bf16 *r1 = reinterpret_cast<__bf16 *>(smem);
   __bf16 *kcol = reinterpret_cast<__bf16 *>(smem + Smem::kR1);
   float *amat = reinterpret_cast<float *>(smem + Smem::kR1 + Smem::kR2);
-  __bf16 *ts_hi = reinterpret_cast<__bf16 *>(amat);
-  __bf16 *ts_lo = ts_hi + 64 * kLdCol;
-  __bf16 *rq = ts_hi;  // q row-major (hi[, lo]) while the products with K run: regions 3-4
+  __bf16 *rq = reinterpret_cast<__bf16 *>(amat);  // q row-major during set-up (regions 3-4)
   float *tmat = reinterpret_cast<float *>(smem + Smem::kR1 + Smem::kR2 + Smem::kR3);
   float *xs = reinterpret_cast<float *>(smem + Smem::kR1 + Smem::kR2 + Smem::kR3 + Smem::kR4);
-  float *gam = xs + 4 * 16 * kLdX;
-  float *bet = gam + 64;
-  float *scl = bet + 64;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
+  float *gsh = xs + 4 * 16 * kLdX + wv * 3 * 64;  // this wave's gate copies
+  float *bsh = gsh + 64;
+  float *swsh = bsh + 64;
   const int2 ent = reinterpret_cast<const int2 *>(table)[blockIdx.x];
   if (ent.x < 0) return;  // sentinel slot
   const int h = blockIdx.y;
@@ -157,47 +185,55 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   const int L = min(kC, cu[ent.x + 1] - t0);
   const int slot = (t0 >> 6) + ent.x;
   constexpr int kNK = kF32In ? 32 : 16;
+  constexpr int kEl = kF32In ? 4 : 2;
+
+  const int lrow = 4 * (tid >> 4);  // this thread's 4 rows and 8 columns of a tile
+  const int lcol = 8 * (tid & 15);
+
+  // ---- requests: K, q, then V / g / beta of the first value head ----------
+  u32x4 khi[4], klo[4], qhi[4], qlo[4], vhi[4], vlo[4];
+  load_rows4x8<kF32In>(static_cast<const char *>(kin) + ((int64_t)t0 * H + h) * kD * kEl,
+                       (int64_t)H * kD, lrow, L, lcol, khi, klo);
+  load_rows4x8<kF32In>(static_cast<const char *>(qin) + ((int64_t)t0 * H + h) * kD * kEl,
+                       (int64_t)H * kD, lrow, L, lcol, qhi, qlo);
+  auto load_v = [&](int hv) __attribute__((always_inline)) {
+    load_rows4x8<kF32In>(static_cast<const char *>(vin) + ((int64_t)t0 * Hv + hv) * kD * kEl,
+                         (int64_t)Hv * kD, lrow, L, lcol, vhi, vlo);
+  };
+  const bool tok_ok = lane < L;
+  auto load_gate = [&](const float *p, int hv) __attribute__((always_inline)) {
+    return tok_ok ? p[(int64_t)(t0 + lane) * Hv + hv] : 0.f;
+  };
+  load_v(h * HG);
+  float g_next = load_gate(g, h * HG);
+  float b_next = load_gate(beta, h * HG);
 
   // ---- K tile -> LDS (row-major in region 1, transposed in region 2) ------
-  const int lrow = 4 * (tid >> 4);  // this thread's 4 rows and 8 columns
-  const int lcol = 8 * (tid & 15);
-  {
-    u32x4 khi[4], klo[4];
-    load_rows4x8<kF32In>(static_cast<const char *>(kin) +
-                             ((int64_t)t0 * H + h) * kD * (kF32In ? 4 : 2),
-                         (int64_t)H * kD, lrow, L, lcol, khi, klo);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      *reinterpret_cast<u32x4 *>(r1 + (lrow + rr) * kLdRow + lcol) = khi[rr];
-      if constexpr (kF32In)
-        *reinterpret_cast<u32x4 *>(r1 + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = klo[rr];
-    }
-    store_col4x8(kcol, lrow, lcol, khi);
-    if constexpr (kF32In) store_col4x8(kcol + 128 * kLdCol, lrow, lcol, klo);
+  for (int rr = 0; rr < 4; ++rr) {
+    *reinterpret_cast<u32x4 *>(r1 + (lrow + rr) * kLdRow + lcol) = khi[rr];
+    if constexpr (kF32In)
+      *reinterpret_cast<u32x4 *>(r1 + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = klo[rr];
   }
+  store_col4x8(kcol, lrow, lcol, khi);
+  if constexpr (kF32In) store_col4x8(kcol + 128 * kLdCol, lrow, lcol, klo);
   // ---- q tile -> LDS row-major, and the fp16 copy q16 ---------------------
-  {
-    u32x4 qhi[4], qlo[4];
-    load_rows4x8<kF32In>(static_cast<const char *>(qin) +
-                             ((int64_t)t0 * H + h) * kD * (kF32In ? 4 : 2),
-                         (int64_t)H * kD, lrow, L, lcol, qhi, qlo);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      *reinterpret_cast<u32x4 *>(rq + (lrow + rr) * kLdRow + lcol) = qhi[rr];
-      if constexpr (kF32In)
-        *reinterpret_cast<u32x4 *>(rq + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = qlo[rr];
-      if (lrow + rr < L) {
-        float f[8], fl[8];
-        unpack8(qhi[rr], f);
-        unpack8(qlo[rr], fl);
-        uint32_t hh[4];
+  for (int rr = 0; rr < 4; ++rr) {
+    *reinterpret_cast<u32x4 *>(rq + (lrow + rr) * kLdRow + lcol) = qhi[rr];
+    if constexpr (kF32In)
+      *reinterpret_cast<u32x4 *>(rq + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = qlo[rr];
+    if (lrow + rr < L) {
+      float f[8], fl[8];
+      unpack8(qhi[rr], f);
+      unpack8(qlo[rr], fl);
+      uint32_t hh[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hh[i] = pack_f16(f[2 * i] + fl[2 * i], f[2 * i + 1] + fl[2 * i + 1]);
-        _Float16 *dst = out.q16 + ((int64_t)(t0 + lrow + rr) * H + h) * kD + 32 * (lcol >> 5);
-        const int m = (lcol & 31) >> 2;  // first group of four columns
-        *reinterpret_cast<u32x2 *>(dst + perm4(m)) = u32x2{hh[0], hh[1]};
-        *reinterpret_cast<u32x2 *>(dst + perm4(m + 1)) = u32x2{hh[2], hh[3]};
-      }
+      for (int i = 0; i < 4; ++i) hh[i] = pack_f16(f[2 * i] + fl[2 * i], f[2 * i + 1] + fl[2 * i + 1]);
+      _Float16 *dst = out.q16 + ((int64_t)(t0 + lrow + rr) * H + h) * kD + 32 * (lcol >> 5);
+      const int m = (lcol & 31) >> 2;  // first group of four columns
+      *reinterpret_cast<u32x2 *>(dst + perm4(m)) = u32x2{hh[0], hh[1]};
+      *reinterpret_cast<u32x2 *>(dst + perm4(m + 1)) = u32x2{hh[2], hh[3]};
     }
   }
   __syncthreads();
@@ -278,27 +314,45 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   }
   __syncthreads();  // regions 1, 3 and 4 are free from here on
 
+  // T's upper blocks (0,1) and (2,3) are read as zeros by the w/u products
+  // (no other step writes them).
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int e = tid + kThreads * m;  // 0..511
+    const int blk = e >> 8, r = (e >> 4) & 15, c = e & 15;
+    tmat[(32 * blk + r) * kLdT + 32 * blk + 16 + c] = 0.f;
+  }
+
   for (int gi = 0; gi < HG; ++gi) {
     const int hv = h * HG + gi;
-    // V tile prefetch (stored after A is formed)
-    u32x4 vhi[4], vlo[4];
-    load_rows4x8<kF32In>(static_cast<const char *>(vin) +
-                             ((int64_t)t0 * Hv + hv) * kD * (kF32In ? 4 : 2),
-                         (int64_t)Hv * kD, lrow, L, lcol, vhi, vlo);
-    if (wv == 0) {
-      const bool ok = lane < L;
-      const float gv = ok ? g[(int64_t)(t0 + lane) * Hv + hv] : 0.f;
-      const float bv = ok ? beta[(int64_t)(t0 + lane) * Hv + hv] : 0.f;
-      const float gc = wave_inclusive_scan(gv, lane);
-      gam[lane] = gc;
-      bet[lane] = bv;
-      const float gl = __shfl(gc, L - 1, 64);  // gamma of the last valid token
-      float *gd = out.gimg + ((int64_t)hv * nt + slot) * kGateStride;
-      gd[lane] = ok ? expf(gl - gc) : 0.f;
-      gd[64 + lane] = ok ? scale * expf(gc) : 0.f;
-      gd[128 + lane] = lane == 0 ? expf(gl) : 0.f;
+    // ---- this value head's operands, next value head's requests -----------
+    u32x4 vh[4], vl[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      vh[rr] = vhi[rr];
+      vl[rr] = vlo[rr];
     }
-    __syncthreads();
+    const float gv = g_next, bv = b_next;
+    if (gi + 1 < HG) {
+      load_v(hv + 1);
+      g_next = load_gate(g, hv + 1);
+      b_next = load_gate(beta, hv + 1);
+    }
+
+    // ---- gates: each wave scans its own copy (lane = token) ---------------
+    const float gam2 = wave_inclusive_scan(gv * kLog2e, lane);  // log2-scaled gamma
+    const float gl2 = __shfl(gam2, L - 1, 64);                   // last valid token
+    const float eg = fast_exp2(gam2);
+    gsh[lane] = gam2;
+    bsh[lane] = bv;
+    swsh[lane] = bv * eg;
+    if (wv == 0) {
+      float *gd = out.gimg + ((int64_t)hv * nt + slot) * kGateStride;
+      gd[lane] = tok_ok ? fast_exp2(gl2 - gam2) : 0.f;
+      gd[64 + lane] = tok_ok ? scale * eg : 0.f;
+      gd[128 + lane] = lane == 0 ? fast_exp2(gl2) : 0.f;
+    }
+    wave_lds_sync();
 
     // ---- P = scale * tril(q k^T * Gamma), this wave's pairs, as hi + lo bf16
     // pair lane (g, c): tile (2q, R) rows 4 g + i then tile (2q + 1, R).
@@ -307,13 +361,16 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
       if (n2 < npair) {
         const int pi = pair0 + n2;
         const int r = 16 * pair_r(pi) + (lane & 15);
+        const float gr = gsh[r];
         float x[8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
+          const int j0 = 32 * pair_q(pi) + 16 * hf + 4 * (lane >> 4);
+          const f32x4 gj = *reinterpret_cast<const f32x4 *>(gsh + j0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int j = 32 * pair_q(pi) + 16 * hf + 4 * (lane >> 4) + i;
-            x[4 * hf + i] = (j <= r && r < L) ? scale * pacc[2 * n2 + hf][i] * expf(gam[r] - gam[j]) : 0.f;
+            const int j = j0 + i;
+            x[4 * hf + i] = (j <= r && r < L) ? scale * pacc[2 * n2 + hf][i] * fast_exp2(gr - gj[i]) : 0.f;
           }
         }
         u32x4 hi, lo;
@@ -329,19 +386,22 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     for (int n = 0; n < 3; ++n) {
       if (n < nblk) {
         const int j = 16 * gbj[n] + (lane & 15);
+        const int r0 = 16 * gbi[n] + 4 * (lane >> 4);
+        const float gj = gsh[j];
+        const f32x4 gr = *reinterpret_cast<const f32x4 *>(gsh + r0);
+        const f32x4 br = *reinterpret_cast<const f32x4 *>(bsh + r0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * gbi[n] + 4 * (lane >> 4) + i;
-          const float a = j < r ? bet[r] * gacc[n][i] * expf(gam[r] - gam[j]) : 0.f;
-          amat[r * kLdA + j] = a;
+          const int r = r0 + i;
+          amat[r * kLdA + j] = j < r ? br[i] * gacc[n][i] * fast_exp2(gr[i] - gj) : 0.f;
         }
       }
     }
-    store_col4x8(r1, lrow, lcol, vhi);
-    if constexpr (kF32In) store_col4x8(r1 + 128 * kLdCol, lrow, lcol, vlo);
+    store_col4x8(r1, lrow, lcol, vh);
+    if constexpr (kF32In) store_col4x8(r1 + 128 * kLdCol, lrow, lcol, vl);
     __syncthreads();
 
-    // ---- solve: diagonal blocks by column forward substitution ------------
+    // ---- solve 1: diagonal blocks by column forward substitution ----------
     if (lane < 16) {
       const int c = lane;
       const float *ab = amat + (16 * wv) * kLdA + 16 * wv;
@@ -354,111 +414,111 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
         tc[r] = r == c ? 1.f : (r < c ? 0.f : -x);
         tmat[(16 * wv + r) * kLdT + 16 * wv + c] = tc[r];
       }
-    } else if (lane < 32 && (wv == 0 || wv == 2)) {
-      // zero the upper blocks (0,1) and (2,3): the w/u products read them
-      const int c = 16 * (wv + 1) + lane - 16;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tmat[(16 * wv + r) * kLdT + c] = 0.f;
     }
     __syncthreads();
-    // ---- solve: off-diagonal blocks, one block diagonal per step ----------
-    {
-      const int r = lane >> 2;
-      const int cq = 4 * (lane & 3);
-      float *xw = xs + wv * 16 * kLdX;
-      for (int d = 1; d < 4; ++d) {
-        const bool act = wv < 4 - d;
-        const int bi = wv + d, bj = wv;
-        if (act) {
-          f32x4 x = zero4();
-          for (int kb = bj; kb < bi; ++kb) {
-            const float *arow = amat + (16 * bi + r) * kLdA + 16 * kb;
-            const float *tcol = tmat + (16 * kb) * kLdT + 16 * bj + cq;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-              const float a = arow[m];
-              const f32x4 t = *reinterpret_cast<const f32x4 *>(tcol + m * kLdT);
-              x += a * t;
-            }
-          }
-          *reinterpret_cast<f32x4 *>(xw + r * kLdX + cq) = x;
-        }
-        __syncthreads();
-        if (act) {
-          f32x4 y = zero4();
-          const float *trow = tmat + (16 * bi + r) * kLdT + 16 * bi;
-#pragma unroll
-          for (int m = 0; m < 16; ++m) y += trow[m] * *reinterpret_cast<const f32x4 *>(xw + m * kLdX + cq);
-          *reinterpret_cast<f32x4 *>(tmat + (16 * bi + r) * kLdT + 16 * bj + cq) = -y;
-        }
-        __syncthreads();
-      }
+    // ---- solve 2: T_10 = -T_11 (A_10 T_00), T_32 = -T_33 (A_32 T_22) -------
+    float *xw = xs + wv * 16 * kLdX;
+    if (wv < 2) {
+      const int b = 2 * wv;  // diagonal pair (b, b + 1)
+      const float *a_lo = amat + (16 * (b + 1)) * kLdA + 16 * b;
+      const float *t_bb = tmat + (16 * b) * kLdT + 16 * b;
+      const float *t_nn = tmat + (16 * (b + 1)) * kLdT + 16 * (b + 1);
+      put16(xw, kLdX, mm16(a_lo, kLdA, t_bb, kLdT, lane, zero4()), 1.f, lane);
+      wave_lds_sync();
+      put16(tmat + (16 * (b + 1)) * kLdT + 16 * b, kLdT, mm16(t_nn, kLdT, xw, kLdX, lane, zero4()),
+            -1.f, lane);
     }
+    __syncthreads();
+    // ---- solve 3: lower-left 32x32 block, X = A_BA T_AA ... ----------------
+    const int bi = 2 + (wv >> 1), bj = wv & 1;
+    {
+      const float *a_i0 = amat + (16 * bi) * kLdA;
+      const float *a_i1 = a_i0 + 16;
+      f32x4 x = zero4();
+      if (bj == 0) {
+        x = mm16(a_i0, kLdA, tmat, kLdT, lane, x);                       // A_i0 T_00
+        x = mm16(a_i1, kLdA, tmat + 16 * kLdT, kLdT, lane, x);           // A_i1 T_10
+      } else {
+        x = mm16(a_i1, kLdA, tmat + 16 * kLdT + 16, kLdT, lane, x);      // A_i1 T_11
+      }
+      put16(xw, kLdX, x, 1.f, lane);
+    }
+    __syncthreads();
+    // ---- ... then T_BA = -T_BB X ------------------------------------------
+    {
+      const float *t22 = tmat + 32 * kLdT + 32;
+      const float *t32 = tmat + 48 * kLdT + 32;
+      const float *t33 = tmat + 48 * kLdT + 48;
+      f32x4 y;
+      if (bi == 2) {
+        y = mm16(t22, kLdT, xw, kLdX, lane, zero4());
+      } else {
+        y = mm16(t32, kLdT, xs + (wv - 2) * 16 * kLdX, kLdX, lane, zero4());
+        y = mm16(t33, kLdT, xw, kLdX, lane, y);
+      }
+      put16(tmat + (16 * bi) * kLdT + 16 * bj, kLdT, y, -1.f, lane);
+    }
+    __syncthreads();
 
-    // ---- w then u: scaled T split to hi/lo bf16, MFMA with K^T / V^T -------
-    for (int pass = 0; pass < 2; ++pass) {
-      if (tid < 64) scl[tid] = pass == 0 ? bet[tid] * expf(gam[tid]) : bet[tid];
-      __syncthreads();
-      {
-        const int r = tid >> 2;
-        const int c0 = 16 * (tid & 3);
+    // ---- w and u in one pass: T diag(beta e^gamma) and T diag(beta), split
+    // hi + lo per lane, against K^T / V^T. Tiles (d-block db, token block rb):
+    // w as W^T = K^T (T s)^T (lane holds four d of one token), u as
+    // U = (T s) V (lane holds four tokens of one d).
 #pragma unroll
-        for (int cc = 0; cc < 16; cc += 2) {
-          const int c = c0 + cc;
-          const float x0 = c <= r ? tmat[r * kLdT + c] * scl[c] : 0.f;
-          const float x1 = c + 1 <= r ? tmat[r * kLdT + c + 1] * scl[c + 1] : 0.f;
-          __bf16 h0, l0, h1, l1;
-          split_bf16(x0, h0, l0);
-          split_bf16(x1, h1, l1);
-          *reinterpret_cast<uint32_t *>(ts_hi + r * kLdCol + c) = pack2(h0, h1);
-          *reinterpret_cast<uint32_t *>(ts_lo + r * kLdCol + c) = pack2(l0, l1);
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 wacc[2] = {zero4(), zero4()}, uacc[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks <= (rb >> 1); ++ks) {
+        const int j0 = 32 * ks + 8 * (lane >> 4);
+        const float *trow = tmat + (16 * rb + (lane & 15)) * kLdT + j0;
+        const f32x4 t_a = *reinterpret_cast<const f32x4 *>(trow);
+        const f32x4 t_b = *reinterpret_cast<const f32x4 *>(trow + 4);
+        const f32x4 sw_a = *reinterpret_cast<const f32x4 *>(swsh + j0);
+        const f32x4 sw_b = *reinterpret_cast<const f32x4 *>(swsh + j0 + 4);
+        const f32x4 su_a = *reinterpret_cast<const f32x4 *>(bsh + j0);
+        const f32x4 su_b = *reinterpret_cast<const f32x4 *>(bsh + j0 + 4);
+        const float xw8[8] = {t_a[0] * sw_a[0], t_a[1] * sw_a[1], t_a[2] * sw_a[2], t_a[3] * sw_a[3],
+                              t_b[0] * sw_b[0], t_b[1] * sw_b[1], t_b[2] * sw_b[2], t_b[3] * sw_b[3]};
+        const float xu8[8] = {t_a[0] * su_a[0], t_a[1] * su_a[1], t_a[2] * su_a[2], t_a[3] * su_a[3],
+                              t_b[0] * su_b[0], t_b[1] * su_b[1], t_b[2] * su_b[2], t_b[3] * su_b[3]};
+        u32x4 wh, wl, uh, ul;
+        split8_words(xw8, wh, wl);
+        split8_words(xu8, uh, ul);
+#pragma unroll
+        for (int db2 = 0; db2 < 2; ++db2) {
+          const int db = 2 * wv + db2;
+          const bf16x8 ka = frag_rows(kcol, kLdCol, 16 * db, 32 * ks, lane);
+          const bf16x8 vb = frag_rows(r1, kLdCol, 16 * db, 32 * ks, lane);
+          f32x4 aw = wacc[db2], au = uacc[db2];
+          aw = mfma(ka, as_bf16x8(wh), aw);
+          aw = mfma(ka, as_bf16x8(wl), aw);
+          au = mfma(as_bf16x8(uh), vb, au);
+          au = mfma(as_bf16x8(ul), vb, au);
+          if constexpr (kF32In) {
+            aw = mfma(frag_rows(kcol + 128 * kLdCol, kLdCol, 16 * db, 32 * ks, lane), as_bf16x8(wh), aw);
+            au = mfma(as_bf16x8(uh), frag_rows(r1 + 128 * kLdCol, kLdCol, 16 * db, 32 * ks, lane), au);
+          }
+          wacc[db2] = aw;
+          uacc[db2] = au;
         }
       }
-      __syncthreads();
-      const __bf16 *src = pass == 0 ? kcol : r1;  // K^T or V^T, [128][72]
-      // tiles (d-block db, token block rb): w as W^T = K^T (T s)^T (lane holds
-      // four d of one token), u as U = (T s) V (lane holds four tokens of one d)
 #pragma unroll
       for (int db2 = 0; db2 < 2; ++db2) {
         const int db = 2 * wv + db2;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          f32x4 acc = zero4();
-          const int nks = (rb >> 1) + 1;
-          for (int ks = 0; ks < nks; ++ks) {
-            const bf16x8 a = frag_rows(src, kLdCol, 16 * db, 32 * ks, lane);
-            const bf16x8 bh = frag_rows(ts_hi, kLdCol, 16 * rb, 32 * ks, lane);
-            const bf16x8 bl = frag_rows(ts_lo, kLdCol, 16 * rb, 32 * ks, lane);
-            if (pass == 0) {
-              acc = mfma(a, bh, acc);
-              acc = mfma(a, bl, acc);
-              if constexpr (kF32In)
-                acc = mfma(frag_rows(src + 128 * kLdCol, kLdCol, 16 * db, 32 * ks, lane), bh, acc);
-            } else {
-              acc = mfma(bh, a, acc);
-              acc = mfma(bl, a, acc);
-              if constexpr (kF32In)
-                acc = mfma(bh, frag_rows(src + 128 * kLdCol, kLdCol, 16 * db, 32 * ks, lane), acc);
-            }
-          }
-          if (pass == 0) {
-            // lane holds w[r = 16 rb + (lane & 15)][d = 16 db + 4 (lane >> 4) + i]
-            const int r = 16 * rb + (lane & 15);
-            if (r < L) {
-              _Float16 *dst = out.w16 + ((int64_t)hv * t_max + t0 + r) * kD + 32 * (db >> 1) +
-                              perm4(4 * (db & 1) + (lane >> 4));
-              *reinterpret_cast<u32x2 *>(dst) =
-                  u32x2{pack_f16(-acc[0], -acc[1]), pack_f16(-acc[2], -acc[3])};
-            }
-          } else {
-            // lane holds u[r = 16 rb + 4 (lane >> 4) + i][d = 16 db + (lane & 15)]
-            float *dst = out.uimg + (((((int64_t)hv * nt + slot) * 8 + db) * 4 + rb) * 64 + lane) * 4;
-            *reinterpret_cast<f32x4 *>(dst) = acc;
-          }
+        // w: lane holds w[r = 16 rb + (lane & 15)][d = 16 db + 4 (lane >> 4) + i]
+        const f32x4 aw = wacc[db2];
+        const int r = 16 * rb + (lane & 15);
+        if (r < L) {
+          _Float16 *dst = out.w16 + ((int64_t)hv * t_max + t0 + r) * kD + 32 * (db >> 1) +
+                          perm4(4 * (db & 1) + (lane >> 4));
+          *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_f16(-aw[0], -aw[1]), pack_f16(-aw[2], -aw[3])};
         }
+        // u: lane holds u[r = 16 rb + 4 (lane >> 4) + i][d = 16 db + (lane & 15)]
+        float *dst = out.uimg + (((((int64_t)hv * nt + slot) * 8 + db) * 4 + rb) * 64 + lane) * 4;
+        *reinterpret_cast<f32x4 *>(dst) = uacc[db2];
       }
-      __syncthreads();
     }
+    __syncthreads();  // region 1 (V^T), A, T and the gate copies are rewritten next
   }
 }
 
@@ -467,15 +527,15 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
 hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const int32_t *cu_seqlens, const int32_t *table,
                         int32_t nt_max, int32_t h, int32_t hv, int32_t t_max, float scale,
-                        const StageBuffers &out, hipStream_t stream) {
+                        const StageBuffers &out, hipStream_t stream, KernelEvents ev) {
   if (nt_max <= 0) return hipSuccess;
   const dim3 grid(nt_max, h);
   if (f32_in) {
-    hipLaunchKernelGGL(intra_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v, g, beta,
-                       cu_seqlens, table, out, h, hv, t_max, nt_max, scale);
+    hipExtLaunchKernelGGL(intra_kernel<true>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop,
+                          0, q, k, v, g, beta, cu_seqlens, table, out, h, hv, t_max, nt_max, scale);
   } else {
-    hipLaunchKernelGGL(intra_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v, g, beta,
-                       cu_seqlens, table, out, h, hv, t_max, nt_max, scale);
+    hipExtLaunchKernelGGL(intra_kernel<false>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop,
+                          0, q, k, v, g, beta, cu_seqlens, table, out, h, hv, t_max, nt_max, scale);
   }
   return hipGetLastError();
 }

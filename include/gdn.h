@@ -165,6 +165,27 @@ gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, co
                          const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
                          float *hT, void *workspace, size_t ws_bytes, void *stream);
 
+/* Timed variants, for measurement. They behave exactly like the entry point
+ * they extend, and in addition each kernel they launch records a pair of HIP
+ * events at its own start and end (the dispatch itself records them, so no
+ * packet is added between launches and the elapsed time between a pair is
+ * the kernel's execution time).
+ *   events (host array of 6 hipEvent_t passed as void*, each created by the
+ *          caller): [0], [1] around the chunk table (recorded only when
+ *          chunk_indices is NULL), [2], [3] around the intra stage, [4], [5]
+ *          around the inter stage.
+ *   ev_start, ev_stop: around the front kernel.
+ * A NULL event returns GDN_ERR_INVALID_ARG before any launch. */
+gdn_status gdn_chunk_fwd_timed(const gdn_config *cfg, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *h0,
+                               const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
+                               float *hT, void *workspace, size_t ws_bytes, void *stream,
+                               void *const *events);
+gdn_status gdn_front_conv_silu_l2_timed(const gdn_config *cfg, const void *qkv,
+                                        const void *conv_w, int32_t d_conv,
+                                        const int32_t *cu_seqlens, float *q, float *k, float *v,
+                                        void *stream, void *ev_start, void *ev_stop);
+
 /* Static string for a status code (never NULL). */
 const char *gdn_status_str(gdn_status status);
 

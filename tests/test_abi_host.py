@@ -143,3 +143,26 @@ def test_stage_entry_points_host_errors(lib):
     assert lib.gdn_front_conv_silu_l2(c, F, F, 9, F, F, F, F, None) == UNSUPPORTED
     assert lib.gdn_front_conv_silu_l2(c, F, F, 0, F, F, F, F, None) == UNSUPPORTED
     assert lib.gdn_front_conv_silu_l2(c, None, F, 4, F, F, F, F, None) == INVALID
+
+
+def test_timed_entry_points_host_errors(lib):
+    """The timed variants reject a missing event, and otherwise validate like
+    the entry points they extend, all before any launch."""
+    cfg = gdn.make_config(256, 2, 16, 32)
+    c = ctypes.byref(cfg)
+    F = FAKE
+    need = gdn.gdn_workspace_size(cfg)
+    vp6 = ctypes.c_void_p * 6
+
+    def timed(events, **over):
+        a = dict(q=F, o=F, ws=F, ws_bytes=need)
+        a.update(over)
+        return lib.gdn_chunk_fwd_timed(c, a["q"], F, F, F, F, None, F, None, a["o"], None, a["ws"],
+                                       a["ws_bytes"], None, events)
+
+    assert timed(None) == INVALID
+    assert timed(vp6(1, 2, 3, 4, 5, None)) == INVALID
+    assert timed(vp6(1, 2, 3, 4, 5, 6), q=None) == INVALID
+    assert timed(vp6(1, 2, 3, 4, 5, 6), ws_bytes=need - 1) == WORKSPACE
+    assert lib.gdn_front_conv_silu_l2_timed(c, F, F, 4, F, F, F, F, None, None, 8) == INVALID
+    assert lib.gdn_front_conv_silu_l2_timed(c, F, F, 9, F, F, F, F, None, 8, 8) == UNSUPPORTED
