@@ -50,8 +50,8 @@ gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   gdn_workspace_layout_t l;
   size_t at = 0;
   auto take = [&](size_t bytes) { const size_t here = at; at += align_up(bytes); return here; };
-  l.w16 = take(hv * t * kD * 2);
-  l.q16 = take(t * h * kD * 2);
+  l.w16 = take(hv * nt * 16 * 1024);
+  l.q16 = take(h * nt * 16 * 1024);
   l.kimg = take(h * nt * nk * 1024);
   l.uimg = take(hv * nt * kD * kChunk * 4);
   l.pimg = take(hv * nt * 12 * 1024);

@@ -144,11 +144,6 @@ __device__ __forceinline__ void split_pack4(const float (&x)[4], u32x2 &hi, u32x
   lo = u32x2{l0, l1};
 }
 
-// Column order inside each 32-column block of the fp16 w and q copies: the
-// four-column group m (columns 4m .. 4m + 3) starts at position perm4(m), so
-// MFMA lane group g reads columns {4g .. 4g + 3, 16 + 4g .. 16 + 4g + 3} as one
-// 16-byte word -- the rows a 16x16 accumulator pair hands to a lane.
-__host__ __device__ constexpr int perm4(int m) { return m < 4 ? 8 * m : 8 * (m - 4) + 4; }
 
 // Floats per (value head, chunk) in the gate block: e^{gamma_last - gamma_t}
 // [64], scale * e^{gamma_t} [64], e^{gamma_last} and zero padding [64].

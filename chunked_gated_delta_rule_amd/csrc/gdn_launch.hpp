@@ -15,8 +15,8 @@ namespace gdn {
 // Intermediates written by the intra stage and read by the inter stage (all
 // device memory inside the caller's workspace; layouts in intra.hip).
 struct StageBuffers {
-  _Float16 *w16;  // [hv, t_max, 128]
-  _Float16 *q16;  // [t_max, h, 128]
+  _Float16 *w16;  // [hv, nt_max, 16 fragments, 64 lanes, 8]
+  _Float16 *q16;  // [h, nt_max, 16 fragments, 64 lanes, 8]
   __bf16 *kimg;   // [h, nt_max, 16 or 32 fragments, 64 lanes, 8]
   float *uimg;    // [hv, nt_max, 8, 4, 64 lanes, 4]
   __bf16 *pimg;   // [hv, nt_max, 6 pairs, 2 terms, 64 lanes, 8]

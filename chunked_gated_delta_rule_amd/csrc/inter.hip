@@ -11,11 +11,11 @@
 //
 // The value columns of S are independent, so the state is blocked over Dv
 // (Alloy page, "How do you parallelize a recurrence for prefill?": the state
-// tile is blocked along the value dimension to fit on chip). Here one wave64
-// owns a 128 x 16 column slice of S for the whole sequence and keeps it in
-// registers, as eight 16 x 16 MFMA accumulators. Every product of the chunk
-// step is arranged so that its operands come either from those accumulators
-// directly or from fragments the intra stage stored in MFMA order:
+// tile is blocked along the value dimension to fit on chip). One work-group of
+// four wave64s owns a 128 x 16 column slice of S for the whole sequence. Every
+// product of the chunk step is arranged so that its operands come either from
+// MFMA accumulators directly or from fragments the intra stage stored in MFMA
+// order:
 //
 //   v'      = u + (-w) S          A = -w fragment, B = S (fp16)      C = v' tiles
 //   o^T     = S^T q^T             A = S (fp16),   B = q16 fragment   C = o^T tiles
@@ -26,24 +26,27 @@
 // column c; two accumulators stacked along the contraction give a lane exactly
 // the eight contraction values of an A (row c) or B (column c) fragment, with
 // the contraction order {4g + i, 16 + 4g + i}. The intra stage writes w, q16,
-// K^T and P in that order, so no value ever moves between lanes or through
-// LDS inside the recurrence, and the chunk step itself has no barrier.
+// K^T and P in that order, so no value moves between lanes inside a product.
 //
-// Each slice is worked by two waves of one work-group, on different SIMDs:
-//   chain wave : S -> fp16, v' = u + (-w) S, the decayed v' as hi + lo and the
-//                state update -- the work that lies on the chunk-to-chunk
-//                dependence chain;
-//   helper wave: y = S^T q^T, v' as hi + lo, P v' and the output, one chunk
-//                behind, from S (fp16) and v' that the chain wave leaves in a
-//                double-buffered LDS exchange (8 KB per chunk).
-// One barrier per chunk hands a chunk from the chain wave to the helper. A
-// single wave issues its MFMA and VALU work one after the other, so splitting
-// the chunk step over two SIMDs shortens the chain itself.
-// Every operand fragment is one coalesced 16-byte-per-lane load straight into
-// registers (rows past the sequence end read as zero). Each fragment array is
+// The four waves run on the four SIMDs of one CU:
+//   chain waves 0 and 1: wave X keeps key rows 64 X .. 64 X + 63 of the slice
+//       in registers (four 16 x 16 fp32 accumulators). Per chunk it forms its
+//       partial (-w) S over those rows (wave 0 starts from u), publishes the
+//       partial and its fp16 rows of S in LDS, and after the chunk's barrier
+//       adds the other wave's partial to get v', then applies the state update
+//       to its own rows. The chunk-to-chunk chain therefore runs half the
+//       products of the step on each of two SIMDs.
+//   helper waves 2 and 3: after the barrier, helper Y reads S (fp16) and both
+//       partials of the chunk and writes output rows 32 Y .. 32 Y + 31:
+//       y = S^T q^T and o = P v' + scale e^gamma y.
+// One barrier per chunk; the exchange is double-buffered (12 KB per chunk),
+// so the chain waves run ahead while the helpers finish the previous chunk.
+// Every operand fragment is one 1 KB block (16 bytes per lane) loaded straight
+// into registers; past the last chunk the buffer range is empty and loads
+// return zero. Each fragment array is
 // refilled with the next chunk's fragments as soon as the current chunk's
 // product has consumed it, so every load has about one chunk step of latency
-// to land, and no wave blocks on issue.
+// to land. Between them the four waves load each operand once per chunk.
 //
 // Work-group numbering is XCD-aware: all work-groups of the value heads that
 // share a key head get the same blockIdx modulo 8, so they run on one XCD and
@@ -57,26 +60,7 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr int kSlices = kD / 16;  // 16-column value slices per head
-
-// Fragments of one chunk (16 bytes per lane each):
-//   w    (token tile R, d block p)   [4 R + p]   A of (-w) S        chain wave
-//   K^T  (d tile tau, token block q) [2 tau + q] (+16: lo term)     chain wave
-//   q16  (token tile R, d block p)   [4 R + p]   B of S^T q^T       helper wave
-//   P    pair pi, term t (hi, lo)    [2 pi + t]  B of v'^T P^T      helper wave
-template <bool kF32In>
-struct ChainOps {
-  static constexpr int kNK = kF32In ? 32 : 16;
-  f16x8 w[16];
-  bf16x8 k[kNK];
-  f32x4 u[4];     // u tile R: rows 16 R + 4 g + i, value column v0 + c
-  f32x4 dec[4];   // e^{gamma_last - gamma} of those rows
-  float el;       // e^{gamma_last}
-};
-struct HelperOps {
-  f16x8 q[16];
-  bf16x8 p[12];
-  float exs[4];   // scale * e^{gamma_r}, r = 16 R + c
-};
+constexpr int kInterThreads = 256;
 
 __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
@@ -127,14 +111,243 @@ __device__ __forceinline__ f16x8 to_f16x8(const f32x4 &a, const f32x4 &b) {
   return __builtin_bit_cast(f16x8, w);
 }
 
+// Chunk hand-off buffer: [2 buffers][12 fragments][64 lanes] x 16 bytes.
+//   fragments 0..3 : S as fp16, contraction block p (key rows 32 p ..)
+//   fragments 4..7 : chain wave 0's partial v' (u + (-w) S over rows 0..63), tile R
+//   fragments 8..11: chain wave 1's partial (-w) S over rows 64..127, tile R
+constexpr int kXchFrags = 12;
+
+struct Lane {
+  int s, h, hv, v0, lane, c16, g4, bos, eos, nc, H, Hv, t_max, nt;
+};
+
+// Per-chunk slot of a sequence's chunk c (chunks of one batch never share one).
+__device__ __forceinline__ int slot_of(const Lane &L, int c) { return ((L.bos + kC * c) >> 6) + L.s; }
+
 template <bool kF32In>
-__global__ __launch_bounds__(128) void inter_kernel(StageBuffers in, const float *__restrict__ h0,
-                                                   const int32_t *__restrict__ cu,
-                                                   float *__restrict__ o, float *__restrict__ hT,
-                                                   int n_max, int H, int Hv, int t_max, int nt) {
-  constexpr int kNK = ChainOps<kF32In>::kNK;
-  // chunk hand-off, two buffers x {S as fp16: 4 fragments, v': 4 tiles} x 1 KB
-  __shared__ __attribute__((aligned(16))) u32x4 xch[2][8][64];
+__device__ __forceinline__ void chain_wave(const int X, const Lane &L, const StageBuffers &in,
+                                           const float *__restrict__ h0, float *__restrict__ hT,
+                                           u32x4 (*xch)[kXchFrags][64]) {
+  constexpr int kNKw = kF32In ? 16 : 8;  // K^T fragments this wave uses per chunk
+  const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;                // 1 KB fragment blocks
+  const int slice = L.v0 / 16;
+  struct Rsrc { rsrc_t w, k, u, g; };
+  auto rsrc_of = [&](int c) __attribute__((always_inline)) {
+    const int slot = slot_of(L, c);
+    const bool ok = c < L.nc;
+    Rsrc r;
+    r.w = make_rsrc(in.w16 + ((int64_t)L.hv * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
+    r.k = make_rsrc(in.kimg + ((int64_t)L.h * L.nt + slot) * (kF32In ? 32 : 16) * 512,
+                    ok ? (kF32In ? 32 : 16) * 1024 : 0);
+    r.u = make_rsrc(in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 256,
+                    ok && X == 0 ? 4096 : 0);
+    r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
+    return r;
+  };
+  f16x8 w[8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
+  bf16x8 k[kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
+  f32x4 u[4];       // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + c
+  f32x4 dec[4];     // e^{gamma_last - gamma} of those rows
+  float el = 0.f;   // e^{gamma_last}
+  auto load_w = [&](const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+      w[f] = __builtin_bit_cast(f16x8, ld16(r.w, vo_f, (4 * (f >> 1) + 2 * X + (f & 1)) * 1024));
+  };
+  auto load_k = [&](const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) k[f] = __builtin_bit_cast(bf16x8, ld16(r.k, vo_f, (8 * X + f) * 1024));
+    if constexpr (kF32In) {
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+        k[8 + f] = __builtin_bit_cast(bf16x8, ld16(r.k, vo_f, (16 + 8 * X + f) * 1024));
+    }
+  };
+  auto load_u = [&](const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      if (X == 0) u[R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, R * 1024));
+      dec[R] = __builtin_bit_cast(f32x4, ld16(r.g, 4 * L.g4, R * 64));
+    }
+    el = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
+  };
+
+  // state rows: S[tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + c]
+  f32x4 S[4];
+  const int64_t sbase = (((int64_t)L.s * L.Hv + L.hv) * kD + L.v0 + L.c16) * kD + 64 * X + L.g4;
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl)
+    S[tl] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + sbase + 16 * tl) : zero4();
+
+  {  // chunk 0's operands, in the loop's order
+    const Rsrc r = rsrc_of(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_u(r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(r);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c = 0; c < L.nc; ++c) {
+    const Rsrc rn = rsrc_of(c + 1);
+    u32x4 *xb = &xch[c & 1][0][L.lane];
+    f16x8 s16[2];
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl) {
+      s16[pl] = to_f16x8(S[2 * pl], S[2 * pl + 1]);
+      xb[64 * (2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
+    }
+    // partial v' over this wave's key rows (wave 0 adds u)
+    f32x4 pv[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) pv[R] = X == 0 ? u[R] : zero4();
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) pv[R] = mfma(w[2 * R + pl], s16[pl], pv[R]);
+#pragma unroll
+    for (int R = 0; R < 4; ++R) xb[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[R]);
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) S[tl] = S[tl] * el;
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(rn);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();  // chunk c's S (fp16) and both partials are published
+    f32x4 v[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      const f32x4 other = __builtin_bit_cast(f32x4, xb[64 * (4 + 4 * (1 - X) + R)]);
+      v[R] = X == 0 ? pv[R] + other : other + pv[R];  // both waves: partial0 + partial1
+    }
+    // S += K^T (e^{gamma_last - gamma} v')
+    bf16x8 eh[2], elo[2];
+    split8(v[0] * dec[0], v[1] * dec[1], eh[0], elo[0]);
+    split8(v[2] * dec[2], v[3] * dec[3], eh[1], elo[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_u(rn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[2 * tl + q], eh[q], S[tl]);
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[2 * tl + q], elo[q], S[tl]);
+      if constexpr (kF32In) {
+#pragma unroll
+        for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[8 + 2 * tl + q], eh[q], S[tl]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(rn);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (hT) {
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) *reinterpret_cast<f32x4 *>(hT + sbase + 16 * tl) = S[tl];
+  }
+}
+
+// Helper wave Y: output token tiles R = 2 Y, 2 Y + 1 (rows 32 Y .. 32 Y + 31).
+template <int Y>
+__device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &in,
+                                            float *__restrict__ o, u32x4 (*xch)[kXchFrags][64]) {
+  constexpr int kNQ = Y + 1;                 // token blocks of v' this wave contracts over
+  constexpr int kPairs = Y == 0 ? 2 : 4;     // P pairs of its tiles
+  constexpr int kPair0 = Y == 0 ? 0 : 2;
+  const uint32_t vo_o = static_cast<uint32_t>(L.c16 * L.Hv * kD + L.g4) * 4;     // o rows
+  const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;
+  const uint32_t row_o = static_cast<uint32_t>(16 * L.Hv * kD * 4);             // 16 o rows
+  struct Rsrc { rsrc_t q, p, g; };
+  auto rsrc_of = [&](int c) __attribute__((always_inline)) {
+    const int slot = slot_of(L, c);
+    const bool ok = c < L.nc;
+    Rsrc r;
+    r.q = make_rsrc(in.q16 + ((int64_t)L.h * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
+    r.p = make_rsrc(in.pimg + ((int64_t)L.hv * L.nt + slot) * 12 * 512, ok ? 12 * 1024 : 0);
+    r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
+    return r;
+  };
+  f16x8 qf[8];          // q16 fragment (token tile 2 Y + Rl, key block p) at [4 Rl + p]
+  bf16x8 pf[2 * kPairs];  // P pair kPair0 + n, term t at [2 n + t]
+  float exs[2];         // scale * e^{gamma_r}, r = 16 R + c
+  auto load_q = [&](const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+      qf[f] = __builtin_bit_cast(f16x8, ld16(r.q, vo_f, (4 * (2 * Y + (f >> 2)) + (f & 3)) * 1024));
+  };
+  auto load_p = [&](const Rsrc &r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 2 * kPairs; ++f)
+      pf[f] = __builtin_bit_cast(bf16x8, ld16(r.p, vo_f, (2 * kPair0 + f) * 1024));
+#pragma unroll
+    for (int Rl = 0; Rl < 2; ++Rl)
+      exs[Rl] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(r.g, 4 * L.c16, 256 + (2 * Y + Rl) * 64, 0));
+  };
+  {
+    const Rsrc r = rsrc_of(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_p(r);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c = 0; c < L.nc; ++c) {
+    const Rsrc rn = rsrc_of(c + 1);
+    lds_barrier();  // chunk c handed over
+    const u32x4 *xb = &xch[c & 1][0][L.lane];
+    f16x8 s16[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) s16[p] = __builtin_bit_cast(f16x8, xb[64 * p]);
+    f32x4 v[2 * kNQ];
+#pragma unroll
+    for (int R = 0; R < 2 * kNQ; ++R)
+      v[R] = __builtin_bit_cast(f32x4, xb[64 * (4 + R)]) + __builtin_bit_cast(f32x4, xb[64 * (8 + R)]);
+    // y^T = S^T q^T for this wave's two token tiles
+    f32x4 ya[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int Rl = 0; Rl < 2; ++Rl) ya[Rl] = mfma(s16[p], qf[4 * Rl + p], ya[Rl]);
+    bf16x8 dh[kNQ], dl[kNQ];
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) split8(v[2 * q], v[2 * q + 1], dh[q], dl[q]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(rn);
+    __builtin_amdgcn_sched_barrier(0);
+    // o^T = v'^T P^T + scale e^gamma y^T
+    f32x4 pa[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int Rl = 0; Rl < 2; ++Rl) {
+      const int R = 2 * Y + Rl;
+#pragma unroll
+      for (int q = 0; q <= (R >> 1); ++q) {
+        const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
+        pa[Rl] = mfma(dh[q], pf[2 * n], pa[Rl]);
+        pa[Rl] = mfma(dl[q], pf[2 * n], pa[Rl]);
+        pa[Rl] = mfma(dh[q], pf[2 * n + 1], pa[Rl]);
+      }
+    }
+    const float ex[2] = {exs[0], exs[1]};
+    __builtin_amdgcn_sched_barrier(0);
+    load_p(rn);
+    __builtin_amdgcn_sched_barrier(0);
+    const int t0 = L.bos + kC * c;
+    const uint32_t lc = static_cast<uint32_t>(min(kC, L.eos - t0));
+    const i32x4 ro = rsrc_words(o + ((int64_t)t0 * L.Hv + L.hv) * kD + L.v0, lc * L.Hv * kD * 4);
+#pragma unroll
+    for (int Rl = 0; Rl < 2; ++Rl)
+      store16(ro, vo_o, (2 * Y + Rl) * row_o, pa[Rl] + ex[Rl] * ya[Rl]);
+  }
+}
+
+template <bool kF32In>
+__global__ __launch_bounds__(kInterThreads) void inter_kernel(StageBuffers in, const float *__restrict__ h0,
+                                                              const int32_t *__restrict__ cu,
+                                                              float *__restrict__ o, float *__restrict__ hT,
+                                                              int n_max, int H, int Hv, int t_max, int nt) {
+  __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags][64];
 
   // ---- XCD-aware work-group -> (sequence, value head, slice) --------------
   const int HG = Hv / H;
@@ -144,205 +357,28 @@ __global__ __launch_bounds__(128) void inter_kernel(StageBuffers in, const float
   const int group = (wslot / members) * kXcds + xcd;  // (sequence, key head)
   const int member = wslot % members;
   if (group >= n_max * H) return;
-  const int s = group / H;
-  const int h = group % H;
-  const int hv = h * HG + member / kSlices;
-  const int slice = member % kSlices;
-  const int v0 = 16 * slice;
+  Lane L;
+  L.s = group / H;
+  L.h = group % H;
+  L.hv = L.h * HG + member / kSlices;
+  L.v0 = 16 * (member % kSlices);
+  L.lane = threadIdx.x & 63;
+  L.c16 = L.lane & 15;
+  L.g4 = 4 * (L.lane >> 4);
+  L.bos = cu[L.s];
+  L.eos = cu[L.s + 1];
+  L.nc = (L.eos - L.bos + kC - 1) / kC;
+  L.H = H;
+  L.Hv = Hv;
+  L.t_max = t_max;
+  L.nt = nt;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  const int lane = threadIdx.x & 63;
-  const int c16 = lane & 15;
-  const int g4 = 4 * (lane >> 4);
-
-  const int bos = cu[s];
-  const int eos = cu[s + 1];
-  const int nc = (eos - bos + kC - 1) / kC;
-
-  const uint32_t vo_f = static_cast<uint32_t>(lane) * 16;  // 1 KB fragment blocks
-
-  if (wave == 0) {
-    // =========================== chain wave ================================
-    const uint32_t vo_w = static_cast<uint32_t>(c16 * kD + 2 * g4) * 2;  // w16 rows
-    struct Rsrc { rsrc_t w, k, u, g; };
-    auto rsrc_of = [&](int c) __attribute__((always_inline)) {
-      const int t0 = bos + kC * c;
-      const int slot = (t0 >> 6) + s;
-      const bool ok = c < nc;
-      const uint32_t lc = ok ? static_cast<uint32_t>(min(kC, eos - t0)) : 0u;
-      Rsrc r;
-      r.w = make_rsrc(in.w16 + ((int64_t)hv * t_max + t0) * kD, lc * kD * 2);
-      r.k = make_rsrc(in.kimg + ((int64_t)h * nt + slot) * kNK * 512, ok ? kNK * 1024 : 0);
-      r.u = make_rsrc(in.uimg + (((int64_t)hv * nt + slot) * kSlices + slice) * 4 * 256, ok ? 4096 : 0);
-      r.g = make_rsrc(in.gimg + ((int64_t)hv * nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
-      return r;
-    };
-    ChainOps<kF32In> x;
-    auto load_w = [&](const Rsrc &r) __attribute__((always_inline)) {
-#pragma unroll
-      for (int f = 0; f < 16; ++f)
-        x.w[f] = __builtin_bit_cast(f16x8, ld16(r.w, vo_w, (f >> 2) * 16 * kD * 2 + (f & 3) * 64));
-    };
-    auto load_k = [&](const Rsrc &r) __attribute__((always_inline)) {
-#pragma unroll
-      for (int f = 0; f < kNK; ++f) x.k[f] = __builtin_bit_cast(bf16x8, ld16(r.k, vo_f, f * 1024));
-    };
-    auto load_u = [&](const Rsrc &r) __attribute__((always_inline)) {
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        x.u[R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, R * 1024));
-        x.dec[R] = __builtin_bit_cast(f32x4, ld16(r.g, 4 * g4, R * 64));
-      }
-      x.el = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
-    };
-
-    // state slice: S[tau] holds S[d = 16 tau + 4g + i][v0 + c]
-    f32x4 S[8];
-    const int64_t sbase = (((int64_t)s * Hv + hv) * kD + v0 + c16) * kD + g4;
-#pragma unroll
-    for (int tau = 0; tau < 8; ++tau)
-      S[tau] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + sbase + 16 * tau) : zero4();
-
-    {  // chunk 0's operands, in the loop's order
-      const Rsrc r = rsrc_of(0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(r);
-      __builtin_amdgcn_sched_barrier(0);
-      load_u(r);
-      __builtin_amdgcn_sched_barrier(0);
-      load_k(r);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int c = 0; c < nc; ++c) {
-      const Rsrc rn = rsrc_of(c + 1);
-      u32x4 *xb = &xch[c & 1][0][lane];
-      f16x8 s16[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        s16[p] = to_f16x8(S[2 * p], S[2 * p + 1]);
-        xb[64 * p] = __builtin_bit_cast(u32x4, s16[p]);
-      }
-      // v' = u + (-w) S
-      f32x4 v[4] = {x.u[0], x.u[1], x.u[2], x.u[3]};
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int R = 0; R < 4; ++R) v[R] = mfma(x.w[4 * R + p], s16[p], v[R]);
-#pragma unroll
-      for (int tau = 0; tau < 8; ++tau) S[tau] = S[tau] * x.el;
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(rn);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int R = 0; R < 4; ++R) xb[64 * (4 + R)] = __builtin_bit_cast(u32x4, v[R]);
-      lds_barrier();  // chunk c's S (fp16) and v' are ready for the helper
-      // S += K^T (e^{gamma_last - gamma} v')
-      bf16x8 eh[2], elo[2];
-      split8(v[0] * x.dec[0], v[1] * x.dec[1], eh[0], elo[0]);
-      split8(v[2] * x.dec[2], v[3] * x.dec[3], eh[1], elo[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      load_u(rn);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int tau = 0; tau < 8; ++tau) {
-          S[tau] = mfma(x.k[2 * tau + q], eh[q], S[tau]);
-          S[tau] = mfma(x.k[2 * tau + q], elo[q], S[tau]);
-          if constexpr (kF32In) S[tau] = mfma(x.k[16 + 2 * tau + q], eh[q], S[tau]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      load_k(rn);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (hT) {
-#pragma unroll
-      for (int tau = 0; tau < 8; ++tau) *reinterpret_cast<f32x4 *>(hT + sbase + 16 * tau) = S[tau];
-    }
-  } else {
-    // =========================== helper wave ===============================
-    const uint32_t vo_q = static_cast<uint32_t>(c16 * H * kD + 2 * g4) * 2;  // q16 rows
-    const uint32_t vo_o = static_cast<uint32_t>(c16 * Hv * kD + g4) * 4;     // o rows
-    const uint32_t row_q = static_cast<uint32_t>(16 * H * kD * 2);           // 16 q16 rows
-    const uint32_t row_o = static_cast<uint32_t>(16 * Hv * kD * 4);          // 16 o rows
-    struct Rsrc { rsrc_t q, p, g; };
-    auto rsrc_of = [&](int c) __attribute__((always_inline)) {
-      const int t0 = bos + kC * c;
-      const int slot = (t0 >> 6) + s;
-      const bool ok = c < nc;
-      const uint32_t lc = ok ? static_cast<uint32_t>(min(kC, eos - t0)) : 0u;
-      Rsrc r;
-      r.q = make_rsrc(in.q16 + ((int64_t)t0 * H + h) * kD, lc * H * kD * 2);
-      r.p = make_rsrc(in.pimg + ((int64_t)hv * nt + slot) * 12 * 512, ok ? 12 * 1024 : 0);
-      r.g = make_rsrc(in.gimg + ((int64_t)hv * nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
-      return r;
-    };
-    HelperOps y;
-    auto load_q = [&](const Rsrc &r) __attribute__((always_inline)) {
-#pragma unroll
-      for (int f = 0; f < 16; ++f)
-        y.q[f] = __builtin_bit_cast(f16x8, ld16(r.q, vo_q, (f >> 2) * row_q + (f & 3) * 64));
-    };
-    auto load_p = [&](const Rsrc &r) __attribute__((always_inline)) {
-#pragma unroll
-      for (int f = 0; f < 12; ++f) y.p[f] = __builtin_bit_cast(bf16x8, ld16(r.p, vo_f, f * 1024));
-#pragma unroll
-      for (int R = 0; R < 4; ++R)
-        y.exs[R] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 4 * c16, 256 + R * 64, 0));
-    };
-    {
-      const Rsrc r = rsrc_of(0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_q(r);
-      __builtin_amdgcn_sched_barrier(0);
-      load_p(r);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int c = 0; c < nc; ++c) {
-      const Rsrc rn = rsrc_of(c + 1);
-      lds_barrier();  // chunk c handed over
-      const u32x4 *xb = &xch[c & 1][0][lane];
-      f16x8 s16[4];
-      f32x4 v[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) s16[p] = __builtin_bit_cast(f16x8, xb[64 * p]);
-#pragma unroll
-      for (int R = 0; R < 4; ++R) v[R] = __builtin_bit_cast(f32x4, xb[64 * (4 + R)]);
-      // y^T = S^T q^T while v' is split into hi + lo
-      f32x4 ya[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int R = 0; R < 4; ++R) ya[R] = mfma(s16[p], y.q[4 * R + p], ya[R]);
-      bf16x8 dh[2], dl[2];
-      split8(v[0], v[1], dh[0], dl[0]);
-      split8(v[2], v[3], dh[1], dl[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      load_q(rn);
-      __builtin_amdgcn_sched_barrier(0);
-      // o^T = v'^T P^T + scale e^gamma y^T
-      f32x4 pa[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-#pragma unroll
-        for (int q = 0; q <= (R >> 1); ++q) {
-          const int pi = R < 2 ? R : 2 * R - 2 + q;
-          pa[R] = mfma(dh[q], y.p[2 * pi], pa[R]);
-          pa[R] = mfma(dl[q], y.p[2 * pi], pa[R]);
-          pa[R] = mfma(dh[q], y.p[2 * pi + 1], pa[R]);
-        }
-      }
-      const float exs[4] = {y.exs[0], y.exs[1], y.exs[2], y.exs[3]};
-      __builtin_amdgcn_sched_barrier(0);
-      load_p(rn);
-      __builtin_amdgcn_sched_barrier(0);
-      const int t0 = bos + kC * c;
-      const uint32_t lc = static_cast<uint32_t>(min(kC, eos - t0));
-      const i32x4 ro = rsrc_words(o + ((int64_t)t0 * Hv + hv) * kD + v0, lc * Hv * kD * 4);
-#pragma unroll
-      for (int R = 0; R < 4; ++R) store16(ro, vo_o, R * row_o, pa[R] + exs[R] * ya[R]);
-    }
-  }
+  if (wave < 2)
+    chain_wave<kF32In>(wave, L, in, h0, hT, xch);
+  else if (wave == 2)
+    helper_wave<0>(L, in, o, xch);
+  else
+    helper_wave<1>(L, in, o, xch);
 }
 
 template <bool kF32In>
@@ -353,8 +389,8 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
   const int groups = n_max * h;
   const int rounds = (groups + kXcds - 1) / kXcds;
   const dim3 grid(rounds * kXcds * members);
-  hipExtLaunchKernelGGL((inter_kernel<kF32In>), grid, dim3(128), 0, stream, ev.start, ev.stop, 0,
-                        in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
+  hipExtLaunchKernelGGL((inter_kernel<kF32In>), grid, dim3(kInterThreads), 0, stream, ev.start,
+                        ev.stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
   return hipGetLastError();
 }
 

@@ -14,8 +14,8 @@
 // produced here, where the work is parallel over chunks, and written in the
 // exact MFMA fragment order the inter stage reads (each fragment one 1 KB
 // block, 16 bytes per lane), so that stage only streams blocks:
-//   w16   fp16 [hv, t, 128]     -w, d permuted inside each 32-column block
-//   q16   fp16 [t, h, 128]      q rounded to fp16, same d permutation
+//   w16   fp16 per (hv, chunk)  -w fragments (A operand of (-w) S)
+//   q16   fp16 per (h, chunk)   q rounded to fp16 (B operand of S^T q^T)
 //   kimg  bf16 per (h, chunk)   K^T fragments for the state update (hi[, lo])
 //   uimg  fp32 per (hv, chunk)  u fragments, one 1 KB block per 16 x 16 tile
 //   pimg  bf16 per (hv, chunk)  P = scale * tril(q k^T * Gamma) as hi + lo
@@ -46,9 +46,8 @@
 //  * w and u are MFMA products of the transposed K (V) tile with the scaled
 //    T; each lane scales and splits its own T fragment into hi + lo bf16 in
 //    registers, so w and u are formed in one pass with no staging buffer.
-// Rows of a partial last chunk are zero-filled, so they add nothing; w and q16
-// are written for valid rows only, the per-chunk blocks in full (zeros past
-// the end).
+// Rows of a partial last chunk are zero-filled, so they add nothing; every
+// per-chunk block is written in full (zeros past the end).
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -217,24 +216,12 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   }
   store_col4x8(kcol, lrow, lcol, khi);
   if constexpr (kF32In) store_col4x8(kcol + 128 * kLdCol, lrow, lcol, klo);
-  // ---- q tile -> LDS row-major, and the fp16 copy q16 ---------------------
+  // ---- q tile -> LDS row-major -------------------------------------------
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     *reinterpret_cast<u32x4 *>(rq + (lrow + rr) * kLdRow + lcol) = qhi[rr];
     if constexpr (kF32In)
       *reinterpret_cast<u32x4 *>(rq + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = qlo[rr];
-    if (lrow + rr < L) {
-      float f[8], fl[8];
-      unpack8(qhi[rr], f);
-      unpack8(qlo[rr], fl);
-      uint32_t hh[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hh[i] = pack_f16(f[2 * i] + fl[2 * i], f[2 * i + 1] + fl[2 * i + 1]);
-      _Float16 *dst = out.q16 + ((int64_t)(t0 + lrow + rr) * H + h) * kD + 32 * (lcol >> 5);
-      const int m = (lcol & 31) >> 2;  // first group of four columns
-      *reinterpret_cast<u32x2 *>(dst + perm4(m)) = u32x2{hh[0], hh[1]};
-      *reinterpret_cast<u32x2 *>(dst + perm4(m + 1)) = u32x2{hh[2], hh[3]};
-    }
   }
   __syncthreads();
 
@@ -256,6 +243,37 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
       const u32x2 bl = *reinterpret_cast<const u32x2 *>(kcol + 128 * kLdCol + off + 16);
       *reinterpret_cast<u32x4 *>(dst + 16 * 64 * 8) = u32x4{al[0], al[1], bl[0], bl[1]};
     }
+  }
+
+  // ---- q16 fragments for y = S^T q^T: fragment (R, p), lane (g, c) holds
+  // q[16 R + c][32 p + 4 g + j] for j < 4 and q[16 R + c][32 p + 16 + 4 g + j - 4]
+  // for j >= 4, rounded to fp16 once (from hi + lo for fp32 input).
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int item = tid + kThreads * m;
+    const int f = item >> 6, l = item & 63;
+    const int off = (16 * (f >> 2) + (l & 15)) * kLdRow + 32 * (f & 3) + 4 * (l >> 4);
+    float x[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const u32x2 a = *reinterpret_cast<const u32x2 *>(rq + off + 16 * half);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        x[4 * half + 2 * i] = __uint_as_float(a[i] << 16);
+        x[4 * half + 2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+      }
+      if constexpr (kF32In) {
+        const u32x2 b = *reinterpret_cast<const u32x2 *>(rq + 64 * kLdRow + off + 16 * half);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          x[4 * half + 2 * i] += __uint_as_float(b[i] << 16);
+          x[4 * half + 2 * i + 1] += __uint_as_float(b[i] & 0xffff0000u);
+        }
+      }
+    }
+    _Float16 *dst = out.q16 + ((((int64_t)h * nt + slot) * 16 + f) * 64 + l) * 8;
+    *reinterpret_cast<u32x4 *>(dst) = u32x4{pack_f16(x[0], x[1]), pack_f16(x[2], x[3]),
+                                            pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
   }
 
   // ---- G = K K^T, lower 16x16 blocks, kept in registers ---------------------
@@ -502,17 +520,17 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
           uacc[db2] = au;
         }
       }
+      {
+        // -w fragment (rb, p = wv): lane (g, c) holds w[r = 16 rb + c][d] for
+        // d = 32 wv + 4 g + i (tile db = 2 wv) and 32 wv + 16 + 4 g + i (db = 2 wv + 1)
+        const f32x4 a0 = wacc[0], a1 = wacc[1];
+        _Float16 *dst = out.w16 + ((((int64_t)hv * nt + slot) * 16 + 4 * rb + wv) * 64 + lane) * 8;
+        *reinterpret_cast<u32x4 *>(dst) = u32x4{pack_f16(-a0[0], -a0[1]), pack_f16(-a0[2], -a0[3]),
+                                                pack_f16(-a1[0], -a1[1]), pack_f16(-a1[2], -a1[3])};
+      }
 #pragma unroll
       for (int db2 = 0; db2 < 2; ++db2) {
         const int db = 2 * wv + db2;
-        // w: lane holds w[r = 16 rb + (lane & 15)][d = 16 db + 4 (lane >> 4) + i]
-        const f32x4 aw = wacc[db2];
-        const int r = 16 * rb + (lane & 15);
-        if (r < L) {
-          _Float16 *dst = out.w16 + ((int64_t)hv * t_max + t0 + r) * kD + 32 * (db >> 1) +
-                          perm4(4 * (db & 1) + (lane >> 4));
-          *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_f16(-aw[0], -aw[1]), pack_f16(-aw[2], -aw[3])};
-        }
         // u: lane holds u[r = 16 rb + 4 (lane >> 4) + i][d = 16 db + (lane & 15)]
         float *dst = out.uimg + (((((int64_t)hv * nt + slot) * 8 + db) * 4 + rb) * 64 + lane) * 4;
         *reinterpret_cast<f32x4 *>(dst) = uacc[db2];

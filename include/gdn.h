@@ -74,12 +74,13 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
 
 /* Byte offsets of the intermediates inside a workspace, each 256-byte aligned.
  * The intra stage writes them and the inter stage reads them; their layouts
- * are an internal contract between the two stages (MFMA fragment order), but
- * they are documented so that they can be inspected:
- *   w16   fp16 [hv, t_max, dk]: -w (AMX page, section 4, negated) with the
- *         columns of each 32-column block in the order 0-3,16-19,4-7,20-23,..,
- *         12-15,28-31
- *   q16   fp16 [t_max, h, dk]: q rounded to fp16, same column order
+ * are an internal contract between the two stages (MFMA fragment order: a
+ * fragment is 64 lanes x 16 bytes, lane (g, c) = (l / 16, l % 16)), but they
+ * are documented so that they can be inspected:
+ *   w16   fp16 [hv, nt_max, 16, 64, 8]: -w (AMX page, section 4, negated);
+ *         fragment 4 R + p, lane (g, c) holds row 16 R + c, columns
+ *         32 p + 4 g + j (j < 4) and 32 p + 16 + 4 g + j - 4 (j >= 4)
+ *   q16   fp16 [h, nt_max, 16, 64, 8]: q rounded to fp16, same fragments
  *   kimg  bf16 [h, nt_max, 16 (32 for fp32 input), 64, 8]: K^T fragments
  *   uimg  fp32 [hv, nt_max, dv / 16, 4, 64, 4]: u (AMX page, section 4), one
  *         16 x 16 tile per 1 KB block

@@ -131,13 +131,6 @@ def lane_errors(wl, o_gpu, hT_gpu, ref):
 # decoders of the intermediates the intra stage writes (layouts in include/gdn.h)
 # --------------------------------------------------------------------------- #
 
-def _perm4(m):
-    return 8 * m if m < 4 else 8 * (m - 4) + 4
-
-
-# column d of a permuted 128-wide row sits at position POS[d]
-POS = np.array([32 * (d // 32) + _perm4((d % 32) // 4) + d % 4 for d in range(128)])
-
 # P pairs: (token block q, output tile R)
 PAIRS = [(0, 0), (0, 1), (0, 2), (1, 2), (0, 3), (1, 3)]
 
@@ -157,13 +150,28 @@ def workspace_views(cfg, ws):
         return ws[lay[name]:lay[name] + n].view(dtype).view(*shape)
 
     return dict(
-        w16=view("w16", torch.float16, (cfg.hv, cfg.t_max, 128)),
-        q16=view("q16", torch.float16, (cfg.t_max, cfg.h, 128)),
+        w16=view("w16", torch.float16, (cfg.hv, nt, 16, 64, 8)),
+        q16=view("q16", torch.float16, (cfg.h, nt, 16, 64, 8)),
         kimg=view("kimg", torch.bfloat16, (cfg.h, nt, nk, 64, 8)),
         uimg=view("uimg", torch.float32, (cfg.hv, nt, 8, 4, 64, 4)),
         pimg=view("pimg", torch.bfloat16, (cfg.hv, nt, 6, 2, 64, 8)),
         gimg=view("gimg", torch.float32, (cfg.hv, nt, 192)),
         nt=nt, nk=nk)
+
+
+def decode_rowfrag(slot):
+    """[16, 64, 8] fp16 fragments (fragment 4 R + p; lane (g, c) holds row
+    16 R + c, columns 32 p + 4 g + j and 32 p + 16 + 4 g + j - 4) -> [64, 128]."""
+    x = slot.float().numpy().astype(np.float64)
+    M = np.zeros((64, 128))
+    for f in range(16):
+        R, p = f // 4, f % 4
+        for lane in range(64):
+            g, c = lane // 16, lane % 16
+            for j in range(8):
+                col = 32 * p + (16 if j >= 4 else 0) + 4 * g + (j & 3)
+                M[16 * R + c, col] = x[f, lane, j]
+    return M
 
 
 def decode_kimg(kimg_slot):

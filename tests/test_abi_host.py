@@ -64,7 +64,7 @@ def test_workspace_layout(lib, dtype, nk):
     cfg = gdn.make_config(T, N, H, Hv, dtype)
     al = lambda x: (x + 255) // 256 * 256
     nt = index_table.nt_max(T, N)
-    sizes = [("w16", Hv * T * 128 * 2), ("q16", T * H * 128 * 2), ("kimg", H * nt * nk * 1024),
+    sizes = [("w16", Hv * nt * 16 * 1024), ("q16", H * nt * 16 * 1024), ("kimg", H * nt * nk * 1024),
              ("uimg", Hv * nt * 64 * 128 * 4), ("pimg", Hv * nt * 12 * 1024),
              ("gimg", Hv * nt * 192 * 4), ("table", nt * 8)]
     lay = gdn.gdn_workspace_layout(cfg)

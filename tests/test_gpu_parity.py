@@ -15,7 +15,7 @@ import chunked_gated_delta_rule_amd as gdn
 import workloads
 from oracle import chunked, index_table, recurrent
 
-from gpu_helpers import (O_TOL, POS, S_TOL, config_of, decode_kimg, decode_pimg, decode_uimg,
+from gpu_helpers import (O_TOL, S_TOL, config_of, decode_kimg, decode_pimg, decode_rowfrag, decode_uimg,
                          device_inputs, lane_errors, log, oracle_inputs_f64, oracle_lanes,
                          run_forward, run_front, workspace_views)
 
@@ -107,17 +107,9 @@ def test_intra_stage_intermediates(dtype):
                                      wl.f64("beta"), wl.cu_seqlens, chunk=64, return_wu=True,
                                      stages=stages)
     T = int(wl.cu_seqlens[-1])
-    # -w (fp16, permuted columns) and q16 (q rounded to fp16, permuted columns)
-    wg = -V["w16"][:, :T][..., POS].double().numpy()  # stored negated
-    ew = np.max(np.abs(wg - W[:, :T])) / np.max(np.abs(W[:, :T]))
-    q16 = V["q16"][:T][..., POS]
-    if dtype == torch.bfloat16:  # bf16 -> fp16 is exact here: one rounding, bit for bit
-        assert torch.equal(q16, wl.q[:T].float().half()), "q16 is not q rounded to fp16"
-    else:  # fp32 input passes through hi + lo bf16 first: within one fp16 ulp
-        qf = wl.q[:T].double()
-        assert torch.all((q16.double() - qf).abs() <= qf.abs() * 2.0 ** -10 + 2.0 ** -24)
     cu = wl.cu_seqlens
-    eu = ep = eg = 0.0
+    eu = ep = eg = ew = 0.0
+    wmax = np.max(np.abs(W[:, :T]))
     pmax = max(np.max(np.abs(la)) for _, la in stages.values()) * scale
     k64 = wl.f64("k")
     for s_ in range(len(cu) - 1):
@@ -126,6 +118,16 @@ def test_intra_stage_intermediates(dtype):
             slot = (t0 >> 6) + s_
             # K^T fragments: exact copy of k (hi[+lo] for fp32 input), zero past the end
             for h in range(wl.H):
+                # q16: q rounded to fp16 (bf16 -> fp16 is exact here, bit for bit; fp32
+                # input passes through hi + lo bf16 first: within one fp16 ulp)
+                q16 = decode_rowfrag(V["q16"][h, slot])
+                qref = np.zeros((64, 128))
+                qref[:L] = wl.q[t0:t0 + L, h].double().numpy()
+                if dtype == torch.bfloat16:
+                    want = torch.from_numpy(qref).float().half().double().numpy()
+                    assert np.array_equal(q16, want), "q16 is not q rounded to fp16"
+                else:
+                    assert np.all(np.abs(q16 - qref) <= np.abs(qref) * 2.0 ** -10 + 2.0 ** -24)
                 terms = decode_kimg(V["kimg"][h, slot])
                 Kd = sum(terms)
                 ref = np.zeros((64, 128))
@@ -134,6 +136,9 @@ def test_intra_stage_intermediates(dtype):
                 assert np.max(np.abs(Kd - ref)) <= tol
             for hv in range(wl.Hv):
                 gamma, la = stages[(hv, t0)]
+                wd = -decode_rowfrag(V["w16"][hv, slot])  # stored negated
+                assert np.all(wd[L:] == 0.0)
+                ew = max(ew, np.max(np.abs(wd[:L] - W[hv, t0:t0 + L])) / wmax)
                 Ud = decode_uimg(V["uimg"][hv, slot])
                 assert np.all(Ud[L:] == 0.0)
                 eu = max(eu, np.max(np.abs(Ud[:L] - U[hv, t0:t0 + L])) / np.max(np.abs(U[hv, :T])))
