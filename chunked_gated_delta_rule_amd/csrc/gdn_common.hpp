@@ -146,7 +146,8 @@ __device__ __forceinline__ void split_pack4(const float (&x)[4], u32x2 &hi, u32x
 
 
 // Floats per (value head, chunk) in the gate block: e^{gamma_last - gamma_t}
-// [64], scale * e^{gamma_t} [64], e^{gamma_last} and zero padding [64].
+// [64], scale * e^{gamma_t} [64] ordered [c][R] for token t = 16 R + c,
+// e^{gamma_last} and zero padding [64].
 constexpr int kGateStride = 192;
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -43,14 +43,14 @@
 // so the chain waves run ahead while the helpers finish the previous chunk.
 // Every operand fragment is one 1 KB block (16 bytes per lane) loaded straight
 // into registers; past the last chunk the buffer range is empty and loads
-// return zero. Each fragment array is
-// refilled with the next chunk's fragments as soon as the current chunk's
-// product has consumed it, so every load has about one chunk step of latency
-// to land. Between them the four waves load each operand once per chunk.
+// return zero. Fragments are prefetched two chunks ahead.
+// Between them the four waves load each operand once per chunk.
 //
 // Work-group numbering is XCD-aware: all work-groups of the value heads that
 // share a key head get the same blockIdx modulo 8, so they run on one XCD and
 // share q16 and K^T through its L2.
+#include <type_traits>
+
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -124,12 +124,24 @@ struct Lane {
 // Per-chunk slot of a sequence's chunk c (chunks of one batch never share one).
 __device__ __forceinline__ int slot_of(const Lane &L, int c) { return ((L.bos + kC * c) >> 6) + L.s; }
 
-template <bool kF32In>
-__device__ __forceinline__ void chain_wave(const int X, const Lane &L, const StageBuffers &in,
+// Both kinds of wave keep two sets of operand fragments (set B serves chunks
+// c with c % 2 == B) and walk the chunks in pairs: while chunk c runs on one
+// set, the loads of chunk c + 1 are landing in the other, and each array of
+// the current set is refilled with chunk c + 2's fragments as soon as chunk c
+// has consumed it. Every load therefore has about two chunk steps to arrive,
+// which the load latency of a busy CU needs. The sets are plain register
+// arrays indexed by a compile-time set number, and every value is consumed
+// before its refill is issued, so each refill lands in the registers it
+// replaces and the compiler's load counting never has to drain.
+template <int B>
+using SetIndex = std::integral_constant<int, B>;
+
+template <bool kF32In, int X>
+__device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in,
                                            const float *__restrict__ h0, float *__restrict__ hT,
                                            u32x4 (*xch)[kXchFrags][64]) {
   constexpr int kNKw = kF32In ? 16 : 8;  // K^T fragments this wave uses per chunk
-  const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;                // 1 KB fragment blocks
+  const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;  // 1 KB fragment blocks
   const int slice = L.v0 / 16;
   struct Rsrc { rsrc_t w, k, u, g; };
   auto rsrc_of = [&](int c) __attribute__((always_inline)) {
@@ -144,32 +156,44 @@ __device__ __forceinline__ void chain_wave(const int X, const Lane &L, const Sta
     r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     return r;
   };
-  f16x8 w[8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
-  bf16x8 k[kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
-  f32x4 u[4];       // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + c
-  f32x4 dec[4];     // e^{gamma_last - gamma} of those rows
-  float el = 0.f;   // e^{gamma_last}
-  auto load_w = [&](const Rsrc &r) __attribute__((always_inline)) {
+  f16x8 w[2][8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
+  bf16x8 k[2][kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
+  f32x4 u[2][4];       // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + c
+  f32x4 dec[2][4];     // e^{gamma_last - gamma} of those rows
+  float el[2];         // e^{gamma_last}
+  auto load_w = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
-      w[f] = __builtin_bit_cast(f16x8, ld16(r.w, vo_f, (4 * (f >> 1) + 2 * X + (f & 1)) * 1024));
+    for (int i = 0; i < 8; ++i)
+      w[B][i] = __builtin_bit_cast(f16x8, ld16(r.w, vo_f, (4 * (i >> 1) + 2 * X + (i & 1)) * 1024));
   };
-  auto load_k = [&](const Rsrc &r) __attribute__((always_inline)) {
+  auto load_k = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
 #pragma unroll
-    for (int f = 0; f < 8; ++f) k[f] = __builtin_bit_cast(bf16x8, ld16(r.k, vo_f, (8 * X + f) * 1024));
+    for (int i = 0; i < 8; ++i) k[B][i] = __builtin_bit_cast(bf16x8, ld16(r.k, vo_f, (8 * X + i) * 1024));
     if constexpr (kF32In) {
 #pragma unroll
-      for (int f = 0; f < 8; ++f)
-        k[8 + f] = __builtin_bit_cast(bf16x8, ld16(r.k, vo_f, (16 + 8 * X + f) * 1024));
+      for (int i = 0; i < 8; ++i)
+        k[B][8 + i] = __builtin_bit_cast(bf16x8, ld16(r.k, vo_f, (16 + 8 * X + i) * 1024));
     }
   };
-  auto load_u = [&](const Rsrc &r) __attribute__((always_inline)) {
+  auto load_u = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      if (X == 0) u[R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, R * 1024));
-      dec[R] = __builtin_bit_cast(f32x4, ld16(r.g, 4 * L.g4, R * 64));
+      if constexpr (X == 0) u[B][R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, R * 1024));
+      dec[B][R] = __builtin_bit_cast(f32x4, ld16(r.g, 4 * L.g4, R * 64));
     }
-    el = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
+    el[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
+  };
+  auto load_all = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(Bc, r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_u(Bc, r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(Bc, r);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // state rows: S[tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + c]
@@ -179,18 +203,13 @@ __device__ __forceinline__ void chain_wave(const int X, const Lane &L, const Sta
   for (int tl = 0; tl < 4; ++tl)
     S[tl] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + sbase + 16 * tl) : zero4();
 
-  {  // chunk 0's operands, in the loop's order
-    const Rsrc r = rsrc_of(0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(r);
-    __builtin_amdgcn_sched_barrier(0);
-    load_u(r);
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(r);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int c = 0; c < L.nc; ++c) {
-    const Rsrc rn = rsrc_of(c + 1);
+  // One chunk step on set B, which is refilled with chunk c + 2. A step past
+  // the last chunk (c == nc when nc is odd) runs on zero fragments with a
+  // decay of 1 and leaves S unchanged.
+  auto step = [&](const int c, auto Bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
+    const Rsrc rn = rsrc_of(c + 2);
+    const float e_last = c < L.nc ? el[B] : 1.f;
     u32x4 *xb = &xch[c & 1][0][L.lane];
     f16x8 s16[2];
 #pragma unroll
@@ -198,20 +217,20 @@ __device__ __forceinline__ void chain_wave(const int X, const Lane &L, const Sta
       s16[pl] = to_f16x8(S[2 * pl], S[2 * pl + 1]);
       xb[64 * (2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
     }
-    // partial v' over this wave's key rows (wave 0 adds u)
+    // partial v' over this wave's key rows (wave 0 starts from u)
     f32x4 pv[4];
 #pragma unroll
-    for (int R = 0; R < 4; ++R) pv[R] = X == 0 ? u[R] : zero4();
+    for (int R = 0; R < 4; ++R) pv[R] = X == 0 ? u[B][R] : zero4();
 #pragma unroll
     for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-      for (int R = 0; R < 4; ++R) pv[R] = mfma(w[2 * R + pl], s16[pl], pv[R]);
+      for (int R = 0; R < 4; ++R) pv[R] = mfma(w[B][2 * R + pl], s16[pl], pv[R]);
 #pragma unroll
     for (int R = 0; R < 4; ++R) xb[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[R]);
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) S[tl] = S[tl] * el;
+    for (int tl = 0; tl < 4; ++tl) S[tl] = S[tl] * e_last;
     __builtin_amdgcn_sched_barrier(0);
-    load_w(rn);
+    load_w(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // chunk c's S (fp16) and both partials are published
     f32x4 v[4];
@@ -222,25 +241,32 @@ __device__ __forceinline__ void chain_wave(const int X, const Lane &L, const Sta
     }
     // S += K^T (e^{gamma_last - gamma} v')
     bf16x8 eh[2], elo[2];
-    split8(v[0] * dec[0], v[1] * dec[1], eh[0], elo[0]);
-    split8(v[2] * dec[2], v[3] * dec[3], eh[1], elo[1]);
+    split8(v[0] * dec[B][0], v[1] * dec[B][1], eh[0], elo[0]);
+    split8(v[2] * dec[B][2], v[3] * dec[B][3], eh[1], elo[1]);
     __builtin_amdgcn_sched_barrier(0);
-    load_u(rn);
+    load_u(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
-      for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[2 * tl + q], eh[q], S[tl]);
+      for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[B][2 * tl + q], eh[q], S[tl]);
 #pragma unroll
-      for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[2 * tl + q], elo[q], S[tl]);
+      for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[B][2 * tl + q], elo[q], S[tl]);
       if constexpr (kF32In) {
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[8 + 2 * tl + q], eh[q], S[tl]);
+        for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[B][8 + 2 * tl + q], eh[q], S[tl]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_k(rn);
+    load_k(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  load_all(SetIndex<0>{}, rsrc_of(0));
+  load_all(SetIndex<1>{}, rsrc_of(1));
+  for (int c = 0; c < L.nc; c += 2) {
+    step(c, SetIndex<0>{});
+    step(c + 1, SetIndex<1>{});
   }
   if (hT) {
 #pragma unroll
@@ -268,33 +294,32 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
     r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     return r;
   };
-  f16x8 qf[8];          // q16 fragment (token tile 2 Y + Rl, key block p) at [4 Rl + p]
-  bf16x8 pf[2 * kPairs];  // P pair kPair0 + n, term t at [2 n + t]
-  float exs[2];         // scale * e^{gamma_r}, r = 16 R + c
-  auto load_q = [&](const Rsrc &r) __attribute__((always_inline)) {
+  f16x8 qf[2][8];            // q16 fragment (token tile 2 Y + Rl, key block p) at [4 Rl + p]
+  bf16x8 pf[2][2 * kPairs];  // P pair kPair0 + n, term t at [2 n + t]
+  u32x2 exs[2];              // scale * e^{gamma_r} (fp32 bits), r = 16 (2 Y + Rl) + c
+  auto load_q = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
-      qf[f] = __builtin_bit_cast(f16x8, ld16(r.q, vo_f, (4 * (2 * Y + (f >> 2)) + (f & 3)) * 1024));
+    for (int i = 0; i < 8; ++i)
+      qf[B][i] = __builtin_bit_cast(f16x8, ld16(r.q, vo_f, (4 * (2 * Y + (i >> 2)) + (i & 3)) * 1024));
   };
-  auto load_p = [&](const Rsrc &r) __attribute__((always_inline)) {
+  auto load_p = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
 #pragma unroll
-    for (int f = 0; f < 2 * kPairs; ++f)
-      pf[f] = __builtin_bit_cast(bf16x8, ld16(r.p, vo_f, (2 * kPair0 + f) * 1024));
-#pragma unroll
-    for (int Rl = 0; Rl < 2; ++Rl)
-      exs[Rl] = __uint_as_float(
-          __builtin_amdgcn_raw_buffer_load_b32(r.g, 4 * L.c16, 256 + (2 * Y + Rl) * 64, 0));
+    for (int i = 0; i < 2 * kPairs; ++i)
+      pf[B][i] = __builtin_bit_cast(bf16x8, ld16(r.p, vo_f, (2 * kPair0 + i) * 1024));
+    exs[B] = __builtin_amdgcn_raw_buffer_load_b64(r.g, 16 * L.c16 + 8 * Y, 256, 0);
   };
-  {
-    const Rsrc r = rsrc_of(0);
+  auto load_all = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    load_q(r);
+    load_q(Bc, r);
     __builtin_amdgcn_sched_barrier(0);
-    load_p(r);
+    load_p(Bc, r);
     __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int c = 0; c < L.nc; ++c) {
-    const Rsrc rn = rsrc_of(c + 1);
+  };
+  auto step = [&](const int c, auto Bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
+    const Rsrc rn = rsrc_of(c + 2);
     lds_barrier();  // chunk c handed over
     const u32x4 *xb = &xch[c & 1][0][L.lane];
     f16x8 s16[4];
@@ -309,12 +334,12 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
-      for (int Rl = 0; Rl < 2; ++Rl) ya[Rl] = mfma(s16[p], qf[4 * Rl + p], ya[Rl]);
+      for (int Rl = 0; Rl < 2; ++Rl) ya[Rl] = mfma(s16[p], qf[B][4 * Rl + p], ya[Rl]);
     bf16x8 dh[kNQ], dl[kNQ];
 #pragma unroll
     for (int q = 0; q < kNQ; ++q) split8(v[2 * q], v[2 * q + 1], dh[q], dl[q]);
     __builtin_amdgcn_sched_barrier(0);
-    load_q(rn);
+    load_q(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
     // o^T = v'^T P^T + scale e^gamma y^T
     f32x4 pa[2] = {zero4(), zero4()};
@@ -324,21 +349,27 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
 #pragma unroll
       for (int q = 0; q <= (R >> 1); ++q) {
         const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
-        pa[Rl] = mfma(dh[q], pf[2 * n], pa[Rl]);
-        pa[Rl] = mfma(dl[q], pf[2 * n], pa[Rl]);
-        pa[Rl] = mfma(dh[q], pf[2 * n + 1], pa[Rl]);
+        pa[Rl] = mfma(dh[q], pf[B][2 * n], pa[Rl]);
+        pa[Rl] = mfma(dl[q], pf[B][2 * n], pa[Rl]);
+        pa[Rl] = mfma(dh[q], pf[B][2 * n + 1], pa[Rl]);
       }
     }
-    const float ex[2] = {exs[0], exs[1]};
-    __builtin_amdgcn_sched_barrier(0);
-    load_p(rn);
-    __builtin_amdgcn_sched_barrier(0);
     const int t0 = L.bos + kC * c;
-    const uint32_t lc = static_cast<uint32_t>(min(kC, L.eos - t0));
+    const uint32_t lc = c < L.nc ? static_cast<uint32_t>(min(kC, L.eos - t0)) : 0u;  // past the end: no store
     const i32x4 ro = rsrc_words(o + ((int64_t)t0 * L.Hv + L.hv) * kD + L.v0, lc * L.Hv * kD * 4);
 #pragma unroll
     for (int Rl = 0; Rl < 2; ++Rl)
-      store16(ro, vo_o, (2 * Y + Rl) * row_o, pa[Rl] + ex[Rl] * ya[Rl]);
+      store16(ro, vo_o, (2 * Y + Rl) * row_o, pa[Rl] + __uint_as_float(exs[B][Rl]) * ya[Rl]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_p(Bc, rn);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  load_all(SetIndex<0>{}, rsrc_of(0));
+  load_all(SetIndex<1>{}, rsrc_of(1));
+  for (int c = 0; c < L.nc; c += 2) {
+    step(c, SetIndex<0>{});
+    step(c + 1, SetIndex<1>{});
   }
 }
 
@@ -373,8 +404,10 @@ __global__ __launch_bounds__(kInterThreads) void inter_kernel(StageBuffers in, c
   L.t_max = t_max;
   L.nt = nt;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 2)
-    chain_wave<kF32In>(wave, L, in, h0, hT, xch);
+  if (wave == 0)
+    chain_wave<kF32In, 0>(L, in, h0, hT, xch);
+  else if (wave == 1)
+    chain_wave<kF32In, 1>(L, in, h0, hT, xch);
   else if (wave == 2)
     helper_wave<0>(L, in, o, xch);
   else

@@ -19,7 +19,8 @@
 //   kimg  bf16 per (h, chunk)   K^T fragments for the state update (hi[, lo])
 //   uimg  fp32 per (hv, chunk)  u fragments, one 1 KB block per 16 x 16 tile
 //   pimg  bf16 per (hv, chunk)  P = scale * tril(q k^T * Gamma) as hi + lo
-//   gimg  fp32 per (hv, chunk)  e^{gamma_last - gamma}, scale e^gamma, e^{gamma_last}
+//   gimg  fp32 per (hv, chunk)  e^{gamma_last - gamma}, scale e^gamma (ordered
+//                               [c][R] for r = 16 R + c), e^{gamma_last}
 // P is the intra-chunk attention term of the output (AMX page, section 5); it
 // shares the masked decay factors with A. Per-chunk blocks are addressed by
 // the slot floor(t0 / 64) + n of chunk start t0 in sequence n, which is
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     if (wv == 0) {
       float *gd = out.gimg + ((int64_t)hv * nt + slot) * kGateStride;
       gd[lane] = tok_ok ? fast_exp2(gl2 - gam2) : 0.f;
-      gd[64 + lane] = tok_ok ? scale * eg : 0.f;
+      gd[64 + 4 * (lane & 15) + (lane >> 4)] = tok_ok ? scale * eg : 0.f;  // [c][R], r = 16 R + c
       gd[128 + lane] = lane == 0 ? fast_exp2(gl2) : 0.f;
     }
     wave_lds_sync();

@@ -85,8 +85,9 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
  *   uimg  fp32 [hv, nt_max, dv / 16, 4, 64, 4]: u (AMX page, section 4), one
  *         16 x 16 tile per 1 KB block
  *   pimg  bf16 [hv, nt_max, 6, 2, 64, 8]: scale * tril(q k^T * Gamma) as hi + lo
- *   gimg  fp32 [hv, nt_max, 192]: per token e^{gamma_last - gamma},
- *         scale * e^gamma, then e^{gamma_last}
+ *   gimg  fp32 [hv, nt_max, 192]: per token e^{gamma_last - gamma} [64],
+ *         scale * e^gamma [64] with token 16 R + c at 4 c + R, then
+ *         e^{gamma_last}
  *   table int32 [nt_max, 2]: the chunk-index table
  * Per-chunk blocks are indexed by slot floor(t0 / 64) + n for a chunk starting
  * at token t0 of sequence n (distinct per chunk, < nt_max). */

@@ -147,6 +147,7 @@ def test_intra_stage_intermediates(dtype):
                 Pref[:L, :L] = scale * la
                 ep = max(ep, np.max(np.abs(Pd - Pref)) / pmax)
                 gd = V["gimg"][hv, slot].double().numpy()
+                gd[64:128] = gd[64:128].reshape(16, 4).T.reshape(64)  # [c][R] -> token order
                 gl = gamma[L - 1]
                 for got, want in ((gd[:L], np.exp(gl - gamma)), (gd[64:64 + L], scale * np.exp(gamma)),
                                   (gd[128:129], np.exp([gl]))):
