@@ -124,19 +124,21 @@ struct Lane {
 // Per-chunk slot of a sequence's chunk c (chunks of one batch never share one).
 __device__ __forceinline__ int slot_of(const Lane &L, int c) { return ((L.bos + kC * c) >> 6) + L.s; }
 
-// Both kinds of wave keep two sets of operand fragments (set B serves chunks
-// c with c % 2 == B) and walk the chunks in pairs: while chunk c runs on one
-// set, the loads of chunk c + 1 are landing in the other, and each array of
-// the current set is refilled with chunk c + 2's fragments as soon as chunk c
-// has consumed it. Every load therefore has about two chunk steps to arrive,
-// which the load latency of a busy CU needs. The sets are plain register
-// arrays indexed by a compile-time set number, and every value is consumed
-// before its refill is issued, so each refill lands in the registers it
-// replaces and the compiler's load counting never has to drain.
+// Both kinds of wave keep kDepth sets of operand fragments (set B serves
+// chunks c with c % kDepth == B) and walk the chunks in groups of kDepth: each
+// array of the current set is refilled with chunk c + kDepth's fragments as
+// soon as chunk c has consumed it, so every load has about kDepth chunk steps
+// to arrive. With one work-group per CU (single-sequence prefill) the load
+// latency of a busy CU needs kDepth = 2; when the grid has more work-groups
+// than CUs, kDepth = 1 keeps two work-groups resident per CU instead and
+// their interleaving hides the latency. The sets are plain register arrays
+// indexed by a compile-time set number, and every value is consumed before
+// its refill is issued, so each refill lands in the registers it replaces and
+// the compiler's load counting never has to drain.
 template <int B>
 using SetIndex = std::integral_constant<int, B>;
 
-template <bool kF32In, int X>
+template <bool kF32In, int kDepth, int X>
 __device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in,
                                            const float *__restrict__ h0, float *__restrict__ hT,
                                            u32x4 (*xch)[kXchFrags][64]) {
@@ -156,11 +158,11 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in
     r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     return r;
   };
-  f16x8 w[2][8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
-  bf16x8 k[2][kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
-  f32x4 u[2][4];       // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + c
-  f32x4 dec[2][4];     // e^{gamma_last - gamma} of those rows
-  float el[2];         // e^{gamma_last}
+  f16x8 w[kDepth][8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
+  bf16x8 k[kDepth][kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
+  f32x4 u[kDepth][4];       // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + c
+  f32x4 dec[kDepth][4];     // e^{gamma_last - gamma} of those rows
+  float el[kDepth];         // e^{gamma_last}
   auto load_w = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
 #pragma unroll
@@ -203,12 +205,12 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in
   for (int tl = 0; tl < 4; ++tl)
     S[tl] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + sbase + 16 * tl) : zero4();
 
-  // One chunk step on set B, which is refilled with chunk c + 2. A step past
-  // the last chunk (c == nc when nc is odd) runs on zero fragments with a
-  // decay of 1 and leaves S unchanged.
+  // One chunk step on set B, which is refilled with chunk c + kDepth. A step
+  // past the last chunk (c >= nc) runs on zero fragments with a decay of 1
+  // and leaves S unchanged.
   auto step = [&](const int c, auto Bc) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
-    const Rsrc rn = rsrc_of(c + 2);
+    const Rsrc rn = rsrc_of(c + kDepth);
     const float e_last = c < L.nc ? el[B] : 1.f;
     u32x4 *xb = &xch[c & 1][0][L.lane];
     f16x8 s16[2];
@@ -263,10 +265,10 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in
   };
 
   load_all(SetIndex<0>{}, rsrc_of(0));
-  load_all(SetIndex<1>{}, rsrc_of(1));
-  for (int c = 0; c < L.nc; c += 2) {
+  if constexpr (kDepth == 2) load_all(SetIndex<1>{}, rsrc_of(1));
+  for (int c = 0; c < L.nc; c += kDepth) {  // a step past the last chunk changes nothing
     step(c, SetIndex<0>{});
-    step(c + 1, SetIndex<1>{});
+    if constexpr (kDepth == 2) step(c + 1, SetIndex<1>{});
   }
   if (hT) {
 #pragma unroll
@@ -275,7 +277,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in
 }
 
 // Helper wave Y: output token tiles R = 2 Y, 2 Y + 1 (rows 32 Y .. 32 Y + 31).
-template <int Y>
+template <int kDepth, int Y>
 __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &in,
                                             float *__restrict__ o, u32x4 (*xch)[kXchFrags][64]) {
   constexpr int kNQ = Y + 1;                 // token blocks of v' this wave contracts over
@@ -294,9 +296,9 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
     r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     return r;
   };
-  f16x8 qf[2][8];            // q16 fragment (token tile 2 Y + Rl, key block p) at [4 Rl + p]
-  bf16x8 pf[2][2 * kPairs];  // P pair kPair0 + n, term t at [2 n + t]
-  u32x2 exs[2];              // scale * e^{gamma_r} (fp32 bits), r = 16 (2 Y + Rl) + c
+  f16x8 qf[kDepth][8];            // q16 fragment (token tile 2 Y + Rl, key block p) at [4 Rl + p]
+  bf16x8 pf[kDepth][2 * kPairs];  // P pair kPair0 + n, term t at [2 n + t]
+  u32x2 exs[kDepth];              // scale * e^{gamma_r} (fp32 bits), r = 16 (2 Y + Rl) + c
   auto load_q = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
 #pragma unroll
@@ -319,7 +321,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
   };
   auto step = [&](const int c, auto Bc) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
-    const Rsrc rn = rsrc_of(c + 2);
+    const Rsrc rn = rsrc_of(c + kDepth);
     lds_barrier();  // chunk c handed over
     const u32x4 *xb = &xch[c & 1][0][L.lane];
     f16x8 s16[4];
@@ -366,14 +368,14 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
   };
 
   load_all(SetIndex<0>{}, rsrc_of(0));
-  load_all(SetIndex<1>{}, rsrc_of(1));
-  for (int c = 0; c < L.nc; c += 2) {
+  if constexpr (kDepth == 2) load_all(SetIndex<1>{}, rsrc_of(1));
+  for (int c = 0; c < L.nc; c += kDepth) {  // a step past the last chunk changes nothing
     step(c, SetIndex<0>{});
-    step(c + 1, SetIndex<1>{});
+    if constexpr (kDepth == 2) step(c + 1, SetIndex<1>{});
   }
 }
 
-template <bool kF32In>
+template <bool kF32In, int kDepth>
 __global__ __launch_bounds__(kInterThreads) void inter_kernel(StageBuffers in, const float *__restrict__ h0,
                                                               const int32_t *__restrict__ cu,
                                                               float *__restrict__ o, float *__restrict__ hT,
@@ -405,13 +407,27 @@ __global__ __launch_bounds__(kInterThreads) void inter_kernel(StageBuffers in, c
   L.nt = nt;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0)
-    chain_wave<kF32In, 0>(L, in, h0, hT, xch);
+    chain_wave<kF32In, kDepth, 0>(L, in, h0, hT, xch);
   else if (wave == 1)
-    chain_wave<kF32In, 1>(L, in, h0, hT, xch);
+    chain_wave<kF32In, kDepth, 1>(L, in, h0, hT, xch);
   else if (wave == 2)
-    helper_wave<0>(L, in, o, xch);
+    helper_wave<kDepth, 0>(L, in, o, xch);
   else
-    helper_wave<1>(L, in, o, xch);
+    helper_wave<kDepth, 1>(L, in, o, xch);
+}
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
 }
 
 template <bool kF32In>
@@ -422,8 +438,12 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
   const int groups = n_max * h;
   const int rounds = (groups + kXcds - 1) / kXcds;
   const dim3 grid(rounds * kXcds * members);
-  hipExtLaunchKernelGGL((inter_kernel<kF32In>), grid, dim3(kInterThreads), 0, stream, ev.start,
-                        ev.stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
+  if (static_cast<int>(grid.x) <= cu_count())
+    hipExtLaunchKernelGGL((inter_kernel<kF32In, 2>), grid, dim3(kInterThreads), 0, stream, ev.start,
+                          ev.stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
+  else
+    hipExtLaunchKernelGGL((inter_kernel<kF32In, 1>), grid, dim3(kInterThreads), 0, stream, ev.start,
+                          ev.stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
   return hipGetLastError();
 }
 
