@@ -2,8 +2,10 @@
 """Benchmark of the chunked gated-delta-rule prefill forward on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input
-already resident in HBM: device chunk-index table -> intra-chunk stage ->
-inter-chunk stage (plus the conv/SiLU/L2 front for workloads that have one),
+already resident in HBM: device chunk-index table (built by stage 1 itself
+for batches of up to 256 sequences, else by its own kernel) -> intra-chunk
+stage -> inter-chunk stage (plus the conv/SiLU/L2 front for workloads that
+have one),
 launched through the C ABI's whole-forward call on torch's current stream.
 W untimed warm-up steps, then exactly K timed steps bracketed by device
 synchronisation; value = tokens x K / wall time of the timed region. Each
@@ -198,7 +200,10 @@ def main():
     else:
         q, k, v = d["q"], d["k"], d["v"]
 
-    stages = (["front"] if has_front else []) + ["index", "intra", "inter"]
+    # without a caller table, batches of at most GDN_FUSED_INDEX_MAX_SEQS
+    # sequences have stage 1 locate its chunks (and fill the table) itself
+    table_kernel = wl.n_max > gdn.GDN_FUSED_INDEX_MAX_SEQS
+    stages = (["front"] if has_front else []) + (["index"] if table_kernel else []) + ["intra", "inter"]
     hip = HipEvents()
 
     def step(evs=None):

@@ -27,11 +27,12 @@ __all__ = [
     "gdn_nt_max", "gdn_workspace_size", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
     "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
     "gdn_workspace_layout", "make_config", "chunk_gated_delta_rule", "EXPORTED_SYMBOLS",
-    "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed",
+    "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "GDN_FUSED_INDEX_MAX_SEQS",
 ]
 
 GDN_BF16 = 0
 GDN_F32 = 1
+GDN_FUSED_INDEX_MAX_SEQS = 256  # include/gdn.h
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
            3: "GDN_ERR_CAPACITY", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_layout", "gdn_workspace_size",

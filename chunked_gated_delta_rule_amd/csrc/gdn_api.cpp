@@ -120,18 +120,19 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
       (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return GDN_ERR_INVALID_ARG;
   hipStream_t s = as_stream(stream);
-  if (!chunk_indices) {
-    int32_t *table = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + l.table);
+  int32_t *ws_table = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + l.table);
+  if (!chunk_indices && cfg->n_max > GDN_FUSED_INDEX_MAX_SEQS) {
     const hipError_t e =
-        gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), table, s, ev[0]);
+        gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), ws_table, s, ev[0]);
     if (e != hipSuccess) return GDN_ERR_HIP;
-    chunk_indices = table;
+    chunk_indices = ws_table;
   }
   const gdn::StageBuffers b = stage_buffers(l, workspace);
   if (cfg->t_max > 0) {
+    // without a table, stage 1 locates its chunks and fills ws_table itself
     const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
-                                           chunk_indices, nt_max_of(cfg), cfg->h, cfg->hv,
-                                           cfg->t_max, scale_of(cfg), b, s, ev[1]);
+                                           chunk_indices, ws_table, cfg->n_max, nt_max_of(cfg),
+                                           cfg->h, cfg->hv, cfg->t_max, scale_of(cfg), b, s, ev[1]);
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
   return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, b, h0, cu_seqlens, cfg->n_max,
@@ -206,8 +207,9 @@ gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *q, const void 
   if (ws != GDN_OK) return ws;
   if (cfg->t_max == 0) return GDN_OK;
   return from_hip(gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
-                                    chunk_indices, nt_max_of(cfg), cfg->h, cfg->hv, cfg->t_max,
-                                    scale_of(cfg), stage_buffers(l, workspace), as_stream(stream)));
+                                    chunk_indices, nullptr, cfg->n_max, nt_max_of(cfg), cfg->h,
+                                    cfg->hv, cfg->t_max, scale_of(cfg), stage_buffers(l, workspace),
+                                    as_stream(stream)));
 }
 
 gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int32_t *cu_seqlens,

@@ -160,4 +160,48 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
   return x;
 }
 
+// Inclusive prefix sum of integers over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan_int(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Batches of at most this many sequences let stage 1 locate its chunk from
+// cu_seqlens itself (one pass of 64-lane scans per wave).
+constexpr int kFusedIndexMaxSeqs = 256;
+
+// Entry `slot` of the chunk-index table, computed by one wave from cu_seqlens
+// (n_max <= kFusedIndexMaxSeqs): (sequence, chunk within the sequence) of the
+// slot-th chunk of the batch in (sequence, chunk) order, or (-1, -1) past the
+// last chunk. Empty sequences own no chunk. Same definition as the table
+// kernel's searchsorted fill.
+__device__ __forceinline__ int2 locate_chunk(const int32_t *__restrict__ cu, int n_max, int slot,
+                                             int lane) {
+  constexpr int kBlocks = kFusedIndexMaxSeqs / 64;
+  int nc[kBlocks];
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) {  // all loads first: one round trip
+    const int s = 64 * b + lane;
+    nc[b] = s < n_max ? (cu[s + 1] - cu[s] + kC - 1) / kC : 0;
+  }
+  int base = 0;  // chunks of the sequences before this block
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) {
+    if (64 * b >= n_max) break;
+    const int incl = wave_inclusive_scan_int(nc[b], lane);
+    const int excl = base + incl - nc[b];
+    const unsigned long long hit = __ballot(nc[b] > 0 && excl <= slot && slot < excl + nc[b]);
+    if (hit) {
+      const int src = __ffsll(static_cast<long long>(hit)) - 1;
+      return make_int2(64 * b + src, slot - __shfl(excl, src, 64));
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return make_int2(-1, -1);
+}
+
 }  // namespace gdn

@@ -37,10 +37,14 @@ hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
                         int32_t hv, float *q, float *k, float *v, hipStream_t stream,
                         KernelEvents ev = {});
 
+// table: the chunk-index table, or null to have each work-group locate its
+// chunk from cu_seqlens (n_max <= kFusedIndexMaxSeqs) and write the table into
+// table_out.
 hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const int32_t *cu_seqlens, const int32_t *table,
-                        int32_t nt_max, int32_t h, int32_t hv, int32_t t_max, float scale,
-                        const StageBuffers &out, hipStream_t stream, KernelEvents ev = {});
+                        int32_t *table_out, int32_t n_max, int32_t nt_max, int32_t h, int32_t hv,
+                        int32_t t_max, float scale, const StageBuffers &out, hipStream_t stream,
+                        KernelEvents ev = {});
 
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,

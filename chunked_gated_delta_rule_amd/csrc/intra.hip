@@ -49,10 +49,13 @@
 //    registers, so w and u are formed in one pass with no staging buffer.
 // Rows of a partial last chunk are zero-filled, so they add nothing; every
 // per-chunk block is written in full (zeros past the end).
+#include "gdn.h"
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
+
+static_assert(kFusedIndexMaxSeqs == GDN_FUSED_INDEX_MAX_SEQS, "fused index bound");
 
 namespace {
 
@@ -159,8 +162,8 @@ template <bool kF32In>
 __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     const void *__restrict__ qin, const void *__restrict__ kin, const void *__restrict__ vin,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ table, StageBuffers out, int H, int Hv, int t_max, int nt,
-    float scale) {
+    const int32_t *__restrict__ table, int32_t *__restrict__ table_out, int n_max,
+    StageBuffers out, int H, int Hv, int t_max, int nt, float scale) {
   using Smem = IntraSmem<kF32In>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Smem::kBytes];
   __bf16 *r1 = reinterpret_cast<__bf16 *>(smem);
@@ -176,7 +179,16 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   float *gsh = xs + 4 * 16 * kLdX + wv * 3 * 64;  // this wave's gate copies
   float *bsh = gsh + 64;
   float *swsh = bsh + 64;
-  const int2 ent = reinterpret_cast<const int2 *>(table)[blockIdx.x];
+  // this work-group's chunk: from the caller's table, or located from
+  // cu_seqlens here (every wave computes it; the key-head-0 work-groups also
+  // fill the workspace copy of the table)
+  int2 ent;
+  if (table) {
+    ent = reinterpret_cast<const int2 *>(table)[blockIdx.x];
+  } else {
+    ent = locate_chunk(cu, n_max, blockIdx.x, lane);
+    if (blockIdx.y == 0 && tid == 0) reinterpret_cast<int2 *>(table_out)[blockIdx.x] = ent;
+  }
   if (ent.x < 0) return;  // sentinel slot
   const int h = blockIdx.y;
   const int HG = Hv / H;
@@ -545,16 +557,20 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
 
 hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const int32_t *cu_seqlens, const int32_t *table,
-                        int32_t nt_max, int32_t h, int32_t hv, int32_t t_max, float scale,
+                        int32_t *table_out, int32_t n_max, int32_t nt_max, int32_t h, int32_t hv,
+                        int32_t t_max, float scale,
                         const StageBuffers &out, hipStream_t stream, KernelEvents ev) {
+  if (!table && (n_max > kFusedIndexMaxSeqs || !table_out)) return hipErrorInvalidValue;
   if (nt_max <= 0) return hipSuccess;
   const dim3 grid(nt_max, h);
   if (f32_in) {
     hipExtLaunchKernelGGL(intra_kernel<true>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop,
-                          0, q, k, v, g, beta, cu_seqlens, table, out, h, hv, t_max, nt_max, scale);
+                          0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, hv, t_max,
+                          nt_max, scale);
   } else {
     hipExtLaunchKernelGGL(intra_kernel<false>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop,
-                          0, q, k, v, g, beta, cu_seqlens, table, out, h, hv, t_max, nt_max, scale);
+                          0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, hv, t_max,
+                          nt_max, scale);
   }
   return hipGetLastError();
 }

@@ -67,6 +67,13 @@ typedef struct {
 #define GDN_T_MAX_LIMIT (1 << 24)
 #define GDN_N_MAX_LIMIT 16384
 
+/* gdn_chunk_fwd without a caller table: up to this many sequences (n_max),
+ * each stage-1 work-group locates its chunk from cu_seqlens itself and the
+ * table is filled in the workspace by stage 1; beyond it a table kernel runs
+ * first. Either way the workspace table ends up as gdn_build_chunk_indices
+ * would write it. */
+#define GDN_FUSED_INDEX_MAX_SEQS 256
+
 /* Static bound on the number of chunks of any batch of at most t_max tokens in
  * at most n_max sequences: cdiv(t_max, chunk) + n_max - 1 (FLA issue 1155,
  * "Core design"). Returns -1 if an argument is not positive (t_max may be 0). */
@@ -157,11 +164,13 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
                                const void *workspace, size_t ws_bytes, void *o, float *hT,
                                void *stream);
 
-/* Whole forward: [chunk table if chunk_indices is NULL] -> intra -> inter, all
- * on `stream`, no host synchronisation. Arguments as above; workspace (device)
- * of at least gdn_workspace_size bytes, 256-byte aligned, holds the
- * intermediates and the table between the stages and may be reused once the
- * stream passes the call. */
+/* Whole forward: [chunk table if chunk_indices is NULL and n_max >
+ * GDN_FUSED_INDEX_MAX_SEQS] -> intra -> inter, all on `stream`, no host
+ * synchronisation. Arguments as above; workspace (device) of at least
+ * gdn_workspace_size bytes, 256-byte aligned, holds the intermediates and the
+ * table between the stages (when chunk_indices is NULL the table is built in
+ * it, by the table kernel or by stage 1) and may be reused once the stream
+ * passes the call. */
 gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,
                          const float *g, const float *beta, const float *h0,
                          const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
@@ -173,9 +182,10 @@ gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, co
  * packet is added between launches and the elapsed time between a pair is
  * the kernel's execution time).
  *   events (host array of 6 hipEvent_t passed as void*, each created by the
- *          caller): [0], [1] around the chunk table (recorded only when
- *          chunk_indices is NULL), [2], [3] around the intra stage, [4], [5]
- *          around the inter stage.
+ *          caller): [0], [1] around the chunk table kernel (recorded only when
+ *          that kernel runs: chunk_indices NULL and n_max >
+ *          GDN_FUSED_INDEX_MAX_SEQS), [2], [3] around the intra stage, [4],
+ *          [5] around the inter stage.
  *   ev_start, ev_stop: around the front kernel.
  * A NULL event returns GDN_ERR_INVALID_ARG before any launch. */
 gdn_status gdn_chunk_fwd_timed(const gdn_config *cfg, const void *q, const void *k, const void *v,

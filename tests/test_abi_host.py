@@ -166,3 +166,9 @@ def test_timed_entry_points_host_errors(lib):
     assert timed(vp6(1, 2, 3, 4, 5, 6), ws_bytes=need - 1) == WORKSPACE
     assert lib.gdn_front_conv_silu_l2_timed(c, F, F, 4, F, F, F, F, None, None, 8) == INVALID
     assert lib.gdn_front_conv_silu_l2_timed(c, F, F, 9, F, F, F, F, None, 8, 8) == UNSUPPORTED
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_FUSED_INDEX_MAX_SEQS (\d+)", text)
+    assert m and int(m.group(1)) == gdn.GDN_FUSED_INDEX_MAX_SEQS

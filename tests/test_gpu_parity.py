@@ -338,3 +338,33 @@ def _front_for(wl, seqs):
                                          128, 128)
         q[a:e], k[a:e], v[a:e] = qs, ks, vs
     return q, k, v
+
+
+@pytest.mark.parametrize("n", [40, 300])
+def test_forward_without_table_builds_it_in_the_workspace(n):
+    """gdn_chunk_fwd with no caller table: up to GDN_FUSED_INDEX_MAX_SEQS
+    sequences stage 1 locates its chunks and fills the workspace table itself,
+    beyond it the table kernel runs first. Either way the workspace table is
+    bit-exact and the outputs match the oracle on every lane."""
+    rng = np.random.Generator(np.random.PCG64(61 + n))
+    lengths = rng.integers(0, 150, size=n)
+    lengths[::7] = 0
+    wl = workloads.make_custom(lengths, 1, 1, seed=62 + n, h0_sigma=0.02,
+                               t_max=int(lengths.sum()) + 77, n_max=n + 3)
+    log(f"forward without table: n={n} tokens={wl.n_tokens}")
+    d = device_inputs(wl)
+    cfg = config_of(wl)
+    lay = gdn.gdn_workspace_layout(cfg)
+    nt = gdn.gdn_nt_max(wl.t_max, wl.n_max)
+    ws = torch.full((gdn.gdn_workspace_size(cfg),), 123, dtype=torch.uint8, device=DEV)
+    o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=DEV)
+    hT = torch.empty((wl.n_max, wl.Hv, 128, 128), dtype=torch.float32, device=DEV)
+    gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], None, o,
+                      hT, ws)
+    torch.cuda.synchronize()
+    table = ws[lay["table"]:lay["table"] + nt * 8].view(torch.int32).view(nt, 2).cpu().numpy()
+    ref = np.array(index_table.chunk_index_table(list(wl.cu_seqlens), nt), dtype=np.int32)
+    assert np.array_equal(table, ref)
+    eo, es = lane_errors(wl, o, hT, oracle_lanes(wl, _all_lanes(wl)))
+    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
