@@ -83,28 +83,56 @@ struct IntraSmem {
   static_assert(kTerms * 64 * kLdRow * 2 <= kR3 + kR4, "q tile must fit regions 3-4");
 };
 
-// Load 4 rows x 8 columns of a [rows, heads, 128] tile starting at token row
-// `row0` (rows >= valid are zero) as bf16 hi (and lo for fp32 input).
+// A tile of a [rows, heads, 128] tensor: rows t0 .. t0 + L - 1 of one head,
+// as a buffer range that ends after row L - 1, so rows past the chunk read as
+// zero with no branch (row stride `heads` x 128 elements).
 template <bool kF32In>
-__device__ __forceinline__ void load_rows4x8(const void *base, int64_t row_stride, int row0,
-                                             int valid, int col, u32x4 (&hi)[4], u32x4 (&lo)[4]) {
+struct Tile {
+  rsrc_t r;
+  uint32_t row_bytes;
+};
+
+template <bool kF32In>
+__device__ __forceinline__ Tile<kF32In> tile_of(const void *base, int t0, int heads, int head,
+                                                int L) {
+  constexpr int kEl = kF32In ? 4 : 2;
+  const uint32_t row_bytes = static_cast<uint32_t>(heads) * kD * kEl;
+  const char *p = static_cast<const char *>(base) + ((int64_t)t0 * heads + head) * kD * kEl;
+  return Tile<kF32In>{make_rsrc(p, static_cast<uint32_t>(L) * row_bytes), row_bytes};
+}
+
+// Raw 16-byte words of 4 rows x 8 columns of a tile starting at row `row0`
+// (fp32 input: two words per row).
+template <bool kF32In>
+struct Raw4x8 {
+  u32x4 w[4][kF32In ? 2 : 1];
+};
+
+template <bool kF32In>
+__device__ __forceinline__ Raw4x8<kF32In> load_raw4x8(const Tile<kF32In> &t, int row0, int col) {
+  constexpr int kEl = kF32In ? 4 : 2;
+  Raw4x8<kF32In> x;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int r = row0 + rr;
-    if (r < valid) {
-      if constexpr (kF32In) {
-        const float *p = static_cast<const float *>(base) + (int64_t)r * row_stride + col;
-        const f32x4 a = reinterpret_cast<const f32x4 *>(p)[0];
-        const f32x4 b = reinterpret_cast<const f32x4 *>(p)[1];
-        const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        split8_words(x, hi[rr], lo[rr]);
-      } else {
-        const uint16_t *p = static_cast<const uint16_t *>(base) + (int64_t)r * row_stride + col;
-        hi[rr] = *reinterpret_cast<const u32x4 *>(p);
-        lo[rr] = u32x4{0u, 0u, 0u, 0u};
-      }
+    const uint32_t off = (row0 + rr) * t.row_bytes + col * kEl;
+    x.w[rr][0] = buf_load16(t.r, off);
+    if constexpr (kF32In) x.w[rr][1] = buf_load16(t.r, off + 16);
+  }
+  return x;
+}
+
+// The raw words as bf16 hi (and lo for fp32 input, x = hi + lo).
+template <bool kF32In>
+__device__ __forceinline__ void to_terms(const Raw4x8<kF32In> &x, u32x4 (&hi)[4], u32x4 (&lo)[4]) {
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    if constexpr (kF32In) {
+      const f32x4 a = __builtin_bit_cast(f32x4, x.w[rr][0]);
+      const f32x4 b = __builtin_bit_cast(f32x4, x.w[rr][1]);
+      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      split8_words(v, hi[rr], lo[rr]);
     } else {
-      hi[rr] = u32x4{0u, 0u, 0u, 0u};
+      hi[rr] = x.w[rr][0];
       lo[rr] = u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -187,6 +215,8 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     ent = reinterpret_cast<const int2 *>(table)[blockIdx.x];
   } else {
     ent = locate_chunk(cu, n_max, blockIdx.x, lane);
+    ent.x = __builtin_amdgcn_readfirstlane(ent.x);  // the same in every lane
+    ent.y = __builtin_amdgcn_readfirstlane(ent.y);
     if (blockIdx.y == 0 && tid == 0) reinterpret_cast<int2 *>(table_out)[blockIdx.x] = ent;
   }
   if (ent.x < 0) return;  // sentinel slot
@@ -197,28 +227,25 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   const int L = min(kC, cu[ent.x + 1] - t0);
   const int slot = (t0 >> 6) + ent.x;
   constexpr int kNK = kF32In ? 32 : 16;
-  constexpr int kEl = kF32In ? 4 : 2;
 
   const int lrow = 4 * (tid >> 4);  // this thread's 4 rows and 8 columns of a tile
   const int lcol = 8 * (tid & 15);
 
-  // ---- requests: K, q, then V / g / beta of the first value head ----------
-  u32x4 khi[4], klo[4], qhi[4], qlo[4], vhi[4], vlo[4];
-  load_rows4x8<kF32In>(static_cast<const char *>(kin) + ((int64_t)t0 * H + h) * kD * kEl,
-                       (int64_t)H * kD, lrow, L, lcol, khi, klo);
-  load_rows4x8<kF32In>(static_cast<const char *>(qin) + ((int64_t)t0 * H + h) * kD * kEl,
-                       (int64_t)H * kD, lrow, L, lcol, qhi, qlo);
-  auto load_v = [&](int hv) __attribute__((always_inline)) {
-    load_rows4x8<kF32In>(static_cast<const char *>(vin) + ((int64_t)t0 * Hv + hv) * kD * kEl,
-                         (int64_t)Hv * kD, lrow, L, lcol, vhi, vlo);
-  };
+  // ---- requests: K, q, then V / g / beta of the first value head (buffer
+  // loads, rows past the chunk read as zero) -------------------------------
+  const Raw4x8<kF32In> kraw = load_raw4x8(tile_of<kF32In>(kin, t0, H, h, L), lrow, lcol);
+  const Raw4x8<kF32In> qraw = load_raw4x8(tile_of<kF32In>(qin, t0, H, h, L), lrow, lcol);
+  Raw4x8<kF32In> vraw = load_raw4x8(tile_of<kF32In>(vin, t0, Hv, h * HG, L), lrow, lcol);
   const bool tok_ok = lane < L;
+  const uint32_t gate_bytes = static_cast<uint32_t>(L) * Hv * 4;
   auto load_gate = [&](const float *p, int hv) __attribute__((always_inline)) {
-    return tok_ok ? p[(int64_t)(t0 + lane) * Hv + hv] : 0.f;
+    return buf_load_f32(make_rsrc(p + (int64_t)t0 * Hv + hv, gate_bytes), lane * Hv * 4);
   };
-  load_v(h * HG);
   float g_next = load_gate(g, h * HG);
   float b_next = load_gate(beta, h * HG);
+  u32x4 khi[4], klo[4], qhi[4], qlo[4];
+  to_terms(kraw, khi, klo);
+  to_terms(qraw, qhi, qlo);
 
   // ---- K tile -> LDS (row-major in region 1, transposed in region 2) ------
 #pragma unroll
@@ -356,18 +383,18 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
 
   for (int gi = 0; gi < HG; ++gi) {
     const int hv = h * HG + gi;
-    // ---- this value head's operands, next value head's requests -----------
+    // ---- this value head's operands, next value head's requests (a request
+    // past the group reads an empty range) ----------------------------------
     u32x4 vh[4], vl[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      vh[rr] = vhi[rr];
-      vl[rr] = vlo[rr];
-    }
+    to_terms(vraw, vh, vl);
     const float gv = g_next, bv = b_next;
-    if (gi + 1 < HG) {
-      load_v(hv + 1);
-      g_next = load_gate(g, hv + 1);
-      b_next = load_gate(beta, hv + 1);
+    {
+      const int nx = gi + 1 < HG ? hv + 1 : hv;
+      const int Ln = gi + 1 < HG ? L : 0;
+      vraw = load_raw4x8(tile_of<kF32In>(vin, t0, Hv, nx, Ln), lrow, lcol);
+      const uint32_t gb = static_cast<uint32_t>(Ln) * Hv * 4;
+      g_next = buf_load_f32(make_rsrc(g + (int64_t)t0 * Hv + nx, gb), lane * Hv * 4);
+      b_next = buf_load_f32(make_rsrc(beta + (int64_t)t0 * Hv + nx, gb), lane * Hv * 4);
     }
 
     // ---- gates: each wave scans its own copy (lane = token) ---------------
