@@ -40,20 +40,22 @@ SOLVE_FLOP = 83328           # 64x64 unit-lower inverse: 41,664 multiply-adds
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
-def algorithmic_work(wl, nt, qkv_bytes):
+def algorithmic_work(wl, nt, qkv_bytes, fused_front=False):
     """Bytes and flops each stage must move / perform (counted once; partial
-    chunks counted as whole 64-token chunks for flops)."""
+    chunks counted as whole 64-token chunks for flops). With the front fused
+    into stage 1, that stage reads the pre-conv bf16 q|k|v channels instead of
+    k and v."""
     T, H, Hv, D = wl.n_tokens, wl.H, wl.Hv, 128
     HG = Hv // H
     n_state = len(wl.cu_seqlens) - 1
-    stage1_bytes = T * (H * D * qkv_bytes + Hv * D * qkv_bytes + Hv * 4 + Hv * 4
-                        + Hv * D * 2 + Hv * D * 4)
+    stage1_in = (2 * H + Hv) * D * 2 if fused_front else H * D * qkv_bytes + Hv * D * qkv_bytes
+    stage1_bytes = T * (stage1_in + Hv * 4 + Hv * 4 + Hv * D * 2 + Hv * D * 4)
     stage2_bytes = T * (2 * H * D * qkv_bytes + Hv * D * 2 + Hv * D * 4 + Hv * 4 + Hv * D * 4)
     stage2_bytes += n_state * Hv * D * D * 4 * (2 if wl.h0 is not None else 1)
     stage1_flop = nt * H * (2 * 64 * 64 * D + HG * (2 * 2 * 64 * 64 * D + SOLVE_FLOP))
     stage2_flop = nt * Hv * (3 * 2 * 64 * D * D + 2 * 2 * 64 * 64 * D)
     front_bytes = 0
-    if wl.qkv is not None:
+    if wl.qkv is not None and not fused_front:
         C = (2 * H + Hv) * D
         front_bytes = T * C * 2 + T * C * 4
     return dict(intra=(stage1_bytes, stage1_flop), inter=(stage2_bytes, stage2_flop),
@@ -158,6 +160,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1, help="named workload 0..4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused-front", action="store_true",
+                    help="front workload: run the standalone front, then the forward "
+                         "(default: the front fused into stage 1)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
@@ -188,12 +193,13 @@ def main():
          for n in ("q", "k", "v", "g", "beta", "h0", "qkv", "conv_w")}
     cu = torch.from_numpy(wl.cu_seqlens).to(dev)
     has_front = wl.qkv is not None
+    fused_front = has_front and not args.unfused_front
     qkv_dtype = torch.float32 if has_front else wl.qkv_dtype
     cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype)
     ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=dev)
     o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
     hT = torch.empty((wl.n_max, wl.Hv, 128, 128), dtype=torch.float32, device=dev)
-    if has_front:
+    if has_front and not fused_front:
         q = torch.empty((wl.t_max, wl.H, 128), dtype=torch.float32, device=dev)
         k = torch.empty_like(q)
         v = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
@@ -203,10 +209,19 @@ def main():
     # without a caller table, batches of at most GDN_FUSED_INDEX_MAX_SEQS
     # sequences have stage 1 locate its chunks (and fill the table) itself
     table_kernel = wl.n_max > gdn.GDN_FUSED_INDEX_MAX_SEQS
-    stages = (["front"] if has_front else []) + (["index"] if table_kernel else []) + ["intra", "inter"]
+    stages = (["front"] if has_front and not fused_front else []) + \
+        (["index"] if table_kernel else []) + ["intra", "inter"]
     hip = HipEvents()
 
     def step(evs=None):
+        if fused_front:
+            if evs is None:
+                gdn.gdn_chunk_fwd_conv(cfg, d["qkv"], d["conv_w"], wl.d_conv, d["g"], d["beta"],
+                                       d["h0"], cu, None, o, hT, ws)
+            else:
+                gdn.gdn_chunk_fwd_conv_timed(cfg, d["qkv"], d["conv_w"], wl.d_conv, d["g"],
+                                             d["beta"], d["h0"], cu, None, o, hT, ws, evs[:6])
+            return
         if has_front:
             if evs is None:
                 gdn.gdn_front_conv_silu_l2(cfg, d["qkv"], d["conv_w"], wl.d_conv, cu, q, k, v)
@@ -236,7 +251,7 @@ def main():
                     for name in stages}
     hip.close()
     chunks = int(sum(-(-int(x) // 64) for x in np.diff(wl.cu_seqlens)))
-    work = algorithmic_work(wl, chunks, 4 if qkv_dtype == torch.float32 else 2)
+    work = algorithmic_work(wl, chunks, 4 if qkv_dtype == torch.float32 else 2, fused_front)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = wl.n_tokens
     detail = {}
@@ -274,7 +289,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": tokens, "sequences": wl.n_seqs, "H": wl.H,
                    "Hv": wl.Hv, "Dk": 128, "Dv": 128, "chunk": 64,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   **({"front": "fused into stage 1" if fused_front else "standalone kernel"}
+                      if has_front else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": detail,

@@ -28,6 +28,7 @@ __all__ = [
     "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
     "gdn_workspace_layout", "make_config", "chunk_gated_delta_rule", "EXPORTED_SYMBOLS",
     "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "GDN_FUSED_INDEX_MAX_SEQS",
+    "gdn_chunk_fwd_conv", "gdn_chunk_fwd_conv_timed",
 ]
 
 GDN_BF16 = 0
@@ -38,7 +39,8 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_layout", "gdn_workspace_size",
                     "gdn_build_chunk_indices", "gdn_front_conv_silu_l2", "gdn_chunk_fwd_intra",
                     "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
-                    "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed")
+                    "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "gdn_chunk_fwd_conv",
+                    "gdn_chunk_fwd_conv_timed")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libgdn.so")
@@ -88,9 +90,13 @@ def load_library():
     lib.gdn_chunk_fwd_timed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                         ctypes.POINTER(vp)]
     lib.gdn_front_conv_silu_l2_timed.argtypes = [cfgp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_conv.argtypes = [cfgp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_chunk_fwd_conv_timed.argtypes = [cfgp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                             vp, ctypes.POINTER(vp)]
     for name in ("gdn_workspace_size", "gdn_workspace_layout", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
                  "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd",
-                 "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed"):
+                 "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "gdn_chunk_fwd_conv",
+                 "gdn_chunk_fwd_conv_timed"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_status_str.restype = ctypes.c_char_p
@@ -223,6 +229,33 @@ def gdn_front_conv_silu_l2_timed(cfg, qkv, conv_w, d_conv, cu_seqlens, q, k, v, 
         ctypes.byref(cfg), _ptr(qkv), _ptr(conv_w), int(d_conv), _ptr(cu_seqlens), _ptr(q),
         _ptr(k), _ptr(v), _stream(stream), int(ev_start), int(ev_stop)),
         "gdn_front_conv_silu_l2_timed")
+
+
+def gdn_chunk_fwd_conv(cfg, qkv, conv_w, d_conv, g, beta, h0, cu_seqlens, chunk_indices, o, hT,
+                       workspace, ws_bytes=None, stream=None):
+    ws_bytes = _ws_bytes(workspace, ws_bytes)
+    _check(load_library().gdn_chunk_fwd_conv(ctypes.byref(cfg), _ptr(qkv), _ptr(conv_w),
+                                             int(d_conv), _ptr(g), _ptr(beta), _ptr(h0),
+                                             _ptr(cu_seqlens), _ptr(chunk_indices), _ptr(o),
+                                             _ptr(hT), _ptr(workspace), int(ws_bytes),
+                                             _stream(stream)),
+           "gdn_chunk_fwd_conv")
+
+
+def gdn_chunk_fwd_conv_timed(cfg, qkv, conv_w, d_conv, g, beta, h0, cu_seqlens, chunk_indices, o,
+                             hT, workspace, events, ws_bytes=None, stream=None):
+    """gdn_chunk_fwd_conv whose kernels record `events` (six raw hipEvent_t
+    handles): table, intra (with the fused front), inter."""
+    ws_bytes = _ws_bytes(workspace, ws_bytes)
+    if len(events) != 6:
+        raise ValueError("six events expected")
+    arr = (ctypes.c_void_p * 6)(*[int(e) for e in events])
+    _check(load_library().gdn_chunk_fwd_conv_timed(ctypes.byref(cfg), _ptr(qkv), _ptr(conv_w),
+                                                   int(d_conv), _ptr(g), _ptr(beta), _ptr(h0),
+                                                   _ptr(cu_seqlens), _ptr(chunk_indices), _ptr(o),
+                                                   _ptr(hT), _ptr(workspace), int(ws_bytes),
+                                                   _stream(stream), arr),
+           "gdn_chunk_fwd_conv_timed")
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, cu_seqlens, initial_state=None,

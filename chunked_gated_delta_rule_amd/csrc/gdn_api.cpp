@@ -107,9 +107,16 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
                           const float *g, const float *beta, const float *h0,
                           const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
                           float *hT, void *workspace, size_t ws_bytes, void *stream,
-                          const gdn::KernelEvents (&ev)[3]) {
+                          const gdn::KernelEvents (&ev)[3], const gdn::ConvIn &conv = {}) {
   const gdn_status st = check_config(cfg);
   if (st != GDN_OK) return st;
+  if (conv.qkv) {  // fused front: q, k, v come from the pre-conv channels
+    if (!conv.conv_w) return GDN_ERR_INVALID_ARG;
+    if (!aligned16(conv.qkv) || (reinterpret_cast<uintptr_t>(conv.conv_w) & 1u))
+      return GDN_ERR_INVALID_ARG;
+    if (conv.d_conv < 1 || conv.d_conv > 4 || cfg->qkv_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+    q = k = v = conv.qkv;
+  }
   if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
   const gdn_workspace_layout_t l = layout_of(cfg);
   const gdn_status ws = check_workspace(l, workspace, ws_bytes);
@@ -132,7 +139,8 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
     // without a table, stage 1 locates its chunks and fills ws_table itself
     const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
                                            chunk_indices, ws_table, cfg->n_max, nt_max_of(cfg),
-                                           cfg->h, cfg->hv, cfg->t_max, scale_of(cfg), b, s, ev[1]);
+                                           cfg->h, cfg->hv, cfg->t_max, scale_of(cfg), b, s, ev[1],
+                                           conv);
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
   return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, b, h0, cu_seqlens, cfg->n_max,
@@ -251,6 +259,40 @@ gdn_status gdn_chunk_fwd_timed(const gdn_config *cfg, const void *q, const void 
     ev[i] = {static_cast<hipEvent_t>(events[2 * i]), static_cast<hipEvent_t>(events[2 * i + 1])};
   return chunk_fwd_impl(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT, workspace,
                         ws_bytes, stream, ev);
+}
+
+gdn_status gdn_chunk_fwd_conv(const gdn_config *cfg, const void *qkv, const void *conv_w,
+                              int32_t d_conv, const float *g, const float *beta, const float *h0,
+                              const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
+                              float *hT, void *workspace, size_t ws_bytes, void *stream) {
+  if (!qkv) return GDN_ERR_INVALID_ARG;
+  const gdn::KernelEvents none[3] = {};
+  gdn::ConvIn conv;
+  conv.qkv = static_cast<const uint16_t *>(qkv);
+  conv.conv_w = static_cast<const uint16_t *>(conv_w);
+  conv.d_conv = d_conv;
+  return chunk_fwd_impl(cfg, nullptr, nullptr, nullptr, g, beta, h0, cu_seqlens, chunk_indices, o,
+                        hT, workspace, ws_bytes, stream, none, conv);
+}
+
+gdn_status gdn_chunk_fwd_conv_timed(const gdn_config *cfg, const void *qkv, const void *conv_w,
+                                    int32_t d_conv, const float *g, const float *beta,
+                                    const float *h0, const int32_t *cu_seqlens,
+                                    const int32_t *chunk_indices, void *o, float *hT,
+                                    void *workspace, size_t ws_bytes, void *stream,
+                                    void *const *events) {
+  if (!qkv || !events) return GDN_ERR_INVALID_ARG;
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return GDN_ERR_INVALID_ARG;
+  gdn::KernelEvents ev[3];
+  for (int i = 0; i < 3; ++i)
+    ev[i] = {static_cast<hipEvent_t>(events[2 * i]), static_cast<hipEvent_t>(events[2 * i + 1])};
+  gdn::ConvIn conv;
+  conv.qkv = static_cast<const uint16_t *>(qkv);
+  conv.conv_w = static_cast<const uint16_t *>(conv_w);
+  conv.d_conv = d_conv;
+  return chunk_fwd_impl(cfg, nullptr, nullptr, nullptr, g, beta, h0, cu_seqlens, chunk_indices, o,
+                        hT, workspace, ws_bytes, stream, ev, conv);
 }
 
 const char *gdn_status_str(gdn_status status) {

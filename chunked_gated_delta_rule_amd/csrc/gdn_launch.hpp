@@ -23,6 +23,14 @@ struct StageBuffers {
   float *gimg;    // [hv, nt_max, 192]
 };
 
+// Pre-conv input of the fused front: stage 1 computes q, k, v itself from the
+// packed bf16 channels q | k | v (conv + SiLU, and the L2 norm of q and k).
+struct ConvIn {
+  const uint16_t *qkv = nullptr;     // [t_max, (2 h + hv) * 128] bf16
+  const uint16_t *conv_w = nullptr;  // [(2 h + hv) * 128, d_conv] bf16
+  int d_conv = 0;                    // 1..4
+};
+
 // Start / end events recorded by one dispatch (both may be null).
 struct KernelEvents {
   hipEvent_t start = nullptr;
@@ -39,12 +47,13 @@ hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
 
 // table: the chunk-index table, or null to have each work-group locate its
 // chunk from cu_seqlens (n_max <= kFusedIndexMaxSeqs) and write the table into
-// table_out.
+// table_out. With conv.qkv set, q, k, v are ignored and computed from the
+// pre-conv channels (f32_in must then be true).
 hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const int32_t *cu_seqlens, const int32_t *table,
                         int32_t *table_out, int32_t n_max, int32_t nt_max, int32_t h, int32_t hv,
                         int32_t t_max, float scale, const StageBuffers &out, hipStream_t stream,
-                        KernelEvents ev = {});
+                        KernelEvents ev = {}, ConvIn conv = {});
 
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,

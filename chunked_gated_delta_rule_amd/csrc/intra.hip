@@ -138,6 +138,75 @@ __device__ __forceinline__ void to_terms(const Raw4x8<kF32In> &x, u32x4 (&hi)[4]
   }
 }
 
+// ---- fused front: 4 rows x 8 channels of q, k or v computed from the
+// pre-conv bf16 channels (rows t0 + row0 - 3 .. t0 + row0 + 3 and the 8
+// channels' taps), with the same arithmetic, in the same order, as the
+// standalone front kernel: conv taps accumulated oldest first by fmaf, SiLU
+// x / (1 + e^-x), and for q and k the 16-lane sum of squares of the head and
+// x / sqrt(sum + 1e-6).
+struct ConvRaw {
+  u32x4 x[7];  // source rows t0 + row0 - 3 + i (zero before the sequence start)
+  u32x4 w[4];  // conv weights of the 8 channels, [channel][tap], up to 4 taps
+};
+
+// tb: first row the buffer range starts at (max(bos, t0 - (d_conv - 1)));
+// rows_end: one past the last row that may be read.
+__device__ __forceinline__ ConvRaw load_conv(const ConvIn &ci, int channels, int ch0, int t0,
+                                             int rows_end, int tb, int row0, int col) {
+  ConvRaw r;
+  const rsrc_t x = make_rsrc(ci.qkv + (int64_t)tb * channels + ch0,
+                             static_cast<uint32_t>(rows_end - tb) * channels * 2);
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    const int rel = t0 + row0 - 3 + i - tb;  // negative: before the range, reads zero
+    r.x[i] = buf_load16(x, static_cast<uint32_t>(rel * channels * 2 + col * 2));
+  }
+  const rsrc_t w = make_rsrc(ci.conv_w, static_cast<uint32_t>(channels) * ci.d_conv * 2);
+  const uint32_t wo = static_cast<uint32_t>(ch0 + col) * ci.d_conv * 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.w[i] = i < ci.d_conv ? buf_load16(w, wo + 16 * i) : u32x4{0u, 0u, 0u, 0u};
+  return r;
+}
+
+// Rows rr < valid of the thread's 4 x 8 block as fp32, split into bf16 hi + lo
+// (rows >= valid are zero, as rows past a sequence are for stored inputs).
+// kTaps = d_conv, a template parameter so that every register index is fixed.
+template <int kTaps>
+__device__ __forceinline__ void conv_terms(const ConvRaw &r, bool l2, int valid,
+                                           u32x4 (&hi)[4], u32x4 (&lo)[4]) {
+  float x[7][8];
+#pragma unroll
+  for (int i = 0; i < 7; ++i) unpack8(r.x[i], x[i]);
+  float wf[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) unpack8(r.w[i], wf + 8 * i);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    float y[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < kTaps; ++j) acc = fmaf(x[rr + j + 4 - kTaps][c], wf[c * kTaps + j], acc);
+      y[c] = acc / (1.f + expf(-acc));
+      ss = fmaf(y[c], y[c], ss);
+    }
+    if (l2) {
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      const float inv = 1.f / sqrtf(ss + 1e-6f);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] *= inv;
+    }
+    if (rr >= valid) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = 0.f;
+    }
+    split8_words(y, hi[rr], lo[rr]);
+  }
+}
+
 __device__ __forceinline__ uint16_t half_of(const u32x4 &w, int i) {
   return static_cast<uint16_t>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu);
 }
@@ -186,12 +255,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <bool kF32In>
+// kTaps: 0 reads q, k, v; 1..4 computes them from the pre-conv channels with a
+// kTaps-tap conv (the fused front).
+template <bool kF32In, int kTaps>
 __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     const void *__restrict__ qin, const void *__restrict__ kin, const void *__restrict__ vin,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ table, int32_t *__restrict__ table_out, int n_max,
-    StageBuffers out, int H, int Hv, int t_max, int nt, float scale) {
+    StageBuffers out, int H, int Hv, int t_max, int nt, float scale, ConvIn ci) {
+  constexpr bool kConv = kTaps > 0;
+  static_assert(!kConv || kF32In, "the fused front produces fp32 q, k, v");
   using Smem = IntraSmem<kF32In>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Smem::kBytes];
   __bf16 *r1 = reinterpret_cast<__bf16 *>(smem);
@@ -232,10 +305,27 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   const int lcol = 8 * (tid & 15);
 
   // ---- requests: K, q, then V / g / beta of the first value head (buffer
-  // loads, rows past the chunk read as zero) -------------------------------
-  const Raw4x8<kF32In> kraw = load_raw4x8(tile_of<kF32In>(kin, t0, H, h, L), lrow, lcol);
-  const Raw4x8<kF32In> qraw = load_raw4x8(tile_of<kF32In>(qin, t0, H, h, L), lrow, lcol);
-  Raw4x8<kF32In> vraw = load_raw4x8(tile_of<kF32In>(vin, t0, Hv, h * HG, L), lrow, lcol);
+  // loads, rows past the chunk read as zero); with the fused front, the
+  // pre-conv rows of those heads' channels and their conv weights ----------
+  const int channels = (2 * H + Hv) * kD;
+  const int tb = max(bos, t0 - (ci.d_conv - 1));  // first pre-conv row of the halo
+  auto load_tile = [&](const void *base, int heads, int head, int ch0, int rows)
+      __attribute__((always_inline)) {
+    if constexpr (kConv)
+      return load_conv(ci, channels, ch0, t0, t0 + rows, tb, lrow, lcol);
+    else
+      return load_raw4x8(tile_of<kF32In>(base, t0, heads, head, rows), lrow, lcol);
+  };
+  auto tile_terms = [&](const auto &raw, bool l2, u32x4 (&hi)[4], u32x4 (&lo)[4])
+      __attribute__((always_inline)) {
+    if constexpr (kConv)
+      conv_terms<kTaps>(raw, l2, L - lrow, hi, lo);
+    else
+      to_terms(raw, hi, lo);
+  };
+  const auto kraw = load_tile(kin, H, h, (H + h) * kD, L);
+  const auto qraw = load_tile(qin, H, h, h * kD, L);
+  auto vraw = load_tile(vin, Hv, h * HG, (2 * H + h * HG) * kD, L);
   const bool tok_ok = lane < L;
   const uint32_t gate_bytes = static_cast<uint32_t>(L) * Hv * 4;
   auto load_gate = [&](const float *p, int hv) __attribute__((always_inline)) {
@@ -244,8 +334,8 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   float g_next = load_gate(g, h * HG);
   float b_next = load_gate(beta, h * HG);
   u32x4 khi[4], klo[4], qhi[4], qlo[4];
-  to_terms(kraw, khi, klo);
-  to_terms(qraw, qhi, qlo);
+  tile_terms(kraw, true, khi, klo);
+  tile_terms(qraw, true, qhi, qlo);
 
   // ---- K tile -> LDS (row-major in region 1, transposed in region 2) ------
 #pragma unroll
@@ -386,12 +476,12 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     // ---- this value head's operands, next value head's requests (a request
     // past the group reads an empty range) ----------------------------------
     u32x4 vh[4], vl[4];
-    to_terms(vraw, vh, vl);
+    tile_terms(vraw, false, vh, vl);
     const float gv = g_next, bv = b_next;
     {
       const int nx = gi + 1 < HG ? hv + 1 : hv;
       const int Ln = gi + 1 < HG ? L : 0;
-      vraw = load_raw4x8(tile_of<kF32In>(vin, t0, Hv, nx, Ln), lrow, lcol);
+      vraw = load_tile(vin, Hv, nx, (2 * H + nx) * kD, Ln);
       const uint32_t gb = static_cast<uint32_t>(Ln) * Hv * 4;
       g_next = buf_load_f32(make_rsrc(g + (int64_t)t0 * Hv + nx, gb), lane * Hv * 4);
       b_next = buf_load_f32(make_rsrc(beta + (int64_t)t0 * Hv + nx, gb), lane * Hv * 4);
@@ -586,19 +676,29 @@ hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v
                         const float *beta, const int32_t *cu_seqlens, const int32_t *table,
                         int32_t *table_out, int32_t n_max, int32_t nt_max, int32_t h, int32_t hv,
                         int32_t t_max, float scale,
-                        const StageBuffers &out, hipStream_t stream, KernelEvents ev) {
+                        const StageBuffers &out, hipStream_t stream, KernelEvents ev, ConvIn conv) {
   if (!table && (n_max > kFusedIndexMaxSeqs || !table_out)) return hipErrorInvalidValue;
+  if (conv.qkv && (!f32_in || !conv.conv_w || conv.d_conv < 1 || conv.d_conv > 4))
+    return hipErrorInvalidValue;
   if (nt_max <= 0) return hipSuccess;
   const dim3 grid(nt_max, h);
-  if (f32_in) {
-    hipExtLaunchKernelGGL(intra_kernel<true>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop,
-                          0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, hv, t_max,
-                          nt_max, scale);
+#define GDN_LAUNCH_INTRA(F32, TAPS)                                                             \
+  hipExtLaunchKernelGGL((intra_kernel<F32, TAPS>), grid, dim3(kThreads), 0, stream, ev.start,   \
+                        ev.stop, 0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, \
+                        hv, t_max, nt_max, scale, conv)
+  if (conv.qkv) {
+    switch (conv.d_conv) {
+      case 1: GDN_LAUNCH_INTRA(true, 1); break;
+      case 2: GDN_LAUNCH_INTRA(true, 2); break;
+      case 3: GDN_LAUNCH_INTRA(true, 3); break;
+      default: GDN_LAUNCH_INTRA(true, 4); break;
+    }
+  } else if (f32_in) {
+    GDN_LAUNCH_INTRA(true, 0);
   } else {
-    hipExtLaunchKernelGGL(intra_kernel<false>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop,
-                          0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, hv, t_max,
-                          nt_max, scale);
+    GDN_LAUNCH_INTRA(false, 0);
   }
+#undef GDN_LAUNCH_INTRA
   return hipGetLastError();
 }
 

@@ -176,6 +176,23 @@ gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, co
                          const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
                          float *hT, void *workspace, size_t ws_bytes, void *stream);
 
+/* Whole forward with the front fused into the intra stage (the "next" step
+ * after gdn_front_conv_silu_l2 + gdn_chunk_fwd): each stage-1 work-group
+ * computes its chunk's q, k (conv, SiLU, per-head L2 norm) and v (conv,
+ * SiLU) itself from the pre-conv channels, reading a (d_conv - 1)-token halo
+ * before the chunk (zero before each sequence start), with the same fp32
+ * arithmetic as gdn_front_conv_silu_l2 (llama.cpp PR 399, "How (exactness)";
+ * AMX page, section 7). The fp32 q, k, v never reach HBM; the result equals
+ * gdn_front_conv_silu_l2 followed by gdn_chunk_fwd on its fp32 outputs.
+ *   qkv    (device) bf16 [t_max, 2*h*dk + hv*dv], channels q | k | v, head-major
+ *   conv_w (device) bf16 [2*h*dk + hv*dv, d_conv], 1 <= d_conv <= 4
+ *   cfg->qkv_dtype must be GDN_F32 (the workspace holds fp32-split q, k, v
+ *   intermediates: size it with GDN_F32); other arguments as gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_conv(const gdn_config *cfg, const void *qkv, const void *conv_w,
+                              int32_t d_conv, const float *g, const float *beta, const float *h0,
+                              const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
+                              float *hT, void *workspace, size_t ws_bytes, void *stream);
+
 /* Timed variants, for measurement. They behave exactly like the entry point
  * they extend, and in addition each kernel they launch records a pair of HIP
  * events at its own start and end (the dispatch itself records them, so no
@@ -197,6 +214,12 @@ gdn_status gdn_front_conv_silu_l2_timed(const gdn_config *cfg, const void *qkv,
                                         const void *conv_w, int32_t d_conv,
                                         const int32_t *cu_seqlens, float *q, float *k, float *v,
                                         void *stream, void *ev_start, void *ev_stop);
+gdn_status gdn_chunk_fwd_conv_timed(const gdn_config *cfg, const void *qkv, const void *conv_w,
+                                    int32_t d_conv, const float *g, const float *beta,
+                                    const float *h0, const int32_t *cu_seqlens,
+                                    const int32_t *chunk_indices, void *o, float *hT,
+                                    void *workspace, size_t ws_bytes, void *stream,
+                                    void *const *events);
 
 /* Static string for a status code (never NULL). */
 const char *gdn_status_str(gdn_status status);

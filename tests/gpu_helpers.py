@@ -70,6 +70,21 @@ def run_forward(wl, d=None, dev="cuda:0", h0=None, hT=None, chunk_indices=None):
     return o, hT, (q, k, v)
 
 
+def run_forward_conv(wl, d=None, dev="cuda:0", chunk_indices=None):
+    """Whole forward with the front fused into stage 1 (gdn_chunk_fwd_conv).
+    Returns (o, hT)."""
+    if d is None:
+        d = device_inputs(wl, dev)
+    cfg = config_of(wl, torch.float32)
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=dev)
+    o = torch.full((wl.t_max, wl.Hv, 128), float("nan"), dtype=torch.float32, device=dev)
+    hT = torch.full((wl.n_max, wl.Hv, 128, 128), float("nan"), dtype=torch.float32, device=dev)
+    gdn.gdn_chunk_fwd_conv(cfg, d["qkv"], d["conv_w"], wl.d_conv, d["g"], d["beta"], d["h0"],
+                           d["cu"], chunk_indices, o, hT, ws)
+    torch.cuda.synchronize()
+    return o, hT
+
+
 def oracle_inputs_f64(wl):
     """q, k, v in float64 as the oracle sees them (through the fp64 front when
     the workload has one)."""

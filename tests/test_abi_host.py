@@ -172,3 +172,27 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     m = re.search(r"#define GDN_FUSED_INDEX_MAX_SEQS (\d+)", text)
     assert m and int(m.group(1)) == gdn.GDN_FUSED_INDEX_MAX_SEQS
+
+
+def test_fused_front_entry_point_host_errors(lib):
+    cfg = gdn.make_config(256, 2, 16, 32, gdn.GDN_F32)
+    c = ctypes.byref(cfg)
+    F = FAKE
+    need = gdn.gdn_workspace_size(cfg)
+    # (cfg, qkv, conv_w, d_conv, g, beta, h0, cu, ci, o, hT, ws, ws_bytes, stream)
+    assert lib.gdn_chunk_fwd_conv(c, None, F, 4, F, F, None, F, None, F, None, F, need, None) == INVALID
+    assert lib.gdn_chunk_fwd_conv(c, F, None, 4, F, F, None, F, None, F, None, F, need, None) == INVALID
+    assert lib.gdn_chunk_fwd_conv(c, F, F, 5, F, F, None, F, None, F, None, F, need, None) == UNSUPPORTED
+    assert lib.gdn_chunk_fwd_conv(c, F, F, 0, F, F, None, F, None, F, None, F, need, None) == UNSUPPORTED
+    assert lib.gdn_chunk_fwd_conv(c, F + 2, F, 4, F, F, None, F, None, F, None, F, need,
+                                  None) == INVALID
+    assert lib.gdn_chunk_fwd_conv(c, F, F, 4, F, F, None, F, None, F, None, F, need - 1,
+                                  None) == WORKSPACE
+    bf = gdn.make_config(256, 2, 16, 32, gdn.GDN_BF16)
+    assert lib.gdn_chunk_fwd_conv(ctypes.byref(bf), F, F, 4, F, F, None, F, None, F, None, F,
+                                  1 << 40, None) == UNSUPPORTED
+    vp6 = ctypes.c_void_p * 6
+    assert lib.gdn_chunk_fwd_conv_timed(c, F, F, 4, F, F, None, F, None, F, None, F, need, None,
+                                        None) == INVALID
+    assert lib.gdn_chunk_fwd_conv_timed(c, F, F, 4, F, F, None, F, None, F, None, F, need, None,
+                                        vp6(1, 2, 3, 4, None, 6)) == INVALID

@@ -17,7 +17,7 @@ from oracle import chunked, index_table, recurrent
 
 from gpu_helpers import (O_TOL, S_TOL, config_of, decode_kimg, decode_pimg, decode_rowfrag, decode_uimg,
                          device_inputs, lane_errors, log, oracle_inputs_f64, oracle_lanes,
-                         run_forward, run_front, workspace_views)
+                         run_forward, run_forward_conv, run_front, workspace_views)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -200,6 +200,51 @@ def test_forward_front_small_every_lane():
     eo, es = lane_errors(wl, o, hT, ref)
     log(f"  o err {eo:.3e}  S err {es:.3e}")
     assert eo <= O_TOL and es <= S_TOL
+
+
+# --------------------------------------------------------------------------- #
+# front fused into stage 1 (gdn_chunk_fwd_conv)
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("d_conv", [4, 2])
+def test_fused_front_equals_front_then_forward_bitwise(d_conv):
+    """The fused front computes q, k, v with the standalone front's fp32
+    arithmetic, so o and the final states are bit for bit those of
+    gdn_front_conv_silu_l2 followed by gdn_chunk_fwd (ragged chunks, a
+    sequence shorter than the halo, an empty one, h0)."""
+    wl = workloads.make_custom([100, 2, 0, 64, 130], 2, 4, seed=71 + d_conv, front=True,
+                               d_conv=d_conv, h0_sigma=0.02, n_max=6, t_max=330)
+    log(f"fused front vs front + forward, d_conv={d_conv}")
+    d = device_inputs(wl)
+    o1, s1, _ = run_forward(wl, d)
+    o2, s2 = run_forward_conv(wl, d)
+    T = wl.n_tokens
+    assert torch.equal(o1[:T], o2[:T]) and torch.equal(s1, s2)
+
+
+def test_fused_front_small_every_lane():
+    wl = workloads.make_custom([100, 37, 0, 64, 3], 2, 4, seed=29, front=True, n_max=6, t_max=230)
+    log("fused front small, every lane")
+    o, hT = run_forward_conv(wl)
+    ref = oracle_lanes(wl, _all_lanes(wl), qkv64=oracle_inputs_f64(wl))
+    eo, es = lane_errors(wl, o, hT, ref)
+    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+
+
+def test_fused_front_workload_full_size():
+    """The front workload (4 x 8192 tokens) through the fused path, in the
+    launch configuration the benchmark times; sampled lanes against the
+    fp64 front + recurrence."""
+    wl = workloads.make(4)
+    log(f"fused front, workload 4 ({wl.name}) tokens={wl.n_tokens}")
+    o, hT = run_forward_conv(wl)
+    lanes = [(0, 0), (1, 13), (3, 31)]
+    ref = oracle_lanes(wl, lanes, qkv64=_front_for(wl, sorted({s for s, _ in lanes})))
+    eo, es = lane_errors(wl, o, hT, ref)
+    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+    assert torch.isfinite(o[:wl.n_tokens]).all()
 
 
 # --------------------------------------------------------------------------- #
