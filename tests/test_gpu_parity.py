@@ -413,3 +413,59 @@ def test_forward_without_table_builds_it_in_the_workspace(n):
     eo, es = lane_errors(wl, o, hT, oracle_lanes(wl, _all_lanes(wl)))
     log(f"  o err {eo:.3e}  S err {es:.3e}")
     assert eo <= O_TOL and es <= S_TOL
+
+
+def test_graph_capture_replay_with_varying_cu_seqlens():
+    """gdn_chunk_fwd captured once into a HIP graph at static sizes (t_max,
+    n_max) and static addresses, then replayed with different cu_seqlens
+    contents written into the same buffer (FLA issue 1155, "Core design":
+    static grids, the device-built table, a sentinel for unused slots). Every
+    replay is checked bit for bit against an eager call on the same inputs,
+    with eager work and synchronisation between the replays."""
+    t_max, n_max, H, Hv = 600, 6, 2, 4
+    rng = np.random.Generator(np.random.PCG64(81))
+    batches = [[600], [1, 63, 64, 65, 200, 0], [100, 0, 0, 37], [300, 300]]
+    base = workloads.make_custom([t_max], H, Hv, seed=82, t_max=t_max, n_max=n_max)
+    d = device_inputs(base)
+    h0 = torch.from_numpy(rng.standard_normal((n_max, Hv, 128, 128)) * 0.02).float().to(DEV)
+    cfg = config_of(base)
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    cu = torch.zeros(n_max + 1, dtype=torch.int32, device=DEV)
+    o = torch.zeros((t_max, Hv, 128), dtype=torch.float32, device=DEV)
+    hT = torch.zeros((n_max, Hv, 128, 128), dtype=torch.float32, device=DEV)
+
+    def cu_of(lengths):
+        c = np.zeros(n_max + 1, np.int32)
+        c[1:len(lengths) + 1] = np.cumsum(lengths)
+        c[len(lengths) + 1:] = c[len(lengths)]
+        return torch.from_numpy(c)
+
+    cu.copy_(cu_of(batches[0]))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):  # warm-up on the capture stream, then capture
+        gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None, o, hT, ws)
+        stream.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None, o, hT,
+                              ws)
+    torch.cuda.synchronize()
+    for rep, lengths in enumerate(batches + batches[::-1]):
+        log(f"graph replay {rep}: lengths {lengths}")
+        cu.copy_(cu_of(lengths))
+        o.fill_(float("nan"))
+        hT.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        T = int(sum(lengths))
+        o_g, s_g = o[:T].clone(), hT.clone()
+        # eager reference on the same inputs, fresh outputs and workspace
+        ws2 = torch.empty_like(ws)
+        o_e = torch.full_like(o, float("nan"))
+        s_e = torch.full_like(hT, float("nan"))
+        gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None, o_e, s_e,
+                          ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e[:T]) and torch.equal(s_g, s_e)
