@@ -60,28 +60,62 @@ static_assert(kFusedIndexMaxSeqs == GDN_FUSED_INDEX_MAX_SEQS, "fused index bound
 namespace {
 
 constexpr int kLdRow = kD + 8;   // bf16 row-major tile [64][136]
-constexpr int kLdCol = kC + 8;   // bf16 transposed tile [128][72]
-constexpr int kLdA = kC + 8;     // fp32 A [64][72]
-constexpr int kLdT = kC + 4;     // fp32 T [64][68]
+constexpr int kLdAT = kC + 4;    // fp32 A, then T in place [64][68]
 constexpr int kLdX = 16 + 4;     // fp32 per-wave 16x16 scratch
 
+// LDS of one work-group (bf16 input: 53 KB; fp32 input: 87 KB). Two bf16
+// work-groups run per CU: a third would fit the LDS, but at the 168 VGPRs it
+// allows the kernel spills and runs 15% slower per chunk.
+//   K rows   [terms][64][136] bf16   for K K^T, K q^T, the K^T fragments and w
+//   A / T    [64][68] fp32           A, solved into T in place
+//   V rows   [terms][64][136] bf16   for u; the solve's per-wave scratch lives
+//                                    here until V is stored after the solve
+//   gates    per wave: log2-scaled gamma and beta (64 floats each)
+// During set-up the q rows occupy the A / T region (and V's for fp32 input).
 template <bool kF32In>
 struct IntraSmem {
   static constexpr int kTerms = kF32In ? 2 : 1;
-  // region 1: K row-major (hi[, lo]) while K K^T runs, then V transposed (hi[, lo])
-  static constexpr int kR1 = kTerms * 128 * kLdCol * 2;
-  // region 2: K transposed (hi[, lo])
-  static constexpr int kR2 = kTerms * 128 * kLdCol * 2;
-  // regions 3 + 4: A (fp32) and T (fp32); q row-major (hi[, lo]) during set-up
-  static constexpr int kR3 = 64 * kLdA * 4;
-  static constexpr int kR4 = 64 * kLdT * 4;
-  static constexpr int kR5 = 4 * 16 * kLdX * 4;
-  // per wave: log2-scaled gamma, beta, beta e^gamma (64 floats each)
-  static constexpr int kGates = 4 * 3 * 64 * 4;
-  static constexpr int kBytes = kR1 + kR2 + kR3 + kR4 + kR5 + kGates;
-  static_assert(kTerms * 64 * kLdRow * 2 <= kR1, "row tile must fit region 1");
-  static_assert(kTerms * 64 * kLdRow * 2 <= kR3 + kR4, "q tile must fit regions 3-4");
+  static constexpr int kTile = 64 * kLdRow * 2;
+  static constexpr int kOffK = 0;
+  static constexpr int kOffAT = kOffK + kTerms * kTile;
+  static constexpr int kOffV = kOffAT + 64 * kLdAT * 4;
+  static constexpr int kOffGates = kOffV + kTerms * kTile;
+  static constexpr int kBytes = kOffGates + 4 * 2 * 64 * 4;
+  static_assert(64 * kLdAT * 4 == kTile, "q rows must fit the A / T region (and V's)");
+  static_assert(4 * 16 * kLdX * 4 <= kTile, "solve scratch must fit the V region");
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed read of a row-major bf16 tile in LDS (ds_read_b64_tr_b16): within
+// each 16-lane group, lane s supplies the 8-byte chunk M[row + (s >> 2)][col +
+// 4 (s & 3) ..], and lane j receives element j of columns col .. col + 15 from
+// rows row .. row + 3, i.e. lane j holds M[row + i][col + j], i = 0..3.
+__device__ __forceinline__ bf16x4 tr4(const __bf16 *base, int ld, int row, int col, int lane) {
+  const int s = lane & 15;
+  const __bf16 *p = base + (row + (s >> 2)) * ld + col + 4 * (s & 3);
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(const_cast<__bf16 *>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// MFMA operand from a row-major tile M[k][n] (k the contraction): lane (g, n)
+// holds M[rowA + i][col + n] (i < 4) then M[rowB + i][col + n], where rowA and
+// rowB may depend on the lane group g.
+__device__ __forceinline__ bf16x8 frag_tr2(const __bf16 *base, int ld, int rowA, int rowB, int col,
+                                           int lane) {
+  const bf16x4 a = tr4(base, ld, rowA, col, lane);
+  const bf16x4 b = tr4(base, ld, rowB, col, lane);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// The same with eight consecutive contraction rows per group: lane (g, n)
+// holds M[row0 + 8 g + e][col + n], e < 8 (the k order of frag_rows).
+__device__ __forceinline__ bf16x8 frag_tr(const __bf16 *base, int ld, int row0, int col, int lane) {
+  const int r = row0 + 8 * (lane >> 4);
+  return frag_tr2(base, ld, r, r + 4, col, lane);
+}
 
 // A tile of a [rows, heads, 128] tensor: rows t0 .. t0 + L - 1 of one head,
 // as a buffer range that ends after row L - 1, so rows past the chunk read as
@@ -207,20 +241,6 @@ __device__ __forceinline__ void conv_terms(const ConvRaw &r, bool l2, int valid,
   }
 }
 
-__device__ __forceinline__ uint16_t half_of(const u32x4 &w, int i) {
-  return static_cast<uint16_t>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu);
-}
-
-// Write a thread's 4x8 block transposed: dst[col + i][row0 .. row0 + 3].
-__device__ __forceinline__ void store_col4x8(__bf16 *dst, int row0, int col, const u32x4 (&v)[4]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t a = half_of(v[0], i) | (static_cast<uint32_t>(half_of(v[1], i)) << 16);
-    const uint32_t b = half_of(v[2], i) | (static_cast<uint32_t>(half_of(v[3], i)) << 16);
-    *reinterpret_cast<u32x2 *>(dst + (col + i) * kLdCol + row0) = u32x2{a, b};
-  }
-}
-
 // P pairs (q, R): token block q (32 tokens) of column tile R (16 outputs);
 // each pair is two 16x16 tiles of P^T, (2q, R) and (2q + 1, R).
 __device__ __forceinline__ int pair_q(int pi) { return pi == 3 || pi == 5 ? 1 : 0; }
@@ -267,19 +287,17 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   static_assert(!kConv || kF32In, "the fused front produces fp32 q, k, v");
   using Smem = IntraSmem<kF32In>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Smem::kBytes];
-  __bf16 *r1 = reinterpret_cast<__bf16 *>(smem);
-  __bf16 *kcol = reinterpret_cast<__bf16 *>(smem + Smem::kR1);
-  float *amat = reinterpret_cast<float *>(smem + Smem::kR1 + Smem::kR2);
-  __bf16 *rq = reinterpret_cast<__bf16 *>(amat);  // q row-major during set-up (regions 3-4)
-  float *tmat = reinterpret_cast<float *>(smem + Smem::kR1 + Smem::kR2 + Smem::kR3);
-  float *xs = reinterpret_cast<float *>(smem + Smem::kR1 + Smem::kR2 + Smem::kR3 + Smem::kR4);
+  __bf16 *rk = reinterpret_cast<__bf16 *>(smem + Smem::kOffK);    // K rows (hi[, lo])
+  float *at = reinterpret_cast<float *>(smem + Smem::kOffAT);      // A, then T in place
+  __bf16 *rv = reinterpret_cast<__bf16 *>(smem + Smem::kOffV);    // V rows (hi[, lo])
+  float *xs = reinterpret_cast<float *>(smem + Smem::kOffV);      // solve scratch (in V's place)
+  __bf16 *rq = reinterpret_cast<__bf16 *>(smem + Smem::kOffAT);   // q rows during set-up
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  float *gsh = xs + 4 * 16 * kLdX + wv * 3 * 64;  // this wave's gate copies
+  float *gsh = reinterpret_cast<float *>(smem + Smem::kOffGates) + wv * 2 * 64;  // this wave's gates
   float *bsh = gsh + 64;
-  float *swsh = bsh + 64;
   // this work-group's chunk: from the caller's table, or located from
   // cu_seqlens here (every wave computes it; the key-head-0 work-groups also
   // fill the workspace copy of the table)
@@ -323,6 +341,16 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     else
       to_terms(raw, hi, lo);
   };
+  // a 4 x 8 block of a row-major tile (hi[, lo]) into LDS
+  auto put_rows = [&](__bf16 *dst, const u32x4 (&hi)[4], const u32x4 (&lo)[4])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      *reinterpret_cast<u32x4 *>(dst + (lrow + rr) * kLdRow + lcol) = hi[rr];
+      if constexpr (kF32In)
+        *reinterpret_cast<u32x4 *>(dst + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = lo[rr];
+    }
+  };
   const auto kraw = load_tile(kin, H, h, (H + h) * kD, L);
   const auto qraw = load_tile(qin, H, h, h * kD, L);
   auto vraw = load_tile(vin, Hv, h * HG, (2 * H + h * HG) * kD, L);
@@ -333,46 +361,29 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   };
   float g_next = load_gate(g, h * HG);
   float b_next = load_gate(beta, h * HG);
-  u32x4 khi[4], klo[4], qhi[4], qlo[4];
-  tile_terms(kraw, true, khi, klo);
-  tile_terms(qraw, true, qhi, qlo);
-
-  // ---- K tile -> LDS (row-major in region 1, transposed in region 2) ------
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    *reinterpret_cast<u32x4 *>(r1 + (lrow + rr) * kLdRow + lcol) = khi[rr];
-    if constexpr (kF32In)
-      *reinterpret_cast<u32x4 *>(r1 + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = klo[rr];
-  }
-  store_col4x8(kcol, lrow, lcol, khi);
-  if constexpr (kF32In) store_col4x8(kcol + 128 * kLdCol, lrow, lcol, klo);
-  // ---- q tile -> LDS row-major -------------------------------------------
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    *reinterpret_cast<u32x4 *>(rq + (lrow + rr) * kLdRow + lcol) = qhi[rr];
-    if constexpr (kF32In)
-      *reinterpret_cast<u32x4 *>(rq + 64 * kLdRow + (lrow + rr) * kLdRow + lcol) = qlo[rr];
+  {
+    u32x4 hi[4], lo[4];
+    tile_terms(kraw, true, hi, lo);
+    put_rows(rk, hi, lo);
+    tile_terms(qraw, true, hi, lo);
+    put_rows(rq, hi, lo);
   }
   __syncthreads();
 
-  // ---- K^T fragments for the state update: fragment (tau, q), lane (g, c)
-  // holds K[32 q + 4 g + j][16 tau + c] for j < 4 and K[32 q + 16 + 4 g + j - 4][..]
-  // for j >= 4 (the token order of the inter stage's delta fragments).
+  // ---- K^T fragments for the state update, read transposed from the K
+  // rows: fragment (tau, q), lane (g, c) holds K[32 q + 4 g + j][16 tau + c]
+  // for j < 4 and K[32 q + 16 + 4 g + j - 4][..] for j >= 4 (the token order of
+  // the inter stage's delta fragments).
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int item = tid + kThreads * m;
-    const int f = item >> 6, l = item & 63;
+    const int f = wv + 4 * m;  // fragment 0..15 = 2 tau + q
     const int tau = f >> 1, qq = f & 1;
-    const int off = (16 * tau + (l & 15)) * kLdCol + 32 * qq + 4 * (l >> 4);
-    __bf16 *dst = out.kimg + ((((int64_t)h * nt + slot) * kNK + f) * 64 + l) * 8;
-    const u32x2 a = *reinterpret_cast<const u32x2 *>(kcol + off);
-    const u32x2 b = *reinterpret_cast<const u32x2 *>(kcol + off + 16);
-    *reinterpret_cast<u32x4 *>(dst) = u32x4{a[0], a[1], b[0], b[1]};
-    if constexpr (kF32In) {
-      const u32x2 al = *reinterpret_cast<const u32x2 *>(kcol + 128 * kLdCol + off);
-      const u32x2 bl = *reinterpret_cast<const u32x2 *>(kcol + 128 * kLdCol + off + 16);
-      *reinterpret_cast<u32x4 *>(dst + 16 * 64 * 8) = u32x4{al[0], al[1], bl[0], bl[1]};
-    }
+    const int g4 = 4 * (lane >> 4);
+    __bf16 *dst = out.kimg + ((((int64_t)h * nt + slot) * kNK + f) * 64 + lane) * 8;
+    *reinterpret_cast<bf16x8 *>(dst) = frag_tr2(rk, kLdRow, 32 * qq + g4, 32 * qq + 16 + g4, 16 * tau, lane);
+    if constexpr (kF32In)
+      *reinterpret_cast<bf16x8 *>(dst + 16 * 64 * 8) =
+          frag_tr2(rk + 64 * kLdRow, kLdRow, 32 * qq + g4, 32 * qq + 16 + g4, 16 * tau, lane);
   }
 
   // ---- q16 fragments for y = S^T q^T: fragment (R, p), lane (g, c) holds
@@ -423,11 +434,11 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     if (n < nblk) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = frag_rows(r1, kLdRow, 16 * bi, 32 * ks, lane);
-        const bf16x8 bb = frag_rows(r1, kLdRow, 16 * bj, 32 * ks, lane);
+        const bf16x8 a = frag_rows(rk, kLdRow, 16 * bi, 32 * ks, lane);
+        const bf16x8 bb = frag_rows(rk, kLdRow, 16 * bj, 32 * ks, lane);
         acc = mfma(a, bb, acc);
         if constexpr (kF32In) {
-          const __bf16 *rlo = r1 + 64 * kLdRow;
+          const __bf16 *rlo = rk + 64 * kLdRow;
           acc = mfma(frag_rows(rlo, kLdRow, 16 * bi, 32 * ks, lane), bb, acc);
           acc = mfma(a, frag_rows(rlo, kLdRow, 16 * bj, 32 * ks, lane), acc);
         }
@@ -449,26 +460,26 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     if ((n >> 1) < npair && tj <= tr) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = frag_rows(r1, kLdRow, 16 * tj, 32 * ks, lane);
+        const bf16x8 a = frag_rows(rk, kLdRow, 16 * tj, 32 * ks, lane);
         const bf16x8 bb = frag_rows(rq, kLdRow, 16 * tr, 32 * ks, lane);
         acc = mfma(a, bb, acc);
         if constexpr (kF32In) {
-          acc = mfma(frag_rows(r1 + 64 * kLdRow, kLdRow, 16 * tj, 32 * ks, lane), bb, acc);
+          acc = mfma(frag_rows(rk + 64 * kLdRow, kLdRow, 16 * tj, 32 * ks, lane), bb, acc);
           acc = mfma(a, frag_rows(rq + 64 * kLdRow, kLdRow, 16 * tr, 32 * ks, lane), acc);
         }
       }
     }
     pacc[n] = acc;
   }
-  __syncthreads();  // regions 1, 3 and 4 are free from here on
+  __syncthreads();  // the q rows (in the A / T and V regions) are dead from here on
 
-  // T's upper blocks (0,1) and (2,3) are read as zeros by the w/u products
-  // (no other step writes them).
+  // T's upper blocks (0,1) and (2,3) are read as zeros by the w/u products;
+  // neither A nor T is ever written there.
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int e = tid + kThreads * m;  // 0..511
     const int blk = e >> 8, r = (e >> 4) & 15, c = e & 15;
-    tmat[(32 * blk + r) * kLdT + 32 * blk + 16 + c] = 0.f;
+    at[(32 * blk + r) * kLdAT + 32 * blk + 16 + c] = 0.f;
   }
 
   for (int gi = 0; gi < HG; ++gi) {
@@ -493,7 +504,6 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     const float eg = fast_exp2(gam2);
     gsh[lane] = gam2;
     bsh[lane] = bv;
-    swsh[lane] = bv * eg;
     if (wv == 0) {
       float *gd = out.gimg + ((int64_t)hv * nt + slot) * kGateStride;
       gd[lane] = tok_ok ? fast_exp2(gl2 - gam2) : 0.f;
@@ -541,26 +551,25 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = r0 + i;
-          amat[r * kLdA + j] = j < r ? br[i] * gacc[n][i] * fast_exp2(gr[i] - gj) : 0.f;
+          at[r * kLdAT + j] = j < r ? br[i] * gacc[n][i] * fast_exp2(gr[i] - gj) : 0.f;
         }
       }
     }
-    store_col4x8(r1, lrow, lcol, vh);
-    if constexpr (kF32In) store_col4x8(r1 + 128 * kLdCol, lrow, lcol, vl);
     __syncthreads();
 
-    // ---- solve 1: diagonal blocks by column forward substitution ----------
+    // ---- solve 1: diagonal blocks by column forward substitution, in place:
+    // row r of the block is read (by every lane) before any lane writes it
     if (lane < 16) {
       const int c = lane;
-      const float *ab = amat + (16 * wv) * kLdA + 16 * wv;
+      float *ab = at + (16 * wv) * kLdAT + 16 * wv;
       float tc[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) x = fmaf(ab[r * kLdA + i], tc[i], x);
+        for (int i = 0; i < r; ++i) x = fmaf(ab[r * kLdAT + i], tc[i], x);
         tc[r] = r == c ? 1.f : (r < c ? 0.f : -x);
-        tmat[(16 * wv + r) * kLdT + 16 * wv + c] = tc[r];
+        ab[r * kLdAT + c] = tc[r];
       }
     }
     __syncthreads();
@@ -568,83 +577,88 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     float *xw = xs + wv * 16 * kLdX;
     if (wv < 2) {
       const int b = 2 * wv;  // diagonal pair (b, b + 1)
-      const float *a_lo = amat + (16 * (b + 1)) * kLdA + 16 * b;
-      const float *t_bb = tmat + (16 * b) * kLdT + 16 * b;
-      const float *t_nn = tmat + (16 * (b + 1)) * kLdT + 16 * (b + 1);
-      put16(xw, kLdX, mm16(a_lo, kLdA, t_bb, kLdT, lane, zero4()), 1.f, lane);
+      float *blk = at + (16 * (b + 1)) * kLdAT + 16 * b;  // A_10 -> T_10 (A_32 -> T_32)
+      const float *t_bb = at + (16 * b) * kLdAT + 16 * b;
+      const float *t_nn = at + (16 * (b + 1)) * kLdAT + 16 * (b + 1);
+      put16(xw, kLdX, mm16(blk, kLdAT, t_bb, kLdAT, lane, zero4()), 1.f, lane);
       wave_lds_sync();
-      put16(tmat + (16 * (b + 1)) * kLdT + 16 * b, kLdT, mm16(t_nn, kLdT, xw, kLdX, lane, zero4()),
-            -1.f, lane);
+      put16(blk, kLdAT, mm16(t_nn, kLdAT, xw, kLdX, lane, zero4()), -1.f, lane);
     }
     __syncthreads();
     // ---- solve 3: lower-left 32x32 block, X = A_BA T_AA ... ----------------
     const int bi = 2 + (wv >> 1), bj = wv & 1;
     {
-      const float *a_i0 = amat + (16 * bi) * kLdA;
+      const float *a_i0 = at + (16 * bi) * kLdAT;
       const float *a_i1 = a_i0 + 16;
       f32x4 x = zero4();
       if (bj == 0) {
-        x = mm16(a_i0, kLdA, tmat, kLdT, lane, x);                       // A_i0 T_00
-        x = mm16(a_i1, kLdA, tmat + 16 * kLdT, kLdT, lane, x);           // A_i1 T_10
+        x = mm16(a_i0, kLdAT, at, kLdAT, lane, x);                        // A_i0 T_00
+        x = mm16(a_i1, kLdAT, at + 16 * kLdAT, kLdAT, lane, x);           // A_i1 T_10
       } else {
-        x = mm16(a_i1, kLdA, tmat + 16 * kLdT + 16, kLdT, lane, x);      // A_i1 T_11
+        x = mm16(a_i1, kLdAT, at + 16 * kLdAT + 16, kLdAT, lane, x);      // A_i1 T_11
       }
       put16(xw, kLdX, x, 1.f, lane);
     }
     __syncthreads();
-    // ---- ... then T_BA = -T_BB X ------------------------------------------
+    // ---- ... then T_BA = -T_BB X, over A_BA ----------------------------------
     {
-      const float *t22 = tmat + 32 * kLdT + 32;
-      const float *t32 = tmat + 48 * kLdT + 32;
-      const float *t33 = tmat + 48 * kLdT + 48;
+      const float *t22 = at + 32 * kLdAT + 32;
+      const float *t32 = at + 48 * kLdAT + 32;
+      const float *t33 = at + 48 * kLdAT + 48;
       f32x4 y;
       if (bi == 2) {
-        y = mm16(t22, kLdT, xw, kLdX, lane, zero4());
+        y = mm16(t22, kLdAT, xw, kLdX, lane, zero4());
       } else {
-        y = mm16(t32, kLdT, xs + (wv - 2) * 16 * kLdX, kLdX, lane, zero4());
-        y = mm16(t33, kLdT, xw, kLdX, lane, y);
+        y = mm16(t32, kLdAT, xs + (wv - 2) * 16 * kLdX, kLdX, lane, zero4());
+        y = mm16(t33, kLdAT, xw, kLdX, lane, y);
       }
-      put16(tmat + (16 * bi) * kLdT + 16 * bj, kLdT, y, -1.f, lane);
+      put16(at + (16 * bi) * kLdAT + 16 * bj, kLdAT, y, -1.f, lane);
     }
+    __syncthreads();  // T complete; the solve scratch (V's region) is free
+    put_rows(rv, vh, vl);
     __syncthreads();
 
     // ---- w and u in one pass: T diag(beta e^gamma) and T diag(beta), split
-    // hi + lo per lane, against K^T / V^T. Tiles (d-block db, token block rb):
-    // w as W^T = K^T (T s)^T (lane holds four d of one token), u as
-    // U = (T s) V (lane holds four tokens of one d).
+    // hi + lo per lane, against K^T / V^T read transposed from the row tiles.
+    // Tiles (d-block db, token block rb): w as W^T = K^T (T s)^T (lane holds
+    // four d of one token), u as U = (T s) V (lane holds four tokens of one d).
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       f32x4 wacc[2] = {zero4(), zero4()}, uacc[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks <= (rb >> 1); ++ks) {
         const int j0 = 32 * ks + 8 * (lane >> 4);
-        const float *trow = tmat + (16 * rb + (lane & 15)) * kLdT + j0;
+        const float *trow = at + (16 * rb + (lane & 15)) * kLdAT + j0;
         const f32x4 t_a = *reinterpret_cast<const f32x4 *>(trow);
         const f32x4 t_b = *reinterpret_cast<const f32x4 *>(trow + 4);
-        const f32x4 sw_a = *reinterpret_cast<const f32x4 *>(swsh + j0);
-        const f32x4 sw_b = *reinterpret_cast<const f32x4 *>(swsh + j0 + 4);
-        const f32x4 su_a = *reinterpret_cast<const f32x4 *>(bsh + j0);
-        const f32x4 su_b = *reinterpret_cast<const f32x4 *>(bsh + j0 + 4);
-        const float xw8[8] = {t_a[0] * sw_a[0], t_a[1] * sw_a[1], t_a[2] * sw_a[2], t_a[3] * sw_a[3],
-                              t_b[0] * sw_b[0], t_b[1] * sw_b[1], t_b[2] * sw_b[2], t_b[3] * sw_b[3]};
-        const float xu8[8] = {t_a[0] * su_a[0], t_a[1] * su_a[1], t_a[2] * su_a[2], t_a[3] * su_a[3],
-                              t_b[0] * su_b[0], t_b[1] * su_b[1], t_b[2] * su_b[2], t_b[3] * su_b[3]};
+        const f32x4 g_a = *reinterpret_cast<const f32x4 *>(gsh + j0);
+        const f32x4 g_b = *reinterpret_cast<const f32x4 *>(gsh + j0 + 4);
+        const f32x4 b_a = *reinterpret_cast<const f32x4 *>(bsh + j0);
+        const f32x4 b_b = *reinterpret_cast<const f32x4 *>(bsh + j0 + 4);
+        float xw8[8], xu8[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xu8[i] = t_a[i] * b_a[i];
+          xu8[4 + i] = t_b[i] * b_b[i];
+          xw8[i] = xu8[i] * fast_exp2(g_a[i]);
+          xw8[4 + i] = xu8[4 + i] * fast_exp2(g_b[i]);
+        }
         u32x4 wh, wl, uh, ul;
         split8_words(xw8, wh, wl);
         split8_words(xu8, uh, ul);
 #pragma unroll
         for (int db2 = 0; db2 < 2; ++db2) {
           const int db = 2 * wv + db2;
-          const bf16x8 ka = frag_rows(kcol, kLdCol, 16 * db, 32 * ks, lane);
-          const bf16x8 vb = frag_rows(r1, kLdCol, 16 * db, 32 * ks, lane);
+          const bf16x8 ka = frag_tr(rk, kLdRow, 32 * ks, 16 * db, lane);
+          const bf16x8 vb = frag_tr(rv, kLdRow, 32 * ks, 16 * db, lane);
           f32x4 aw = wacc[db2], au = uacc[db2];
           aw = mfma(ka, as_bf16x8(wh), aw);
           aw = mfma(ka, as_bf16x8(wl), aw);
           au = mfma(as_bf16x8(uh), vb, au);
           au = mfma(as_bf16x8(ul), vb, au);
           if constexpr (kF32In) {
-            aw = mfma(frag_rows(kcol + 128 * kLdCol, kLdCol, 16 * db, 32 * ks, lane), as_bf16x8(wh), aw);
-            au = mfma(as_bf16x8(uh), frag_rows(r1 + 128 * kLdCol, kLdCol, 16 * db, 32 * ks, lane), au);
+            aw = mfma(frag_tr(rk + 64 * kLdRow, kLdRow, 32 * ks, 16 * db, lane), as_bf16x8(wh), aw);
+            au = mfma(as_bf16x8(uh), frag_tr(rv + 64 * kLdRow, kLdRow, 32 * ks, 16 * db, lane), au);
           }
           wacc[db2] = aw;
           uacc[db2] = au;
@@ -666,7 +680,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
         *reinterpret_cast<f32x4 *>(dst) = uacc[db2];
       }
     }
-    __syncthreads();  // region 1 (V^T), A, T and the gate copies are rewritten next
+    __syncthreads();  // A / T, V and the gate copies are rewritten next
   }
 }
 
