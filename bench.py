@@ -8,11 +8,13 @@ stage -> inter-chunk stage (plus the conv/SiLU/L2 front for workloads that
 have one),
 launched through the C ABI's whole-forward call on torch's current stream.
 W untimed warm-up steps, then exactly K timed steps bracketed by device
-synchronisation; value = tokens x K / wall time of the timed region. Each
-kernel records a pair of HIP events at its own start and end (the timed
-variants of the entry points launch with hipExtLaunchKernel), so no packet
-sits between the launches and each kernel's average duration over the timed
-region is its execution time; the dominant kernel's algorithmic bytes per
+synchronisation; value = tokens x K / wall time of the timed region. On
+every E-th timed step (default 8) each kernel records a pair of HIP events
+at its own start and end (the timed variants of the entry points launch with
+hipExtLaunchKernel, so no packet sits between the launches); the other steps
+call the plain entry points, because per-dispatch events cost the step they
+are on a few microseconds. Each kernel's duration averaged over the sampled
+steps is its execution time; the dominant kernel's algorithmic bytes per
 launch divided by that duration is the roofline figure.
 
 Prints ONE JSON line. Default workload: single sequence, T = 4096, H = 16,
@@ -156,8 +158,12 @@ def cpu_baseline(wl, max_seconds=20.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--event-every", type=int, default=8, metavar="E",
+                    help="time the kernels of every E-th step with dispatch events (the "
+                         "others run the plain entry point: per-dispatch events add a few "
+                         "microseconds to the step they are on)")
     ap.add_argument("--workload", type=int, default=1, help="named workload 0..4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused-front", action="store_true",
@@ -237,13 +243,16 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [hip.create(8 if has_front else 6) for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    timed = [s_ % every == every - 1 or s_ == args.steps - 1 for s_ in range(args.steps)]
+    events = [hip.create(8 if has_front else 6) if t else None for t in timed]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(args.steps):
         step(events[s_])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    events = [ev for ev in events if ev is not None]
 
     pair = {"index": (0, 1), "intra": (2, 3), "inter": (4, 5), "front": (6, 7)}
     per_stage_ms = {name: statistics.fmean(hip.ms(ev[pair[name][0]], ev[pair[name][1]])
