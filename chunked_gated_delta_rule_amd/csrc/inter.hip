@@ -50,6 +50,7 @@
 // share a key head get the same blockIdx modulo 8, so they run on one XCD and
 // share q16 and K^T through its L2.
 #include <type_traits>
+#include <utility>
 
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
@@ -60,7 +61,16 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr int kSlices = kD / 16;  // 16-column value slices per head
-constexpr int kInterThreads = 256;
+constexpr int kDepthSingle = 2;  // prefetch depth with one work-group per CU
+constexpr int kL2Lead = 2;       // chunks between the L2 warm-up and the operand loads
+
+// The L2 warm-up wave is a fifth wave of the work-group; fp32 input at depth 2
+// needs more than the 256 VGPRs a SIMD with two waves of it could give, and
+// runs without it.
+template <bool kF32In, int kDepth>
+constexpr bool kWarmWave = !(kF32In && kDepth == 2);
+template <bool kF32In, int kDepth>
+constexpr int kInterThreads = kWarmWave<kF32In, kDepth> ? 320 : 256;
 
 __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
@@ -137,6 +147,16 @@ __device__ __forceinline__ int slot_of(const Lane &L, int c) { return ((L.bos + 
 // the compiler's load counting never has to drain.
 template <int B>
 using SetIndex = std::integral_constant<int, B>;
+
+// f(SetIndex<0>{}), f(SetIndex<1>{}), ..., f(SetIndex<kDepth - 1>{}) in order.
+template <int kDepth, typename F, int... B>
+__device__ __forceinline__ void for_sets_impl(F &&f, std::integer_sequence<int, B...>) {
+  (f(SetIndex<B>{}), ...);
+}
+template <int kDepth, typename F>
+__device__ __forceinline__ void for_sets(F &&f) {
+  for_sets_impl<kDepth>(f, std::make_integer_sequence<int, kDepth>{});
+}
 
 template <bool kF32In, int kDepth, int X>
 __device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in,
@@ -264,12 +284,13 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  load_all(SetIndex<0>{}, rsrc_of(0));
-  if constexpr (kDepth == 2) load_all(SetIndex<1>{}, rsrc_of(1));
-  for (int c = 0; c < L.nc; c += kDepth) {  // a step past the last chunk changes nothing
-    step(c, SetIndex<0>{});
-    if constexpr (kDepth == 2) step(c + 1, SetIndex<1>{});
-  }
+  for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+    load_all(Bc, rsrc_of(decltype(Bc)::value));
+  });
+  for (int c = 0; c < L.nc; c += kDepth)  // a step past the last chunk changes nothing
+    for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+      step(c + decltype(Bc)::value, Bc);
+    });
   if (hT) {
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl) *reinterpret_cast<f32x4 *>(hT + sbase + 16 * tl) = S[tl];
@@ -367,20 +388,78 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  load_all(SetIndex<0>{}, rsrc_of(0));
-  if constexpr (kDepth == 2) load_all(SetIndex<1>{}, rsrc_of(1));
-  for (int c = 0; c < L.nc; c += kDepth) {  // a step past the last chunk changes nothing
-    step(c, SetIndex<0>{});
-    if constexpr (kDepth == 2) step(c + 1, SetIndex<1>{});
-  }
+  for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+    load_all(Bc, rsrc_of(decltype(Bc)::value));
+  });
+  for (int c = 0; c < L.nc; c += kDepth)  // a step past the last chunk changes nothing
+    for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+      step(c + decltype(Bc)::value, Bc);
+    });
+}
+
+// L2 warm-up wave. The work-groups of one key head (and of one value head)
+// read the same per-chunk blocks, at nearly the same time, from one XCD's L2;
+// their first requests for a chunk would all wait on the same misses to the
+// last-level cache or HBM. Per chunk step this wave requests, one 128-byte
+// line per lane, this work-group's share of the lines of chunk c + kDepth +
+// kL2Lead: 1/members of the key head's K^T and q16 blocks, 1/8 of the value
+// head's w16, P and gate blocks, and its own u slice. The loads go to LDS
+// (LDS-DMA: no register is written) and are never read, so nothing waits on
+// them until the wave ends. Requests past the last chunk repeat its lines.
+template <bool kF32In, int kDepth>
+__device__ __forceinline__ void l2_warm_wave(const Lane &L, const StageBuffers &in, int member,
+                                             int members, uint32_t *sink) {
+  constexpr int kKLines = (kF32In ? 32 : 16) * 8;
+  constexpr int kHLines = kKLines + 128;             // K^T image, q16
+  constexpr int kWLines = 128, kPLines = 96;
+  constexpr int kVLines = kWLines + kPLines + kGateStride * 4 / 128;  // w16, P, gates
+  constexpr int kULines = 32;
+  static_assert(kGateStride * 4 % 128 == 0, "gate block is whole lines");
+  if (L.nc == 0) return;
+  const int slice = L.v0 / 16;
+  const int nh = (kHLines + members - 1) / members;
+  const int nv = (kVLines + kSlices - 1) / kSlices;
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    const int slot = slot_of(L, min(c, L.nc - 1));
+    const uint64_t kb = reinterpret_cast<uint64_t>(in.kimg + ((int64_t)L.h * L.nt + slot) * kKLines * 64);
+    const uint64_t qb = reinterpret_cast<uint64_t>(in.q16 + ((int64_t)L.h * L.nt + slot) * 16 * 512);
+    const uint64_t wb = reinterpret_cast<uint64_t>(in.w16 + ((int64_t)L.hv * L.nt + slot) * 16 * 512);
+    const uint64_t pb = reinterpret_cast<uint64_t>(in.pimg + ((int64_t)L.hv * L.nt + slot) * 12 * 512);
+    const uint64_t gb = reinterpret_cast<uint64_t>(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride);
+    const uint64_t ub = reinterpret_cast<uint64_t>(
+        in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 256);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = L.lane + 64 * i;
+      const int lh = min(member * nh + j, kHLines - 1);
+      const int lv = min(slice * nv + (j - nh), kVLines - 1);
+      const int lu = min(j - nh - nv, kULines - 1);
+      const uint64_t ah = lh < kKLines ? kb + 128u * lh : qb + 128u * (lh - kKLines);
+      const uint64_t av = lv < kWLines ? wb + 128u * lv
+                          : lv < kWLines + kPLines ? pb + 128u * (lv - kWLines)
+                                                   : gb + 128u * (lv - kWLines - kPLines);
+      const uint64_t a = j < nh ? ah : j < nh + nv ? av : ub + 128u * max(lu, 0);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)a,
+                                       (__attribute__((address_space(3))) void *)sink, 4, 0, 0);
+    }
+  };
+  for (int c = kDepth; c < kDepth + kL2Lead; ++c) issue(c);
+  for (int c = 0; c < L.nc; c += kDepth)
+    for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+      issue(c + decltype(Bc)::value + kDepth + kL2Lead);
+      lds_barrier();
+    });
+  // the LDS-DMA writes must land before the work-group's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <bool kF32In, int kDepth>
-__global__ __launch_bounds__(kInterThreads) void inter_kernel(StageBuffers in, const float *__restrict__ h0,
+__global__ __launch_bounds__((kInterThreads<kF32In, kDepth>)) void inter_kernel(StageBuffers in, const float *__restrict__ h0,
                                                               const int32_t *__restrict__ cu,
                                                               float *__restrict__ o, float *__restrict__ hT,
                                                               int n_max, int H, int Hv, int t_max, int nt) {
   __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags][64];
+  __shared__ uint32_t l2_sink[64];
 
   // ---- XCD-aware work-group -> (sequence, value head, slice) --------------
   const int HG = Hv / H;
@@ -412,8 +491,10 @@ __global__ __launch_bounds__(kInterThreads) void inter_kernel(StageBuffers in, c
     chain_wave<kF32In, kDepth, 1>(L, in, h0, hT, xch);
   else if (wave == 2)
     helper_wave<kDepth, 0>(L, in, o, xch);
-  else
+  else if (wave == 3)
     helper_wave<kDepth, 1>(L, in, o, xch);
+  else if constexpr (kWarmWave<kF32In, kDepth>)
+    l2_warm_wave<kF32In, kDepth>(L, in, member, members, l2_sink);
 }
 
 // Compute units of the current device (queried once per device).
@@ -439,10 +520,11 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
   const int rounds = (groups + kXcds - 1) / kXcds;
   const dim3 grid(rounds * kXcds * members);
   if (static_cast<int>(grid.x) <= cu_count())
-    hipExtLaunchKernelGGL((inter_kernel<kF32In, 2>), grid, dim3(kInterThreads), 0, stream, ev.start,
+    hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepthSingle>), grid,
+                          dim3(kInterThreads<kF32In, kDepthSingle>), 0, stream, ev.start,
                           ev.stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
   else
-    hipExtLaunchKernelGGL((inter_kernel<kF32In, 1>), grid, dim3(kInterThreads), 0, stream, ev.start,
+    hipExtLaunchKernelGGL((inter_kernel<kF32In, 1>), grid, dim3(kInterThreads<kF32In, 1>), 0, stream, ev.start,
                           ev.stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
   return hipGetLastError();
 }
