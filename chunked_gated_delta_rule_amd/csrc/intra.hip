@@ -41,12 +41,14 @@
 //  * Each wave scans the chunk's gates itself (one token per lane) and keeps
 //    its own copy in LDS, so the gates need no work-group barrier.
 //  * The solve runs in fp32: the four diagonal 16x16 blocks by column forward
-//    substitution, then the off-diagonal blocks in two doubling levels on
-//    v_mfma_f32_16x16x4_f32 (T_10 = -T_11 A_10 T_00 and T_32 likewise, then
-//    the lower-left 32x32 block = -T_BB A_BA T_AA).
+//    substitution (four lanes per column, quad reductions), then the
+//    off-diagonal blocks in two doubling levels on v_mfma_f32_16x16x4_f32
+//    (T_10 = -T_11 A_10 T_00 and T_32 likewise, then the lower-left 32x32
+//    block = -T_BB A_BA T_AA).
 //  * w and u are MFMA products of the transposed K (V) tile with the scaled
-//    T; each lane scales and splits its own T fragment into hi + lo bf16 in
-//    registers, so w and u are formed in one pass with no staging buffer.
+//    T. The six nonzero 16x32 pieces of T diag(beta e^gamma) and T diag(beta)
+//    are scaled and split into hi + lo bf16 once each, into LDS in fragment
+//    order, and every wave reads them for its own d-blocks.
 // Rows of a partial last chunk are zero-filled, so they add nothing; every
 // per-chunk block is written in full (zeros past the end).
 #include "gdn.h"
@@ -63,14 +65,15 @@ constexpr int kLdRow = kD + 8;   // bf16 row-major tile [64][136]
 constexpr int kLdAT = kC + 4;    // fp32 A, then T in place [64][68]
 constexpr int kLdX = 16 + 4;     // fp32 per-wave 16x16 scratch
 
-// LDS of one work-group (bf16 input: 53 KB; fp32 input: 87 KB). Two bf16
-// work-groups run per CU: a third would fit the LDS, but at the 168 VGPRs it
-// allows the kernel spills and runs 15% slower per chunk.
+// LDS of one work-group (bf16 input: 77 KB, two work-groups per CU; fp32
+// input: 111 KB):
 //   K rows   [terms][64][136] bf16   for K K^T, K q^T, the K^T fragments and w
 //   A / T    [64][68] fp32           A, solved into T in place
 //   V rows   [terms][64][136] bf16   for u; the solve's per-wave scratch lives
 //                                    here until V is stored after the solve
 //   gates    per wave: log2-scaled gamma and beta (64 floats each)
+//   T s      six 4 KB items: hi / lo bf16 fragments of T diag(beta e^gamma)
+//            and T diag(beta) for the w / u products
 // During set-up the q rows occupy the A / T region (and V's for fp32 input).
 template <bool kF32In>
 struct IntraSmem {
@@ -80,10 +83,18 @@ struct IntraSmem {
   static constexpr int kOffAT = kOffK + kTerms * kTile;
   static constexpr int kOffV = kOffAT + 64 * kLdAT * 4;
   static constexpr int kOffGates = kOffV + kTerms * kTile;
-  static constexpr int kBytes = kOffGates + 4 * 2 * 64 * 4;
+  static constexpr int kOffTS = kOffGates + 4 * 2 * 64 * 4;
+  static constexpr int kBytes = kOffTS + 6 * 4 * 64 * 16;
   static_assert(64 * kLdAT * 4 == kTile, "q rows must fit the A / T region (and V's)");
   static_assert(4 * 16 * kLdX * 4 <= kTile, "solve scratch must fit the V region");
 };
+
+// x of the lane that quad permutation kCtrl (DPP quad_perm) selects.
+template <int kCtrl>
+__device__ __forceinline__ float quad_swap(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                                0xf, 0xf, true));
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -291,6 +302,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   float *at = reinterpret_cast<float *>(smem + Smem::kOffAT);      // A, then T in place
   __bf16 *rv = reinterpret_cast<__bf16 *>(smem + Smem::kOffV);    // V rows (hi[, lo])
   float *xs = reinterpret_cast<float *>(smem + Smem::kOffV);      // solve scratch (in V's place)
+  u32x4 *ts = reinterpret_cast<u32x4 *>(smem + Smem::kOffTS);     // T s items (hi / lo)
   __bf16 *rq = reinterpret_cast<__bf16 *>(smem + Smem::kOffAT);   // q rows during set-up
 
   const int tid = threadIdx.x;
@@ -557,20 +569,29 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     }
     __syncthreads();
 
-    // ---- solve 1: diagonal blocks by column forward substitution, in place:
-    // row r of the block is read (by every lane) before any lane writes it
-    if (lane < 16) {
-      const int c = lane;
+    // ---- solve 1: diagonal blocks by column forward substitution, in place
+    // (T[r][c] = delta_rc - sum_{i < r} A[r][i] T[i][c]). Four lanes per
+    // column: lane (c, q) = (lane >> 2, lane & 3) keeps T[4 q .. 4 q + 3][c]
+    // and forms that quarter of each row's sum; a quad reduction completes
+    // it. A is strictly lower and unknown T entries are still zero, so the
+    // quarters need no mask. The whole block is read before T is written.
+    {
+      const int c = lane >> 2, q = lane & 3;
       float *ab = at + (16 * wv) * kLdAT + 16 * wv;
-      float tc[16];
+      f32x4 arow[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) arow[r] = *reinterpret_cast<const f32x4 *>(ab + r * kLdAT + 4 * q);
+      f32x4 t = zero4();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = 0.f;
-#pragma unroll
-        for (int i = 0; i < r; ++i) x = fmaf(ab[r * kLdAT + i], tc[i], x);
-        tc[r] = r == c ? 1.f : (r < c ? 0.f : -x);
-        ab[r * kLdAT + c] = tc[r];
+        float part = fmaf(arow[r][0], t[0], arow[r][1] * t[1]) + fmaf(arow[r][2], t[2], arow[r][3] * t[3]);
+        part += quad_swap<0xB1>(part);  // lanes 4c + {1, 0, 3, 2}
+        part += quad_swap<0x4E>(part);  // lanes 4c + {2, 3, 0, 1}
+        const float val = r == c ? 1.f : (r < c ? 0.f : -part);
+        t[r & 3] = q == (r >> 2) ? val : t[r & 3];
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ab[(4 * q + j) * kLdAT + c] = t[j];
     }
     __syncthreads();
     // ---- solve 2: T_10 = -T_11 (A_10 T_00), T_32 = -T_33 (A_32 T_22) -------
@@ -615,37 +636,48 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
       put16(at + (16 * bi) * kLdAT + 16 * bj, kLdAT, y, -1.f, lane);
     }
     __syncthreads();  // T complete; the solve scratch (V's region) is free
+
+    // ---- T diag(beta e^gamma) and T diag(beta), split hi + lo, once per
+    // nonzero (token block rb, contraction block ks) of T: item it in the
+    // order (0,0)(1,0)(2,0)(2,1)(3,0)(3,1); lane (g, c) holds row 16 rb + c,
+    // columns j = 32 ks + 8 g .. + 7 (an A fragment of U = (T s) V and a B
+    // fragment of W^T = K^T (T s)^T alike).
+    for (int it = wv; it < 6; it += 4) {
+      const int rb = it < 2 ? it : 1 + (it >> 1), ks = it < 2 ? 0 : (it & 1);
+      const int j0 = 32 * ks + 8 * (lane >> 4);
+      const float *trow = at + (16 * rb + (lane & 15)) * kLdAT + j0;
+      const f32x4 t_a = *reinterpret_cast<const f32x4 *>(trow);
+      const f32x4 t_b = *reinterpret_cast<const f32x4 *>(trow + 4);
+      const f32x4 g_a = *reinterpret_cast<const f32x4 *>(gsh + j0);
+      const f32x4 g_b = *reinterpret_cast<const f32x4 *>(gsh + j0 + 4);
+      const f32x4 b_a = *reinterpret_cast<const f32x4 *>(bsh + j0);
+      const f32x4 b_b = *reinterpret_cast<const f32x4 *>(bsh + j0 + 4);
+      float xw8[8], xu8[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xu8[i] = t_a[i] * b_a[i];
+        xu8[4 + i] = t_b[i] * b_b[i];
+        xw8[i] = xu8[i] * fast_exp2(g_a[i]);
+        xw8[4 + i] = xu8[4 + i] * fast_exp2(g_b[i]);
+      }
+      u32x4 *d = ts + it * 4 * 64 + lane;
+      split8_words(xw8, d[0], d[64]);
+      split8_words(xu8, d[128], d[192]);
+    }
     put_rows(rv, vh, vl);
     __syncthreads();
 
-    // ---- w and u in one pass: T diag(beta e^gamma) and T diag(beta), split
-    // hi + lo per lane, against K^T / V^T read transposed from the row tiles.
-    // Tiles (d-block db, token block rb): w as W^T = K^T (T s)^T (lane holds
-    // four d of one token), u as U = (T s) V (lane holds four tokens of one d).
+    // ---- w and u in one pass: the T s items against K^T / V^T read
+    // transposed from the row tiles. Tiles (d-block db, token block rb): w as
+    // W^T = K^T (T s)^T (lane holds four d of one token), u as U = (T s) V
+    // (lane holds four tokens of one d).
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       f32x4 wacc[2] = {zero4(), zero4()}, uacc[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks <= (rb >> 1); ++ks) {
-        const int j0 = 32 * ks + 8 * (lane >> 4);
-        const float *trow = at + (16 * rb + (lane & 15)) * kLdAT + j0;
-        const f32x4 t_a = *reinterpret_cast<const f32x4 *>(trow);
-        const f32x4 t_b = *reinterpret_cast<const f32x4 *>(trow + 4);
-        const f32x4 g_a = *reinterpret_cast<const f32x4 *>(gsh + j0);
-        const f32x4 g_b = *reinterpret_cast<const f32x4 *>(gsh + j0 + 4);
-        const f32x4 b_a = *reinterpret_cast<const f32x4 *>(bsh + j0);
-        const f32x4 b_b = *reinterpret_cast<const f32x4 *>(bsh + j0 + 4);
-        float xw8[8], xu8[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xu8[i] = t_a[i] * b_a[i];
-          xu8[4 + i] = t_b[i] * b_b[i];
-          xw8[i] = xu8[i] * fast_exp2(g_a[i]);
-          xw8[4 + i] = xu8[4 + i] * fast_exp2(g_b[i]);
-        }
-        u32x4 wh, wl, uh, ul;
-        split8_words(xw8, wh, wl);
-        split8_words(xu8, uh, ul);
+        const u32x4 *item = ts + (rb < 2 ? rb : 2 * rb - 2 + ks) * 4 * 64 + lane;
+        const u32x4 wh = item[0], wl = item[64], uh = item[128], ul = item[192];
 #pragma unroll
         for (int db2 = 0; db2 < 2; ++db2) {
           const int db = 2 * wv + db2;
