@@ -17,6 +17,10 @@ are on a few microseconds. Each kernel's duration averaged over the sampled
 steps is its execution time; the dominant kernel's algorithmic bytes per
 launch divided by that duration is the roofline figure.
 
+Workloads 5 and 6 (a draft-verify batch of 64 x 8 tokens, a decode batch of
+256 x 1 token) time the token-serial recurrent kernel (gdn_recurrent_fwd)
+instead: a step is one call of it, and its roofline is HBM.
+
 Prints ONE JSON line. Default workload: single sequence, T = 4096, H = 16,
 Hv = 32, D = 128, bf16 q/k/v (the configuration the metric is quoted on).
 The CPU baseline is the fp64 oracle timed on this host's cores.
@@ -36,6 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GDN chunk-prefill tokens/s at 1 GPU; % MFMA peak (intra), % HBM BW (inter)"
+METRIC_RECURRENT = "GDN token-serial decode/verify tokens/s at 1 GPU; % HBM BW"
+RECURRENT_WORKLOADS = (5, 6)  # run by gdn_recurrent_fwd instead of the chunked forward
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 SOLVE_FLOP = 83328           # 64x64 unit-lower inverse: 41,664 multiply-adds
@@ -60,8 +66,14 @@ def algorithmic_work(wl, nt, qkv_bytes, fused_front=False):
     if wl.qkv is not None and not fused_front:
         C = (2 * H + Hv) * D
         front_bytes = T * C * 2 + T * C * 4
+    # token-serial kernel: q, k, v, g, beta in, o out per token, the state read
+    # (if given) and written once; per token and value head the two sums over
+    # the state and its rank-1 update, 6 D^2 flops
+    rec_bytes = T * (2 * H * D * qkv_bytes + Hv * D * qkv_bytes + Hv * 8 + Hv * D * 4)
+    rec_bytes += n_state * Hv * D * D * 4 * (2 if wl.h0 is not None else 1)
+    rec_flop = T * Hv * 6 * D * D
     return dict(intra=(stage1_bytes, stage1_flop), inter=(stage2_bytes, stage2_flop),
-                front=(front_bytes, 0), index=(0, 0))
+                front=(front_bytes, 0), index=(0, 0), recurrent=(rec_bytes, rec_flop))
 
 
 def kernel_source_digest(name):
@@ -164,7 +176,8 @@ def main():
                     help="time the kernels of every E-th step with dispatch events (the "
                          "others run the plain entry point: per-dispatch events add a few "
                          "microseconds to the step they are on)")
-    ap.add_argument("--workload", type=int, default=1, help="named workload 0..4")
+    ap.add_argument("--workload", type=int, default=1,
+                    help="named workload 0..6 (5 and 6 time the token-serial kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused-front", action="store_true",
                     help="front workload: run the standalone front, then the forward "
@@ -200,6 +213,7 @@ def main():
     cu = torch.from_numpy(wl.cu_seqlens).to(dev)
     has_front = wl.qkv is not None
     fused_front = has_front and not args.unfused_front
+    serial = args.workload in RECURRENT_WORKLOADS
     qkv_dtype = torch.float32 if has_front else wl.qkv_dtype
     cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype)
     ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=dev)
@@ -217,9 +231,18 @@ def main():
     table_kernel = wl.n_max > gdn.GDN_FUSED_INDEX_MAX_SEQS
     stages = (["front"] if has_front and not fused_front else []) + \
         (["index"] if table_kernel else []) + ["intra", "inter"]
+    if serial:
+        stages = ["recurrent"]
     hip = HipEvents()
 
     def step(evs=None):
+        if serial:
+            if evs is None:
+                gdn.gdn_recurrent_fwd(cfg, q, k, v, d["g"], d["beta"], d["h0"], cu, o, hT)
+            else:
+                gdn.gdn_recurrent_fwd_timed(cfg, q, k, v, d["g"], d["beta"], d["h0"], cu, o, hT,
+                                            evs[0], evs[1])
+            return
         if fused_front:
             if evs is None:
                 gdn.gdn_chunk_fwd_conv(cfg, d["qkv"], d["conv_w"], wl.d_conv, d["g"], d["beta"],
@@ -254,7 +277,8 @@ def main():
     elapsed = time.perf_counter() - t0
     events = [ev for ev in events if ev is not None]
 
-    pair = {"index": (0, 1), "intra": (2, 3), "inter": (4, 5), "front": (6, 7)}
+    pair = {"index": (0, 1), "intra": (2, 3), "inter": (4, 5), "front": (6, 7),
+            "recurrent": (0, 1)}
     per_stage_ms = {name: statistics.fmean(hip.ms(ev[pair[name][0]], ev[pair[name][1]])
                                            for ev in events)
                     for name in stages}
@@ -271,7 +295,7 @@ def main():
                         "alg_bytes": b, "alg_flop": f,
                         "hbm_frac": round(b / t_s / (HBM_PEAK_GBS * 1e9), 4) if b else None,
                         "mfma_frac": round(f / t_s / (BF16_PEAK_TFLOPS * 1e12), 4) if f else None}
-    dom = max(("intra", "inter"), key=lambda n: per_stage_ms[n])
+    dom = "recurrent" if serial else max(("intra", "inter"), key=lambda n: per_stage_ms[n])
     b_dom = work[dom][0]
     t_dom = per_stage_ms[dom] * 1e-3
     ach = b_dom / t_dom / 1e9
@@ -284,7 +308,7 @@ def main():
         cpu = cpu_baseline(wl)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC_RECURRENT if serial else METRIC,
         "value": round(args.steps * tokens / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

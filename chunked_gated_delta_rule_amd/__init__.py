@@ -28,7 +28,8 @@ __all__ = [
     "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
     "gdn_workspace_layout", "make_config", "chunk_gated_delta_rule", "EXPORTED_SYMBOLS",
     "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "GDN_FUSED_INDEX_MAX_SEQS",
-    "gdn_chunk_fwd_conv", "gdn_chunk_fwd_conv_timed",
+    "gdn_chunk_fwd_conv", "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd",
+    "gdn_recurrent_fwd_timed", "recurrent_gated_delta_rule",
 ]
 
 GDN_BF16 = 0
@@ -40,7 +41,7 @@ EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_layout", "gdn_workspace_size",
                     "gdn_build_chunk_indices", "gdn_front_conv_silu_l2", "gdn_chunk_fwd_intra",
                     "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
                     "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "gdn_chunk_fwd_conv",
-                    "gdn_chunk_fwd_conv_timed")
+                    "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd", "gdn_recurrent_fwd_timed")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libgdn.so")
@@ -93,10 +94,12 @@ def load_library():
     lib.gdn_chunk_fwd_conv.argtypes = [cfgp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_chunk_fwd_conv_timed.argtypes = [cfgp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                              vp, ctypes.POINTER(vp)]
+    lib.gdn_recurrent_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_recurrent_fwd_timed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     for name in ("gdn_workspace_size", "gdn_workspace_layout", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
                  "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd",
                  "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "gdn_chunk_fwd_conv",
-                 "gdn_chunk_fwd_conv_timed"):
+                 "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd", "gdn_recurrent_fwd_timed"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_status_str.restype = ctypes.c_char_p
@@ -256,6 +259,37 @@ def gdn_chunk_fwd_conv_timed(cfg, qkv, conv_w, d_conv, g, beta, h0, cu_seqlens, 
                                                    _ptr(hT), _ptr(workspace), int(ws_bytes),
                                                    _stream(stream), arr),
            "gdn_chunk_fwd_conv_timed")
+
+
+def gdn_recurrent_fwd(cfg, q, k, v, g, beta, h0, cu_seqlens, o, hT, stream=None):
+    _check(load_library().gdn_recurrent_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                            _ptr(beta), _ptr(h0), _ptr(cu_seqlens), _ptr(o),
+                                            _ptr(hT), _stream(stream)),
+           "gdn_recurrent_fwd")
+
+
+def gdn_recurrent_fwd_timed(cfg, q, k, v, g, beta, h0, cu_seqlens, o, hT, ev_start, ev_stop,
+                            stream=None):
+    """gdn_recurrent_fwd whose kernel records raw hipEvent_t handles at its start and end."""
+    _check(load_library().gdn_recurrent_fwd_timed(
+        ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+        _ptr(cu_seqlens), _ptr(o), _ptr(hT), _stream(stream), int(ev_start), int(ev_stop)),
+        "gdn_recurrent_fwd_timed")
+
+
+def recurrent_gated_delta_rule(q, k, v, g, beta, cu_seqlens, initial_state=None,
+                               output_final_state=True, scale=None, n_max=None):
+    """Allocate outputs with torch and run gdn_recurrent_fwd (token-serial decode /
+    verify) on the current stream. Arguments as chunk_gated_delta_rule."""
+    T, H, _ = q.shape
+    Hv = v.shape[1]
+    n = cu_seqlens.numel() - 1 if n_max is None else n_max
+    cfg = make_config(T, n, H, Hv, q.dtype, scale or 0.0)
+    o = torch.empty((T, Hv, 128), dtype=torch.float32, device=q.device)
+    hT = torch.empty((n, Hv, 128, 128), dtype=torch.float32, device=q.device) \
+        if output_final_state else None
+    gdn_recurrent_fwd(cfg, q, k, v, g, beta, initial_state, cu_seqlens, o, hT)
+    return o, hT
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, cu_seqlens, initial_state=None,

@@ -148,6 +148,22 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
                                     static_cast<float *>(o), hT, s, ev[2]));
 }
 
+gdn_status recurrent_impl(const gdn_config *cfg, const void *q, const void *k, const void *v,
+                          const float *g, const float *beta, const float *h0,
+                          const int32_t *cu_seqlens, void *o, float *hT, void *stream,
+                          gdn::KernelEvents ev) {
+  const gdn_status st = check_config(cfg);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return GDN_ERR_INVALID_ARG;
+  return from_hip(gdn::launch_recurrent(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, h0,
+                                        cu_seqlens, cfg->n_max, cfg->h, cfg->hv, scale_of(cfg),
+                                        static_cast<float *>(o), hT, as_stream(stream), ev));
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,6 +309,21 @@ gdn_status gdn_chunk_fwd_conv_timed(const gdn_config *cfg, const void *qkv, cons
   conv.d_conv = d_conv;
   return chunk_fwd_impl(cfg, nullptr, nullptr, nullptr, g, beta, h0, cu_seqlens, chunk_indices, o,
                         hT, workspace, ws_bytes, stream, ev, conv);
+}
+
+gdn_status gdn_recurrent_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const float *h0,
+                             const int32_t *cu_seqlens, void *o, float *hT, void *stream) {
+  return recurrent_impl(cfg, q, k, v, g, beta, h0, cu_seqlens, o, hT, stream, {});
+}
+
+gdn_status gdn_recurrent_fwd_timed(const gdn_config *cfg, const void *q, const void *k,
+                                   const void *v, const float *g, const float *beta,
+                                   const float *h0, const int32_t *cu_seqlens, void *o, float *hT,
+                                   void *stream, void *ev_start, void *ev_stop) {
+  if (!ev_start || !ev_stop) return GDN_ERR_INVALID_ARG;
+  return recurrent_impl(cfg, q, k, v, g, beta, h0, cu_seqlens, o, hT, stream,
+                        {static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)});
 }
 
 const char *gdn_status_str(gdn_status status) {

@@ -55,6 +55,12 @@ hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v
                         int32_t t_max, float scale, const StageBuffers &out, hipStream_t stream,
                         KernelEvents ev = {}, ConvIn conv = {});
 
+hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const void *v,
+                            const float *g, const float *beta, const float *h0,
+                            const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
+                            float scale, float *o, float *hT, hipStream_t stream,
+                            KernelEvents ev = {});
+
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
                         int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,

@@ -193,6 +193,26 @@ gdn_status gdn_chunk_fwd_conv(const gdn_config *cfg, const void *qkv, const void
                               const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
                               float *hT, void *workspace, size_t ws_bytes, void *stream);
 
+/* Token-serial recurrent forward, for decode and speculative verify (1 to 16
+ * tokens per sequence is its purpose; any length is computed). Each sequence's
+ * tokens are applied one at a time in fp32, in the order of the Alloy page's
+ * section "What is the gated delta rule in Qwen3.5?": S <- e^{g_t} S,
+ * d = beta_t (v_t - S^T k_t), S <- S + k_t d^T, o_t = scale S^T q_t. The state
+ * stays on chip between tokens (section "How does decode run a sequential
+ * update on a GPU?"), and a verify batch reproduces decode's arithmetic
+ * token by token (section "Why keep the serial kernel at all?"; llama.cpp PR
+ * 399, "What": verify widths of 1 to 16 tokens). No workspace.
+ *   q, k (device) [t_max, h, dk]; v (device) [t_max, hv, dv]; dtype qkv_dtype
+ *   g, beta (device) fp32 [t_max, hv]
+ *   h0 (device, nullable = zero state) fp32 [n_max, hv, dv, dk]
+ *   o  (device) fp32 [t_max, hv, dv]: valid rows written, others untouched
+ *   hT (device, nullable) fp32 [n_max, hv, dv, dk]; hT may alias h0 exactly.
+ * cfg->chunk must be valid (64) but is not used. A zero-length sequence writes
+ * hT = h0 (or zeros when h0 is null). */
+gdn_status gdn_recurrent_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const float *h0,
+                             const int32_t *cu_seqlens, void *o, float *hT, void *stream);
+
 /* Timed variants, for measurement. They behave exactly like the entry point
  * they extend, and in addition each kernel they launch records a pair of HIP
  * events at its own start and end (the dispatch itself records them, so no
@@ -203,7 +223,7 @@ gdn_status gdn_chunk_fwd_conv(const gdn_config *cfg, const void *qkv, const void
  *          that kernel runs: chunk_indices NULL and n_max >
  *          GDN_FUSED_INDEX_MAX_SEQS), [2], [3] around the intra stage, [4],
  *          [5] around the inter stage.
- *   ev_start, ev_stop: around the front kernel.
+ *   ev_start, ev_stop: around the front kernel (the recurrent kernel).
  * A NULL event returns GDN_ERR_INVALID_ARG before any launch. */
 gdn_status gdn_chunk_fwd_timed(const gdn_config *cfg, const void *q, const void *k, const void *v,
                                const float *g, const float *beta, const float *h0,
@@ -220,6 +240,11 @@ gdn_status gdn_chunk_fwd_conv_timed(const gdn_config *cfg, const void *qkv, cons
                                     const int32_t *chunk_indices, void *o, float *hT,
                                     void *workspace, size_t ws_bytes, void *stream,
                                     void *const *events);
+
+gdn_status gdn_recurrent_fwd_timed(const gdn_config *cfg, const void *q, const void *k,
+                                   const void *v, const float *g, const float *beta,
+                                   const float *h0, const int32_t *cu_seqlens, void *o, float *hT,
+                                   void *stream, void *ev_start, void *ev_stop);
 
 /* Static string for a status code (never NULL). */
 const char *gdn_status_str(gdn_status status);

@@ -196,3 +196,29 @@ def test_fused_front_entry_point_host_errors(lib):
                                         None) == INVALID
     assert lib.gdn_chunk_fwd_conv_timed(c, F, F, 4, F, F, None, F, None, F, None, F, need, None,
                                         vp6(1, 2, 3, 4, None, 6)) == INVALID
+
+
+def test_recurrent_entry_points_host_errors(lib):
+    """gdn_recurrent_fwd validates like the chunk forward (no workspace); its
+    timed variant also rejects a missing event; nothing is launched."""
+    c = ctypes.byref(gdn.make_config(256, 2, 16, 32))
+    F = FAKE
+    # (cfg, q, k, v, g, beta, h0, cu, o, hT, stream)
+    assert lib.gdn_recurrent_fwd(None, F, F, F, F, F, None, F, F, None, None) == INVALID
+    for i in range(8):
+        args = [F] * 8
+        args[i] = None
+        q, k, v, g, b, cu, o = args[:5] + args[6:8]
+        if i == 5:
+            continue  # that slot is h0 below, which may be null
+        assert lib.gdn_recurrent_fwd(c, q, k, v, g, b, None, cu, o, None, None) == INVALID, i
+    assert lib.gdn_recurrent_fwd(c, F + 8, F, F, F, F, None, F, F, None, None) == INVALID
+    assert lib.gdn_recurrent_fwd(c, F, F, F, F + 2, F, None, F, F, None, None) == INVALID
+    assert lib.gdn_recurrent_fwd(c, F, F, F, F, F, F + 4, F, F, None, None) == INVALID
+    assert lib.gdn_recurrent_fwd(c, F, F, F, F, F, None, F, F, F + 4, None) == INVALID
+    bad = gdn.make_config(256, 2, 16, 24)
+    assert lib.gdn_recurrent_fwd(ctypes.byref(bad), F, F, F, F, F, None, F, F, None,
+                                 None) == UNSUPPORTED
+    assert lib.gdn_recurrent_fwd_timed(c, F, F, F, F, F, None, F, F, None, None, None, 8) == INVALID
+    assert lib.gdn_recurrent_fwd_timed(c, F, F, F, F, F, None, F, F, None, None, 8, None) == INVALID
+    assert lib.gdn_recurrent_fwd_timed(c, None, F, F, F, F, None, F, F, None, None, 8, 8) == INVALID

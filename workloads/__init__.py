@@ -17,7 +17,8 @@ the rounded values exactly.
   h0        N(0, sigma_h0) fp32, value-major [N_max, Hv, Dv, Dk], or none
   front     pre-conv q|k|v channels N(0, 1) bf16, conv weights N(0, 0.5) bf16
 
-The five named workloads are the ones the benchmark and the parity tests use:
+The named workloads are the ones the benchmark and the parity tests use (0-4
+for the chunked prefill; 5 and 6 for the token-serial decode / verify kernel):
   0 tiny dense     N=1,  T=256,  H=Hv=2,            fp32 q/k/v
   1 single seq     N=1,  T=4096, H=16, Hv=32,       bf16
   2 varlen batch   N=32, lengths U{1..1024}, H=16, Hv=32, bf16, h0 ~ N(0, 0.02),
@@ -25,6 +26,9 @@ The five named workloads are the ones the benchmark and the parity tests use:
   3 long context   N=1,  T=32768, H=Hv=16, bf16, g mean 2, h0 ~ N(0, 0.02)
   4 front + GDN    N=4 x 8192, H=16, Hv=32, d_conv=4; q/k/v come out of the
                    conv/SiLU/L2 front as fp32
+  5 verify         N=64 sequences x 8 tokens (a draft-verify width), H=16, Hv=32,
+                   bf16, h0 ~ N(0, 0.02)
+  6 decode         N=256 sequences x 1 token, H=16, Hv=32, bf16, h0 ~ N(0, 0.02)
 """
 
 from __future__ import annotations
@@ -147,11 +151,13 @@ NAMES = {
     2: "varlen-32seq-U1..1024-H16-Hv32-bf16-h0",
     3: "long-T32768-H16-Hv16-bf16-strong-decay-h0",
     4: "front-4x8192-H16-Hv32-dconv4",
+    5: "verify-64x8-H16-Hv32-bf16-h0",
+    6: "decode-256x1-H16-Hv32-bf16-h0",
 }
 
 
 def make(cfg: int, seed: Optional[int] = None) -> Workload:
-    """The five named workloads (see the module docstring)."""
+    """The named workloads (see the module docstring)."""
     s = cfg if seed is None else seed
     if cfg == 0:
         return make_custom([256], 2, 2, seed=s, dtype=torch.float32, name=NAMES[0])
@@ -168,4 +174,8 @@ def make(cfg: int, seed: Optional[int] = None) -> Workload:
         return make_custom([32768], 16, 16, seed=s, g_mu=2.0, h0_sigma=0.02, name=NAMES[3])
     if cfg == 4:
         return make_custom([8192] * 4, 16, 32, seed=s, front=True, d_conv=4, name=NAMES[4])
+    if cfg == 5:
+        return make_custom([8] * 64, 16, 32, seed=s, h0_sigma=0.02, name=NAMES[5])
+    if cfg == 6:
+        return make_custom([1] * 256, 16, 32, seed=s, h0_sigma=0.02, name=NAMES[6])
     raise ValueError(cfg)
