@@ -15,11 +15,13 @@
 // the whole 128 x 128 fp32 state in registers, 64 values per thread, and walks
 // the sequence's tokens in order. States are value-major (St[v][d] = S[d][v],
 // as h0 / hT). Thread (rg, ds) = (tid / 8, tid % 8) owns rows v = 4 rg .. 4 rg
-// + 3 and columns d = 16 ds .. 16 ds + 15, so the eight threads of a row group
-// are eight consecutive lanes of one wave: the two sums over d of each token
-// (S^T k before the write, S^T q after it) finish with three DPP steps and no
-// LDS or barrier. The state is read from h0 and written to hT once, with
-// 16-byte accesses that cover whole rows per eight lanes. The next token's
+// + 3 and columns d = 32 j + 4 ds .. 32 j + 4 ds + 3 (j < 4), so the eight
+// threads of a row group are eight consecutive lanes of one wave: the two sums
+// over d of each token (S^T k before the write, S^T q after it) finish with
+// three DPP steps and no LDS or barrier. The state is read from h0 and written
+// to hT once, each 16-byte access instruction covering whole 128-byte lines
+// (eight lanes per line), with non-temporal loads and stores: the state is
+// streamed through once, so it is not kept in the caches. The next token's
 // k, q, v, g and beta are requested while the current one is processed (one
 // buffer range per token row, empty past the sequence, so that request reads
 // zeros).
@@ -49,29 +51,6 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-// Sixteen consecutive elements (bf16 or fp32) of a row as floats.
-template <bool kF32In>
-__device__ __forceinline__ void load16(rsrc_t r, uint32_t off, float (&x)[16]) {
-  if constexpr (kF32In) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 w = buf_load16(r, off + 16 * j);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) x[4 * j + c] = __uint_as_float(w[c]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const u32x4 w = buf_load16(r, off + 16 * j);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        x[8 * j + 2 * c] = __uint_as_float(w[c] << 16);
-        x[8 * j + 2 * c + 1] = __uint_as_float(w[c] & 0xffff0000u);
-      }
-    }
-  }
-}
-
 // Four consecutive elements of a row as floats.
 template <bool kF32In>
 __device__ __forceinline__ void load4(rsrc_t r, uint32_t off, float (&x)[4]) {
@@ -89,6 +68,19 @@ __device__ __forceinline__ void load4(rsrc_t r, uint32_t off, float (&x)[4]) {
   }
 }
 
+// Elements 32 j + d4 .. 32 j + d4 + 3 (j < 4) of a row (bf16 or fp32) as
+// floats x[4 j + c].
+template <bool kF32In>
+__device__ __forceinline__ void load16(rsrc_t r, int d4, float (&x)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float y[4];
+    load4<kF32In>(r, (32 * j + d4) * (kF32In ? 4 : 2), y);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[4 * j + c] = y[c];
+  }
+}
+
 template <bool kF32In>
 __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     const void *__restrict__ qin, const void *__restrict__ kin, const void *__restrict__ vin,
@@ -99,7 +91,7 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
   const int s = blockIdx.x / Hv, hv = blockIdx.x % Hv;
   const int h = hv / (Hv / H);
   const int tid = threadIdx.x;
-  const int v0 = 4 * (tid >> 3), d0 = 16 * (tid & 7);
+  const int v0 = 4 * (tid >> 3), d4 = 4 * (tid & 7);
   const int bos = cu[s], eos = cu[s + 1];
   const int n = eos - bos;
 
@@ -117,7 +109,7 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     return p[(int64_t)(bos + min(i, n - 1)) * Hv + hv];
   };
 
-  // state rows v0 .. v0 + 3, columns d0 .. d0 + 15
+  // state rows v0 .. v0 + 3, columns 32 j + d4 .. 32 j + d4 + 3
   f32x4 St[4][4];
   const int64_t sb = ((int64_t)s * Hv + hv) * kD * kD;
   if (h0) {
@@ -125,7 +117,8 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        St[i][j] = *reinterpret_cast<const f32x4 *>(h0 + sb + (v0 + i) * kD + d0 + 4 * j);
+        St[i][j] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4 *>(h0 + sb + (v0 + i) * kD + 32 * j + d4));
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -135,8 +128,8 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
 
   float kx[16], qx[16], vx[4], gx = 0.f, bx = 0.f;
   if (n > 0) {
-    load16<kF32In>(row(kb, qk_row, 0), d0 * kEl, kx);
-    load16<kF32In>(row(qb, qk_row, 0), d0 * kEl, qx);
+    load16<kF32In>(row(kb, qk_row, 0), d4, kx);
+    load16<kF32In>(row(qb, qk_row, 0), d4, qx);
     load4<kF32In>(row(vb, v_row, 0), v0 * kEl, vx);
     gx = gate(g, 0);
     bx = gate(beta, 0);
@@ -150,8 +143,8 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
                           qx[8], qx[9], qx[10], qx[11], qx[12], qx[13], qx[14], qx[15]};
     const float vc[4] = {vx[0], vx[1], vx[2], vx[3]};
     // the next token's operands (zeros past the end)
-    load16<kF32In>(row(kb, qk_row, i + 1), d0 * kEl, kx);
-    load16<kF32In>(row(qb, qk_row, i + 1), d0 * kEl, qx);
+    load16<kF32In>(row(kb, qk_row, i + 1), d4, kx);
+    load16<kF32In>(row(qb, qk_row, i + 1), d4, qx);
     load4<kF32In>(row(vb, v_row, i + 1), v0 * kEl, vx);
     gx = gate(g, i + 1);
     bx = gate(beta, i + 1);
@@ -192,7 +185,8 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4 *>(hT + sb + (v0 + i) * kD + d0 + 4 * j) = St[i][j];
+        __builtin_nontemporal_store(St[i][j],
+                                    reinterpret_cast<f32x4 *>(hT + sb + (v0 + i) * kD + 32 * j + d4));
   }
 }
 
