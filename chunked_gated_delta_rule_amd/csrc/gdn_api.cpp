@@ -30,6 +30,7 @@ gdn_status check_config(const gdn_config *cfg) {
   if (cfg->qkv_dtype != GDN_BF16 && cfg->qkv_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
   if (cfg->o_dtype != GDN_BF16 && cfg->o_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
   if (std::isnan(cfg->scale) || std::isinf(cfg->scale)) return GDN_ERR_INVALID_ARG;
+  if (cfg->segments < 0 || cfg->segments > 2) return GDN_ERR_INVALID_ARG;
   if (cfg->dk != kD || cfg->dv != kD || cfg->chunk != kChunk) return GDN_ERR_UNSUPPORTED;
   if (cfg->hv % cfg->h != 0) return GDN_ERR_UNSUPPORTED;
   if (cfg->o_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
@@ -41,6 +42,17 @@ gdn_status check_config(const gdn_config *cfg) {
 int32_t nt_max_of(const gdn_config *cfg) {
   return static_cast<int32_t>((static_cast<int64_t>(cfg->t_max) + kChunk - 1) / kChunk +
                               cfg->n_max - 1);
+}
+
+// Stage-2 segments of a (validated) config: automatic = two when t_max allows
+// long sequences and the one-piece grid fills at most half of the device.
+int segments_of(const gdn_config *cfg) {
+  if (cfg->segments != 0) return cfg->segments;
+  if (cfg->t_max < GDN_SEGMENT_MIN_TOKENS) return 1;
+  return 2 * static_cast<int64_t>(gdn::inter_one_walk_grid(cfg->n_max, cfg->h, cfg->hv)) <=
+                 gdn::cu_count()
+             ? 2
+             : 1;
 }
 
 gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
@@ -57,8 +69,27 @@ gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   l.pimg = take(hv * nt * 12 * 1024);
   l.gimg = take(hv * nt * 192 * 4);
   l.table = take(nt * 2 * 4);
+  if (segments_of(cfg) == 2) {
+    const size_t state = static_cast<size_t>(cfg->n_max) * hv * kD * kD * 4;
+    l.seg_sa = take(state);
+    l.seg_z = take(state);
+    l.seg_phi = take(state);
+    l.seg_oh = take(t * hv * kD * 4);
+  } else {
+    l.seg_sa = l.seg_z = l.seg_phi = l.seg_oh = at;
+  }
   l.total = at;
   return l;
+}
+
+gdn::SegScratch seg_scratch(const gdn_workspace_layout_t &l, const void *workspace) {
+  char *ws = static_cast<char *>(const_cast<void *>(workspace));
+  gdn::SegScratch g;
+  g.sa = reinterpret_cast<float *>(ws + l.seg_sa);
+  g.z = reinterpret_cast<float *>(ws + l.seg_z);
+  g.phi = reinterpret_cast<float *>(ws + l.seg_phi);
+  g.oh = reinterpret_cast<float *>(ws + l.seg_oh);
+  return g;
 }
 
 gdn::StageBuffers stage_buffers(const gdn_workspace_layout_t &l, const void *workspace) {
@@ -145,7 +176,8 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
   }
   return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, b, h0, cu_seqlens, cfg->n_max,
                                     cfg->h, cfg->hv, cfg->t_max, nt_max_of(cfg),
-                                    static_cast<float *>(o), hT, s, ev[2]));
+                                    static_cast<float *>(o), hT, s, ev[2], segments_of(cfg),
+                                    seg_scratch(l, workspace)));
 }
 
 gdn_status recurrent_impl(const gdn_config *cfg, const void *q, const void *k, const void *v,
@@ -250,7 +282,8 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
   if (ws != GDN_OK) return ws;
   return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, stage_buffers(l, workspace), h0,
                                     cu_seqlens, cfg->n_max, cfg->h, cfg->hv, cfg->t_max,
-                                    nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream)));
+                                    nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream),
+                                    {}, segments_of(cfg), seg_scratch(l, workspace)));
 }
 
 gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,

@@ -61,9 +61,27 @@ hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const voi
                             float scale, float *o, float *hT, hipStream_t stream,
                             KernelEvents ev = {});
 
+// Scratch of the two-segment stage 2 (per (sequence, value head): the state
+// after segment A and segment B's zero-start end state, value-major
+// [dv][dk]; segment B's homogeneous end state, key-major [dk][dv]; and the
+// homogeneous output rows [t_max, hv, dv]).
+struct SegScratch {
+  float *sa = nullptr, *z = nullptr, *phi = nullptr, *oh = nullptr;
+};
+
+// Compute units of the current device (queried once per device).
+int cu_count();
+
+// Work-groups of the one-walk stage-2 grid (one per (sequence, value head,
+// 16-column slice), rounded to whole XCD rounds).
+int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv);
+
+// segments: 1 walks each sequence in one piece; 2 walks its two halves at once
+// (the second carrying the zero-start and the homogeneous state) and then
+// combines them with a fix-up kernel, using `seg`.
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
                         int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,
-                        KernelEvents ev = {});
+                        KernelEvents ev = {}, int segments = 1, SegScratch seg = {});
 
 }  // namespace gdn

@@ -67,10 +67,11 @@ constexpr int kL2Lead = 2;       // chunks between the L2 warm-up and the operan
 // The L2 warm-up wave is a fifth wave of the work-group; fp32 input at depth 2
 // needs more than the 256 VGPRs a SIMD with two waves of it could give, and
 // runs without it.
-template <bool kF32In, int kDepth>
-constexpr bool kWarmWave = !(kF32In && kDepth == 2);
-template <bool kF32In, int kDepth>
-constexpr int kInterThreads = kWarmWave<kF32In, kDepth> ? 320 : 256;
+template <bool kF32In, int kDepth, int kS>
+constexpr bool kWarmWave = !(kF32In && kDepth == 2) && (kS == 1 || kDepth == 1);
+constexpr int kDepthSeg = 1;  // prefetch depth of the two-state walk (keeps the warm-up wave)
+template <bool kF32In, int kDepth, int kS>
+constexpr int kInterThreads = kWarmWave<kF32In, kDepth, kS> ? 320 : 256;
 
 __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
@@ -158,17 +159,30 @@ __device__ __forceinline__ void for_sets(F &&f) {
   for_sets_impl<kDepth>(f, std::make_integer_sequence<int, kDepth>{});
 }
 
-template <bool kF32In, int kDepth, int X>
-__device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in,
-                                           const float *__restrict__ h0, float *__restrict__ hT,
-                                           u32x4 (*xch)[kXchFrags][64]) {
+// What one work-group walks: chunks [c0, c1) of its sequence, carrying kS
+// states of its 16-column slice. State 0 takes u and starts from init0
+// (value-major [dv][dk] states of this head, or zero when null); state 1,
+// when carried, takes no u and starts from the identity (the homogeneous
+// part of the recurrence). out[st]: where state st's output rows go; fin[st]:
+// where its final slice goes (state 0 value-major like hT, state 1 key-major
+// [dk][dv]); a null pointer is not written.
+struct Walk {
+  int c0, c1;
+  const float *init0;
+  float *out[2];
+  float *fin[2];
+};
+
+template <bool kF32In, int kDepth, int X, int kS>
+__device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const StageBuffers &in,
+                                           u32x4 (*xch)[kXchFrags * kS][64]) {
   constexpr int kNKw = kF32In ? 16 : 8;  // K^T fragments this wave uses per chunk
   const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;  // 1 KB fragment blocks
   const int slice = L.v0 / 16;
   struct Rsrc { rsrc_t w, k, u, g; };
   auto rsrc_of = [&](int c) __attribute__((always_inline)) {
     const int slot = slot_of(L, c);
-    const bool ok = c < L.nc;
+    const bool ok = c < W.c1;
     Rsrc r;
     r.w = make_rsrc(in.w16 + ((int64_t)L.hv * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
     r.k = make_rsrc(in.kimg + ((int64_t)L.h * L.nt + slot) * (kF32In ? 32 : 16) * 512,
@@ -218,89 +232,118 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const StageBuffers &in
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // state rows: S[tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + c]
-  f32x4 S[4];
+  // state rows: S[st][tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + c]
+  f32x4 S[kS][4];
   const int64_t sbase = (((int64_t)L.s * L.Hv + L.hv) * kD + L.v0 + L.c16) * kD + 64 * X + L.g4;
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl)
-    S[tl] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + sbase + 16 * tl) : zero4();
+    S[0][tl] = W.init0 ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + 16 * tl) : zero4();
+  if constexpr (kS == 2) {
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[1][tl][i] = 64 * X + 16 * tl + L.g4 + i == L.v0 + L.c16 ? 1.f : 0.f;
+  }
 
   // One chunk step on set B, which is refilled with chunk c + kDepth. A step
-  // past the last chunk (c >= nc) runs on zero fragments with a decay of 1
-  // and leaves S unchanged.
+  // past the last chunk (c >= c1) runs on zero fragments with a decay of 1
+  // and leaves the states unchanged.
   auto step = [&](const int c, auto Bc) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
     const Rsrc rn = rsrc_of(c + kDepth);
-    const float e_last = c < L.nc ? el[B] : 1.f;
+    const float e_last = c < W.c1 ? el[B] : 1.f;
     u32x4 *xb = &xch[c & 1][0][L.lane];
-    f16x8 s16[2];
+    f32x4 pv[kS][4];
 #pragma unroll
-    for (int pl = 0; pl < 2; ++pl) {
-      s16[pl] = to_f16x8(S[2 * pl], S[2 * pl + 1]);
-      xb[64 * (2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
+    for (int st = 0; st < kS; ++st) {
+      f16x8 s16[2];
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        s16[pl] = to_f16x8(S[st][2 * pl], S[st][2 * pl + 1]);
+        xb[64 * (kXchFrags * st + 2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
+      }
+      // partial v' over this wave's key rows (wave 0 starts state 0 from u)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) pv[st][R] = X == 0 && st == 0 ? u[B][R] : zero4();
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int R = 0; R < 4; ++R) pv[st][R] = mfma(w[B][2 * R + pl], s16[pl], pv[st][R]);
+#pragma unroll
+      for (int R = 0; R < 4; ++R)
+        xb[64 * (kXchFrags * st + 4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[st][R]);
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) S[st][tl] = S[st][tl] * e_last;
     }
-    // partial v' over this wave's key rows (wave 0 starts from u)
-    f32x4 pv[4];
-#pragma unroll
-    for (int R = 0; R < 4; ++R) pv[R] = X == 0 ? u[B][R] : zero4();
-#pragma unroll
-    for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-      for (int R = 0; R < 4; ++R) pv[R] = mfma(w[B][2 * R + pl], s16[pl], pv[R]);
-#pragma unroll
-    for (int R = 0; R < 4; ++R) xb[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[R]);
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl) S[tl] = S[tl] * e_last;
     __builtin_amdgcn_sched_barrier(0);
     load_w(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();  // chunk c's S (fp16) and both partials are published
-    f32x4 v[4];
-#pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      const f32x4 other = __builtin_bit_cast(f32x4, xb[64 * (4 + 4 * (1 - X) + R)]);
-      v[R] = X == 0 ? pv[R] + other : other + pv[R];  // both waves: partial0 + partial1
-    }
+    lds_barrier();  // chunk c's states (fp16) and all partials are published
     // S += K^T (e^{gamma_last - gamma} v')
-    bf16x8 eh[2], elo[2];
-    split8(v[0] * dec[B][0], v[1] * dec[B][1], eh[0], elo[0]);
-    split8(v[2] * dec[B][2], v[3] * dec[B][3], eh[1], elo[1]);
+    bf16x8 eh[kS][2], elo[kS][2];
+#pragma unroll
+    for (int st = 0; st < kS; ++st) {
+      f32x4 v[4];
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const f32x4 other =
+            __builtin_bit_cast(f32x4, xb[64 * (kXchFrags * st + 4 + 4 * (1 - X) + R)]);
+        v[R] = X == 0 ? pv[st][R] + other : other + pv[st][R];  // both waves: partial0 + partial1
+      }
+      split8(v[0] * dec[B][0], v[1] * dec[B][1], eh[st][0], elo[st][0]);
+      split8(v[2] * dec[B][2], v[3] * dec[B][3], eh[st][1], elo[st][1]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_u(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int st = 0; st < kS; ++st)
 #pragma unroll
-      for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[B][2 * tl + q], eh[q], S[tl]);
+      for (int q = 0; q < 2; ++q) {
 #pragma unroll
-      for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[B][2 * tl + q], elo[q], S[tl]);
-      if constexpr (kF32In) {
+        for (int tl = 0; tl < 4; ++tl) S[st][tl] = mfma(k[B][2 * tl + q], eh[st][q], S[st][tl]);
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl) S[tl] = mfma(k[B][8 + 2 * tl + q], eh[q], S[tl]);
+        for (int tl = 0; tl < 4; ++tl) S[st][tl] = mfma(k[B][2 * tl + q], elo[st][q], S[st][tl]);
+        if constexpr (kF32In) {
+#pragma unroll
+          for (int tl = 0; tl < 4; ++tl)
+            S[st][tl] = mfma(k[B][8 + 2 * tl + q], eh[st][q], S[st][tl]);
+        }
       }
-    }
     __builtin_amdgcn_sched_barrier(0);
     load_k(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
-    load_all(Bc, rsrc_of(decltype(Bc)::value));
+    load_all(Bc, rsrc_of(W.c0 + decltype(Bc)::value));
   });
-  for (int c = 0; c < L.nc; c += kDepth)  // a step past the last chunk changes nothing
+  for (int c = W.c0; c < W.c1; c += kDepth)  // a step past the last chunk changes nothing
     for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
       step(c + decltype(Bc)::value, Bc);
     });
-  if (hT) {
+  if (W.fin[0]) {
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) *reinterpret_cast<f32x4 *>(hT + sbase + 16 * tl) = S[tl];
+    for (int tl = 0; tl < 4; ++tl) *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + 16 * tl) = S[0][tl];
+  }
+  if constexpr (kS == 2) {
+    if (W.fin[1]) {
+      // key-major: row d = 64 X + 16 tl + 4 g + i, column v0 + c
+      float *f = W.fin[1] + ((int64_t)L.s * L.Hv + L.hv) * kD * kD + L.v0 + L.c16;
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[(64 * X + 16 * tl + L.g4 + i) * kD] = S[1][tl][i];
+    }
   }
 }
 
-// Helper wave Y: output token tiles R = 2 Y, 2 Y + 1 (rows 32 Y .. 32 Y + 31).
-template <int kDepth, int Y>
-__device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &in,
-                                            float *__restrict__ o, u32x4 (*xch)[kXchFrags][64]) {
+// Helper wave Y: output token tiles R = 2 Y, 2 Y + 1 (rows 32 Y .. 32 Y + 31)
+// of every carried state.
+template <int kDepth, int Y, int kS>
+__device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const StageBuffers &in,
+                                            u32x4 (*xch)[kXchFrags * kS][64]) {
   constexpr int kNQ = Y + 1;                 // token blocks of v' this wave contracts over
   constexpr int kPairs = Y == 0 ? 2 : 4;     // P pairs of its tiles
   constexpr int kPair0 = Y == 0 ? 0 : 2;
@@ -310,7 +353,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
   struct Rsrc { rsrc_t q, p, g; };
   auto rsrc_of = [&](int c) __attribute__((always_inline)) {
     const int slot = slot_of(L, c);
-    const bool ok = c < L.nc;
+    const bool ok = c < W.c1;
     Rsrc r;
     r.q = make_rsrc(in.q16 + ((int64_t)L.h * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
     r.p = make_rsrc(in.pimg + ((int64_t)L.hv * L.nt + slot) * 12 * 512, ok ? 12 * 1024 : 0);
@@ -345,53 +388,66 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
     const Rsrc rn = rsrc_of(c + kDepth);
     lds_barrier();  // chunk c handed over
     const u32x4 *xb = &xch[c & 1][0][L.lane];
-    f16x8 s16[4];
+    f32x4 ya[kS][2];
+    bf16x8 dh[kS][kNQ], dl[kS][kNQ];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) s16[p] = __builtin_bit_cast(f16x8, xb[64 * p]);
-    f32x4 v[2 * kNQ];
+    for (int st = 0; st < kS; ++st) {
+      f16x8 s16[4];
 #pragma unroll
-    for (int R = 0; R < 2 * kNQ; ++R)
-      v[R] = __builtin_bit_cast(f32x4, xb[64 * (4 + R)]) + __builtin_bit_cast(f32x4, xb[64 * (8 + R)]);
-    // y^T = S^T q^T for this wave's two token tiles
-    f32x4 ya[2] = {zero4(), zero4()};
+      for (int p = 0; p < 4; ++p) s16[p] = __builtin_bit_cast(f16x8, xb[64 * (kXchFrags * st + p)]);
+      f32x4 v[2 * kNQ];
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+      for (int R = 0; R < 2 * kNQ; ++R)
+        v[R] = __builtin_bit_cast(f32x4, xb[64 * (kXchFrags * st + 4 + R)]) +
+               __builtin_bit_cast(f32x4, xb[64 * (kXchFrags * st + 8 + R)]);
+      // y^T = S^T q^T for this wave's two token tiles
+      ya[st][0] = zero4();
+      ya[st][1] = zero4();
 #pragma unroll
-      for (int Rl = 0; Rl < 2; ++Rl) ya[Rl] = mfma(s16[p], qf[B][4 * Rl + p], ya[Rl]);
-    bf16x8 dh[kNQ], dl[kNQ];
+      for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int q = 0; q < kNQ; ++q) split8(v[2 * q], v[2 * q + 1], dh[q], dl[q]);
+        for (int Rl = 0; Rl < 2; ++Rl) ya[st][Rl] = mfma(s16[p], qf[B][4 * Rl + p], ya[st][Rl]);
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) split8(v[2 * q], v[2 * q + 1], dh[st][q], dl[st][q]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_q(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
     // o^T = v'^T P^T + scale e^gamma y^T
-    f32x4 pa[2] = {zero4(), zero4()};
-#pragma unroll
-    for (int Rl = 0; Rl < 2; ++Rl) {
-      const int R = 2 * Y + Rl;
-#pragma unroll
-      for (int q = 0; q <= (R >> 1); ++q) {
-        const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
-        pa[Rl] = mfma(dh[q], pf[B][2 * n], pa[Rl]);
-        pa[Rl] = mfma(dl[q], pf[B][2 * n], pa[Rl]);
-        pa[Rl] = mfma(dh[q], pf[B][2 * n + 1], pa[Rl]);
-      }
-    }
     const int t0 = L.bos + kC * c;
-    const uint32_t lc = c < L.nc ? static_cast<uint32_t>(min(kC, L.eos - t0)) : 0u;  // past the end: no store
-    const i32x4 ro = rsrc_words(o + ((int64_t)t0 * L.Hv + L.hv) * kD + L.v0, lc * L.Hv * kD * 4);
+    const uint32_t lc = c < W.c1 ? static_cast<uint32_t>(min(kC, L.eos - t0)) : 0u;  // past the end: no store
 #pragma unroll
-    for (int Rl = 0; Rl < 2; ++Rl)
-      store16(ro, vo_o, (2 * Y + Rl) * row_o, pa[Rl] + __uint_as_float(exs[B][Rl]) * ya[Rl]);
+    for (int st = 0; st < kS; ++st) {
+      f32x4 pa[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int Rl = 0; Rl < 2; ++Rl) {
+        const int R = 2 * Y + Rl;
+#pragma unroll
+        for (int q = 0; q <= (R >> 1); ++q) {
+          const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
+          pa[Rl] = mfma(dh[st][q], pf[B][2 * n], pa[Rl]);
+          pa[Rl] = mfma(dl[st][q], pf[B][2 * n], pa[Rl]);
+          pa[Rl] = mfma(dh[st][q], pf[B][2 * n + 1], pa[Rl]);
+        }
+      }
+      // a state without an output destination gets an empty store range
+      const uintptr_t ob = reinterpret_cast<uintptr_t>(W.out[st]) +
+                           (((uintptr_t)t0 * L.Hv + L.hv) * kD + L.v0) * 4;
+      const i32x4 ro = rsrc_words(reinterpret_cast<const void *>(ob),
+                                  W.out[st] ? lc * L.Hv * kD * 4 : 0u);
+#pragma unroll
+      for (int Rl = 0; Rl < 2; ++Rl)
+        store16(ro, vo_o, (2 * Y + Rl) * row_o, pa[Rl] + __uint_as_float(exs[B][Rl]) * ya[st][Rl]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_p(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
-    load_all(Bc, rsrc_of(decltype(Bc)::value));
+    load_all(Bc, rsrc_of(W.c0 + decltype(Bc)::value));
   });
-  for (int c = 0; c < L.nc; c += kDepth)  // a step past the last chunk changes nothing
+  for (int c = W.c0; c < W.c1; c += kDepth)  // a step past the last chunk changes nothing
     for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
       step(c + decltype(Bc)::value, Bc);
     });
@@ -407,20 +463,20 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const StageBuffers &i
 // (LDS-DMA: no register is written) and are never read, so nothing waits on
 // them until the wave ends. Requests past the last chunk repeat its lines.
 template <bool kF32In, int kDepth>
-__device__ __forceinline__ void l2_warm_wave(const Lane &L, const StageBuffers &in, int member,
-                                             int members, uint32_t *sink) {
+__device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const StageBuffers &in,
+                                             int member, int members, uint32_t *sink) {
   constexpr int kKLines = (kF32In ? 32 : 16) * 8;
   constexpr int kHLines = kKLines + 128;             // K^T image, q16
   constexpr int kWLines = 128, kPLines = 96;
   constexpr int kVLines = kWLines + kPLines + kGateStride * 4 / 128;  // w16, P, gates
   constexpr int kULines = 32;
   static_assert(kGateStride * 4 % 128 == 0, "gate block is whole lines");
-  if (L.nc == 0) return;
+  if (W.c1 <= W.c0) return;
   const int slice = L.v0 / 16;
   const int nh = (kHLines + members - 1) / members;
   const int nv = (kVLines + kSlices - 1) / kSlices;
   auto issue = [&](int c) __attribute__((always_inline)) {
-    const int slot = slot_of(L, min(c, L.nc - 1));
+    const int slot = slot_of(L, min(c, W.c1 - 1));
     const uint64_t kb = reinterpret_cast<uint64_t>(in.kimg + ((int64_t)L.h * L.nt + slot) * kKLines * 64);
     const uint64_t qb = reinterpret_cast<uint64_t>(in.q16 + ((int64_t)L.h * L.nt + slot) * 16 * 512);
     const uint64_t wb = reinterpret_cast<uint64_t>(in.w16 + ((int64_t)L.hv * L.nt + slot) * 16 * 512);
@@ -443,8 +499,8 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const StageBuffers &
                                        (__attribute__((address_space(3))) void *)sink, 4, 0, 0);
     }
   };
-  for (int c = kDepth; c < kDepth + kL2Lead; ++c) issue(c);
-  for (int c = 0; c < L.nc; c += kDepth)
+  for (int c = W.c0 + kDepth; c < W.c0 + kDepth + kL2Lead; ++c) issue(c);
+  for (int c = W.c0; c < W.c1; c += kDepth)
     for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
       issue(c + decltype(Bc)::value + kDepth + kL2Lead);
       lds_barrier();
@@ -453,19 +509,28 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const StageBuffers &
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool kF32In, int kDepth>
-__global__ __launch_bounds__((kInterThreads<kF32In, kDepth>)) void inter_kernel(StageBuffers in, const float *__restrict__ h0,
-                                                              const int32_t *__restrict__ cu,
-                                                              float *__restrict__ o, float *__restrict__ hT,
-                                                              int n_max, int H, int Hv, int t_max, int nt) {
-  __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags][64];
+// With kS = 1 every work-group walks its whole sequence. With kS = 2 the grid
+// is twice the one-walk grid: the first half walks the first ceil(nc / 2)
+// chunks of each sequence from h0 (its final slice goes to seg.sa), the
+// second half walks the rest carrying the zero-start state (outputs into o,
+// final slice to seg.z) and the identity-start homogeneous state (outputs to
+// seg.oh, final slice to seg.phi); segfix_kernel then combines them.
+template <bool kF32In, int kDepth, int kS>
+__global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS>)) void inter_kernel(
+    StageBuffers in, const float *__restrict__ h0, const int32_t *__restrict__ cu,
+    float *__restrict__ o, float *__restrict__ hT, int n_max, int H, int Hv, int t_max, int nt,
+    SegScratch seg) {
+  __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags * kS][64];
   __shared__ uint32_t l2_sink[64];
 
   // ---- XCD-aware work-group -> (sequence, value head, slice) --------------
   const int HG = Hv / H;
   const int members = HG * kSlices;
-  const int xcd = blockIdx.x % kXcds;
-  const int wslot = blockIdx.x / kXcds;
+  const int one_walk = (n_max * H + kXcds - 1) / kXcds * kXcds * members;
+  const int role = kS == 2 && static_cast<int>(blockIdx.x) >= one_walk ? 1 : 0;
+  const int b = static_cast<int>(blockIdx.x) - role * one_walk;
+  const int xcd = b % kXcds;
+  const int wslot = b / kXcds;
   const int group = (wslot / members) * kXcds + xcd;  // (sequence, key head)
   const int member = wslot % members;
   if (group >= n_max * H) return;
@@ -484,18 +549,198 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth>)) void inter_kernel(
   L.Hv = Hv;
   L.t_max = t_max;
   L.nt = nt;
+  Walk W;
+  if (kS == 1) {
+    W = Walk{0, L.nc, h0, {o, nullptr}, {hT, nullptr}};
+  } else {
+    const int cm = (L.nc + 1) / 2;
+    W = role == 0 ? Walk{0, cm, h0, {o, nullptr}, {seg.sa, nullptr}}
+                  : Walk{cm, L.nc, nullptr, {o, seg.oh}, {seg.z, seg.phi}};
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0)
-    chain_wave<kF32In, kDepth, 0>(L, in, h0, hT, xch);
+    chain_wave<kF32In, kDepth, 0, kS>(L, W, in, xch);
   else if (wave == 1)
-    chain_wave<kF32In, kDepth, 1>(L, in, h0, hT, xch);
+    chain_wave<kF32In, kDepth, 1, kS>(L, W, in, xch);
   else if (wave == 2)
-    helper_wave<kDepth, 0>(L, in, o, xch);
+    helper_wave<kDepth, 0, kS>(L, W, in, xch);
   else if (wave == 3)
-    helper_wave<kDepth, 1>(L, in, o, xch);
-  else if constexpr (kWarmWave<kF32In, kDepth>)
-    l2_warm_wave<kF32In, kDepth>(L, in, member, members, l2_sink);
+    helper_wave<kDepth, 1, kS>(L, W, in, xch);
+  else if constexpr (kWarmWave<kF32In, kDepth, kS>)
+    l2_warm_wave<kF32In, kDepth>(L, W, in, member, members, l2_sink);
 }
+
+// ---- two-segment fix-up ------------------------------------------------------
+// The recurrence is affine in the state a segment starts from: with S_A the
+// state after segment A, segment B's true state is Z + Phi S_A and its true
+// output rows are o_zero + o_hom S_A (Z, o_zero: the walk from zero with u;
+// Phi, o_hom: the walk from the identity without u). In the stored layouts
+// (value-major St[v][d]; Phi key-major) both updates are C = A B^T products:
+//   o rows:  C[v][t] = sum_j SA_t[v][j] o_hom[t][j],   o[t][v] += C[v][t]
+//   state:   C[d][v] = sum_j Phi[d][j] SA_t[v][j],     hT[v][d] = Z_t[v][d] + C[d][v]
+// One 256-thread work-group computes one 128 x 128 C (128 output rows of a
+// (sequence, value head), or its final state) on v_mfma_f32_16x16x32_bf16,
+// both fp32 operands split into bf16 hi + lo and three product terms; A is
+// staged in LDS, each wave owns 32 columns of C, and the wave's B^T rows and
+// the output tile are requested before A is staged.
+constexpr int kFixThreads = 256;
+constexpr int kLdFix = kD + 8;
+
+__global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__restrict__ cu,
+                                                             float *__restrict__ o,
+                                                             float *__restrict__ hT, SegScratch seg,
+                                                             int n_max, int Hv, int nbo) {
+  __shared__ __attribute__((aligned(16))) __bf16 ahi[kD * kLdFix];
+  __shared__ __attribute__((aligned(16))) __bf16 alo[kD * kLdFix];
+  const int per = nbo + 1;
+  const int pair = blockIdx.x / per, blk = blockIdx.x % per;
+  const int s = pair / Hv, hv = pair % Hv;
+  if (s >= n_max) return;
+  const int bos = cu[s], eos = cu[s + 1];
+  const int nc = (eos - bos + kC - 1) / kC, cm = (nc + 1) / 2;
+  const int64_t st = ((int64_t)s * Hv + hv) * kD * kD;
+  const bool fin = blk == nbo;
+  const int t_begin = bos + kC * (cm + 2 * blk);  // 128 output rows per work-group
+  if (fin ? hT == nullptr : t_begin >= eos) return;
+  const float *A = fin ? seg.phi + st : seg.sa + st;
+  const float *Bt = fin ? seg.sa + st : seg.oh + ((int64_t)t_begin * Hv + hv) * kD;
+  const uint32_t bt_row = fin ? kD * 4 : static_cast<uint32_t>(Hv) * kD * 4;
+  const int rows = fin ? kD : min(2 * kC, eos - t_begin);
+  const rsrc_t rb = make_rsrc(Bt, static_cast<uint32_t>(rows) * bt_row);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  // requests first: this wave's B^T rows (32 wv + 16 nt + c, all k) and the
+  // output tile the products are added to, so they arrive while A is staged
+  u32x4 braw[4][2][2];  // [ks][nt][half]
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint32_t off = (32 * wv + 16 * nt + c) * bt_row + (32 * ks + 8 * g) * 4;
+      braw[ks][nt][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+      braw[ks][nt][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, off + 16, 0, 0);
+    }
+  // C tile (mt, nt) element i: row 16 mt + 4 g + i, column n = 32 wv + 16 nt + c;
+  // its base: hT row n / Z row n (final state) or o row t_begin + n (rows past
+  // the sequence read as zero and are not written)
+  const float *base = fin ? seg.z + st : o + ((int64_t)t_begin * Hv + hv) * kD;
+  const uint32_t base_row = fin ? kD * 4 : static_cast<uint32_t>(Hv) * kD * 4;
+  const rsrc_t rc = make_rsrc(base, static_cast<uint32_t>(rows) * base_row);
+  f32x4 add[8][2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      add[mt][nt] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rc, (32 * wv + 16 * nt + c) * base_row + (16 * mt + 4 * g) * 4, 0, 0));
+  {  // A (128 x 128 fp32) -> LDS as bf16 hi / lo rows
+    const int r = tid >> 1, c0 = 64 * (tid & 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4 *>(A + r * kD + c0 + 8 * q);
+      const f32x4 x1 = *reinterpret_cast<const f32x4 *>(A + r * kD + c0 + 8 * q + 4);
+      const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      u32x4 h, l;
+      split8_words(x, h, l);
+      *reinterpret_cast<u32x4 *>(ahi + r * kLdFix + c0 + 8 * q) = h;
+      *reinterpret_cast<u32x4 *>(alo + r * kLdFix + c0 + 8 * q) = l;
+    }
+  }
+  __syncthreads();
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) acc[mt][0] = acc[mt][1] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8 bh[2], bl[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const u32x4 w0 = braw[ks][nt][0], w1 = braw[ks][nt][1];
+      const float x[8] = {__uint_as_float(w0[0]), __uint_as_float(w0[1]), __uint_as_float(w0[2]),
+                          __uint_as_float(w0[3]), __uint_as_float(w1[0]), __uint_as_float(w1[1]),
+                          __uint_as_float(w1[2]), __uint_as_float(w1[3])};
+      u32x4 h, l;
+      split8_words(x, h, l);
+      bh[nt] = __builtin_bit_cast(bf16x8, h);
+      bl[nt] = __builtin_bit_cast(bf16x8, l);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const int off = (16 * mt + c) * kLdFix + 32 * ks + 8 * g;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(ahi + off);
+      const bf16x8 al = *reinterpret_cast<const bf16x8 *>(alo + off);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        acc[mt][nt] = mfma(ah, bh[nt], acc[mt][nt]);
+        acc[mt][nt] = mfma(ah, bl[nt], acc[mt][nt]);
+        acc[mt][nt] = mfma(al, bh[nt], acc[mt][nt]);
+      }
+    }
+  }
+  // hT[v = n][d = 16 mt + 4 g ..] = Z + C, or o[t_begin + n][hv][v = 16 mt + 4 g ..] += C
+  float *dst_base = fin ? hT + st : o + ((int64_t)t_begin * Hv + hv) * kD;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = 32 * wv + 16 * nt + c;
+    if (n < rows) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<f32x4 *>(dst_base + (int64_t)n * (base_row / 4) + 16 * mt + 4 * g) =
+            add[mt][nt] + acc[mt][nt];
+    }
+  }
+}
+
+template <bool kF32In, int kDepth, int kS>
+void launch_walk(dim3 grid, const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
+                 int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
+                 const SegScratch &seg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS>), grid,
+                        dim3(kInterThreads<kF32In, kDepth, kS>), 0, stream, start, stop, 0, in, h0,
+                        cu, o, hT, n_max, h, hv, t_max, nt, seg);
+}
+
+template <bool kF32In>
+hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
+                        int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
+                        hipStream_t stream, KernelEvents ev, int segments, const SegScratch &seg) {
+  const int members = (hv / h) * kSlices;
+  const int groups = n_max * h;
+  const int rounds = (groups + kXcds - 1) / kXcds;
+  const int one_walk = rounds * kXcds * members;
+  if (segments != 2) {
+    const dim3 grid(one_walk);
+    if (one_walk <= cu_count())
+      launch_walk<kF32In, kDepthSingle, 1>(grid, in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
+                                           stream, ev.start, ev.stop);
+    else
+      launch_walk<kF32In, 1, 1>(grid, in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                                ev.start, ev.stop);
+    return hipGetLastError();
+  }
+  const dim3 grid(2 * one_walk);
+  if (2 * one_walk <= cu_count())
+    launch_walk<kF32In, kDepthSeg, 2>(grid, in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
+                                      stream, ev.start, nullptr);
+  else
+    launch_walk<kF32In, 1, 2>(grid, in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                              ev.start, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // work-groups of 128 output rows over the at most floor(ceil(t_max / 64) / 2)
+  // chunks of segment B, plus one final-state work-group, per (sequence,
+  // value head)
+  const int nbo = ((t_max + kC - 1) / kC / 2 + 1) / 2;
+  const int64_t blocks = static_cast<int64_t>(n_max) * hv * (nbo + 1);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL(segfix_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kFixThreads), 0,
+                        stream, nullptr, ev.stop, 0, cu, o, hT, seg, n_max, hv, nbo);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 // Compute units of the current device (queried once per device).
 int cu_count() {
@@ -511,33 +756,20 @@ int cu_count() {
   return counts[dev];
 }
 
-template <bool kF32In>
-hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
-                        int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
-                        hipStream_t stream, KernelEvents ev) {
-  const int members = (hv / h) * kSlices;
-  const int groups = n_max * h;
-  const int rounds = (groups + kXcds - 1) / kXcds;
-  const dim3 grid(rounds * kXcds * members);
-  if (static_cast<int>(grid.x) <= cu_count())
-    hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepthSingle>), grid,
-                          dim3(kInterThreads<kF32In, kDepthSingle>), 0, stream, ev.start,
-                          ev.stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
-  else
-    hipExtLaunchKernelGGL((inter_kernel<kF32In, 1>), grid, dim3(kInterThreads<kF32In, 1>), 0, stream, ev.start,
-                          ev.stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt);
-  return hipGetLastError();
+int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv) {
+  const int64_t rounds = (static_cast<int64_t>(n_max) * h + kXcds - 1) / kXcds;
+  const int64_t g = rounds * kXcds * (hv / h) * kSlices;
+  return g > 0x3fffffff ? 0x3fffffff : static_cast<int>(g);
 }
-
-}  // namespace
 
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
                         int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,
-                        KernelEvents ev) {
-  return f32_in
-             ? launch_waves<true>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream, ev)
-             : launch_waves<false>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream, ev);
+                        KernelEvents ev, int segments, SegScratch seg) {
+  return f32_in ? launch_waves<true>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream,
+                                     ev, segments, seg)
+                : launch_waves<false>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT,
+                                      stream, ev, segments, seg);
 }
 
 }  // namespace gdn

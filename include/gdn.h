@@ -61,7 +61,15 @@ typedef struct {
   gdn_dtype qkv_dtype; /* dtype of q, k, v: GDN_BF16 or GDN_F32 */
   gdn_dtype o_dtype;   /* dtype of o: GDN_F32 (the only one supported) */
   float scale;         /* output scale; <= 0 selects 1 / sqrt(dk) */
+  int32_t segments;    /* stage-2 walk of each sequence: 1 = one piece; 2 = its two
+                          halves at once, then a fix-up (the recurrence is affine in
+                          the starting state); 0 = automatic: 2 when t_max >=
+                          GDN_SEGMENT_MIN_TOKENS and the one-piece stage-2 grid fills
+                          at most half of the current device's compute units */
 } gdn_config;
+
+/* Token capacity from which the automatic choice considers two segments. */
+#define GDN_SEGMENT_MIN_TOKENS 2048
 
 /* Largest valid gdn_config.t_max / n_max. */
 #define GDN_T_MAX_LIMIT (1 << 24)
@@ -96,10 +104,18 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
  *         scale * e^gamma [64] with token 16 R + c at 4 c + R, then
  *         e^{gamma_last}
  *   table int32 [nt_max, 2]: the chunk-index table
+ *   seg_sa, seg_z fp32 [n_max, hv, dv, dk]: with two segments, the state after
+ *         the first half, and the second half's end state from zero
+ *   seg_phi fp32 [n_max, hv, dk, dk]: the second half's homogeneous end state
+ *         (the product of its chunk transitions), key-major
+ *   seg_oh fp32 [t_max, hv, dv]: the second half's homogeneous output rows
  * Per-chunk blocks are indexed by slot floor(t0 / 64) + n for a chunk starting
- * at token t0 of sequence n (distinct per chunk, < nt_max). */
+ * at token t0 of sequence n (distinct per chunk, < nt_max). With automatic
+ * segments the size depends on the current device (its compute units). */
 typedef struct {
   size_t w16, q16, kimg, uimg, pimg, gimg, table;
+  size_t seg_sa, seg_z, seg_phi, seg_oh; /* two-segment scratch (equal to total when the
+                                            config resolves to one segment) */
   size_t total; /* bytes of workspace gdn_chunk_fwd needs */
 } gdn_workspace_layout_t;
 
@@ -150,7 +166,8 @@ gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *q, const void 
                                const int32_t *chunk_indices, void *workspace, size_t ws_bytes,
                                void *stream);
 
-/* Inter-chunk stage over [n_max, hv, dv / 16] (AMX page, section 5): chunks in
+/* Inter-chunk stage over [n_max, hv, dv / 16] (AMX page, section 5), or with
+ * two segments over twice that grid plus a fix-up (cfg->segments): chunks in
  * order with S on chip: v' = u - w S; o = scale (diag(e^gamma) q S +
  * tril(q k^T * Gamma) v'); S = e^{gamma_last} S + (diag(e^{gamma_last - gamma}) k)^T v',
  * Gamma[r, i] = exp(gamma_r - gamma_i) for i <= r (diagonal kept). Reads only

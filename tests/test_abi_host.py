@@ -75,11 +75,40 @@ def test_workspace_layout(lib, dtype, nk):
     assert lay["total"] == at == gdn.gdn_workspace_size(cfg)
 
 
+def test_workspace_layout_segments(lib):
+    """Two segments append the stage-2 scratch (three state arrays and the
+    homogeneous output rows); one segment appends nothing."""
+    T, N, H, Hv = 5000, 2, 2, 4
+    al = lambda x: (x + 255) // 256 * 256
+    one = gdn.gdn_workspace_layout(gdn.make_config(T, N, H, Hv, segments=1))
+    two = gdn.gdn_workspace_layout(gdn.make_config(T, N, H, Hv, segments=2))
+    for name in ("seg_sa", "seg_z", "seg_phi", "seg_oh"):
+        assert one[name] == one["total"]
+    state = al(N * Hv * 128 * 128 * 4)
+    assert two["seg_sa"] == one["total"]
+    assert two["seg_z"] == two["seg_sa"] + state
+    assert two["seg_phi"] == two["seg_z"] + state
+    assert two["seg_oh"] == two["seg_phi"] + state
+    assert two["total"] == two["seg_oh"] + al(T * Hv * 128 * 4)
+    # automatic: needs the token capacity and a stage-2 grid of at most half
+    # the device (one sequence, 16 value heads: 128 work-groups; without a
+    # device the library assumes 256 compute units, as on an MI355X)
+    lay = gdn.gdn_workspace_layout(gdn.make_config(32768, 1, 16, 16))
+    assert lay["seg_oh"] < lay["total"]
+    short = gdn.make_config(gdn.GDN_SEGMENT_MIN_TOKENS - 1, 1, 16, 16)
+    lay = gdn.gdn_workspace_layout(short)
+    assert lay["seg_oh"] == lay["total"]
+    wide = gdn.make_config(32768, 1, 16, 32)  # 256 work-groups: one segment
+    lay = gdn.gdn_workspace_layout(wide)
+    assert lay["seg_oh"] == lay["total"]
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("dk", 64, UNSUPPORTED), ("dv", 256, UNSUPPORTED), ("chunk", 32, UNSUPPORTED),
     ("hv", 24, UNSUPPORTED), ("o_dtype", gdn.GDN_BF16, UNSUPPORTED),
     ("t_max", -1, INVALID), ("n_max", 0, INVALID), ("h", 0, INVALID), ("qkv_dtype", 7, INVALID),
     ("scale", float("nan"), INVALID), ("t_max", (1 << 24) + 1, CAPACITY), ("n_max", 16385, CAPACITY),
+    ("segments", 3, INVALID), ("segments", -1, INVALID),
 ])
 def test_config_validation(lib, field, value, status):
     cfg = gdn.make_config(256, 2, 16, 32)
@@ -172,6 +201,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     m = re.search(r"#define GDN_FUSED_INDEX_MAX_SEQS (\d+)", text)
     assert m and int(m.group(1)) == gdn.GDN_FUSED_INDEX_MAX_SEQS
+    m = re.search(r"#define GDN_SEGMENT_MIN_TOKENS (\d+)", text)
+    assert m and int(m.group(1)) == gdn.GDN_SEGMENT_MIN_TOKENS
 
 
 def test_fused_front_entry_point_host_errors(lib):
