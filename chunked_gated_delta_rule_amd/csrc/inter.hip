@@ -195,7 +195,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   f16x8 w[kDepth][8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
   bf16x8 k[kDepth][kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
   f32x4 u[kDepth][4];       // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + c
-  f32x4 dec[kDepth][4];     // e^{gamma_last - gamma} of those rows
+  float dec[kDepth];        // e^{gamma_last - gamma} of token L.lane (spread by lane permutes)
   float el[kDepth];         // e^{gamma_last}
   auto load_w = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
@@ -215,11 +215,11 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   };
   auto load_u = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
+    if constexpr (X == 0) {
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      if constexpr (X == 0) u[B][R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, R * 1024));
-      dec[B][R] = __builtin_bit_cast(f32x4, ld16(r.g, 4 * L.g4, R * 64));
+      for (int R = 0; R < 4; ++R) u[B][R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, R * 1024));
     }
+    dec[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 4 * L.lane, 0, 0));
     el[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
   };
   auto load_all = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
@@ -280,7 +280,13 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     load_w(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // chunk c's states (fp16) and all partials are published
-    // S += K^T (e^{gamma_last - gamma} v')
+    // S += K^T (e^{gamma_last - gamma} v'): rows 16 R + 4 g + i of this lane
+    // take their factors from lanes 16 R + 4 g + i (ds_bpermute)
+    f32x4 dr[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dr[R][i] = __shfl(dec[B], 16 * R + L.g4 + i, 64);
     bf16x8 eh[kS][2], elo[kS][2];
 #pragma unroll
     for (int st = 0; st < kS; ++st) {
@@ -291,8 +297,8 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
             __builtin_bit_cast(f32x4, xb[64 * (kXchFrags * st + 4 + 4 * (1 - X) + R)]);
         v[R] = X == 0 ? pv[st][R] + other : other + pv[st][R];  // both waves: partial0 + partial1
       }
-      split8(v[0] * dec[B][0], v[1] * dec[B][1], eh[st][0], elo[st][0]);
-      split8(v[2] * dec[B][2], v[3] * dec[B][3], eh[st][1], elo[st][1]);
+      split8(v[0] * dr[0], v[1] * dr[1], eh[st][0], elo[st][0]);
+      split8(v[2] * dr[2], v[3] * dr[3], eh[st][1], elo[st][1]);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_u(Bc, rn);
