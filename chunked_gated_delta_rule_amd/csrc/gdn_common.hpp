@@ -150,13 +150,25 @@ __device__ __forceinline__ void split_pack4(const float (&x)[4], u32x2 &hi, u32x
 // e^{gamma_last} and zero padding [64].
 constexpr int kGateStride = 192;
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+// The value DPP control kCtrl moves into each lane of the rows in kRowMask (0
+// in the other rows, and where the source lane is outside the row).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_in(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                               kRowMask, 0xf, true));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: within each row of 16
+// lanes x[i] += x[i - 1], x[i - 2], x[i - 4], x[i - 8] (row_shr), then rows 1
+// and 3 add lane 15 of the row before (row_bcast:15) and rows 2 and 3 add
+// lane 31 (row_bcast:31). All on DPP: no LDS round trip.
+__device__ __forceinline__ float wave_inclusive_scan(float x, int /*lane*/) {
+  x += dpp_in<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_in<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_in<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_in<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_in<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+  x += dpp_in<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
