@@ -415,22 +415,32 @@ def test_forward_without_table_builds_it_in_the_workspace(n):
     assert eo <= O_TOL and es <= S_TOL
 
 
-def test_graph_capture_replay_with_varying_cu_seqlens():
-    """gdn_chunk_fwd captured once into a HIP graph at static sizes (t_max,
-    n_max) and static addresses, then replayed with different cu_seqlens
-    contents written into the same buffer (FLA issue 1155, "Core design":
-    static grids, the device-built table, a sentinel for unused slots). Every
-    replay is checked bit for bit against an eager call on the same inputs,
-    with eager work and synchronisation between the replays."""
+@pytest.mark.parametrize("entry,segments", [("chunk", 1), ("chunk", 2), ("recurrent", 0)])
+def test_graph_capture_replay_with_varying_cu_seqlens(entry, segments):
+    """gdn_chunk_fwd (one-piece and two-segment stage 2) or gdn_recurrent_fwd
+    captured once into a HIP graph at static sizes (t_max, n_max) and static
+    addresses, then replayed with different cu_seqlens contents written into
+    the same buffer (FLA issue 1155, "Core design": static grids, the
+    device-built table, a sentinel for unused slots). Every replay is checked
+    bit for bit against an eager call on the same inputs, with eager work and
+    synchronisation between the replays."""
     t_max, n_max, H, Hv = 600, 6, 2, 4
     rng = np.random.Generator(np.random.PCG64(81))
     batches = [[600], [1, 63, 64, 65, 200, 0], [100, 0, 0, 37], [300, 300]]
     base = workloads.make_custom([t_max], H, Hv, seed=82, t_max=t_max, n_max=n_max)
     d = device_inputs(base)
     h0 = torch.from_numpy(rng.standard_normal((n_max, Hv, 128, 128)) * 0.02).float().to(DEV)
-    cfg = config_of(base)
+    cfg = gdn.make_config(base.t_max, base.n_max, base.H, base.Hv, base.qkv_dtype,
+                          segments=segments)
     ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
     cu = torch.zeros(n_max + 1, dtype=torch.int32, device=DEV)
+
+    def call(o_, h_, ws_):
+        if entry == "recurrent":
+            gdn.gdn_recurrent_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, o_, h_)
+        else:
+            gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None, o_, h_,
+                              ws_)
     o = torch.zeros((t_max, Hv, 128), dtype=torch.float32, device=DEV)
     hT = torch.zeros((n_max, Hv, 128, 128), dtype=torch.float32, device=DEV)
 
@@ -445,14 +455,13 @@ def test_graph_capture_replay_with_varying_cu_seqlens():
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):  # warm-up on the capture stream, then capture
-        gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None, o, hT, ws)
+        call(o, hT, ws)
         stream.synchronize()
         with torch.cuda.graph(graph, stream=stream):
-            gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None, o, hT,
-                              ws)
+            call(o, hT, ws)
     torch.cuda.synchronize()
     for rep, lengths in enumerate(batches + batches[::-1]):
-        log(f"graph replay {rep}: lengths {lengths}")
+        log(f"graph replay {rep} ({entry}, segments={segments}): lengths {lengths}")
         cu.copy_(cu_of(lengths))
         o.fill_(float("nan"))
         hT.fill_(float("nan"))
@@ -465,7 +474,6 @@ def test_graph_capture_replay_with_varying_cu_seqlens():
         ws2 = torch.empty_like(ws)
         o_e = torch.full_like(o, float("nan"))
         s_e = torch.full_like(hT, float("nan"))
-        gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None, o_e, s_e,
-                          ws2)
+        call(o_e, s_e, ws2)
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e[:T]) and torch.equal(s_g, s_e)
