@@ -477,3 +477,33 @@ def test_graph_capture_replay_with_varying_cu_seqlens(entry, segments):
         call(o_e, s_e, ws2)
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e[:T]) and torch.equal(s_g, s_e)
+
+
+@pytest.mark.parametrize("H,Hv,dtype", [(2, 8, torch.bfloat16), (1, 8, torch.float32),
+                                        (4, 32, torch.bfloat16), (24, 24, torch.bfloat16)])
+def test_gqa_group_sizes_every_lane(H, Hv, dtype):
+    """Other key/value head ratios than the named workloads (groups of 4 and 8,
+    and many heads with a group of 1) through the chunked path (one and two
+    stage-2 segments) and the token-serial kernel, every lane against the
+    oracle."""
+    lengths = [130, 0, 64, 257]
+    wl = workloads.make_custom(lengths, H, Hv, seed=31 + H + Hv, dtype=dtype, h0_sigma=0.02,
+                               n_max=len(lengths) + 1, t_max=sum(lengths) + 3)
+    d = device_inputs(wl)
+    ref = oracle_lanes(wl, _all_lanes(wl))
+    for tag in ("one segment", "two segments", "token-serial"):
+        cfg = gdn.make_config(wl.t_max, wl.n_max, H, Hv, dtype,
+                              segments=2 if tag == "two segments" else 1)
+        o = torch.full((wl.t_max, Hv, 128), float("nan"), dtype=torch.float32, device=DEV)
+        hT = torch.full((wl.n_max, Hv, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+        if tag == "token-serial":
+            gdn.gdn_recurrent_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"],
+                                  o, hT)
+        else:
+            ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+            gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"],
+                              None, o, hT, ws)
+        torch.cuda.synchronize()
+        eo, es = lane_errors(wl, o, hT, ref)
+        log(f"  H={H} Hv={Hv} {dtype} {tag}: o err {eo:.3e}  S err {es:.3e}")
+        assert eo <= O_TOL and es <= S_TOL
