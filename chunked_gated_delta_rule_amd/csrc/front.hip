@@ -3,7 +3,7 @@
 //
 //  * Causal depthwise conv, tap d_conv-1 is the current token, zero history at
 //    each sequence start, no bias (llama.cpp PR 399, "How (exactness)").
-//  * SiLU y = x / (1 + e^-x) on every channel.
+//  * SiLU y = x / (1 + e^-x) on every channel (hardware exp2 and reciprocal).
 //  * Each q and k head (128 channels) is scaled by 1 / sqrt(sum y^2 + 1e-6)
 //    with the whole row kept in registers (AMX page, section 7).
 //
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      y[c] = acc[c] / (1.f + expf(-acc[c]));
+      y[c] = silu(acc[c]);
       ss = fmaf(y[c], y[c], ss);
     }
     // 16 consecutive lanes hold one head (heads start on 128-channel boundaries)

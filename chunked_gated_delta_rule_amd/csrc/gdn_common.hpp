@@ -113,6 +113,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// SiLU x / (1 + e^-x) as x * rcp(1 + 2^(-x log2 e)) on the hardware exp2 and
+// reciprocal (about one ulp each); the front kernel and the front fused into
+// stage 1 both use this, so they produce the same bits.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * kLog2e));
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 

@@ -187,8 +187,8 @@ __device__ __forceinline__ void to_terms(const Raw4x8<kF32In> &x, u32x4 (&hi)[4]
 // pre-conv bf16 channels (rows t0 + row0 - 3 .. t0 + row0 + 3 and the 8
 // channels' taps), with the same arithmetic, in the same order, as the
 // standalone front kernel: conv taps accumulated oldest first by fmaf, SiLU
-// x / (1 + e^-x), and for q and k the 16-lane sum of squares of the head and
-// x / sqrt(sum + 1e-6).
+// x / (1 + e^-x) by the shared silu(), and for q and k the 16-lane sum of
+// squares of the head and x / sqrt(sum + 1e-6).
 struct ConvRaw {
   u32x4 x[7];  // source rows t0 + row0 - 3 + i (zero before the sequence start)
   u32x4 w[4];  // conv weights of the 8 channels, [channel][tap], up to 4 taps
@@ -234,7 +234,7 @@ __device__ __forceinline__ void conv_terms(const ConvRaw &r, bool l2, int valid,
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < kTaps; ++j) acc = fmaf(x[rr + j + 4 - kTaps][c], wf[c * kTaps + j], acc);
-      y[c] = acc / (1.f + expf(-acc));
+      y[c] = silu(acc);
       ss = fmaf(y[c], y[c], ss);
     }
     if (l2) {
