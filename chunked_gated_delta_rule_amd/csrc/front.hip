@@ -74,8 +74,7 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
       ss = fmaf(y[c], y[c], ss);
     }
     // 16 consecutive lanes hold one head (heads start on 128-channel boundaries)
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    ss = sum16(ss);
     if (!active) continue;
     float *dst;
     if (c0 < h * kD) {

@@ -165,6 +165,19 @@ __device__ __forceinline__ float dpp_in(float v) {
                                                                kRowMask, 0xf, true));
 }
 
+// Sum over each aligned group of 16 lanes, left in every lane of the group:
+// pairs, quads (quad_perm), halves (row_half_mirror pairs lane i with 7 - i)
+// and rows (row_mirror pairs i with 15 - i). Addition commutes, so all 16
+// lanes hold the same bits. The front kernel and the fused front use it for
+// the per-head sum of squares.
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp_in<0xB1, 0xf>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_in<0x4E, 0xf>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_in<0x141, 0xf>(x);  // row_half_mirror
+  x += dpp_in<0x140, 0xf>(x);  // row_mirror
+  return x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: within each row of 16
 // lanes x[i] += x[i - 1], x[i - 2], x[i - 4], x[i - 8] (row_shr), then rows 1
 // and 3 add lane 15 of the row before (row_bcast:15) and rows 2 and 3 add

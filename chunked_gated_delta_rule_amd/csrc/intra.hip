@@ -238,8 +238,7 @@ __device__ __forceinline__ void conv_terms(const ConvRaw &r, bool l2, int valid,
       ss = fmaf(y[c], y[c], ss);
     }
     if (l2) {
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      ss = sum16(ss);
       const float inv = 1.f / sqrtf(ss + 1e-6f);
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[c] *= inv;
