@@ -1,0 +1,72 @@
+"""Seeded sweep of random problem shapes through the C ABI, every lane against
+the CPU oracle: key heads, GQA group size, sequence count and lengths (empty
+sequences, partial and exact chunks), input dtype, initial state or none,
+stage-2 segments, and the token-serial kernel on the same inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_rule_amd as gdn
+import workloads
+
+from gpu_helpers import O_TOL, S_TOL, device_inputs, lane_errors, log, oracle_lanes
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+N_CASES = 16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    gdn.load_library()  # raises if the HIP library is missing
+
+
+def _case(i):
+    rng = np.random.Generator(np.random.PCG64(1000 + i))
+    H = int(rng.choice([1, 2, 4]))
+    Hv = H * int(rng.choice([1, 2, 4]))
+    n = int(rng.integers(1, 7))
+    lengths = [int(x) for x in rng.integers(0, 400, size=n)]
+    if n > 1:
+        lengths[int(rng.integers(0, n))] = 64 * int(rng.integers(0, 5))  # exact chunks or empty
+    dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+    h0 = 0.02 if rng.random() < 0.6 else 0.0
+    segments = int(rng.choice([0, 1, 2]))
+    g_scale = float(rng.choice([1.0, 0.05]))
+    extra = int(rng.integers(0, 70))
+    return dict(H=H, Hv=Hv, lengths=lengths, dtype=dtype, h0=h0, segments=segments,
+                g_scale=g_scale, extra=extra, seed=2000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape_every_lane(i):
+    c = _case(i)
+    log(f"sweep {i}: {c}")
+    wl = workloads.make_custom(c["lengths"], c["H"], c["Hv"], seed=c["seed"], dtype=c["dtype"],
+                               t_max=sum(c["lengths"]) + c["extra"],
+                               n_max=len(c["lengths"]) + 1, h0_sigma=c["h0"],
+                               g_scale=c["g_scale"])
+    d = device_inputs(wl, DEV)
+    lanes = [(s, hv) for s in range(wl.n_max) for hv in range(wl.Hv)]
+    ref = oracle_lanes(wl, lanes)
+    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, c["dtype"], segments=c["segments"])
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    for path in ("chunked", "token-serial"):
+        o = torch.full((wl.t_max, wl.Hv, 128), float("nan"), dtype=torch.float32, device=DEV)
+        hT = torch.full((wl.n_max, wl.Hv, 128, 128), float("nan"), dtype=torch.float32,
+                        device=DEV)
+        if path == "chunked":
+            gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"],
+                              None, o, hT, ws)
+        else:
+            gdn.gdn_recurrent_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                  d["cu"], o, hT)
+        torch.cuda.synchronize()
+        eo, es = lane_errors(wl, o, hT, ref)
+        log(f"  {path}: o err {eo:.3e}  S err {es:.3e}")
+        assert eo <= O_TOL and es <= S_TOL
+        T = int(wl.cu_seqlens[-1])
+        assert torch.isnan(o[T:]).all()
