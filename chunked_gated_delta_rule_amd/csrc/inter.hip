@@ -12,7 +12,8 @@
 // The value columns of S are independent, so the state is blocked over Dv
 // (Alloy page, "How do you parallelize a recurrence for prefill?": the state
 // tile is blocked along the value dimension to fit on chip). One work-group of
-// four wave64s owns a 128 x 16 column slice of S for the whole sequence. Every
+// four wave64s owns a 128 x 16 column slice of S (one column tile), or a
+// 128 x 32 slice (two tiles), for the whole sequence. Every
 // product of the chunk step is arranged so that its operands come either from
 // MFMA accumulators directly or from fragments the intra stage stored in MFMA
 // order:
@@ -43,8 +44,15 @@
 // so the chain waves run ahead while the helpers finish the previous chunk.
 // Every operand fragment is one 1 KB block (16 bytes per lane) loaded straight
 // into registers; past the last chunk the buffer range is empty and loads
-// return zero. Fragments are prefetched two chunks ahead.
-// Between them the four waves load each operand once per chunk.
+// return zero. Between them the four waves load each operand once per chunk.
+//
+// Two launch shapes. When the grid of one-tile work-groups fits the device
+// (one per CU), fragments are prefetched two chunks ahead and a fifth wave
+// warms the L2. Larger grids use two column tiles per work-group: w, K^T, q16
+// and P are then loaded once for twice the columns (68 KB per chunk for 32
+// columns instead of 2 x 74 KB), every product is done once per tile in the
+// same order as for one tile (so the results are bitwise those of the one-tile
+// shape), and two work-groups stay resident per CU with one chunk of prefetch.
 //
 // Work-group numbering is XCD-aware: all work-groups of the value heads that
 // share a key head get the same blockIdx modulo 8, so they run on one XCD and
@@ -66,12 +74,16 @@ constexpr int kL2Lead = 2;       // chunks between the L2 warm-up and the operan
 
 // The L2 warm-up wave is a fifth wave of the work-group; fp32 input at depth 2
 // needs more than the 256 VGPRs a SIMD with two waves of it could give, and
-// runs without it.
-template <bool kF32In, int kDepth, int kS>
-constexpr bool kWarmWave = !(kF32In && kDepth == 2) && (kS == 1 || kDepth == 1);
+// runs without it. Work-groups of two column tiles (kNV = 2) run two per CU
+// with four waves each, within 256 VGPRs, and have no warm-up wave either.
+template <bool kF32In, int kDepth, int kS, int kNV>
+constexpr bool kWarmWave = kNV == 1 && !(kF32In && kDepth == 2) && (kS == 1 || kDepth == 1);
 constexpr int kDepthSeg = 1;  // prefetch depth of the two-state walk (keeps the warm-up wave)
-template <bool kF32In, int kDepth, int kS>
-constexpr int kInterThreads = kWarmWave<kF32In, kDepth, kS> ? 320 : 256;
+template <bool kF32In, int kDepth, int kS, int kNV>
+constexpr int kInterThreads = kWarmWave<kF32In, kDepth, kS, kNV> ? 320 : 256;
+// waves per SIMD the register allocation must leave room for
+template <int kNV>
+constexpr int kInterWavesPerSimd = kNV == 2 ? 2 : 1;
 
 __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
@@ -160,7 +172,7 @@ __device__ __forceinline__ void for_sets(F &&f) {
 }
 
 // What one work-group walks: chunks [c0, c1) of its sequence, carrying kS
-// states of its 16-column slice. State 0 takes u and starts from init0
+// states of its column slice. State 0 takes u and starts from init0
 // (value-major [dv][dk] states of this head, or zero when null); state 1,
 // when carried, takes no u and starts from the identity (the homogeneous
 // part of the recurrence). out[st]: where state st's output rows go; fin[st]:
@@ -173,9 +185,10 @@ struct Walk {
   float *fin[2];
 };
 
-template <bool kF32In, int kDepth, int X, int kS>
+template <bool kF32In, int kDepth, int X, int kS, int kNV>
 __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const StageBuffers &in,
-                                           u32x4 (*xch)[kXchFrags * kS][64]) {
+                                           u32x4 (*xch)[kXchFrags * kS * kNV][64]) {
+  static_assert(kS == 1 || kNV == 1, "the two-state walk covers one column tile");
   constexpr int kNKw = kF32In ? 16 : 8;  // K^T fragments this wave uses per chunk
   const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;  // 1 KB fragment blocks
   const int slice = L.v0 / 16;
@@ -188,13 +201,13 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     r.k = make_rsrc(in.kimg + ((int64_t)L.h * L.nt + slot) * (kF32In ? 32 : 16) * 512,
                     ok ? (kF32In ? 32 : 16) * 1024 : 0);
     r.u = make_rsrc(in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 256,
-                    ok && X == 0 ? 4096 : 0);
+                    ok && X == 0 ? 4096 * kNV : 0);
     r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     return r;
   };
   f16x8 w[kDepth][8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
   bf16x8 k[kDepth][kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
-  f32x4 u[kDepth][4];       // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + c
+  f32x4 u[kDepth][kNV][4];  // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + 16 ct + c
   float dec[kDepth];        // e^{gamma_last - gamma} of token L.lane (spread by lane permutes)
   float el[kDepth];         // e^{gamma_last}
   auto load_w = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
@@ -217,7 +230,10 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     constexpr int B = decltype(Bc)::value;
     if constexpr (X == 0) {
 #pragma unroll
-      for (int R = 0; R < 4; ++R) u[B][R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, R * 1024));
+      for (int ct = 0; ct < kNV; ++ct)
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+          u[B][ct][R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, (4 * ct + R) * 1024));
     }
     dec[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 4 * L.lane, 0, 0));
     el[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
@@ -232,18 +248,21 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // state rows: S[st][tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + c]
-  f32x4 S[kS][4];
+  // state rows: S[st][ct][tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + 16 ct + c]
+  f32x4 S[kS][kNV][4];
   const int64_t sbase = (((int64_t)L.s * L.Hv + L.hv) * kD + L.v0 + L.c16) * kD + 64 * X + L.g4;
 #pragma unroll
-  for (int tl = 0; tl < 4; ++tl)
-    S[0][tl] = W.init0 ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + 16 * tl) : zero4();
+  for (int ct = 0; ct < kNV; ++ct)
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl)
+      S[0][ct][tl] = W.init0 ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + 16 * ct * kD + 16 * tl)
+                             : zero4();
   if constexpr (kS == 2) {
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S[1][tl][i] = 64 * X + 16 * tl + L.g4 + i == L.v0 + L.c16 ? 1.f : 0.f;
+        S[1][0][tl][i] = 64 * X + 16 * tl + L.g4 + i == L.v0 + L.c16 ? 1.f : 0.f;
   }
 
   // One chunk step on set B, which is refilled with chunk c + kDepth. A step
@@ -254,28 +273,30 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     const Rsrc rn = rsrc_of(c + kDepth);
     const float e_last = c < W.c1 ? el[B] : 1.f;
     u32x4 *xb = &xch[c & 1][0][L.lane];
-    f32x4 pv[kS][4];
+    f32x4 pv[kS][kNV][4];
 #pragma unroll
-    for (int st = 0; st < kS; ++st) {
-      f16x8 s16[2];
+    for (int st = 0; st < kS; ++st)
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl) {
-        s16[pl] = to_f16x8(S[st][2 * pl], S[st][2 * pl + 1]);
-        xb[64 * (kXchFrags * st + 2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
+      for (int ct = 0; ct < kNV; ++ct) {
+        u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
+        f16x8 s16[2];
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+          s16[pl] = to_f16x8(S[st][ct][2 * pl], S[st][ct][2 * pl + 1]);
+          xs[64 * (2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
+        }
+        // partial v' over this wave's key rows (wave 0 starts state 0 from u)
+#pragma unroll
+        for (int R = 0; R < 4; ++R) pv[st][ct][R] = X == 0 && st == 0 ? u[B][ct][R] : zero4();
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+          for (int R = 0; R < 4; ++R) pv[st][ct][R] = mfma(w[B][2 * R + pl], s16[pl], pv[st][ct][R]);
+#pragma unroll
+        for (int R = 0; R < 4; ++R) xs[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[st][ct][R]);
+#pragma unroll
+        for (int tl = 0; tl < 4; ++tl) S[st][ct][tl] = S[st][ct][tl] * e_last;
       }
-      // partial v' over this wave's key rows (wave 0 starts state 0 from u)
-#pragma unroll
-      for (int R = 0; R < 4; ++R) pv[st][R] = X == 0 && st == 0 ? u[B][R] : zero4();
-#pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-        for (int R = 0; R < 4; ++R) pv[st][R] = mfma(w[B][2 * R + pl], s16[pl], pv[st][R]);
-#pragma unroll
-      for (int R = 0; R < 4; ++R)
-        xb[64 * (kXchFrags * st + 4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[st][R]);
-#pragma unroll
-      for (int tl = 0; tl < 4; ++tl) S[st][tl] = S[st][tl] * e_last;
-    }
     __builtin_amdgcn_sched_barrier(0);
     load_w(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
@@ -287,36 +308,43 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     for (int R = 0; R < 4; ++R)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dr[R][i] = __shfl(dec[B], 16 * R + L.g4 + i, 64);
-    bf16x8 eh[kS][2], elo[kS][2];
+    bf16x8 eh[kS][kNV][2], elo[kS][kNV][2];
 #pragma unroll
-    for (int st = 0; st < kS; ++st) {
-      f32x4 v[4];
+    for (int st = 0; st < kS; ++st)
 #pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        const f32x4 other =
-            __builtin_bit_cast(f32x4, xb[64 * (kXchFrags * st + 4 + 4 * (1 - X) + R)]);
-        v[R] = X == 0 ? pv[st][R] + other : other + pv[st][R];  // both waves: partial0 + partial1
+      for (int ct = 0; ct < kNV; ++ct) {
+        const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
+        f32x4 v[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          const f32x4 other = __builtin_bit_cast(f32x4, xs[64 * (4 + 4 * (1 - X) + R)]);
+          // both waves: partial0 + partial1
+          v[R] = X == 0 ? pv[st][ct][R] + other : other + pv[st][ct][R];
+        }
+        split8(v[0] * dr[0], v[1] * dr[1], eh[st][ct][0], elo[st][ct][0]);
+        split8(v[2] * dr[2], v[3] * dr[3], eh[st][ct][1], elo[st][ct][1]);
       }
-      split8(v[0] * dr[0], v[1] * dr[1], eh[st][0], elo[st][0]);
-      split8(v[2] * dr[2], v[3] * dr[3], eh[st][1], elo[st][1]);
-    }
     __builtin_amdgcn_sched_barrier(0);
     load_u(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < kS; ++st)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl) S[st][tl] = mfma(k[B][2 * tl + q], eh[st][q], S[st][tl]);
-#pragma unroll
-        for (int tl = 0; tl < 4; ++tl) S[st][tl] = mfma(k[B][2 * tl + q], elo[st][q], S[st][tl]);
-        if constexpr (kF32In) {
+        for (int ct = 0; ct < kNV; ++ct) {
 #pragma unroll
           for (int tl = 0; tl < 4; ++tl)
-            S[st][tl] = mfma(k[B][8 + 2 * tl + q], eh[st][q], S[st][tl]);
+            S[st][ct][tl] = mfma(k[B][2 * tl + q], eh[st][ct][q], S[st][ct][tl]);
+#pragma unroll
+          for (int tl = 0; tl < 4; ++tl)
+            S[st][ct][tl] = mfma(k[B][2 * tl + q], elo[st][ct][q], S[st][ct][tl]);
+          if constexpr (kF32In) {
+#pragma unroll
+            for (int tl = 0; tl < 4; ++tl)
+              S[st][ct][tl] = mfma(k[B][8 + 2 * tl + q], eh[st][ct][q], S[st][ct][tl]);
+          }
         }
-      }
     __builtin_amdgcn_sched_barrier(0);
     load_k(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
@@ -331,7 +359,10 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     });
   if (W.fin[0]) {
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + 16 * tl) = S[0][tl];
+    for (int ct = 0; ct < kNV; ++ct)
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl)
+        *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + 16 * ct * kD + 16 * tl) = S[0][ct][tl];
   }
   if constexpr (kS == 2) {
     if (W.fin[1]) {
@@ -340,16 +371,16 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
 #pragma unroll
       for (int tl = 0; tl < 4; ++tl)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[(64 * X + 16 * tl + L.g4 + i) * kD] = S[1][tl][i];
+        for (int i = 0; i < 4; ++i) f[(64 * X + 16 * tl + L.g4 + i) * kD] = S[1][0][tl][i];
     }
   }
 }
 
 // Helper wave Y: output token tiles R = 2 Y, 2 Y + 1 (rows 32 Y .. 32 Y + 31)
 // of every carried state.
-template <int kDepth, int Y, int kS>
+template <int kDepth, int Y, int kS, int kNV>
 __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const StageBuffers &in,
-                                            u32x4 (*xch)[kXchFrags * kS][64]) {
+                                            u32x4 (*xch)[kXchFrags * kS * kNV][64]) {
   constexpr int kNQ = Y + 1;                 // token blocks of v' this wave contracts over
   constexpr int kPairs = Y == 0 ? 2 : 4;     // P pairs of its tiles
   constexpr int kPair0 = Y == 0 ? 0 : 2;
@@ -394,28 +425,32 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     const Rsrc rn = rsrc_of(c + kDepth);
     lds_barrier();  // chunk c handed over
     const u32x4 *xb = &xch[c & 1][0][L.lane];
-    f32x4 ya[kS][2];
-    bf16x8 dh[kS][kNQ], dl[kS][kNQ];
+    f32x4 ya[kS][kNV][2];
+    bf16x8 dh[kS][kNV][kNQ], dl[kS][kNV][kNQ];
 #pragma unroll
-    for (int st = 0; st < kS; ++st) {
-      f16x8 s16[4];
+    for (int st = 0; st < kS; ++st)
 #pragma unroll
-      for (int p = 0; p < 4; ++p) s16[p] = __builtin_bit_cast(f16x8, xb[64 * (kXchFrags * st + p)]);
-      f32x4 v[2 * kNQ];
+      for (int ct = 0; ct < kNV; ++ct) {
+        const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
+        f16x8 s16[4];
 #pragma unroll
-      for (int R = 0; R < 2 * kNQ; ++R)
-        v[R] = __builtin_bit_cast(f32x4, xb[64 * (kXchFrags * st + 4 + R)]) +
-               __builtin_bit_cast(f32x4, xb[64 * (kXchFrags * st + 8 + R)]);
-      // y^T = S^T q^T for this wave's two token tiles
-      ya[st][0] = zero4();
-      ya[st][1] = zero4();
+        for (int p = 0; p < 4; ++p) s16[p] = __builtin_bit_cast(f16x8, xs[64 * p]);
+        f32x4 v[2 * kNQ];
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
+        for (int R = 0; R < 2 * kNQ; ++R)
+          v[R] = __builtin_bit_cast(f32x4, xs[64 * (4 + R)]) +
+                 __builtin_bit_cast(f32x4, xs[64 * (8 + R)]);
+        // y^T = S^T q^T for this wave's two token tiles
+        ya[st][ct][0] = zero4();
+        ya[st][ct][1] = zero4();
 #pragma unroll
-        for (int Rl = 0; Rl < 2; ++Rl) ya[st][Rl] = mfma(s16[p], qf[B][4 * Rl + p], ya[st][Rl]);
+        for (int p = 0; p < 4; ++p)
 #pragma unroll
-      for (int q = 0; q < kNQ; ++q) split8(v[2 * q], v[2 * q + 1], dh[st][q], dl[st][q]);
-    }
+          for (int Rl = 0; Rl < 2; ++Rl)
+            ya[st][ct][Rl] = mfma(s16[p], qf[B][4 * Rl + p], ya[st][ct][Rl]);
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) split8(v[2 * q], v[2 * q + 1], dh[st][ct][q], dl[st][ct][q]);
+      }
     __builtin_amdgcn_sched_barrier(0);
     load_q(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
@@ -423,28 +458,31 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     const int t0 = L.bos + kC * c;
     const uint32_t lc = c < W.c1 ? static_cast<uint32_t>(min(kC, L.eos - t0)) : 0u;  // past the end: no store
 #pragma unroll
-    for (int st = 0; st < kS; ++st) {
-      f32x4 pa[2] = {zero4(), zero4()};
+    for (int st = 0; st < kS; ++st)
 #pragma unroll
-      for (int Rl = 0; Rl < 2; ++Rl) {
-        const int R = 2 * Y + Rl;
+      for (int ct = 0; ct < kNV; ++ct) {
+        f32x4 pa[2] = {zero4(), zero4()};
 #pragma unroll
-        for (int q = 0; q <= (R >> 1); ++q) {
-          const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
-          pa[Rl] = mfma(dh[st][q], pf[B][2 * n], pa[Rl]);
-          pa[Rl] = mfma(dl[st][q], pf[B][2 * n], pa[Rl]);
-          pa[Rl] = mfma(dh[st][q], pf[B][2 * n + 1], pa[Rl]);
+        for (int Rl = 0; Rl < 2; ++Rl) {
+          const int R = 2 * Y + Rl;
+#pragma unroll
+          for (int q = 0; q <= (R >> 1); ++q) {
+            const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
+            pa[Rl] = mfma(dh[st][ct][q], pf[B][2 * n], pa[Rl]);
+            pa[Rl] = mfma(dl[st][ct][q], pf[B][2 * n], pa[Rl]);
+            pa[Rl] = mfma(dh[st][ct][q], pf[B][2 * n + 1], pa[Rl]);
+          }
         }
-      }
-      // a state without an output destination gets an empty store range
-      const uintptr_t ob = reinterpret_cast<uintptr_t>(W.out[st]) +
-                           (((uintptr_t)t0 * L.Hv + L.hv) * kD + L.v0) * 4;
-      const i32x4 ro = rsrc_words(reinterpret_cast<const void *>(ob),
-                                  W.out[st] ? lc * L.Hv * kD * 4 : 0u);
+        // a state without an output destination gets an empty store range
+        const uintptr_t ob = reinterpret_cast<uintptr_t>(W.out[st]) +
+                             (((uintptr_t)t0 * L.Hv + L.hv) * kD + L.v0 + 16 * ct) * 4;
+        const i32x4 ro = rsrc_words(reinterpret_cast<const void *>(ob),
+                                    W.out[st] ? lc * L.Hv * kD * 4 : 0u);
 #pragma unroll
-      for (int Rl = 0; Rl < 2; ++Rl)
-        store16(ro, vo_o, (2 * Y + Rl) * row_o, pa[Rl] + __uint_as_float(exs[B][Rl]) * ya[st][Rl]);
-    }
+        for (int Rl = 0; Rl < 2; ++Rl)
+          store16(ro, vo_o, (2 * Y + Rl) * row_o,
+                  pa[Rl] + __uint_as_float(exs[B][Rl]) * ya[st][ct][Rl]);
+      }
     __builtin_amdgcn_sched_barrier(0);
     load_p(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
@@ -521,17 +559,19 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
 // second half walks the rest carrying the zero-start state (outputs into o,
 // final slice to seg.z) and the identity-start homogeneous state (outputs to
 // seg.oh, final slice to seg.phi); segfix_kernel then combines them.
-template <bool kF32In, int kDepth, int kS>
-__global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS>)) void inter_kernel(
+template <bool kF32In, int kDepth, int kS, int kNV>
+__global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
+                             kInterWavesPerSimd<kNV>) void inter_kernel(
     StageBuffers in, const float *__restrict__ h0, const int32_t *__restrict__ cu,
     float *__restrict__ o, float *__restrict__ hT, int n_max, int H, int Hv, int t_max, int nt,
     SegScratch seg) {
-  __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags * kS][64];
+  __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags * kS * kNV][64];
   __shared__ uint32_t l2_sink[64];
 
   // ---- XCD-aware work-group -> (sequence, value head, slice) --------------
+  constexpr int kWgSlices = kSlices / kNV;  // work-groups per value head
   const int HG = Hv / H;
-  const int members = HG * kSlices;
+  const int members = HG * kWgSlices;
   const int one_walk = (n_max * H + kXcds - 1) / kXcds * kXcds * members;
   const int role = kS == 2 && static_cast<int>(blockIdx.x) >= one_walk ? 1 : 0;
   const int b = static_cast<int>(blockIdx.x) - role * one_walk;
@@ -543,8 +583,8 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS>)) void inter_ker
   Lane L;
   L.s = group / H;
   L.h = group % H;
-  L.hv = L.h * HG + member / kSlices;
-  L.v0 = 16 * (member % kSlices);
+  L.hv = L.h * HG + member / kWgSlices;
+  L.v0 = 16 * kNV * (member % kWgSlices);
   L.lane = threadIdx.x & 63;
   L.c16 = L.lane & 15;
   L.g4 = 4 * (L.lane >> 4);
@@ -565,14 +605,14 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS>)) void inter_ker
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0)
-    chain_wave<kF32In, kDepth, 0, kS>(L, W, in, xch);
+    chain_wave<kF32In, kDepth, 0, kS, kNV>(L, W, in, xch);
   else if (wave == 1)
-    chain_wave<kF32In, kDepth, 1, kS>(L, W, in, xch);
+    chain_wave<kF32In, kDepth, 1, kS, kNV>(L, W, in, xch);
   else if (wave == 2)
-    helper_wave<kDepth, 0, kS>(L, W, in, xch);
+    helper_wave<kDepth, 0, kS, kNV>(L, W, in, xch);
   else if (wave == 3)
-    helper_wave<kDepth, 1, kS>(L, W, in, xch);
-  else if constexpr (kWarmWave<kF32In, kDepth, kS>)
+    helper_wave<kDepth, 1, kS, kNV>(L, W, in, xch);
+  else if constexpr (kWarmWave<kF32In, kDepth, kS, kNV>)
     l2_warm_wave<kF32In, kDepth>(L, W, in, member, members, l2_sink);
 }
 
@@ -699,40 +739,38 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
   }
 }
 
-template <bool kF32In, int kDepth, int kS>
-void launch_walk(dim3 grid, const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
+template <bool kF32In, int kDepth, int kS, int kNV = 1>
+void launch_walk(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
                  int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
                  const SegScratch &seg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS>), grid,
-                        dim3(kInterThreads<kF32In, kDepth, kS>), 0, stream, start, stop, 0, in, h0,
-                        cu, o, hT, n_max, h, hv, t_max, nt, seg);
+  const int members = (hv / h) * (kSlices / kNV);
+  const int rounds = (n_max * h + kXcds - 1) / kXcds;
+  const dim3 grid(kS * rounds * kXcds * members);
+  hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS, kNV>), grid,
+                        dim3(kInterThreads<kF32In, kDepth, kS, kNV>), 0, stream, start, stop, 0, in,
+                        h0, cu, o, hT, n_max, h, hv, t_max, nt, seg);
 }
 
 template <bool kF32In>
 hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
                         int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
                         hipStream_t stream, KernelEvents ev, int segments, const SegScratch &seg) {
-  const int members = (hv / h) * kSlices;
-  const int groups = n_max * h;
-  const int rounds = (groups + kXcds - 1) / kXcds;
-  const int one_walk = rounds * kXcds * members;
+  const int one_walk = inter_one_walk_grid(n_max, h, hv);
   if (segments != 2) {
-    const dim3 grid(one_walk);
     if (one_walk <= cu_count())
-      launch_walk<kF32In, kDepthSingle, 1>(grid, in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
-                                           stream, ev.start, ev.stop);
+      launch_walk<kF32In, kDepthSingle, 1>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                                           ev.start, ev.stop);
     else
-      launch_walk<kF32In, 1, 1>(grid, in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
-                                ev.start, ev.stop);
+      launch_walk<kF32In, 1, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                                   ev.start, ev.stop);
     return hipGetLastError();
   }
-  const dim3 grid(2 * one_walk);
   if (2 * one_walk <= cu_count())
-    launch_walk<kF32In, kDepthSeg, 2>(grid, in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
-                                      stream, ev.start, nullptr);
+    launch_walk<kF32In, kDepthSeg, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                                      ev.start, nullptr);
   else
-    launch_walk<kF32In, 1, 2>(grid, in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
-                              ev.start, nullptr);
+    launch_walk<kF32In, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream, ev.start,
+                              nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // work-groups of 128 output rows over the at most floor(ceil(t_max / 64) / 2)
