@@ -50,15 +50,16 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 def algorithmic_work(wl, nt, qkv_bytes, fused_front=False):
     """Bytes and flops each stage must move / perform (counted once; partial
-    chunks counted as whole 64-token chunks for flops). With the front fused
-    into stage 1, that stage reads the pre-conv bf16 q|k|v channels instead of
-    k and v."""
+    chunks counted as whole 64-token chunks for flops). w crosses between the
+    stages in 2 bytes and u in 3 (24-bit floats) per value. With the front
+    fused into stage 1, that stage reads the pre-conv bf16 q|k|v channels
+    instead of k and v."""
     T, H, Hv, D = wl.n_tokens, wl.H, wl.Hv, 128
     HG = Hv // H
     n_state = len(wl.cu_seqlens) - 1
     stage1_in = (2 * H + Hv) * D * 2 if fused_front else H * D * qkv_bytes + Hv * D * qkv_bytes
-    stage1_bytes = T * (stage1_in + Hv * 4 + Hv * 4 + Hv * D * 2 + Hv * D * 4)
-    stage2_bytes = T * (2 * H * D * qkv_bytes + Hv * D * 2 + Hv * D * 4 + Hv * 4 + Hv * D * 4)
+    stage1_bytes = T * (stage1_in + Hv * 4 + Hv * 4 + Hv * D * 2 + Hv * D * 3)
+    stage2_bytes = T * (2 * H * D * qkv_bytes + Hv * D * 2 + Hv * D * 3 + Hv * 4 + Hv * D * 4)
     stage2_bytes += n_state * Hv * D * D * 4 * (2 if wl.h0 is not None else 1)
     stage1_flop = nt * H * (2 * 64 * 64 * D + HG * (2 * 2 * 64 * 64 * D + SOLVE_FLOP))
     stage2_flop = nt * Hv * (3 * 2 * 64 * D * D + 2 * 2 * 64 * 64 * D)

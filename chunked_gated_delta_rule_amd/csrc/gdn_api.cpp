@@ -65,7 +65,7 @@ gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   l.w16 = take(hv * nt * 16 * 1024);
   l.q16 = take(h * nt * 16 * 1024);
   l.kimg = take(h * nt * nk * 1024);
-  l.uimg = take(hv * nt * kD * kChunk * 4);
+  l.uimg = take(hv * nt * kD * kChunk * 3);  // 24-bit u
   l.pimg = take(hv * nt * 12 * 1024);
   l.gimg = take(hv * nt * 192 * 4);
   l.table = take(nt * 2 * 4);
@@ -98,7 +98,7 @@ gdn::StageBuffers stage_buffers(const gdn_workspace_layout_t &l, const void *wor
   b.w16 = reinterpret_cast<_Float16 *>(ws + l.w16);
   b.q16 = reinterpret_cast<_Float16 *>(ws + l.q16);
   b.kimg = reinterpret_cast<__bf16 *>(ws + l.kimg);
-  b.uimg = reinterpret_cast<float *>(ws + l.uimg);
+  b.uimg = reinterpret_cast<uint32_t *>(ws + l.uimg);
   b.pimg = reinterpret_cast<__bf16 *>(ws + l.pimg);
   b.gimg = reinterpret_cast<float *>(ws + l.gimg);
   return b;

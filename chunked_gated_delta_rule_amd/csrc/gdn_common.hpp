@@ -107,6 +107,45 @@ __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 24-bit float: the upper three bytes of an fp32 (sign, 8-bit exponent, 15
+// mantissa bits). It keeps fp32's range with a relative step of 2^-16. Four
+// of them pack into three words: value i takes bytes 3 i .. 3 i + 2 (little
+// endian).
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+// the same three words at 4-byte alignment (a lane's 12 bytes in a block)
+typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+
+// x rounded to nearest with 16 significant bits by Veltkamp's split (Dekker,
+// "A floating-point technique for extending the available precision", 1971):
+// with c = (2^8 + 1) x, hi = c - (c - x) has its low 8 mantissa bits zero, so
+// bytes 1..3 of its word are the 24-bit value. A NaN stays a NaN; an infinity
+// or |x| above about 1.3e36 (where c overflows) becomes a NaN. Each step is
+// written as an FMA with an exact product (by 1, or plus 0), i.e. one rounding
+// each: left as a product and differences, contraction would fuse c - x into
+// fma(x, 257, -x) and return x unrounded.
+__device__ __forceinline__ uint32_t round_f24_word(float x) {
+  const float c = __builtin_fmaf(x, 257.f, 0.f);   // RN(257 x)
+  const float d = __builtin_fmaf(-1.f, x, c);      // RN(c - x)
+  return __float_as_uint(__builtin_fmaf(-1.f, d, c));  // RN(c - d)
+}
+
+__device__ __forceinline__ u32x3 pack_f24x4(const f32x4 &v) {
+  const uint32_t a = round_f24_word(v[0]), b = round_f24_word(v[1]), c = round_f24_word(v[2]),
+                 d = round_f24_word(v[3]);
+  // v_perm_b32 (hi, lo, sel): result byte i is byte sel_i of lo (sel_i < 4) or
+  // byte sel_i - 4 of hi (4..7)
+  return u32x3{__builtin_amdgcn_perm(b, a, 0x05030201u), __builtin_amdgcn_perm(c, b, 0x06050302u),
+               __builtin_amdgcn_perm(d, c, 0x07060503u)};
+}
+
+__device__ __forceinline__ f32x4 unpack_f24x4(const u32x3 &w) {
+  // selector 0x0c gives a zero byte (the dropped low byte)
+  return f32x4{__uint_as_float(__builtin_amdgcn_perm(0u, w[0], 0x0201000cu)),
+               __uint_as_float(__builtin_amdgcn_perm(w[1], w[0], 0x0504030cu)),
+               __uint_as_float(__builtin_amdgcn_perm(w[2], w[1], 0x0403020cu)),
+               __uint_as_float(__builtin_amdgcn_perm(0u, w[2], 0x0302010cu))};
+}
+
 // 2^x on the hardware transcendental unit (v_exp_f32); used with exponents
 // that are differences of log2-scaled cumulative gates, always <= 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -18,7 +18,7 @@ struct StageBuffers {
   _Float16 *w16;  // [hv, nt_max, 16 fragments, 64 lanes, 8]
   _Float16 *q16;  // [h, nt_max, 16 fragments, 64 lanes, 8]
   __bf16 *kimg;   // [h, nt_max, 16 or 32 fragments, 64 lanes, 8]
-  float *uimg;    // [hv, nt_max, 8, 4, 64 lanes, 4]
+  uint32_t *uimg; // [hv, nt_max, 8, 4, 64 lanes, 3 words]: four 24-bit floats per lane
   __bf16 *pimg;   // [hv, nt_max, 6 pairs, 2 terms, 64 lanes, 8]
   float *gimg;    // [hv, nt_max, 192]
 };

@@ -200,14 +200,14 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     r.w = make_rsrc(in.w16 + ((int64_t)L.hv * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
     r.k = make_rsrc(in.kimg + ((int64_t)L.h * L.nt + slot) * (kF32In ? 32 : 16) * 512,
                     ok ? (kF32In ? 32 : 16) * 1024 : 0);
-    r.u = make_rsrc(in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 256,
-                    ok && X == 0 ? 4096 * kNV : 0);
+    r.u = make_rsrc(in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 64 * 3,
+                    ok && X == 0 ? 3072 * kNV : 0);
     r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     return r;
   };
   f16x8 w[kDepth][8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
   bf16x8 k[kDepth][kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
-  f32x4 u[kDepth][kNV][4];  // wave 0: u tile R, rows 16 R + 4 g + i, value column v0 + 16 ct + c
+  u32x3 u[kDepth][kNV][4];  // wave 0: u tile R (24-bit), rows 16 R + 4 g + i, column v0 + 16 ct + c
   float dec[kDepth];        // e^{gamma_last - gamma} of token L.lane (spread by lane permutes)
   float el[kDepth];         // e^{gamma_last}
   auto load_w = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
@@ -233,7 +233,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
       for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
         for (int R = 0; R < 4; ++R)
-          u[B][ct][R] = __builtin_bit_cast(f32x4, ld16(r.u, vo_f, (4 * ct + R) * 1024));
+          u[B][ct][R] = __builtin_amdgcn_raw_buffer_load_b96(r.u, L.lane * 12, (4 * ct + R) * 768, 0);
     }
     dec[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 4 * L.lane, 0, 0));
     el[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
@@ -287,7 +287,8 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
         }
         // partial v' over this wave's key rows (wave 0 starts state 0 from u)
 #pragma unroll
-        for (int R = 0; R < 4; ++R) pv[st][ct][R] = X == 0 && st == 0 ? u[B][ct][R] : zero4();
+        for (int R = 0; R < 4; ++R)
+          pv[st][ct][R] = X == 0 && st == 0 ? unpack_f24x4(u[B][ct][R]) : zero4();
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
@@ -513,7 +514,7 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
   constexpr int kHLines = kKLines + 128;             // K^T image, q16
   constexpr int kWLines = 128, kPLines = 96;
   constexpr int kVLines = kWLines + kPLines + kGateStride * 4 / 128;  // w16, P, gates
-  constexpr int kULines = 32;
+  constexpr int kULines = 24;  // one slice of u: 4 tiles x 768 bytes
   static_assert(kGateStride * 4 % 128 == 0, "gate block is whole lines");
   if (W.c1 <= W.c0) return;
   const int slice = L.v0 / 16;
@@ -527,7 +528,7 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
     const uint64_t pb = reinterpret_cast<uint64_t>(in.pimg + ((int64_t)L.hv * L.nt + slot) * 12 * 512);
     const uint64_t gb = reinterpret_cast<uint64_t>(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride);
     const uint64_t ub = reinterpret_cast<uint64_t>(
-        in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 256);
+        in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 64 * 3);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = L.lane + 64 * i;

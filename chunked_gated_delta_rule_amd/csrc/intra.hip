@@ -13,11 +13,12 @@
 // Everything the inter-chunk stage needs that does not depend on the state is
 // produced here, where the work is parallel over chunks, and written in the
 // exact MFMA fragment order the inter stage reads (each fragment one 1 KB
-// block, 16 bytes per lane), so that stage only streams blocks:
+// block, 16 bytes per lane; u's 768 bytes), so that stage only streams blocks:
 //   w16   fp16 per (hv, chunk)  -w fragments (A operand of (-w) S)
 //   q16   fp16 per (h, chunk)   q rounded to fp16 (B operand of S^T q^T)
 //   kimg  bf16 per (h, chunk)   K^T fragments for the state update (hi[, lo])
-//   uimg  fp32 per (hv, chunk)  u fragments, one 1 KB block per 16 x 16 tile
+//   uimg  f24 per (hv, chunk)   u fragments rounded to 24-bit floats (fp32's top
+//                               three bytes), one 768-byte block per 16 x 16 tile
 //   pimg  bf16 per (hv, chunk)  P = scale * tril(q k^T * Gamma) as hi + lo
 //   gimg  fp32 per (hv, chunk)  e^{gamma_last - gamma}, scale e^gamma (ordered
 //                               [c][R] for r = 16 R + c), e^{gamma_last}
@@ -706,9 +707,10 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
 #pragma unroll
       for (int db2 = 0; db2 < 2; ++db2) {
         const int db = 2 * wv + db2;
-        // u: lane holds u[r = 16 rb + 4 (lane >> 4) + i][d = 16 db + (lane & 15)]
-        float *dst = out.uimg + (((((int64_t)hv * nt + slot) * 8 + db) * 4 + rb) * 64 + lane) * 4;
-        *reinterpret_cast<f32x4 *>(dst) = uacc[db2];
+        // u: lane holds u[r = 16 rb + 4 (lane >> 4) + i][d = 16 db + (lane & 15)],
+        // stored as four 24-bit floats in 12 bytes
+        uint32_t *dst = out.uimg + (((((int64_t)hv * nt + slot) * 8 + db) * 4 + rb) * 64 + lane) * 3;
+        *reinterpret_cast<u32x3_a4 *>(dst) = pack_f24x4(uacc[db2]);
       }
     }
     __syncthreads();  // A / T, V and the gate copies are rewritten next

@@ -97,8 +97,10 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
  *         32 p + 4 g + j (j < 4) and 32 p + 16 + 4 g + j - 4 (j >= 4)
  *   q16   fp16 [h, nt_max, 16, 64, 8]: q rounded to fp16, same fragments
  *   kimg  bf16 [h, nt_max, 16 (32 for fp32 input), 64, 8]: K^T fragments
- *   uimg  fp32 [hv, nt_max, dv / 16, 4, 64, 4]: u (AMX page, section 4), one
- *         16 x 16 tile per 1 KB block
+ *   uimg  u32 [hv, nt_max, dv / 16, 4, 64, 3]: u (AMX page, section 4), one
+ *         16 x 16 tile per 768-byte block; each lane's four values are 24-bit
+ *         floats (the upper three bytes of fp32, rounded to nearest even),
+ *         value i in bytes 3 i .. 3 i + 2 of the lane's 12
  *   pimg  bf16 [hv, nt_max, 6, 2, 64, 8]: scale * tril(q k^T * Gamma) as hi + lo
  *   gimg  fp32 [hv, nt_max, 192]: per token e^{gamma_last - gamma} [64],
  *         scale * e^gamma [64] with token 16 R + c at 4 c + R, then

@@ -168,7 +168,7 @@ def workspace_views(cfg, ws):
         w16=view("w16", torch.float16, (cfg.hv, nt, 16, 64, 8)),
         q16=view("q16", torch.float16, (cfg.h, nt, 16, 64, 8)),
         kimg=view("kimg", torch.bfloat16, (cfg.h, nt, nk, 64, 8)),
-        uimg=view("uimg", torch.float32, (cfg.hv, nt, 8, 4, 64, 4)),
+        uimg=view("uimg", torch.int32, (cfg.hv, nt, 8, 4, 64, 3)),
         pimg=view("pimg", torch.bfloat16, (cfg.hv, nt, 6, 2, 64, 8)),
         gimg=view("gimg", torch.float32, (cfg.hv, nt, 192)),
         nt=nt, nk=nk)
@@ -205,9 +205,18 @@ def decode_kimg(kimg_slot):
     return out
 
 
+def unpack_f24(words):
+    """[..., 3] little-endian words holding four 24-bit floats (the upper three
+    bytes of fp32) -> [..., 4] float64."""
+    b = np.ascontiguousarray(words).view(np.uint8).reshape(words.shape[:-1] + (4, 3))
+    full = np.zeros(words.shape[:-1] + (4, 4), np.uint8)
+    full[..., 1:] = b  # the dropped low byte is zero
+    return full.view("<f4").reshape(words.shape[:-1] + (4,)).astype(np.float64)
+
+
 def decode_uimg(uimg_slot):
-    """[8, 4, 64, 4] -> u [64 tokens, 128]."""
-    x = uimg_slot.numpy().astype(np.float64)
+    """[8, 4, 64, 3] packed 24-bit words -> u [64 tokens, 128]."""
+    x = unpack_f24(uimg_slot.numpy())
     U = np.zeros((64, 128))
     for sl in range(8):
         for R in range(4):

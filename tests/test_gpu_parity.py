@@ -507,3 +507,58 @@ def test_gqa_group_sizes_every_lane(H, Hv, dtype):
         eo, es = lane_errors(wl, o, hT, ref)
         log(f"  H={H} Hv={Hv} {dtype} {tag}: o err {eo:.3e}  S err {es:.3e}")
         assert eo <= O_TOL and es <= S_TOL
+
+
+def _nan_bits(dtype):
+    """A NaN whose mantissa bits are all ones (the pattern of memory filled with
+    0xff), as one element of the given dtype."""
+    if dtype == torch.bfloat16:
+        return torch.tensor([-1], dtype=torch.int16).view(torch.bfloat16)
+    return torch.tensor([-1], dtype=torch.int32).view(torch.float32)
+
+
+@pytest.mark.parametrize("shape", ["one tile", "two tiles", "token-serial"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_nan_in_v_reaches_exactly_its_column(shape, dtype):
+    """A NaN in v[t0, hv, j] must reach column j of that head's outputs for the
+    rest of its sequence and column j of its final state, and nothing else:
+    value columns are independent and sequences do not mix. The token-serial
+    kernel starts exactly at t0. The chunked form may also reach earlier tokens
+    of t0's chunk, because its block products multiply the NaN by zeros of the
+    triangular T and P (0 * NaN is NaN; which blocks are skipped is the
+    kernel's choice), never tokens of earlier chunks. In the chunked form the
+    NaN crosses from stage 1 to stage 2 inside u's 24-bit storage, which keeps
+    it a NaN."""
+    n = 9 if shape == "two tiles" else 3
+    lengths = [150, 170, 200, 33, 129, 64, 90, 1, 120][:n]
+    wl = workloads.make_custom(lengths, 4, 8, seed=71, dtype=dtype, h0_sigma=0.02)
+    d = device_inputs(wl)
+    s, hv, j, off = 1, 5, 37, 100  # sequence 1, value head 5, column 37, its 101st token
+    bos, e = int(wl.cu_seqlens[s]), int(wl.cu_seqlens[s + 1])
+    t0 = bos + off
+    first = t0 if shape == "token-serial" else bos + 64 * (off // 64)
+    d["v"][t0, hv, j] = _nan_bits(dtype).to(d["v"].device)[0]
+    cfg = config_of(wl)
+    o = torch.full((wl.t_max, wl.Hv, 128), 0.0, dtype=torch.float32, device=DEV)
+    hT = torch.zeros((wl.n_max, wl.Hv, 128, 128), dtype=torch.float32, device=DEV)
+    if shape == "token-serial":
+        gdn.gdn_recurrent_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], o,
+                              hT)
+    else:
+        ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+        gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], None,
+                          o, hT, ws)
+    torch.cuda.synchronize()
+    must = torch.zeros_like(o, dtype=torch.bool)
+    must[t0:e, hv, j] = True
+    may = torch.zeros_like(o, dtype=torch.bool)
+    may[first:e, hv, j] = True
+    nan_o = torch.isnan(o)
+    assert bool((must & ~nan_o).any()) is False, "a NaN did not reach a later output"
+    assert torch.isfinite(o[~may]).all(), "a NaN or inf reached another column, head or chunk"
+    want_h = torch.zeros_like(hT, dtype=torch.bool)
+    want_h[s, hv, j, :] = True  # value-major: row j of the state
+    assert torch.equal(torch.isnan(hT), want_h)
+    assert torch.isfinite(hT[~want_h]).all()
+    if shape == "token-serial":
+        assert torch.equal(nan_o, must)
