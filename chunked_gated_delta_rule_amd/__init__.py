@@ -57,7 +57,7 @@ class gdn_config(ctypes.Structure):
 
 class gdn_workspace_layout_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("w16", "q16", "kimg", "uimg", "pimg", "gimg", "table", "seg_sa", "seg_z",
+                ("w16", "q16", "kimg", "uimg", "pimg", "gimg", "table", "order", "seg_sa", "seg_z",
                  "seg_phi", "seg_oh", "total")]
 
 

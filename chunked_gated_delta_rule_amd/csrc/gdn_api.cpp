@@ -55,6 +55,12 @@ int segments_of(const gdn_config *cfg) {
              : 1;
 }
 
+// Whether stage 1 ranks the sequences for stage 2 (longest walks first): with
+// more than one sequence, up to one per stage-1 thread.
+bool ranks_sequences(const gdn_config *cfg) {
+  return cfg->n_max >= 2 && cfg->n_max <= GDN_FUSED_INDEX_MAX_SEQS;
+}
+
 gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   const size_t t = static_cast<size_t>(cfg->t_max), nt = static_cast<size_t>(nt_max_of(cfg));
   const size_t h = static_cast<size_t>(cfg->h), hv = static_cast<size_t>(cfg->hv);
@@ -69,6 +75,7 @@ gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   l.pimg = take(hv * nt * 12 * 1024);
   l.gimg = take(hv * nt * 192 * 4);
   l.table = take(nt * 2 * 4);
+  l.order = take(ranks_sequences(cfg) ? static_cast<size_t>(cfg->n_max) * 4 : 0);
   if (segments_of(cfg) == 2) {
     const size_t state = static_cast<size_t>(cfg->n_max) * hv * kD * kD * 4;
     l.seg_sa = take(state);
@@ -92,7 +99,8 @@ gdn::SegScratch seg_scratch(const gdn_workspace_layout_t &l, const void *workspa
   return g;
 }
 
-gdn::StageBuffers stage_buffers(const gdn_workspace_layout_t &l, const void *workspace) {
+gdn::StageBuffers stage_buffers(const gdn_config *cfg, const gdn_workspace_layout_t &l,
+                                const void *workspace) {
   char *ws = static_cast<char *>(const_cast<void *>(workspace));
   gdn::StageBuffers b;
   b.w16 = reinterpret_cast<_Float16 *>(ws + l.w16);
@@ -101,6 +109,7 @@ gdn::StageBuffers stage_buffers(const gdn_workspace_layout_t &l, const void *wor
   b.uimg = reinterpret_cast<uint32_t *>(ws + l.uimg);
   b.pimg = reinterpret_cast<__bf16 *>(ws + l.pimg);
   b.gimg = reinterpret_cast<float *>(ws + l.gimg);
+  b.order = ranks_sequences(cfg) ? reinterpret_cast<int32_t *>(ws + l.order) : nullptr;
   return b;
 }
 
@@ -165,7 +174,7 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
     if (e != hipSuccess) return GDN_ERR_HIP;
     chunk_indices = ws_table;
   }
-  const gdn::StageBuffers b = stage_buffers(l, workspace);
+  const gdn::StageBuffers b = stage_buffers(cfg, l, workspace);
   if (cfg->t_max > 0) {
     // without a table, stage 1 locates its chunks and fills ws_table itself
     const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
@@ -264,7 +273,7 @@ gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *q, const void 
   if (cfg->t_max == 0) return GDN_OK;
   return from_hip(gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
                                     chunk_indices, nullptr, cfg->n_max, nt_max_of(cfg), cfg->h,
-                                    cfg->hv, cfg->t_max, scale_of(cfg), stage_buffers(l, workspace),
+                                    cfg->hv, cfg->t_max, scale_of(cfg), stage_buffers(cfg, l, workspace),
                                     as_stream(stream)));
 }
 
@@ -280,7 +289,7 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
   const gdn_workspace_layout_t l = layout_of(cfg);
   const gdn_status ws = check_workspace(l, workspace, ws_bytes);
   if (ws != GDN_OK) return ws;
-  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, stage_buffers(l, workspace), h0,
+  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, stage_buffers(cfg, l, workspace), h0,
                                     cu_seqlens, cfg->n_max, cfg->h, cfg->hv, cfg->t_max,
                                     nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream),
                                     {}, segments_of(cfg), seg_scratch(l, workspace)));

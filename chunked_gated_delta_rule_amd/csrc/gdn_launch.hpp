@@ -21,6 +21,11 @@ struct StageBuffers {
   uint32_t *uimg; // [hv, nt_max, 8, 4, 64 lanes, 3 words]: four 24-bit floats per lane
   __bf16 *pimg;   // [hv, nt_max, 6 pairs, 2 terms, 64 lanes, 8]
   float *gimg;    // [hv, nt_max, 192]
+  // [n_max]: sequence indices ranked by chunk count, longest first (ties by
+  // index), written by stage 1 and read by stage 2 to start the longest walks
+  // first; null when the batch is not ranked (one sequence, or more than
+  // kThreads sequences)
+  int32_t *order;
 };
 
 // Pre-conv input of the fused front: stage 1 computes q, k, v itself from the

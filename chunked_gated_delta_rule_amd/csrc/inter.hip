@@ -578,11 +578,13 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   const int b = static_cast<int>(blockIdx.x) - role * one_walk;
   const int xcd = b % kXcds;
   const int wslot = b / kXcds;
-  const int group = (wslot / members) * kXcds + xcd;  // (sequence, key head)
+  const int group = (wslot / members) * kXcds + xcd;  // (rank of the sequence, key head)
   const int member = wslot % members;
   if (group >= n_max * H) return;
   Lane L;
-  L.s = group / H;
+  // the sequence of that rank when stage 1 ranked them (longest walks first)
+  L.s = in.order ? in.order[group / H] : group / H;
+  if (L.s < 0 || L.s >= n_max) return;
   L.h = group % H;
   L.hv = L.h * HG + member / kWgSlices;
   L.v0 = 16 * kNV * (member % kWgSlices);

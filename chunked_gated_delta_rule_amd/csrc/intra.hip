@@ -286,6 +286,33 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Stage 2 walks every chunk of a sequence in order, so with many sequences
+// the longest walks should start first (the longest-processing-time rule:
+// the work-groups of the last sequences to start then finish with the rest
+// instead of after them). One work-group of stage 1 ranks the n <= kThreads
+// sequences by chunk count, longest first and ties by index, so the ranks
+// are a permutation: thread t compares its sequence with all n (their chunk
+// counts staged in LDS, read as broadcasts) and writes order[rank] = t.
+// The caller's LDS must be free (no other wave still reading it).
+__device__ __forceinline__ void write_walk_order(const int32_t *__restrict__ cu, int n,
+                                                 int32_t *__restrict__ order, int *ncs) {
+  const int t = threadIdx.x;
+  int mine = 0;
+  if (t < n) {
+    mine = (cu[t + 1] - cu[t] + kC - 1) / kC;
+    ncs[t] = mine;
+  }
+  __syncthreads();
+  if (t < n) {
+    int rank = 0;
+    for (int s = 0; s < n; ++s) {
+      const int x = ncs[s];
+      rank += (x > mine || (x == mine && s < t)) ? 1 : 0;
+    }
+    order[rank] = t;
+  }
+}
+
 // kTaps: 0 reads q, k, v; 1..4 computes them from the pre-conv channels with a
 // kTaps-tap conv (the fused front).
 template <bool kF32In, int kTaps>
@@ -322,7 +349,13 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     ent.y = __builtin_amdgcn_readfirstlane(ent.y);
     if (blockIdx.y == 0 && tid == 0) reinterpret_cast<int2 *>(table_out)[blockIdx.x] = ent;
   }
-  if (ent.x < 0) return;  // sentinel slot
+  // the work-group of slot 0, key head 0 ranks the sequences for stage 2,
+  // after its own chunk (its LDS is then free) or here if it has none
+  const bool ranks = out.order && blockIdx.x == 0 && blockIdx.y == 0;
+  if (ent.x < 0) {  // sentinel slot
+    if (ranks) write_walk_order(cu, n_max, out.order, reinterpret_cast<int *>(smem));
+    return;
+  }
   const int h = blockIdx.y;
   const int HG = Hv / H;
   const int bos = cu[ent.x];
@@ -715,6 +748,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     }
     __syncthreads();  // A / T, V and the gate copies are rewritten next
   }
+  if (ranks) write_walk_order(cu, n_max, out.order, reinterpret_cast<int *>(smem));
 }
 
 }  // namespace
@@ -725,6 +759,7 @@ hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v
                         int32_t t_max, float scale,
                         const StageBuffers &out, hipStream_t stream, KernelEvents ev, ConvIn conv) {
   if (!table && (n_max > kFusedIndexMaxSeqs || !table_out)) return hipErrorInvalidValue;
+  if (out.order && n_max > kThreads) return hipErrorInvalidValue;  // one thread per sequence
   if (conv.qkv && (!f32_in || !conv.conv_w || conv.d_conv < 1 || conv.d_conv > 4))
     return hipErrorInvalidValue;
   if (nt_max <= 0) return hipSuccess;

@@ -106,6 +106,10 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
  *         scale * e^gamma [64] with token 16 R + c at 4 c + R, then
  *         e^{gamma_last}
  *   table int32 [nt_max, 2]: the chunk-index table
+ *   order int32 [n_max] when 2 <= n_max <= GDN_FUSED_INDEX_MAX_SEQS, else
+ *         empty: the sequence indices ranked by chunk count, longest first
+ *         (ties by index). Stage 1 writes it and stage 2 starts the walks in
+ *         that order, so that the longest sequences do not start last.
  *   seg_sa, seg_z fp32 [n_max, hv, dv, dk]: with two segments, the state after
  *         the first half, and the second half's end state from zero
  *   seg_phi fp32 [n_max, hv, dk, dk]: the second half's homogeneous end state
@@ -115,7 +119,7 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
  * at token t0 of sequence n (distinct per chunk, < nt_max). With automatic
  * segments the size depends on the current device (its compute units). */
 typedef struct {
-  size_t w16, q16, kimg, uimg, pimg, gimg, table;
+  size_t w16, q16, kimg, uimg, pimg, gimg, table, order;
   size_t seg_sa, seg_z, seg_phi, seg_oh; /* two-segment scratch (equal to total when the
                                             config resolves to one segment) */
   size_t total; /* bytes of workspace gdn_chunk_fwd needs */

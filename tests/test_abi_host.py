@@ -66,13 +66,24 @@ def test_workspace_layout(lib, dtype, nk):
     nt = index_table.nt_max(T, N)
     sizes = [("w16", Hv * nt * 16 * 1024), ("q16", H * nt * 16 * 1024), ("kimg", H * nt * nk * 1024),
              ("uimg", Hv * nt * 64 * 128 * 3), ("pimg", Hv * nt * 12 * 1024),
-             ("gimg", Hv * nt * 192 * 4), ("table", nt * 8)]
+             ("gimg", Hv * nt * 192 * 4), ("table", nt * 8), ("order", N * 4)]
     lay = gdn.gdn_workspace_layout(cfg)
     at = 0
     for name, size in sizes:
         assert lay[name] == at, name
         at += al(size)
     assert lay["total"] == at == gdn.gdn_workspace_size(cfg)
+
+
+@pytest.mark.parametrize("n,ranked", [(1, False), (2, True), (256, True), (257, False)])
+def test_workspace_order_region(lib, n, ranked):
+    """The sequence ranking for stage 2 takes n_max int32 when stage 1 ranks
+    the batch (2 to GDN_FUSED_INDEX_MAX_SEQS sequences), else nothing."""
+    assert gdn.GDN_FUSED_INDEX_MAX_SEQS == 256
+    lay = gdn.gdn_workspace_layout(gdn.make_config(1000, n, 2, 4))
+    al = lambda x: (x + 255) // 256 * 256
+    assert lay["order"] == lay["table"] + al(index_table.nt_max(1000, n) * 8)
+    assert lay["total"] - lay["order"] == (al(n * 4) if ranked else 0)
 
 
 def test_workspace_layout_segments(lib):

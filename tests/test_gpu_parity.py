@@ -562,3 +562,41 @@ def test_nan_in_v_reaches_exactly_its_column(shape, dtype):
     assert torch.isfinite(hT[~want_h]).all()
     if shape == "token-serial":
         assert torch.equal(nan_o, must)
+
+
+@pytest.mark.parametrize("lengths,with_table", [
+    ([300, 64, 0, 64, 1000, 65, 1, 128], False),
+    ([300, 64, 0, 64, 1000, 65, 1, 128], True),
+    ([0, 0, 0], False),
+])
+def test_walk_order_table_bit_exact(lengths, with_table):
+    """Stage 1 ranks the sequences by chunk count, longest first and ties by
+    index (capacity slots past the batch count as empty sequences), for stage
+    2 to start the longest walks first. Integer work: compared exactly, with
+    the workspace filled with 0xff beforehand; also when every sequence is
+    empty (no stage-1 work-group has a chunk) and with a caller table."""
+    n_max = len(lengths) + 2
+    wl = workloads.make_custom(lengths, 2, 4, seed=81, t_max=sum(lengths) + 10, n_max=n_max)
+    d = device_inputs(wl)
+    cfg = config_of(wl)
+    lay = gdn.gdn_workspace_layout(cfg)
+    ws = torch.full((gdn.gdn_workspace_size(cfg),), 255, dtype=torch.uint8, device=DEV)
+    table = None
+    if with_table:
+        table = torch.empty((gdn.gdn_nt_max(wl.t_max, n_max), 2), dtype=torch.int32, device=DEV)
+        gdn.gdn_build_chunk_indices(cfg, d["cu"], table)
+    o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=DEV)
+    hT = torch.empty((n_max, wl.Hv, 128, 128), dtype=torch.float32, device=DEV)
+    gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], table, o,
+                      hT, ws)
+    torch.cuda.synchronize()
+    got = ws[lay["order"]:lay["order"] + 4 * n_max].cpu().view(torch.int32).numpy()
+    nc = (np.diff(wl.cu_seqlens) + 63) // 64
+    want = sorted(range(n_max), key=lambda s: (-int(nc[s]), s))
+    assert got.tolist() == want
+    # and the forward itself is right (every sequence walked exactly once)
+    T = int(wl.cu_seqlens[-1])
+    if T:
+        ref = oracle_lanes(wl, [(s, hv) for s in range(len(lengths)) for hv in range(wl.Hv)])
+        eo, es = lane_errors(wl, o, hT, ref)
+        assert eo <= O_TOL and es <= S_TOL
