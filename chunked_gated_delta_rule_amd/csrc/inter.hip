@@ -112,12 +112,20 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
 // for the prefetched fragments stay counts of loads (loads return in order)
 // instead of draining every load at each store. Out-of-range lanes are
 // dropped like any buffer store; the leading s_nop covers a scalar operand
-// written just before.
+// written just before. kStream marks the store non-temporal (streamed through
+// the caches), for output that nothing reads back soon.
+template <bool kStream>
 __device__ __forceinline__ void store16(const i32x4 &r, uint32_t voff, uint32_t soff, const f32x4 &v) {
-  asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %0, %1, %2, %3 offen"
-               :
-               : "v"(v), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
+  if constexpr (kStream)
+    asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %0, %1, %2, %3 offen nt"
+                 :
+                 : "v"(v), "v"(voff), "s"(r), "s"(soff)
+                 : "memory");
+  else
+    asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %0, %1, %2, %3 offen"
+                 :
+                 : "v"(v), "v"(voff), "s"(r), "s"(soff)
+                 : "memory");
 }
 
 // Work-group barrier for the LDS hand-off: waits for this wave's LDS
@@ -383,6 +391,12 @@ template <int kDepth, int Y, int kS, int kNV>
 __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const StageBuffers &in,
                                             u32x4 (*xch)[kXchFrags * kS * kNV][64]) {
   constexpr int kNQ = Y + 1;                 // token blocks of v' this wave contracts over
+  // o rows stream past the caches in the one-tile, one-piece walk: at one
+  // work-group per CU, o's dirty lines otherwise displace what the next
+  // kernels read (T = 4096: the following stage 1 ran 53 -> 44 us). Not in the
+  // two-segment walk (the fix-up reads o back) nor with two tiles (each store
+  // covers half a 128-byte line, which then went out as partial writes).
+  constexpr bool kStreamO = kS == 1 && kNV == 1;
   constexpr int kPairs = Y == 0 ? 2 : 4;     // P pairs of its tiles
   constexpr int kPair0 = Y == 0 ? 0 : 2;
   const uint32_t vo_o = static_cast<uint32_t>(L.c16 * L.Hv * kD + L.g4) * 4;     // o rows
@@ -481,8 +495,8 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
                                     W.out[st] ? lc * L.Hv * kD * 4 : 0u);
 #pragma unroll
         for (int Rl = 0; Rl < 2; ++Rl)
-          store16(ro, vo_o, (2 * Y + Rl) * row_o,
-                  pa[Rl] + __uint_as_float(exs[B][Rl]) * ya[st][ct][Rl]);
+          store16<kStreamO>(ro, vo_o, (2 * Y + Rl) * row_o,
+                            pa[Rl] + __uint_as_float(exs[B][Rl]) * ya[st][ct][Rl]);
       }
     __builtin_amdgcn_sched_barrier(0);
     load_p(Bc, rn);
