@@ -72,7 +72,7 @@ gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   l.q16 = take(h * nt * 16 * 1024);
   l.kimg = take(h * nt * nk * 1024);
   l.uimg = take(hv * nt * kD * kChunk * 3);  // 24-bit u
-  l.pimg = take(hv * nt * 12 * 1024);
+  l.pimg = take(hv * nt * gdn::kPBytes);
   l.gimg = take(hv * nt * 192 * 4);
   l.table = take(nt * 2 * 4);
   l.order = take(ranks_sequences(cfg) ? static_cast<size_t>(cfg->n_max) * 4 : 0);

@@ -12,6 +12,21 @@
 
 namespace gdn {
 
+// P = scale * tril(q k^T * Gamma) per (value head, chunk): six pairs of
+// 16 x 16 tiles of P^T, each a 16 x 32 MFMA fragment in a hi and a lo bf16
+// term. In pairs 0 and 3 (output tiles 0 and 2, against the token block that
+// starts with their own tile) the second half of every lane's contraction
+// slots lies above the diagonal and is always zero, so those pairs keep 8
+// bytes per lane and term (512-byte terms) and the others 16 (1 KB terms).
+constexpr int kPBytes = 10 * 1024;
+__host__ __device__ constexpr bool p_half(int pi) { return pi == 0 || pi == 3; }
+__host__ __device__ constexpr int p_term_bytes(int pi) { return p_half(pi) ? 512 : 1024; }
+// byte offset of pair pi's hi term in its block (the lo term follows it)
+__host__ __device__ constexpr int p_offset(int pi) {
+  return pi == 0 ? 0 : pi == 1 ? 1024 : pi == 2 ? 3072 : pi == 3 ? 5120 : pi == 4 ? 6144 : 8192;
+}
+static_assert(p_offset(5) + 2 * p_term_bytes(5) == kPBytes, "P block layout");
+
 // Intermediates written by the intra stage and read by the inter stage (all
 // device memory inside the caller's workspace; layouts in intra.hip).
 struct StageBuffers {

@@ -408,7 +408,8 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     const bool ok = c < W.c1;
     Rsrc r;
     r.q = make_rsrc(in.q16 + ((int64_t)L.h * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
-    r.p = make_rsrc(in.pimg + ((int64_t)L.hv * L.nt + slot) * 12 * 512, ok ? 12 * 1024 : 0);
+    r.p = make_rsrc(reinterpret_cast<const char *>(in.pimg) + ((int64_t)L.hv * L.nt + slot) * kPBytes,
+                    ok ? kPBytes : 0);
     r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     return r;
   };
@@ -424,8 +425,15 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
   auto load_p = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
 #pragma unroll
-    for (int i = 0; i < 2 * kPairs; ++i)
-      pf[B][i] = __builtin_bit_cast(bf16x8, ld16(r.p, vo_f, (2 * kPair0 + i) * 1024));
+    for (int i = 0; i < 2 * kPairs; ++i) {
+      const int pi = kPair0 + (i >> 1), off = p_offset(pi) + (i & 1) * p_term_bytes(pi);
+      if (p_half(pi)) {  // the upper half of the lane's slots is zero
+        const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(r.p, L.lane * 8, off, 0);
+        pf[B][i] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], 0u, 0u});
+      } else {
+        pf[B][i] = __builtin_bit_cast(bf16x8, ld16(r.p, vo_f, off));
+      }
+    }
     exs[B] = __builtin_amdgcn_raw_buffer_load_b64(r.g, 16 * L.c16 + 8 * Y, 256, 0);
   };
   auto load_all = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
@@ -526,7 +534,7 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
                                              int member, int members, uint32_t *sink) {
   constexpr int kKLines = (kF32In ? 32 : 16) * 8;
   constexpr int kHLines = kKLines + 128;             // K^T image, q16
-  constexpr int kWLines = 128, kPLines = 96;
+  constexpr int kWLines = 128, kPLines = kPBytes / 128;
   constexpr int kVLines = kWLines + kPLines + kGateStride * 4 / 128;  // w16, P, gates
   constexpr int kULines = 24;  // one slice of u: 4 tiles x 768 bytes
   static_assert(kGateStride * 4 % 128 == 0, "gate block is whole lines");
@@ -539,7 +547,8 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
     const uint64_t kb = reinterpret_cast<uint64_t>(in.kimg + ((int64_t)L.h * L.nt + slot) * kKLines * 64);
     const uint64_t qb = reinterpret_cast<uint64_t>(in.q16 + ((int64_t)L.h * L.nt + slot) * 16 * 512);
     const uint64_t wb = reinterpret_cast<uint64_t>(in.w16 + ((int64_t)L.hv * L.nt + slot) * 16 * 512);
-    const uint64_t pb = reinterpret_cast<uint64_t>(in.pimg + ((int64_t)L.hv * L.nt + slot) * 12 * 512);
+    const uint64_t pb = reinterpret_cast<uint64_t>(reinterpret_cast<const char *>(in.pimg) +
+                                                   ((int64_t)L.hv * L.nt + slot) * kPBytes);
     const uint64_t gb = reinterpret_cast<uint64_t>(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride);
     const uint64_t ub = reinterpret_cast<uint64_t>(
         in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 64 * 3);

@@ -19,7 +19,8 @@
 //   kimg  bf16 per (h, chunk)   K^T fragments for the state update (hi[, lo])
 //   uimg  f24 per (hv, chunk)   u fragments rounded to 24-bit floats (fp32's top
 //                               three bytes), one 768-byte block per 16 x 16 tile
-//   pimg  bf16 per (hv, chunk)  P = scale * tril(q k^T * Gamma) as hi + lo
+//   pimg  bf16 per (hv, chunk)  P = scale * tril(q k^T * Gamma) as hi + lo, the
+//                               two half-zero pairs packed to 8 bytes per lane
 //   gimg  fp32 per (hv, chunk)  e^{gamma_last - gamma}, scale e^gamma (ordered
 //                               [c][R] for r = 16 R + c), e^{gamma_last}
 // P is the intra-chunk attention term of the output (AMX page, section 5); it
@@ -578,9 +579,15 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
         }
         u32x4 hi, lo;
         split8_words(x, hi, lo);
-        __bf16 *dst = out.pimg + ((((int64_t)hv * nt + slot) * 6 + pi) * 2 * 64 + lane) * 8;
-        *reinterpret_cast<u32x4 *>(dst) = hi;
-        *reinterpret_cast<u32x4 *>(dst + 64 * 8) = lo;
+        char *dst = reinterpret_cast<char *>(out.pimg) + ((int64_t)hv * nt + slot) * kPBytes +
+                    p_offset(pi);
+        if (p_half(pi)) {  // x[4..7] are above the diagonal: only the first 8 bytes
+          *reinterpret_cast<u32x2 *>(dst + lane * 8) = u32x2{hi[0], hi[1]};
+          *reinterpret_cast<u32x2 *>(dst + 512 + lane * 8) = u32x2{lo[0], lo[1]};
+        } else {
+          *reinterpret_cast<u32x4 *>(dst + lane * 16) = hi;
+          *reinterpret_cast<u32x4 *>(dst + 1024 + lane * 16) = lo;
+        }
       }
     }
 
