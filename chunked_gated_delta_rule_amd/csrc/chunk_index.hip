@@ -18,6 +18,7 @@ constexpr int kMaxSeqs = 16384;  // (n_max + 1) offsets live in LDS
 
 __global__ __launch_bounds__(kIndexThreads) void chunk_index_kernel(const int32_t *__restrict__ cu,
                                                                     int32_t n_max, int32_t nt_max,
+                                                                    int32_t t_max,
                                                                     int32_t *__restrict__ table) {
   __shared__ int32_t co[kMaxSeqs + 1];
   __shared__ int32_t part[kIndexThreads];
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(kIndexThreads) void chunk_index_kernel(const int32_
   const int s0 = min(tid * per, n_max);
   const int s1 = min(s0 + per, n_max);
   int local = 0;
-  for (int s = s0; s < s1; ++s) local += (cu[s + 1] - cu[s] + kC - 1) / kC;
+  for (int s = s0; s < s1; ++s) local += seq_chunks(cu, s, t_max);
   part[tid] = local;
   __syncthreads();
   // Hillis-Steele inclusive scan of the per-thread totals.
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(kIndexThreads) void chunk_index_kernel(const int32_
   int run = part[tid] - local;  // exclusive offset of this thread's segment
   for (int s = s0; s < s1; ++s) {
     co[s] = run;
-    run += (cu[s + 1] - cu[s] + kC - 1) / kC;
+    run += seq_chunks(cu, s, t_max);
   }
   if (tid == kIndexThreads - 1) co[n_max] = part[kIndexThreads - 1];
   __syncthreads();
@@ -62,10 +63,10 @@ __global__ __launch_bounds__(kIndexThreads) void chunk_index_kernel(const int32_
 }  // namespace
 
 hipError_t launch_chunk_index(const int32_t *cu_seqlens, int32_t n_max, int32_t nt_max,
-                              int32_t *table, hipStream_t stream, KernelEvents ev) {
+                              int32_t t_max, int32_t *table, hipStream_t stream, KernelEvents ev) {
   if (n_max > kMaxSeqs) return hipErrorInvalidValue;
   hipExtLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(kIndexThreads), 0, stream, ev.start,
-                        ev.stop, 0, cu_seqlens, n_max, nt_max, table);
+                        ev.stop, 0, cu_seqlens, n_max, nt_max, t_max, table);
   return hipGetLastError();
 }
 

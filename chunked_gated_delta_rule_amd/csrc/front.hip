@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
   const bool active = c0 < channels;  // inactive lanes still join the butterfly
   const int t_begin = blockIdx.y * kTokens;
-  const int t_total = cu[n_max];
+  const int t_total = cu_at(cu, n_max, t_max);
   if (t_begin >= t_total) return;
 
   float wt[8][kMaxTaps];
@@ -45,14 +45,14 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
   int lo = 0, hi = n_max;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t_begin) lo = mid; else hi = mid;
+    if (cu_at(cu, mid, t_max) <= t_begin) lo = mid; else hi = mid;
   }
   int s = lo;
   const bool is_qk = c0 < 2 * h * kD;
   const int t_end = min(t_begin + kTokens, t_total);
   for (int t = t_begin; t < t_end; ++t) {
-    while (cu[s + 1] <= t) ++s;
-    const int bos = cu[s];
+    while (s + 1 < n_max && cu_at(cu, s + 1, t_max) <= t) ++s;
+    const int bos = min(cu_at(cu, s, t_max), t);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (active) {
 #pragma unroll

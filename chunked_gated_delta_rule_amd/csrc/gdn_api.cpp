@@ -170,7 +170,8 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
   int32_t *ws_table = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + l.table);
   if (!chunk_indices && cfg->n_max > GDN_FUSED_INDEX_MAX_SEQS) {
     const hipError_t e =
-        gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), ws_table, s, ev[0]);
+        gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), cfg->t_max, ws_table, s,
+                                ev[0]);
     if (e != hipSuccess) return GDN_ERR_HIP;
     chunk_indices = ws_table;
   }
@@ -201,7 +202,8 @@ gdn_status recurrent_impl(const gdn_config *cfg, const void *q, const void *k, c
       (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return GDN_ERR_INVALID_ARG;
   return from_hip(gdn::launch_recurrent(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, h0,
-                                        cu_seqlens, cfg->n_max, cfg->h, cfg->hv, scale_of(cfg),
+                                        cu_seqlens, cfg->n_max, cfg->t_max, cfg->h, cfg->hv,
+                                        scale_of(cfg),
                                         static_cast<float *>(o), hT, as_stream(stream), ev));
 }
 
@@ -237,7 +239,8 @@ gdn_status gdn_build_chunk_indices(const gdn_config *cfg, const int32_t *cu_seql
   if (!cu_seqlens || !chunk_indices || !aligned16(chunk_indices) ||
       (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return GDN_ERR_INVALID_ARG;
-  return from_hip(gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), chunk_indices,
+  return from_hip(gdn::launch_chunk_index(cu_seqlens, cfg->n_max, nt_max_of(cfg), cfg->t_max,
+                                          chunk_indices,
                                           as_stream(stream)));
 }
 

@@ -241,6 +241,24 @@ __device__ __forceinline__ int wave_inclusive_scan_int(int x, int lane) {
   return x;
 }
 
+// Entry s of cu_seqlens as every kernel reads it: clamped to [0, t_max]. A
+// valid cu_seqlens (cu[0] = 0, non-decreasing, cu[n_max] <= t_max) is a
+// documented precondition and passes unchanged; with an invalid one the
+// results are unspecified, but every row a kernel touches stays inside the
+// caller's [t_max, ...] buffers.
+__device__ __forceinline__ int cu_at(const int32_t *__restrict__ cu, int s, int t_max) {
+  return min(max(cu[s], 0), t_max);
+}
+// End of sequence s given its (clamped) start: never before it.
+__device__ __forceinline__ int cu_end(const int32_t *__restrict__ cu, int s, int bos, int t_max) {
+  return max(cu_at(cu, s + 1, t_max), bos);
+}
+// Chunks of sequence s.
+__device__ __forceinline__ int seq_chunks(const int32_t *__restrict__ cu, int s, int t_max) {
+  const int bos = cu_at(cu, s, t_max);
+  return (cu_end(cu, s, bos, t_max) - bos + kC - 1) / kC;
+}
+
 // Batches of at most this many sequences let stage 1 locate its chunk from
 // cu_seqlens itself (one pass of 64-lane scans per wave).
 constexpr int kFusedIndexMaxSeqs = 256;
@@ -250,14 +268,14 @@ constexpr int kFusedIndexMaxSeqs = 256;
 // slot-th chunk of the batch in (sequence, chunk) order, or (-1, -1) past the
 // last chunk. Empty sequences own no chunk. Same definition as the table
 // kernel's searchsorted fill.
-__device__ __forceinline__ int2 locate_chunk(const int32_t *__restrict__ cu, int n_max, int slot,
-                                             int lane) {
+__device__ __forceinline__ int2 locate_chunk(const int32_t *__restrict__ cu, int n_max, int t_max,
+                                             int slot, int lane) {
   constexpr int kBlocks = kFusedIndexMaxSeqs / 64;
   int nc[kBlocks];
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) {  // all loads first: one round trip
     const int s = 64 * b + lane;
-    nc[b] = s < n_max ? (cu[s + 1] - cu[s] + kC - 1) / kC : 0;
+    nc[b] = s < n_max ? seq_chunks(cu, s, t_max) : 0;
   }
   int base = 0;  // chunks of the sequences before this block
 #pragma unroll

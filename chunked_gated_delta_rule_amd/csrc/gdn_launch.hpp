@@ -58,7 +58,8 @@ struct KernelEvents {
 };
 
 hipError_t launch_chunk_index(const int32_t *cu_seqlens, int32_t n_max, int32_t nt_max,
-                              int32_t *table, hipStream_t stream, KernelEvents ev = {});
+                              int32_t t_max, int32_t *table, hipStream_t stream,
+                              KernelEvents ev = {});
 
 hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t t_max, int32_t h,
@@ -77,8 +78,8 @@ hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v
 
 hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const void *v,
                             const float *g, const float *beta, const float *h0,
-                            const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
-                            float scale, float *o, float *hT, hipStream_t stream,
+                            const int32_t *cu_seqlens, int32_t n_max, int32_t t_max, int32_t h,
+                            int32_t hv, float scale, float *o, float *hT, hipStream_t stream,
                             KernelEvents ev = {});
 
 // Scratch of the two-segment stage 2 (per (sequence, value head): the state

@@ -614,8 +614,8 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   L.lane = threadIdx.x & 63;
   L.c16 = L.lane & 15;
   L.g4 = 4 * (L.lane >> 4);
-  L.bos = cu[L.s];
-  L.eos = cu[L.s + 1];
+  L.bos = cu_at(cu, L.s, t_max);
+  L.eos = cu_end(cu, L.s, L.bos, t_max);
   L.nc = (L.eos - L.bos + kC - 1) / kC;
   L.H = H;
   L.Hv = Hv;
@@ -661,14 +661,14 @@ constexpr int kLdFix = kD + 8;
 __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__restrict__ cu,
                                                              float *__restrict__ o,
                                                              float *__restrict__ hT, SegScratch seg,
-                                                             int n_max, int Hv, int nbo) {
+                                                             int n_max, int Hv, int t_max, int nbo) {
   __shared__ __attribute__((aligned(16))) __bf16 ahi[kD * kLdFix];
   __shared__ __attribute__((aligned(16))) __bf16 alo[kD * kLdFix];
   const int per = nbo + 1;
   const int pair = blockIdx.x / per, blk = blockIdx.x % per;
   const int s = pair / Hv, hv = pair % Hv;
   if (s >= n_max) return;
-  const int bos = cu[s], eos = cu[s + 1];
+  const int bos = cu_at(cu, s, t_max), eos = cu_end(cu, s, bos, t_max);
   const int nc = (eos - bos + kC - 1) / kC, cm = (nc + 1) / 2;
   const int64_t st = ((int64_t)s * Hv + hv) * kD * kD;
   const bool fin = blk == nbo;
@@ -806,7 +806,7 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
   const int64_t blocks = static_cast<int64_t>(n_max) * hv * (nbo + 1);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipExtLaunchKernelGGL(segfix_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kFixThreads), 0,
-                        stream, nullptr, ev.stop, 0, cu, o, hT, seg, n_max, hv, nbo);
+                        stream, nullptr, ev.stop, 0, cu, o, hT, seg, n_max, hv, t_max, nbo);
   return hipGetLastError();
 }
 

@@ -295,12 +295,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // are a permutation: thread t compares its sequence with all n (their chunk
 // counts staged in LDS, read as broadcasts) and writes order[rank] = t.
 // The caller's LDS must be free (no other wave still reading it).
-__device__ __forceinline__ void write_walk_order(const int32_t *__restrict__ cu, int n,
+__device__ __forceinline__ void write_walk_order(const int32_t *__restrict__ cu, int n, int t_max,
                                                  int32_t *__restrict__ order, int *ncs) {
   const int t = threadIdx.x;
   int mine = 0;
   if (t < n) {
-    mine = (cu[t + 1] - cu[t] + kC - 1) / kC;
+    mine = seq_chunks(cu, t, t_max);
     ncs[t] = mine;
   }
   __syncthreads();
@@ -344,8 +344,11 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   int2 ent;
   if (table) {
     ent = reinterpret_cast<const int2 *>(table)[blockIdx.x];
+    // an entry naming no sequence, or a chunk that starts past its sequence's
+    // end, is treated as a sentinel (checked below, after the bounds)
+    if (ent.x < 0 || ent.x >= n_max || ent.y < 0 || ent.y > t_max / kC) ent = make_int2(-1, -1);
   } else {
-    ent = locate_chunk(cu, n_max, blockIdx.x, lane);
+    ent = locate_chunk(cu, n_max, t_max, blockIdx.x, lane);
     ent.x = __builtin_amdgcn_readfirstlane(ent.x);  // the same in every lane
     ent.y = __builtin_amdgcn_readfirstlane(ent.y);
     if (blockIdx.y == 0 && tid == 0) reinterpret_cast<int2 *>(table_out)[blockIdx.x] = ent;
@@ -353,15 +356,15 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   // the work-group of slot 0, key head 0 ranks the sequences for stage 2,
   // after its own chunk (its LDS is then free) or here if it has none
   const bool ranks = out.order && blockIdx.x == 0 && blockIdx.y == 0;
-  if (ent.x < 0) {  // sentinel slot
-    if (ranks) write_walk_order(cu, n_max, out.order, reinterpret_cast<int *>(smem));
+  const int bos = ent.x < 0 ? 0 : cu_at(cu, ent.x, t_max);
+  const int t0 = bos + max(ent.y, 0) * kC;
+  const int L = ent.x < 0 ? 0 : min(kC, cu_end(cu, ent.x, bos, t_max) - t0);
+  if (L <= 0) {  // sentinel slot
+    if (ranks) write_walk_order(cu, n_max, t_max, out.order, reinterpret_cast<int *>(smem));
     return;
   }
   const int h = blockIdx.y;
   const int HG = Hv / H;
-  const int bos = cu[ent.x];
-  const int t0 = bos + ent.y * kC;
-  const int L = min(kC, cu[ent.x + 1] - t0);
   const int slot = (t0 >> 6) + ent.x;
   constexpr int kNK = kF32In ? 32 : 16;
 
@@ -755,7 +758,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     }
     __syncthreads();  // A / T, V and the gate copies are rewritten next
   }
-  if (ranks) write_walk_order(cu, n_max, out.order, reinterpret_cast<int *>(smem));
+  if (ranks) write_walk_order(cu, n_max, t_max, out.order, reinterpret_cast<int *>(smem));
 }
 
 }  // namespace

@@ -86,13 +86,13 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     const void *__restrict__ qin, const void *__restrict__ kin, const void *__restrict__ vin,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ h0,
     const int32_t *__restrict__ cu, float *__restrict__ o, float *__restrict__ hT, int H, int Hv,
-    float scale) {
+    int t_max, float scale) {
   constexpr int kEl = kF32In ? 4 : 2;
   const int s = blockIdx.x / Hv, hv = blockIdx.x % Hv;
   const int h = hv / (Hv / H);
   const int tid = threadIdx.x;
   const int v0 = 4 * (tid >> 3), d4 = 4 * (tid & 7);
-  const int bos = cu[s], eos = cu[s + 1];
+  const int bos = cu_at(cu, s, t_max), eos = cu_end(cu, s, bos, t_max);
   const int n = eos - bos;
 
   // token i's row of q, k (key head h) or v (value head hv) as a buffer range;
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
 
 hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const void *v,
                             const float *g, const float *beta, const float *h0,
-                            const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
-                            float scale, float *o, float *hT, hipStream_t stream,
+                            const int32_t *cu_seqlens, int32_t n_max, int32_t t_max, int32_t h,
+                            int32_t hv, float scale, float *o, float *hT, hipStream_t stream,
                             KernelEvents ev) {
   const int64_t blocks = static_cast<int64_t>(n_max) * hv;
   if (blocks <= 0) return hipSuccess;
@@ -203,10 +203,10 @@ hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const voi
   const dim3 grid(static_cast<uint32_t>(blocks));
   if (f32_in)
     hipExtLaunchKernelGGL((recurrent_kernel<true>), grid, dim3(kRecThreads), 0, stream, ev.start,
-                          ev.stop, 0, q, k, v, g, beta, h0, cu_seqlens, o, hT, h, hv, scale);
+                          ev.stop, 0, q, k, v, g, beta, h0, cu_seqlens, o, hT, h, hv, t_max, scale);
   else
     hipExtLaunchKernelGGL((recurrent_kernel<false>), grid, dim3(kRecThreads), 0, stream, ev.start,
-                          ev.stop, 0, q, k, v, g, beta, h0, cu_seqlens, o, hT, h, hv, scale);
+                          ev.stop, 0, q, k, v, g, beta, h0, cu_seqlens, o, hT, h, hv, t_max, scale);
   return hipGetLastError();
 }
 

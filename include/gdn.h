@@ -20,7 +20,12 @@
  *    (AMX page, section 9): token rows [t_max, ...].
  *  - cu_seqlens (device, int32, n_max + 1 entries): cu[0] = 0, non-decreasing,
  *    cu[n_max] <= t_max; unused tail sequences are zero-length (FLA issue 1155,
- *    "Core design"). It is a precondition: it is never read on the host.
+ *    "Core design"). It is a precondition: it is never read on the host. The
+ *    kernels clamp every entry they read to [0, t_max] and never let a
+ *    sequence end before it starts, so a malformed cu_seqlens gives
+ *    unspecified results but no access outside the buffers that cfg sizes.
+ *    Likewise a caller's chunk table entry that names no sequence (< 0 or
+ *    >= n_max) or no chunk of its sequence is treated as a sentinel.
  *  - GQA: value head hv reads key/query head hv / (hv_count / h_count) (AMX
  *    page, section 4).
  *  - States h0 / hT: [n_max, hv, dv, dk] fp32, value-major (AMX page, s. 9).
