@@ -29,13 +29,14 @@ __all__ = [
     "gdn_workspace_layout", "make_config", "chunk_gated_delta_rule", "EXPORTED_SYMBOLS",
     "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "GDN_FUSED_INDEX_MAX_SEQS",
     "gdn_chunk_fwd_conv", "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd",
-    "gdn_recurrent_fwd_timed", "recurrent_gated_delta_rule", "GDN_SEGMENT_MIN_TOKENS",
+    "gdn_recurrent_fwd_timed", "recurrent_gated_delta_rule", "GDN_SEGMENT_MIN_TOKENS", "GDN_FOUR_TILE_MIN_TOKENS",
 ]
 
 GDN_BF16 = 0
 GDN_F32 = 1
 GDN_FUSED_INDEX_MAX_SEQS = 256  # include/gdn.h
 GDN_SEGMENT_MIN_TOKENS = 2048  # include/gdn.h
+GDN_FOUR_TILE_MIN_TOKENS = 384  # include/gdn.h
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
            3: "GDN_ERR_CAPACITY", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_layout", "gdn_workspace_size",
@@ -52,7 +53,8 @@ class gdn_config(ctypes.Structure):
     _fields_ = [("t_max", ctypes.c_int32), ("n_max", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("hv", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int), ("o_dtype", ctypes.c_int),
-                ("scale", ctypes.c_float), ("segments", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("segments", ctypes.c_int32),
+                ("tiles", ctypes.c_int32)]
 
 
 class gdn_workspace_layout_t(ctypes.Structure):
@@ -110,11 +112,11 @@ def load_library():
 
 
 def make_config(t_max, n_max, h, hv, qkv_dtype=GDN_BF16, scale=0.0, o_dtype=GDN_F32,
-                dk=128, dv=128, chunk=64, segments=0) -> gdn_config:
+                dk=128, dv=128, chunk=64, segments=0, tiles=0) -> gdn_config:
     if isinstance(qkv_dtype, torch.dtype):
         qkv_dtype = GDN_F32 if qkv_dtype == torch.float32 else GDN_BF16
     return gdn_config(int(t_max), int(n_max), int(h), int(hv), int(dk), int(dv), int(chunk),
-                      int(qkv_dtype), int(o_dtype), float(scale), int(segments))
+                      int(qkv_dtype), int(o_dtype), float(scale), int(segments), int(tiles))
 
 
 def _ptr(x) -> Optional[int]:

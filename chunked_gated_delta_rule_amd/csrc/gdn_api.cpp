@@ -31,6 +31,8 @@ gdn_status check_config(const gdn_config *cfg) {
   if (cfg->o_dtype != GDN_BF16 && cfg->o_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
   if (std::isnan(cfg->scale) || std::isinf(cfg->scale)) return GDN_ERR_INVALID_ARG;
   if (cfg->segments < 0 || cfg->segments > 2) return GDN_ERR_INVALID_ARG;
+  if (cfg->tiles != 0 && cfg->tiles != 1 && cfg->tiles != 2 && cfg->tiles != 4)
+    return GDN_ERR_INVALID_ARG;
   if (cfg->dk != kD || cfg->dv != kD || cfg->chunk != kChunk) return GDN_ERR_UNSUPPORTED;
   if (cfg->hv % cfg->h != 0) return GDN_ERR_UNSUPPORTED;
   if (cfg->o_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
@@ -53,6 +55,19 @@ int segments_of(const gdn_config *cfg) {
                  gdn::cu_count()
              ? 2
              : 1;
+}
+
+// 16-column tiles per work-group of the one-piece stage-2 walk (validated
+// config).
+int tiles_of(const gdn_config *cfg) {
+  if (cfg->tiles != 0) return cfg->tiles;
+  const int64_t one = gdn::inter_one_walk_grid(cfg->n_max, cfg->h, cfg->hv);
+  const int64_t cus = gdn::cu_count();
+  if (one <= cus) return 1;
+  if (one >= 4 * cus &&
+      static_cast<int64_t>(cfg->t_max) >= static_cast<int64_t>(cfg->n_max) * GDN_FOUR_TILE_MIN_TOKENS)
+    return 4;
+  return 2;
 }
 
 // Whether stage 1 ranks the sequences for stage 2 (longest walks first): with
@@ -187,6 +202,7 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
   return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, b, h0, cu_seqlens, cfg->n_max,
                                     cfg->h, cfg->hv, cfg->t_max, nt_max_of(cfg),
                                     static_cast<float *>(o), hT, s, ev[2], segments_of(cfg),
+                                    tiles_of(cfg),
                                     seg_scratch(l, workspace)));
 }
 
@@ -295,7 +311,7 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
   return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, stage_buffers(cfg, l, workspace), h0,
                                     cu_seqlens, cfg->n_max, cfg->h, cfg->hv, cfg->t_max,
                                     nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream),
-                                    {}, segments_of(cfg), seg_scratch(l, workspace)));
+                                    {}, segments_of(cfg), tiles_of(cfg), seg_scratch(l, workspace)));
 }
 
 gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,

@@ -103,6 +103,7 @@ int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv);
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
                         int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,
-                        KernelEvents ev = {}, int segments = 1, SegScratch seg = {});
+                        KernelEvents ev = {}, int segments = 1, int tiles = 1,
+                        SegScratch seg = {});
 
 }  // namespace gdn

@@ -13,7 +13,7 @@
 // (Alloy page, "How do you parallelize a recurrence for prefill?": the state
 // tile is blocked along the value dimension to fit on chip). One work-group of
 // four wave64s owns a 128 x 16 column slice of S (one column tile), or a
-// 128 x 32 slice (two tiles), for the whole sequence. Every
+// 128 x 32 or 128 x 64 slice (two or four tiles), for the whole sequence. Every
 // product of the chunk step is arranged so that its operands come either from
 // MFMA accumulators directly or from fragments the intra stage stored in MFMA
 // order:
@@ -46,13 +46,17 @@
 // into registers; past the last chunk the buffer range is empty and loads
 // return zero. Between them the four waves load each operand once per chunk.
 //
-// Two launch shapes. When the grid of one-tile work-groups fits the device
+// Three launch shapes (the caller's choice, or automatic by grid size and
+// tokens per sequence). When the grid of one-tile work-groups fits the device
 // (one per CU), fragments are prefetched two chunks ahead and a fifth wave
-// warms the L2. Larger grids use two column tiles per work-group: w, K^T, q16
-// and P are then loaded once for twice the columns (68 KB per chunk for 32
-// columns instead of 2 x 74 KB), every product is done once per tile in the
-// same order as for one tile (so the results are bitwise those of the one-tile
-// shape), and two work-groups stay resident per CU with one chunk of prefetch.
+// warms the L2. Larger grids use two or four column tiles per work-group: w,
+// K^T, q16 and P are then loaded once for all its columns (for two tiles 64 KB
+// per chunk instead of 2 x 61 KB), every product is done once per tile in the
+// same order as for one tile (so the results are bitwise those of the
+// one-tile shape), and fragments are prefetched one chunk ahead. Two-tile
+// work-groups stay resident two per CU, which hides the start and end of
+// short walks; four-tile ones run one per CU and load least per column, which
+// pays on long walks.
 //
 // Work-group numbering is XCD-aware: all work-groups of the value heads that
 // share a key head get the same blockIdx modulo 8, so they run on one XCD and
@@ -75,7 +79,8 @@ constexpr int kL2Lead = 2;       // chunks between the L2 warm-up and the operan
 // The L2 warm-up wave is a fifth wave of the work-group; fp32 input at depth 2
 // needs more than the 256 VGPRs a SIMD with two waves of it could give, and
 // runs without it. Work-groups of two column tiles (kNV = 2) run two per CU
-// with four waves each, within 256 VGPRs, and have no warm-up wave either.
+// with four waves each, within 256 VGPRs, and have no warm-up wave either;
+// four tiles (kNV = 4) run one per CU with four waves of up to 512 registers.
 template <bool kF32In, int kDepth, int kS, int kNV>
 constexpr bool kWarmWave = kNV == 1 && !(kF32In && kDepth == 2) && (kS == 1 || kDepth == 1);
 constexpr int kDepthSeg = 1;  // prefetch depth of the two-state walk (keeps the warm-up wave)
@@ -780,15 +785,19 @@ void launch_walk(const StageBuffers &in, const float *h0, const int32_t *cu, int
 template <bool kF32In>
 hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
                         int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
-                        hipStream_t stream, KernelEvents ev, int segments, const SegScratch &seg) {
+                        hipStream_t stream, KernelEvents ev, int segments, int tiles,
+                        const SegScratch &seg) {
   const int one_walk = inter_one_walk_grid(n_max, h, hv);
   if (segments != 2) {
-    if (one_walk <= cu_count())
-      launch_walk<kF32In, kDepthSingle, 1>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
-                                           ev.start, ev.stop);
-    else
+    if (tiles == 4)
+      launch_walk<kF32In, 1, 1, 4>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                                   ev.start, ev.stop);
+    else if (tiles == 2)
       launch_walk<kF32In, 1, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
                                    ev.start, ev.stop);
+    else
+      launch_walk<kF32In, kDepthSingle, 1>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                                           ev.start, ev.stop);
     return hipGetLastError();
   }
   if (2 * one_walk <= cu_count())
@@ -835,11 +844,11 @@ int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv) {
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
                         int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,
-                        KernelEvents ev, int segments, SegScratch seg) {
+                        KernelEvents ev, int segments, int tiles, SegScratch seg) {
   return f32_in ? launch_waves<true>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream,
-                                     ev, segments, seg)
+                                     ev, segments, tiles, seg)
                 : launch_waves<false>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT,
-                                      stream, ev, segments, seg);
+                                      stream, ev, segments, tiles, seg);
 }
 
 }  // namespace gdn

@@ -71,7 +71,18 @@ typedef struct {
                           the starting state); 0 = automatic: 2 when t_max >=
                           GDN_SEGMENT_MIN_TOKENS and the one-piece stage-2 grid fills
                           at most half of the current device's compute units */
+  int32_t tiles;       /* 16-column tiles of the state per stage-2 work-group in the
+                          one-piece walk: 1, 2 or 4 (the results are bitwise the same);
+                          0 = automatic: 1 when the one-tile grid fits the device, 4
+                          when it is at least 4x the device and t_max >= n_max *
+                          GDN_FOUR_TILE_MIN_TOKENS (long sequences), else 2. The
+                          two-segment walk always uses 1. */
 } gdn_config;
+
+/* Token capacity per sequence from which the automatic choice considers
+ * four-tile stage-2 work-groups (one per CU: fewer loads per column, but the
+ * start and end of each walk are not hidden behind another work-group). */
+#define GDN_FOUR_TILE_MIN_TOKENS 384
 
 /* Token capacity from which the automatic choice considers two segments. */
 #define GDN_SEGMENT_MIN_TOKENS 2048

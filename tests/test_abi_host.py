@@ -119,7 +119,8 @@ def test_workspace_layout_segments(lib):
     ("hv", 24, UNSUPPORTED), ("o_dtype", gdn.GDN_BF16, UNSUPPORTED),
     ("t_max", -1, INVALID), ("n_max", 0, INVALID), ("h", 0, INVALID), ("qkv_dtype", 7, INVALID),
     ("scale", float("nan"), INVALID), ("t_max", (1 << 24) + 1, CAPACITY), ("n_max", 16385, CAPACITY),
-    ("segments", 3, INVALID), ("segments", -1, INVALID),
+    ("segments", 3, INVALID), ("segments", -1, INVALID), ("tiles", 3, INVALID),
+    ("tiles", -1, INVALID), ("tiles", 8, INVALID), ("tiles", 4, OK), ("tiles", 1, OK),
 ])
 def test_config_validation(lib, field, value, status):
     cfg = gdn.make_config(256, 2, 16, 32)
@@ -214,6 +215,8 @@ def test_header_constants_match_binding():
     assert m and int(m.group(1)) == gdn.GDN_FUSED_INDEX_MAX_SEQS
     m = re.search(r"#define GDN_SEGMENT_MIN_TOKENS (\d+)", text)
     assert m and int(m.group(1)) == gdn.GDN_SEGMENT_MIN_TOKENS
+    m = re.search(r"#define GDN_FOUR_TILE_MIN_TOKENS (\d+)", text)
+    assert m and int(m.group(1)) == gdn.GDN_FOUR_TILE_MIN_TOKENS
 
 
 def test_fused_front_entry_point_host_errors(lib):

@@ -1,10 +1,10 @@
-"""GPU parity of the stage-2 shape with two 16-column tiles per work-group,
-which the library picks when the grid of one-tile work-groups is larger than
-the device (here 9 sequences x 4 key heads: 384 one-tile work-groups).
+"""GPU parity of the stage-2 shapes with two and four 16-column tiles per
+work-group (gdn_config.tiles; automatic for grids larger than the device).
 Checked on every lane against the CPU oracle (bf16 and fp32 input, with and
 without initial states, lengths around the chunk size and empty sequences),
-and bitwise against each sequence run alone, which takes the one-tile shape
-(the two shapes do the same products in the same order)."""
+bitwise across tiles = 1, 2 and 4 on the same batch (every shape does the
+same products in the same order per tile), and bitwise against each sequence
+run alone, which takes the one-tile shape."""
 
 import numpy as np
 import pytest
@@ -13,7 +13,8 @@ import torch
 import chunked_gated_delta_rule_amd as gdn
 import workloads
 
-from gpu_helpers import O_TOL, S_TOL, lane_errors, log, oracle_lanes, run_forward
+from gpu_helpers import (O_TOL, S_TOL, device_inputs, lane_errors, log, oracle_lanes,
+                         run_forward)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -39,18 +40,33 @@ def _one_tile_grid(n, h, hv):
     return -(-n * h // 8) * 8 * (hv // h) * 8
 
 
+def _forward(wl, tiles, d=None):
+    if d is None:
+        d = device_inputs(wl, DEV)
+    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, wl.qkv_dtype, segments=1, tiles=tiles)
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    o = torch.full((wl.t_max, wl.Hv, 128), float("nan"), dtype=torch.float32, device=DEV)
+    hT = torch.full((wl.n_max, wl.Hv, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+    gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], None, o,
+                      hT, ws)
+    torch.cuda.synchronize()
+    return o, hT
+
+
 def test_batch_takes_the_two_tile_shape():
-    # more one-tile work-groups than an MI355X has CUs
-    assert _one_tile_grid(len(LENGTHS), H, HV) > 256
+    # more one-tile work-groups than an MI355X has CUs, fewer than four times
+    # as many: the automatic choice is two tiles; one sequence alone takes one
+    assert 256 < _one_tile_grid(len(LENGTHS), H, HV) < 4 * 256
     assert _one_tile_grid(1, H, HV) <= 256
 
 
+@pytest.mark.parametrize("tiles", [2, 4])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("h0_sigma", [0.02, 0.0])
-def test_two_tiles_every_lane(dtype, h0_sigma):
+def test_column_tiles_every_lane(tiles, dtype, h0_sigma):
     wl = _batch(dtype, h0_sigma)
-    log(f"two tiles: lengths {LENGTHS} dtype={dtype} h0={h0_sigma}")
-    o, hT, _ = run_forward(wl)
+    log(f"{tiles} tiles: lengths {LENGTHS} dtype={dtype} h0={h0_sigma}")
+    o, hT = _forward(wl, tiles)
     lanes = [(s, hv) for s in range(len(LENGTHS)) for hv in range(HV)]
     ref = oracle_lanes(wl, lanes)
     eo, es = lane_errors(wl, o, hT, ref)
@@ -58,6 +74,18 @@ def test_two_tiles_every_lane(dtype, h0_sigma):
     assert eo <= O_TOL and es <= S_TOL
     T = int(wl.cu_seqlens[-1])
     assert torch.isnan(o[T:]).all()  # rows past the batch untouched
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_tile_shapes_bitwise_equal(dtype):
+    wl = _batch(dtype, 0.02, seed=63)
+    d = device_inputs(wl, DEV)
+    o1, h1 = _forward(wl, 1, d)
+    T = int(wl.cu_seqlens[-1])
+    for tiles in (2, 4, 0):
+        o, h = _forward(wl, tiles, d)
+        assert torch.equal(o[:T], o1[:T]), tiles
+        assert torch.equal(h, h1), tiles
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
