@@ -64,7 +64,7 @@ int tiles_of(const gdn_config *cfg) {
   const int64_t one = gdn::inter_one_walk_grid(cfg->n_max, cfg->h, cfg->hv);
   const int64_t cus = gdn::cu_count();
   if (one <= cus) return 1;
-  if (one >= 4 * cus &&
+  if (one > 2 * cus &&
       static_cast<int64_t>(cfg->t_max) >= static_cast<int64_t>(cfg->n_max) * GDN_FOUR_TILE_MIN_TOKENS)
     return 4;
   return 2;

@@ -74,7 +74,7 @@ typedef struct {
   int32_t tiles;       /* 16-column tiles of the state per stage-2 work-group in the
                           one-piece walk: 1, 2 or 4 (the results are bitwise the same);
                           0 = automatic: 1 when the one-tile grid fits the device, 4
-                          when it is at least 4x the device and t_max >= n_max *
+                          when it is more than 2x the device and t_max >= n_max *
                           GDN_FOUR_TILE_MIN_TOKENS (long sequences), else 2. The
                           two-segment walk always uses 1. */
 } gdn_config;

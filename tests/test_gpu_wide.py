@@ -54,9 +54,11 @@ def _forward(wl, tiles, d=None):
 
 
 def test_batch_takes_the_two_tile_shape():
-    # more one-tile work-groups than an MI355X has CUs, fewer than four times
-    # as many: the automatic choice is two tiles; one sequence alone takes one
-    assert 256 < _one_tile_grid(len(LENGTHS), H, HV) < 4 * 256
+    # more one-tile work-groups than an MI355X has CUs, and less capacity
+    # than GDN_FOUR_TILE_MIN_TOKENS per sequence: the automatic choice is two
+    # tiles; one sequence alone takes one
+    assert _one_tile_grid(len(LENGTHS), H, HV) > 256
+    assert sum(LENGTHS) + 40 < len(LENGTHS) * gdn.GDN_FOUR_TILE_MIN_TOKENS
     assert _one_tile_grid(1, H, HV) <= 256
 
 
