@@ -8,10 +8,15 @@
 //    with the whole row kept in registers (AMX page, section 7).
 //
 // Thread layout: a thread owns 8 consecutive channels (one 16-byte load per
-// tap); 16 threads cover one 128-channel head, so the head's sum of squares is
+// row); 16 threads cover one 128-channel head, so the head's sum of squares is
 // a 16-lane butterfly inside the wave. A work-group covers 2048 channels of
-// kTokens consecutive tokens. HBM-bound: bf16 rows are read once from HBM (the
-// d_conv-1 re-reads hit cache) and fp32 rows written once.
+// kTokens consecutive tokens and walks them in order, keeping the last
+// kTaps - 1 rows in registers: each token loads one new row, requested one
+// token ahead. The tap count is a template parameter (the window is a register
+// array and needs constant indices). Taps are accumulated oldest first with
+// rows before the sequence start skipped, the order the front fused into
+// stage 1 uses, so both produce the same bits. HBM-bound: bf16 rows are read
+// once (plus a kTaps - 1 row halo per work-group) and fp32 rows written once.
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -19,11 +24,12 @@ namespace gdn {
 
 namespace {
 
-constexpr int kTokens = 16;
+constexpr int kTokens = 64;
 constexpr int kMaxTaps = 8;
 
+template <int kTaps>
 __global__ __launch_bounds__(kThreads) void front_kernel(
-    const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ conv_w, int d_conv,
+    const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ conv_w,
     const int32_t *__restrict__ cu, int n_max, int t_max, int h, int hv,
     float *__restrict__ q, float *__restrict__ k, float *__restrict__ v) {
   const int channels = (2 * h + hv) * kD;
@@ -32,15 +38,18 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
   const int t_begin = blockIdx.y * kTokens;
   const int t_total = cu_at(cu, n_max, t_max);
   if (t_begin >= t_total) return;
+  const int t_end = min(t_begin + kTokens, t_total);
 
-  float wt[8][kMaxTaps];
-  if (active) {
+  float wt[8][kTaps];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int j = 0; j < kMaxTaps; ++j)
-        wt[c][j] = j < d_conv ? bf16_bits_to_float(conv_w[(int64_t)(c0 + c) * d_conv + j]) : 0.f;
-  }
+    for (int j = 0; j < kTaps; ++j)
+      wt[c][j] = active ? bf16_bits_to_float(conv_w[(int64_t)(c0 + c) * kTaps + j]) : 0.f;
+  auto row = [&](int r) __attribute__((always_inline)) {
+    return active ? *reinterpret_cast<const u32x4 *>(qkv + (int64_t)r * channels + c0)
+                  : u32x4{0u, 0u, 0u, 0u};
+  };
   // sequence containing t_begin: last s with cu[s] <= t_begin (and cu[s+1] > t_begin)
   int lo = 0, hi = n_max;
   while (hi - lo > 1) {
@@ -49,22 +58,26 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
   }
   int s = lo;
   const bool is_qk = c0 < 2 * h * kD;
-  const int t_end = min(t_begin + kTokens, t_total);
+  // win[j] holds row t - (kTaps - 1) + j (raw bf16); rows before 0 are never used
+  u32x4 win[kTaps];
+#pragma unroll
+  for (int j = 0; j < kTaps - 1; ++j) {
+    const int r = t_begin - (kTaps - 1) + j;
+    win[j] = r >= 0 ? row(r) : u32x4{0u, 0u, 0u, 0u};
+  }
+  win[kTaps - 1] = row(t_begin);
   for (int t = t_begin; t < t_end; ++t) {
+    const u32x4 next = t + 1 < t_end ? row(t + 1) : u32x4{0u, 0u, 0u, 0u};
     while (s + 1 < n_max && cu_at(cu, s + 1, t_max) <= t) ++s;
     const int bos = min(cu_at(cu, s, t_max), t);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (active) {
 #pragma unroll
-      for (int j = 0; j < kMaxTaps; ++j) {
-        const int src = t - (d_conv - 1) + j;
-        if (j >= d_conv || src < bos) continue;
-        const u32x4 raw = *reinterpret_cast<const u32x4 *>(qkv + (int64_t)src * channels + c0);
-        float x[8];
-        unpack8(raw, x);
+    for (int j = 0; j < kTaps; ++j) {
+      if (t - (kTaps - 1) + j < bos) continue;  // before the sequence start (same for all lanes)
+      float x[8];
+      unpack8(win[j], x);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = fmaf(x[c], wt[c][j], acc[c]);
-      }
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(x[c], wt[c][j], acc[c]);
     }
     float y[8];
     float ss = 0.f;
@@ -75,6 +88,9 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
     }
     // 16 consecutive lanes hold one head (heads start on 128-channel boundaries)
     ss = sum16(ss);
+#pragma unroll
+    for (int j = 0; j < kTaps - 1; ++j) win[j] = win[j + 1];
+    win[kTaps - 1] = next;
     if (!active) continue;
     float *dst;
     if (c0 < h * kD) {
@@ -104,9 +120,22 @@ hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
   const int channels = (2 * h + hv) * kD;
   const dim3 grid((channels / 8 + kThreads - 1) / kThreads, (t_max + kTokens - 1) / kTokens);
   if (grid.y == 0) return hipSuccess;
-  hipExtLaunchKernelGGL(front_kernel, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
-                        static_cast<const uint16_t *>(qkv), static_cast<const uint16_t *>(conv_w),
-                        d_conv, cu_seqlens, n_max, t_max, h, hv, q, k, v);
+  const uint16_t *x = static_cast<const uint16_t *>(qkv);
+  const uint16_t *w = static_cast<const uint16_t *>(conv_w);
+#define GDN_LAUNCH_FRONT(TAPS)                                                                   \
+  hipExtLaunchKernelGGL(front_kernel<TAPS>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, \
+                        0, x, w, cu_seqlens, n_max, t_max, h, hv, q, k, v)
+  switch (d_conv) {
+    case 1: GDN_LAUNCH_FRONT(1); break;
+    case 2: GDN_LAUNCH_FRONT(2); break;
+    case 3: GDN_LAUNCH_FRONT(3); break;
+    case 4: GDN_LAUNCH_FRONT(4); break;
+    case 5: GDN_LAUNCH_FRONT(5); break;
+    case 6: GDN_LAUNCH_FRONT(6); break;
+    case 7: GDN_LAUNCH_FRONT(7); break;
+    default: GDN_LAUNCH_FRONT(8); break;
+  }
+#undef GDN_LAUNCH_FRONT
   return hipGetLastError();
 }
 
