@@ -40,11 +40,13 @@
 //   helper waves 2 and 3: after the barrier, helper Y reads S (fp16) and both
 //       partials of the chunk and writes output rows 32 Y .. 32 Y + 31:
 //       y = S^T q^T and o = P v' + scale e^gamma y.
-// One barrier per chunk; the exchange is double-buffered (12 KB per chunk),
-// so the chain waves run ahead while the helpers finish the previous chunk.
-// Every operand fragment is one 1 KB block (16 bytes per lane) loaded straight
-// into registers; past the last chunk the buffer range is empty and loads
-// return zero. Between them the four waves load each operand once per chunk.
+// One barrier per chunk; the exchange is double-buffered (12 KB per chunk and
+// column tile), so the chain waves run ahead while the helpers finish the
+// previous chunk. Every operand fragment is one block loaded straight into
+// registers, 16 bytes per lane (u: four 24-bit floats in 12; the two
+// half-zero pairs of P: 8); past the last chunk the buffer range is empty and
+// loads return zero. Between them the four waves load each operand once per
+// chunk.
 //
 // Three launch shapes (the caller's choice, or automatic by grid size and
 // tokens per sequence). When the grid of one-tile work-groups fits the device
@@ -60,7 +62,10 @@
 //
 // Work-group numbering is XCD-aware: all work-groups of the value heads that
 // share a key head get the same blockIdx modulo 8, so they run on one XCD and
-// share q16 and K^T through its L2.
+// share q16 and K^T through its L2. Sequences are numbered by the rank stage 1
+// gives them (longest first) when it ranks the batch, so the longest walks
+// start first. o rows of the one-tile, one-piece walk are stored streaming
+// (non-temporal).
 #include <type_traits>
 #include <utility>
 
