@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -78,11 +79,15 @@ def algorithmic_work(wl, nt, qkv_bytes, fused_front=False):
 
 
 def kernel_source_digest(name):
+    """Digest of a kernel's code (its source and the shared device headers),
+    with // comments and blank lines left out, so that counter figures stay
+    attached to the code they were measured on and not to its comments."""
     csrc = os.path.join(ROOT, "chunked_gated_delta_rule_amd", "csrc")
     h = hashlib.sha256()
-    for f in (name + ".hip", "gdn_common.hpp"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+    for f in (name + ".hip", "gdn_common.hpp", "gdn_launch.hpp"):
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = re.sub(r"//[^\n]*", "", fh.read())
+        h.update("\n".join(l.strip() for l in code.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
