@@ -600,3 +600,48 @@ def test_walk_order_table_bit_exact(lengths, with_table):
         ref = oracle_lanes(wl, [(s, hv) for s in range(len(lengths)) for hv in range(wl.Hv)])
         eo, es = lane_errors(wl, o, hT, ref)
         assert eo <= O_TOL and es <= S_TOL
+
+
+def _with_capacity(wl, t_max, n_max):
+    """The same batch in buffers of another capacity (extra rows zero, extra
+    sequences empty)."""
+    pad = t_max - wl.t_max
+    grow = lambda x: torch.cat([x, torch.zeros((pad,) + tuple(x.shape[1:]), dtype=x.dtype)])
+    cu = np.concatenate([wl.cu_seqlens[:len(wl.cu_seqlens)],
+                         np.full(n_max + 1 - len(wl.cu_seqlens), wl.cu_seqlens[-1], np.int32)])
+    h0 = None
+    if wl.h0 is not None:
+        h0 = torch.cat([wl.h0, torch.zeros((n_max - wl.h0.shape[0],) + tuple(wl.h0.shape[1:]))])
+    return workloads.Workload(name="capacity", cu_seqlens=cu.astype(np.int32), t_max=t_max,
+                              n_max=n_max, H=wl.H, Hv=wl.Hv, qkv_dtype=wl.qkv_dtype,
+                              q=grow(wl.q), k=grow(wl.k), v=grow(wl.v), g=grow(wl.g),
+                              beta=grow(wl.beta), h0=h0)
+
+
+@pytest.mark.parametrize("lengths", [[256], [300, 64, 1, 129, 0, 77]])
+@pytest.mark.parametrize("with_table", [False, True])
+def test_capacity_invariance_bitwise(lengths, with_table):
+    """A batch run at its exact capacity (for one 256-token sequence NT_max is
+    exactly its chunk count: no sentinel slot) and at a larger one (sentinel
+    slots, empty extra sequences, and possibly another stage-2 shape) gives
+    the same bits, with the table built on the fly or passed in."""
+    n = len(lengths)
+    exact = workloads.make_custom(lengths, 2, 4, seed=101, h0_sigma=0.02)
+    big = _with_capacity(exact, exact.t_max + 500, n + 7)
+    outs = []
+    for wl in (exact, big):
+        d = device_inputs(wl)
+        table = None
+        if with_table:
+            table = torch.empty((gdn.gdn_nt_max(wl.t_max, wl.n_max), 2), dtype=torch.int32,
+                                device=DEV)
+            gdn.gdn_build_chunk_indices(config_of(wl), d["cu"], table)
+        o, hT, _ = run_forward(wl, d, chunk_indices=table)
+        outs.append((o, hT))
+    if lengths == [256]:
+        assert gdn.gdn_nt_max(exact.t_max, exact.n_max) == 4
+    T = int(exact.cu_seqlens[-1])
+    assert torch.equal(outs[0][0][:T], outs[1][0][:T])
+    assert torch.equal(outs[0][1], outs[1][1][:n])
+    # the extra sequences are empty: their final state is their (zero) initial state
+    assert (outs[1][1][n:] == 0).all()
