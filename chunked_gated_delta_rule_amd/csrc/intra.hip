@@ -321,7 +321,8 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     const void *__restrict__ qin, const void *__restrict__ kin, const void *__restrict__ vin,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ table, int32_t *__restrict__ table_out, int n_max,
-    StageBuffers out, int H, int Hv, int t_max, int nt, float scale, ConvIn ci) {
+    StageBuffers out, int H, int Hv, int t_max, int nt, float scale, ConvIn ci,
+    bool head_fastest) {
   constexpr bool kConv = kTaps > 0;
   static_assert(!kConv || kF32In, "the fused front produces fp32 q, k, v");
   using Smem = IntraSmem<kF32In>;
@@ -338,24 +339,40 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   const int wv = tid >> 6;
   float *gsh = reinterpret_cast<float *>(smem + Smem::kOffGates) + wv * 2 * 64;  // this wave's gates
   float *bsh = gsh + 64;
+  // work-group -> (item = table slot, key head). With several sequences the
+  // numbering is key head fastest, so the dispatch reaches the sentinel slots
+  // past the batch's last chunk only at the end (a varlen batch of 32
+  // sequences has more sentinel slots than chunks); with one sequence, which
+  // has no such slots, it is slot fastest, which keeps the work-groups in
+  // flight spread over the whole sequence.
+  // slot fastest: grid (nt, H); key head fastest: a one-dimensional grid of
+  // nt * H (measured faster for batches than a (H, nt) grid)
+  int item, h;
+  if (!head_fastest) {
+    item = blockIdx.x;
+    h = blockIdx.y;
+  } else {
+    item = static_cast<int>(blockIdx.x / static_cast<uint32_t>(H));
+    h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(H));
+  }
   // this work-group's chunk: from the caller's table, or located from
   // cu_seqlens here (every wave computes it; the key-head-0 work-groups also
   // fill the workspace copy of the table)
   int2 ent;
   if (table) {
-    ent = reinterpret_cast<const int2 *>(table)[blockIdx.x];
+    ent = reinterpret_cast<const int2 *>(table)[item];
     // an entry naming no sequence, or a chunk that starts past its sequence's
     // end, is treated as a sentinel (checked below, after the bounds)
     if (ent.x < 0 || ent.x >= n_max || ent.y < 0 || ent.y > t_max / kC) ent = make_int2(-1, -1);
   } else {
-    ent = locate_chunk(cu, n_max, t_max, blockIdx.x, lane);
+    ent = locate_chunk(cu, n_max, t_max, item, lane);
     ent.x = __builtin_amdgcn_readfirstlane(ent.x);  // the same in every lane
     ent.y = __builtin_amdgcn_readfirstlane(ent.y);
-    if (blockIdx.y == 0 && tid == 0) reinterpret_cast<int2 *>(table_out)[blockIdx.x] = ent;
+    if (h == 0 && tid == 0) reinterpret_cast<int2 *>(table_out)[item] = ent;
   }
   // the work-group of slot 0, key head 0 ranks the sequences for stage 2,
   // after its own chunk (its LDS is then free) or here if it has none
-  const bool ranks = out.order && blockIdx.x == 0 && blockIdx.y == 0;
+  const bool ranks = out.order && blockIdx.x == 0;
   const int bos = ent.x < 0 ? 0 : cu_at(cu, ent.x, t_max);
   const int t0 = bos + max(ent.y, 0) * kC;
   const int L = ent.x < 0 ? 0 : min(kC, cu_end(cu, ent.x, bos, t_max) - t0);
@@ -363,7 +380,6 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     if (ranks) write_walk_order(cu, n_max, t_max, out.order, reinterpret_cast<int *>(smem));
     return;
   }
-  const int h = blockIdx.y;
   const int HG = Hv / H;
   const int slot = (t0 >> 6) + ent.x;
   constexpr int kNK = kF32In ? 32 : 16;
@@ -773,11 +789,19 @@ hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v
   if (conv.qkv && (!f32_in || !conv.conv_w || conv.d_conv < 1 || conv.d_conv > 4))
     return hipErrorInvalidValue;
   if (nt_max <= 0) return hipSuccess;
-  const dim3 grid(nt_max, h);
+  // work-group order (see the kernel): slot fastest for one sequence, key head
+  // fastest for batches
+  const bool head_fastest = n_max > 1;
+  dim3 grid(nt_max, h);
+  if (head_fastest) {
+    const int64_t blocks = static_cast<int64_t>(nt_max) * h;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    grid = dim3(static_cast<uint32_t>(blocks));
+  }
 #define GDN_LAUNCH_INTRA(F32, TAPS)                                                             \
   hipExtLaunchKernelGGL((intra_kernel<F32, TAPS>), grid, dim3(kThreads), 0, stream, ev.start,   \
                         ev.stop, 0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, \
-                        hv, t_max, nt_max, scale, conv)
+                        hv, t_max, nt_max, scale, conv, head_fastest)
   if (conv.qkv) {
     switch (conv.d_conv) {
       case 1: GDN_LAUNCH_INTRA(true, 1); break;

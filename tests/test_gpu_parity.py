@@ -645,3 +645,32 @@ def test_capacity_invariance_bitwise(lengths, with_table):
     assert torch.equal(outs[0][1], outs[1][1][:n])
     # the extra sequences are empty: their final state is their (zero) initial state
     assert (outs[1][1][n:] == 0).all()
+
+
+def test_more_chunk_slots_than_a_grid_dimension_bitwise():
+    """A batch whose capacity has more chunk slots than a grid's second
+    dimension takes (NT_max > 65535; stage 1's one-dimensional grid then has
+    over a million work-groups, nearly all sentinels) gives the bits of the
+    same batch at exact capacity."""
+    exact = workloads.make_custom([100, 200], 1, 1, seed=111, h0_sigma=0.02)
+    t_big = 64 * 65536 + 64
+    assert gdn.gdn_nt_max(t_big, 2) > 65535
+    d = device_inputs(exact)
+    o1, h1, _ = run_forward(exact, d)
+    big = {}
+    for name in ("q", "k", "v", "g", "beta"):
+        x = d[name]
+        big[name] = torch.zeros((t_big,) + tuple(x.shape[1:]), dtype=x.dtype, device=DEV)
+        big[name][:x.shape[0]] = x
+    # one-piece stage 2 as at the exact capacity (this capacity would
+    # otherwise pick the two-segment walk, which rounds differently)
+    cfg = gdn.make_config(t_big, 2, 1, 1, exact.qkv_dtype, segments=1)
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    o = torch.empty((t_big, 1, 128), dtype=torch.float32, device=DEV)
+    hT = torch.empty((2, 1, 128, 128), dtype=torch.float32, device=DEV)
+    gdn.gdn_chunk_fwd(cfg, big["q"], big["k"], big["v"], big["g"], big["beta"], d["h0"], d["cu"],
+                      None, o, hT, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:300], o1[:300]) and torch.equal(hT, h1)
+    del big, ws, o
+    torch.cuda.empty_cache()
