@@ -197,7 +197,7 @@ def main():
                     help="only run a plain device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
 
