@@ -345,12 +345,12 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   // sequences has more sentinel slots than chunks); with one sequence, which
   // has no such slots, it is slot fastest, which keeps the work-groups in
   // flight spread over the whole sequence.
-  // slot fastest: grid (nt, H); key head fastest: a one-dimensional grid of
-  // nt * H (measured faster for batches than a (H, nt) grid)
+  // a one-dimensional grid of nt * H work-groups (for batches it measured
+  // faster than a two-dimensional (H, nt) grid in the same order)
   int item, h;
   if (!head_fastest) {
-    item = blockIdx.x;
-    h = blockIdx.y;
+    item = static_cast<int>(blockIdx.x % static_cast<uint32_t>(nt));
+    h = static_cast<int>(blockIdx.x / static_cast<uint32_t>(nt));
   } else {
     item = static_cast<int>(blockIdx.x / static_cast<uint32_t>(H));
     h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(H));
@@ -792,12 +792,9 @@ hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v
   // work-group order (see the kernel): slot fastest for one sequence, key head
   // fastest for batches
   const bool head_fastest = n_max > 1;
-  dim3 grid(nt_max, h);
-  if (head_fastest) {
-    const int64_t blocks = static_cast<int64_t>(nt_max) * h;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    grid = dim3(static_cast<uint32_t>(blocks));
-  }
+  const int64_t blocks = static_cast<int64_t>(nt_max) * h;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(blocks));
 #define GDN_LAUNCH_INTRA(F32, TAPS)                                                             \
   hipExtLaunchKernelGGL((intra_kernel<F32, TAPS>), grid, dim3(kThreads), 0, stream, ev.start,   \
                         ev.stop, 0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, \
