@@ -94,9 +94,9 @@ def oracle_inputs_f64(wl):
                                128, 128)
 
 
-def oracle_lanes(wl, lanes, qkv64=None):
-    """fp64 recurrence on the given (sequence, value head) lanes only.
-    Returns {lane: (o [len, 128], hT [128, 128])}."""
+def oracle_lanes(wl, lanes, qkv64=None, scale=None):
+    """fp64 recurrence on the given (sequence, value head) lanes only (output
+    scale 1/sqrt(128) unless given). Returns {lane: (o [len, 128], hT [128, 128])}."""
     cu = wl.cu_seqlens
     HG = wl.Hv // wl.H
     out = {}
@@ -114,7 +114,7 @@ def oracle_lanes(wl, lanes, qkv64=None):
             q, k, v = qkv64[0][a:e, h:h + 1], qkv64[1][a:e, h:h + 1], qkv64[2][a:e, hv:hv + 1]
         s0 = None if h0 is None else h0[s:s + 1, hv:hv + 1]
         o, hT = recurrent.gdn_recurrent(q, k, v, g[a:e, hv:hv + 1], b[a:e, hv:hv + 1],
-                                        np.array([0, e - a], np.int32), h0=s0)
+                                        np.array([0, e - a], np.int32), h0=s0, scale=scale)
         out[(s, hv)] = (o[:, 0], hT[0, 0])
     return out
 

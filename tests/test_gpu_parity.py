@@ -70,9 +70,13 @@ def test_chunk_index_table_bit_exact(case):
 # front: conv + SiLU + L2 norm (fp32) against the fp64 front
 # --------------------------------------------------------------------------- #
 
-def test_front_small_varlen():
-    wl = workloads.make_custom([5, 0, 130, 1, 64], 2, 4, seed=11, front=True, t_max=230, n_max=6)
-    log("front small varlen")
+@pytest.mark.parametrize("d_conv", range(1, 9))
+def test_front_small_varlen(d_conv):
+    """Every tap count the standalone front accepts (one kernel instance
+    each), on sequences shorter than the conv window and an empty one."""
+    wl = workloads.make_custom([5, 0, 130, 1, 64], 2, 4, seed=11 + d_conv, front=True,
+                               d_conv=d_conv, t_max=230, n_max=6)
+    log(f"front small varlen, d_conv={d_conv}")
     d = device_inputs(wl)
     q, k, v = run_front(wl, d)
     torch.cuda.synchronize()
@@ -206,7 +210,7 @@ def test_forward_front_small_every_lane():
 # front fused into stage 1 (gdn_chunk_fwd_conv)
 # --------------------------------------------------------------------------- #
 
-@pytest.mark.parametrize("d_conv", [4, 2])
+@pytest.mark.parametrize("d_conv", [1, 2, 3, 4])
 def test_fused_front_equals_front_then_forward_bitwise(d_conv):
     """The fused front computes q, k, v with the standalone front's fp32
     arithmetic, so o and the final states are bit for bit those of
@@ -506,6 +510,38 @@ def test_gqa_group_sizes_every_lane(H, Hv, dtype):
         torch.cuda.synchronize()
         eo, es = lane_errors(wl, o, hT, ref)
         log(f"  H={H} Hv={Hv} {dtype} {tag}: o err {eo:.3e}  S err {es:.3e}")
+        assert eo <= O_TOL and es <= S_TOL
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_caller_output_scale_every_lane(dtype):
+    """A caller-set output scale (not 1/sqrt(dk)) multiplies both parts of o,
+    the inter-chunk read and the masked intra-chunk attention, and leaves the
+    state alone: one and two segments, two column tiles and the token-serial
+    kernel, every lane against the oracle at that scale."""
+    lengths = [200, 0, 64, 131]
+    scale = 0.37
+    wl = workloads.make_custom(lengths, 2, 4, seed=41, dtype=dtype, h0_sigma=0.02,
+                               n_max=len(lengths) + 1, t_max=sum(lengths) + 5)
+    d = device_inputs(wl)
+    ref = oracle_lanes(wl, _all_lanes(wl), scale=scale)
+    for tag, segments, tiles in (("one segment", 1, 1), ("two segments", 2, 0),
+                                 ("two tiles", 1, 2), ("token-serial", 1, 0)):
+        cfg = gdn.make_config(wl.t_max, wl.n_max, 2, 4, dtype, scale=scale, segments=segments,
+                              tiles=tiles)
+        o = torch.full((wl.t_max, 4, 128), float("nan"), dtype=torch.float32, device=DEV)
+        hT = torch.full((wl.n_max, 4, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+        log(f"output scale {scale}, {dtype}, {tag}")
+        if tag == "token-serial":
+            gdn.gdn_recurrent_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"],
+                                  o, hT)
+        else:
+            ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+            gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"],
+                              None, o, hT, ws)
+        torch.cuda.synchronize()
+        eo, es = lane_errors(wl, o, hT, ref)
+        log(f"  o err {eo:.3e}  S err {es:.3e}")
         assert eo <= O_TOL and es <= S_TOL
 
 
