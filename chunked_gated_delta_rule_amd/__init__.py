@@ -30,6 +30,7 @@ __all__ = [
     "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "GDN_FUSED_INDEX_MAX_SEQS",
     "gdn_chunk_fwd_conv", "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd",
     "gdn_recurrent_fwd_timed", "recurrent_gated_delta_rule", "GDN_SEGMENT_MIN_TOKENS", "GDN_FOUR_TILE_MIN_TOKENS",
+    "GDN_T_MAX_LIMIT", "GDN_N_MAX_LIMIT",
 ]
 
 GDN_BF16 = 0
@@ -37,6 +38,8 @@ GDN_F32 = 1
 GDN_FUSED_INDEX_MAX_SEQS = 256  # include/gdn.h
 GDN_SEGMENT_MIN_TOKENS = 2048  # include/gdn.h
 GDN_FOUR_TILE_MIN_TOKENS = 384  # include/gdn.h
+GDN_T_MAX_LIMIT = 1 << 24  # include/gdn.h
+GDN_N_MAX_LIMIT = 16384  # include/gdn.h
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
            3: "GDN_ERR_CAPACITY", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_layout", "gdn_workspace_size",

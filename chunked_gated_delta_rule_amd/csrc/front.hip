@@ -33,9 +33,12 @@ __global__ __launch_bounds__(kThreads) void front_kernel(
     const int32_t *__restrict__ cu, int n_max, int t_max, int h, int hv,
     float *__restrict__ q, float *__restrict__ k, float *__restrict__ v) {
   const int channels = (2 * h + hv) * kD;
-  const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
+  // flat work-group number -> (channel block, token block), channels fastest
+  const int cblocks = (channels / 8 + kThreads - 1) / kThreads;
+  const int wg = flat_block();
+  const int c0 = (wg % cblocks * kThreads + threadIdx.x) * 8;
   const bool active = c0 < channels;  // inactive lanes still join the butterfly
-  const int t_begin = blockIdx.y * kTokens;
+  const int t_begin = wg / cblocks * kTokens;
   const int t_total = cu_at(cu, n_max, t_max);
   if (t_begin >= t_total) return;
   const int t_end = min(t_begin + kTokens, t_total);
@@ -118,8 +121,11 @@ hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
                         KernelEvents ev) {
   if (d_conv < 1 || d_conv > kMaxTaps) return hipErrorInvalidValue;
   const int channels = (2 * h + hv) * kD;
-  const dim3 grid((channels / 8 + kThreads - 1) / kThreads, (t_max + kTokens - 1) / kTokens);
-  if (grid.y == 0) return hipSuccess;
+  const int64_t cblocks = (channels / 8 + kThreads - 1) / kThreads;
+  const int64_t tblocks = (static_cast<int64_t>(t_max) + kTokens - 1) / kTokens;
+  if (tblocks == 0) return hipSuccess;
+  dim3 grid;
+  if (!flat_grid(cblocks * tblocks, kThreads, grid)) return hipErrorInvalidValue;
   const uint16_t *x = static_cast<const uint16_t *>(qkv);
   const uint16_t *w = static_cast<const uint16_t *>(conv_w);
 #define GDN_LAUNCH_FRONT(TAPS)                                                                   \

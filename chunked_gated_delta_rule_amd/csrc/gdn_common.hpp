@@ -293,4 +293,10 @@ __device__ __forceinline__ int2 locate_chunk(const int32_t *__restrict__ cu, int
   return make_int2(-1, -1);
 }
 
+// Flat work-group number of a grid made by flat_grid (rows of gridDim.x);
+// numbers past the requested count occur in the last row only.
+__device__ __forceinline__ int flat_block() {
+  return static_cast<int>(blockIdx.x + gridDim.x * blockIdx.y);
+}
+
 }  // namespace gdn

@@ -52,6 +52,21 @@ struct ConvIn {
 };
 
 // Start / end events recorded by one dispatch (both may be null).
+// Grid of `blocks` work-groups of `threads` threads, numbered flat (see
+// flat_block): the dispatch packet takes each grid dimension in work-items as
+// a 32-bit number, so one row holds at most 2^31 - 1 work-items (a multiple of
+// 64 work-groups, which keeps work-group i on XCD i mod 8) and larger grids
+// take further rows (at most 65535). Returns false when that is not enough.
+inline bool flat_grid(int64_t blocks, int threads, dim3 &grid) {
+  const int64_t row = (0x7fffffffLL / threads) / 64 * 64;
+  const int64_t x = blocks < row ? blocks : row;
+  const int64_t y = x > 0 ? (blocks + x - 1) / x : 0;
+  // every flat number, the last row's surplus included, must fit an int
+  if (blocks < 0 || x * y > 0x7fffffffLL || y > 65535) return false;
+  grid = dim3(static_cast<uint32_t>(x), static_cast<uint32_t>(y));
+  return true;
+}
+
 struct KernelEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;

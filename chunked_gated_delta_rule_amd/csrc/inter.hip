@@ -607,8 +607,9 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   const int HG = Hv / H;
   const int members = HG * kWgSlices;
   const int one_walk = (n_max * H + kXcds - 1) / kXcds * kXcds * members;
-  const int role = kS == 2 && static_cast<int>(blockIdx.x) >= one_walk ? 1 : 0;
-  const int b = static_cast<int>(blockIdx.x) - role * one_walk;
+  const int wg = flat_block();
+  const int role = kS == 2 && wg >= one_walk ? 1 : 0;
+  const int b = wg - role * one_walk;
   const int xcd = b % kXcds;
   const int wslot = b / kXcds;
   const int group = (wslot / members) * kXcds + xcd;  // (rank of the sequence, key head)
@@ -675,7 +676,7 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
   __shared__ __attribute__((aligned(16))) __bf16 ahi[kD * kLdFix];
   __shared__ __attribute__((aligned(16))) __bf16 alo[kD * kLdFix];
   const int per = nbo + 1;
-  const int pair = blockIdx.x / per, blk = blockIdx.x % per;
+  const int pair = flat_block() / per, blk = flat_block() % per;
   const int s = pair / Hv, hv = pair % Hv;
   if (s >= n_max) return;
   const int bos = cu_at(cu, s, t_max), eos = cu_end(cu, s, bos, t_max);
@@ -776,15 +777,18 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
 }
 
 template <bool kF32In, int kDepth, int kS, int kNV = 1>
-void launch_walk(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
-                 int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
-                 const SegScratch &seg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  const int members = (hv / h) * (kSlices / kNV);
-  const int rounds = (n_max * h + kXcds - 1) / kXcds;
-  const dim3 grid(kS * rounds * kXcds * members);
-  hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS, kNV>), grid,
-                        dim3(kInterThreads<kF32In, kDepth, kS, kNV>), 0, stream, start, stop, 0, in,
-                        h0, cu, o, hT, n_max, h, hv, t_max, nt, seg);
+hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
+                       int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
+                       const SegScratch &seg, hipStream_t stream, hipEvent_t start,
+                       hipEvent_t stop) {
+  const int64_t members = (hv / h) * (kSlices / kNV);
+  const int64_t rounds = (static_cast<int64_t>(n_max) * h + kXcds - 1) / kXcds;
+  constexpr int kThr = kInterThreads<kF32In, kDepth, kS, kNV>;
+  dim3 grid;
+  if (!flat_grid(kS * rounds * kXcds * members, kThr, grid)) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS, kNV>), grid, dim3(kThr), 0, stream,
+                        start, stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt, seg);
+  return hipGetLastError();
 }
 
 template <bool kF32In>
@@ -795,31 +799,29 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
   const int one_walk = inter_one_walk_grid(n_max, h, hv);
   if (segments != 2) {
     if (tiles == 4)
-      launch_walk<kF32In, 1, 1, 4>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
-                                   ev.start, ev.stop);
-    else if (tiles == 2)
-      launch_walk<kF32In, 1, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
-                                   ev.start, ev.stop);
-    else
-      launch_walk<kF32In, kDepthSingle, 1>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
-                                           ev.start, ev.stop);
-    return hipGetLastError();
+      return launch_walk<kF32In, 1, 1, 4>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                                          ev.start, ev.stop);
+    if (tiles == 2)
+      return launch_walk<kF32In, 1, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+                                          ev.start, ev.stop);
+    return launch_walk<kF32In, kDepthSingle, 1>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
+                                                stream, ev.start, ev.stop);
   }
-  if (2 * one_walk <= cu_count())
-    launch_walk<kF32In, kDepthSeg, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
+  const hipError_t e =
+      2 * one_walk <= cu_count()
+          ? launch_walk<kF32In, kDepthSeg, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
+                                              stream, ev.start, nullptr)
+          : launch_walk<kF32In, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
                                       ev.start, nullptr);
-  else
-    launch_walk<kF32In, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream, ev.start,
-                              nullptr);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // work-groups of 128 output rows over the at most floor(ceil(t_max / 64) / 2)
   // chunks of segment B, plus one final-state work-group, per (sequence,
   // value head)
   const int nbo = ((t_max + kC - 1) / kC / 2 + 1) / 2;
-  const int64_t blocks = static_cast<int64_t>(n_max) * hv * (nbo + 1);
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipExtLaunchKernelGGL(segfix_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kFixThreads), 0,
+  dim3 grid;
+  if (!flat_grid(static_cast<int64_t>(n_max) * hv * (nbo + 1), kFixThreads, grid))
+    return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL(segfix_kernel, grid, dim3(kFixThreads), 0,
                         stream, nullptr, ev.stop, 0, cu, o, hT, seg, n_max, hv, t_max, nbo);
   return hipGetLastError();
 }

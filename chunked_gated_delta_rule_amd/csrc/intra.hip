@@ -347,13 +347,15 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   // flight spread over the whole sequence.
   // a one-dimensional grid of nt * H work-groups (for batches it measured
   // faster than a two-dimensional (H, nt) grid in the same order)
+  const int wg = flat_block();
+  if (wg >= nt * H) return;  // past the grid's count (last row)
   int item, h;
   if (!head_fastest) {
-    item = static_cast<int>(blockIdx.x % static_cast<uint32_t>(nt));
-    h = static_cast<int>(blockIdx.x / static_cast<uint32_t>(nt));
+    item = wg % nt;
+    h = wg / nt;
   } else {
-    item = static_cast<int>(blockIdx.x / static_cast<uint32_t>(H));
-    h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(H));
+    item = wg / H;
+    h = wg % H;
   }
   // this work-group's chunk: from the caller's table, or located from
   // cu_seqlens here (every wave computes it; the key-head-0 work-groups also
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   }
   // the work-group of slot 0, key head 0 ranks the sequences for stage 2,
   // after its own chunk (its LDS is then free) or here if it has none
-  const bool ranks = out.order && blockIdx.x == 0;
+  const bool ranks = out.order && wg == 0;
   const int bos = ent.x < 0 ? 0 : cu_at(cu, ent.x, t_max);
   const int t0 = bos + max(ent.y, 0) * kC;
   const int L = ent.x < 0 ? 0 : min(kC, cu_end(cu, ent.x, bos, t_max) - t0);
@@ -792,9 +794,8 @@ hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v
   // work-group order (see the kernel): slot fastest for one sequence, key head
   // fastest for batches
   const bool head_fastest = n_max > 1;
-  const int64_t blocks = static_cast<int64_t>(nt_max) * h;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(blocks));
+  dim3 grid;
+  if (!flat_grid(static_cast<int64_t>(nt_max) * h, kThreads, grid)) return hipErrorInvalidValue;
 #define GDN_LAUNCH_INTRA(F32, TAPS)                                                             \
   hipExtLaunchKernelGGL((intra_kernel<F32, TAPS>), grid, dim3(kThreads), 0, stream, ev.start,   \
                         ev.stop, 0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, \

@@ -85,10 +85,11 @@ template <bool kF32In>
 __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     const void *__restrict__ qin, const void *__restrict__ kin, const void *__restrict__ vin,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ h0,
-    const int32_t *__restrict__ cu, float *__restrict__ o, float *__restrict__ hT, int H, int Hv,
-    int t_max, float scale) {
+    const int32_t *__restrict__ cu, float *__restrict__ o, float *__restrict__ hT, int n_max, int H,
+    int Hv, int t_max, float scale) {
   constexpr int kEl = kF32In ? 4 : 2;
-  const int s = blockIdx.x / Hv, hv = blockIdx.x % Hv;
+  const int s = flat_block() / Hv, hv = flat_block() % Hv;
+  if (s >= n_max) return;  // past the grid's count (last row)
   const int h = hv / (Hv / H);
   const int tid = threadIdx.x;
   const int v0 = 4 * (tid >> 3), d4 = 4 * (tid & 7);
@@ -199,14 +200,14 @@ hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const voi
                             KernelEvents ev) {
   const int64_t blocks = static_cast<int64_t>(n_max) * hv;
   if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(blocks));
+  dim3 grid;
+  if (!flat_grid(blocks, kRecThreads, grid)) return hipErrorInvalidValue;
   if (f32_in)
     hipExtLaunchKernelGGL((recurrent_kernel<true>), grid, dim3(kRecThreads), 0, stream, ev.start,
-                          ev.stop, 0, q, k, v, g, beta, h0, cu_seqlens, o, hT, h, hv, t_max, scale);
+                          ev.stop, 0, q, k, v, g, beta, h0, cu_seqlens, o, hT, n_max, h, hv, t_max, scale);
   else
     hipExtLaunchKernelGGL((recurrent_kernel<false>), grid, dim3(kRecThreads), 0, stream, ev.start,
-                          ev.stop, 0, q, k, v, g, beta, h0, cu_seqlens, o, hT, h, hv, t_max, scale);
+                          ev.stop, 0, q, k, v, g, beta, h0, cu_seqlens, o, hT, n_max, h, hv, t_max, scale);
   return hipGetLastError();
 }
 

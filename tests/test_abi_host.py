@@ -217,6 +217,10 @@ def test_header_constants_match_binding():
     assert m and int(m.group(1)) == gdn.GDN_SEGMENT_MIN_TOKENS
     m = re.search(r"#define GDN_FOUR_TILE_MIN_TOKENS (\d+)", text)
     assert m and int(m.group(1)) == gdn.GDN_FOUR_TILE_MIN_TOKENS
+    m = re.search(r"#define GDN_T_MAX_LIMIT \(1 << (\d+)\)", text)
+    assert m and 1 << int(m.group(1)) == gdn.GDN_T_MAX_LIMIT
+    m = re.search(r"#define GDN_N_MAX_LIMIT (\d+)", text)
+    assert m and int(m.group(1)) == gdn.GDN_N_MAX_LIMIT
 
 
 def test_fused_front_entry_point_host_errors(lib):

@@ -710,3 +710,52 @@ def test_more_chunk_slots_than_a_grid_dimension_bitwise():
     assert torch.equal(o[:300], o1[:300]) and torch.equal(hT, h1)
     del big, ws, o
     torch.cuda.empty_cache()
+
+
+def test_maximum_capacities_with_sequences_at_the_end_of_the_token_range():
+    """t_max and n_max at their limits with the checked sequences at the very
+    end of the token range, so that token rows, workspace slots and states sit
+    at the largest offsets the limits allow (byte offsets far beyond 2^31): a
+    zero-input filler sequence takes the first 2^24 - 277 tokens, two ragged
+    sequences end at row t_max, and the other 16381 sequences are empty. The
+    automatic launch shape and the two-segment walk, each against the oracle on
+    every tail lane; the filler's output is zero and every empty sequence keeps
+    its initial state bit for bit."""
+    t_max, n_max = gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT
+    tail = workloads.make_custom([200, 77], 1, 1, seed=131, h0_sigma=0.02)
+    T_tail = tail.n_tokens
+    F = t_max - T_tail
+    log(f"maximum capacities: t_max={t_max} n_max={n_max} filler={F} tail={T_tail}")
+    cu = np.full(n_max + 1, t_max, np.int64)
+    cu[0], cu[1], cu[2] = 0, F, F + 200
+    cu_d = torch.from_numpy(cu.astype(np.int32)).to(DEV)
+    d = device_inputs(tail)
+    x = {}
+    for name in ("q", "k", "v", "g", "beta"):
+        src = d[name]
+        x[name] = torch.zeros((t_max,) + tuple(src.shape[1:]), dtype=src.dtype, device=DEV)
+        x[name][F:] = src
+    h0 = torch.zeros((n_max, 1, 128, 128), dtype=torch.float32, device=DEV)
+    h0[1:3] = d["h0"]
+    h0[3:] = 0.25  # the empty sequences must hand these back unchanged
+    ref = oracle_lanes(tail, [(0, 0), (1, 0)])
+    o = torch.empty((t_max, 1, 128), dtype=torch.float32, device=DEV)
+    hT = torch.empty((n_max, 1, 128, 128), dtype=torch.float32, device=DEV)
+    for segments in (0, 2):
+        cfg = gdn.make_config(t_max, n_max, 1, 1, tail.qkv_dtype, segments=segments)
+        log(f"  segments={segments}: workspace {gdn.gdn_workspace_size(cfg) / 2**30:.1f} GiB")
+        ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+        o.fill_(float("nan"))
+        hT.fill_(float("nan"))
+        gdn.gdn_chunk_fwd(cfg, x["q"], x["k"], x["v"], x["g"], x["beta"], h0, cu_d, None, o, hT,
+                          ws)
+        torch.cuda.synchronize()
+        del ws
+        torch.cuda.empty_cache()
+        eo, es = lane_errors(tail, o[F:], hT[1:3], ref)
+        log(f"    tail: o err {eo:.3e}  S err {es:.3e}")
+        assert eo <= O_TOL and es <= S_TOL
+        assert (o[:F] == 0).all() and (hT[0] == 0).all()
+        assert torch.equal(hT[3:], h0[3:])
+    del x, o, hT, h0
+    torch.cuda.empty_cache()
