@@ -759,3 +759,54 @@ def test_maximum_capacities_with_sequences_at_the_end_of_the_token_range():
         assert torch.equal(hT[3:], h0[3:])
     del x, o, hT, h0
     torch.cuda.empty_cache()
+
+
+def test_front_and_fused_front_at_the_maximum_token_capacity():
+    """The standalone front (its token blocks then number 2^18) and the
+    forward with the front fused into stage 1 at t_max = 2^24, with the
+    checked sequences ending at row t_max after a zero-input filler sequence:
+    the tail against the fp64 front and recurrence, the filler's rows zero."""
+    t_max = gdn.GDN_T_MAX_LIMIT
+    tail = workloads.make_custom([200, 77], 1, 1, seed=137, front=True, d_conv=4, h0_sigma=0.02)
+    F = t_max - tail.n_tokens
+    n_max = 4
+    log(f"front at maximum capacity: t_max={t_max} filler={F}")
+    cu = np.full(n_max + 1, t_max, np.int64)
+    cu[0], cu[1], cu[2] = 0, F, F + 200
+    cu_d = torch.from_numpy(cu.astype(np.int32)).to(DEV)
+    d = device_inputs(tail)
+    qkv = torch.zeros((t_max, d["qkv"].shape[1]), dtype=d["qkv"].dtype, device=DEV)
+    qkv[F:] = d["qkv"]
+    cfg = gdn.make_config(t_max, n_max, 1, 1, torch.float32)
+    q = torch.full((t_max, 1, 128), float("nan"), dtype=torch.float32, device=DEV)
+    k = torch.full_like(q, float("nan"))
+    v = torch.full_like(q, float("nan"))
+    gdn.gdn_front_conv_silu_l2(cfg, qkv, d["conv_w"], 4, cu_d, q, k, v)
+    torch.cuda.synchronize()
+    ref = recurrent.gdn_front(tail.f64("qkv"), tail.f64("conv_w"), tail.cu_seqlens, 1, 1, 128, 128)
+    for got, want in zip((q, k, v), ref):
+        g64 = got[F:].cpu().double().numpy()
+        assert np.max(np.abs(g64 - want)) / np.max(np.abs(want)) < 1e-5
+        assert (got[:F] == 0).all()
+    del q, k, v
+    torch.cuda.empty_cache()
+    log("  fused front forward")
+    x = {}
+    for name in ("g", "beta"):
+        x[name] = torch.zeros((t_max,) + tuple(d[name].shape[1:]), dtype=d[name].dtype, device=DEV)
+        x[name][F:] = d[name]
+    h0 = torch.zeros((n_max, 1, 128, 128), dtype=torch.float32, device=DEV)
+    h0[1:3] = d["h0"]
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    o = torch.full((t_max, 1, 128), float("nan"), dtype=torch.float32, device=DEV)
+    hT = torch.full((n_max, 1, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+    gdn.gdn_chunk_fwd_conv(cfg, qkv, d["conv_w"], 4, x["g"], x["beta"], h0, cu_d, None, o, hT, ws)
+    torch.cuda.synchronize()
+    del ws
+    lanes = oracle_lanes(tail, [(0, 0), (1, 0)], qkv64=oracle_inputs_f64(tail))
+    eo, es = lane_errors(tail, o[F:], hT[1:3], lanes)
+    log(f"    tail: o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+    assert (o[:F] == 0).all() and (hT[0] == 0).all()
+    del qkv, x, o, hT, h0
+    torch.cuda.empty_cache()
