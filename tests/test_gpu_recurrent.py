@@ -121,3 +121,40 @@ def test_recurrent_matches_chunked_forward_within_tolerance():
     es = float((h_r - h_c).norm() / h_r.norm())
     log(f"  serial vs chunked: o {eo:.3e}  S {es:.3e}")
     assert eo <= O_TOL and es <= S_TOL
+
+
+def test_recurrent_at_both_capacity_limits_with_sequences_at_the_end():
+    """t_max = 2^24 and n_max = 16384 (a grid of n_max * Hv work-groups) with
+    the checked sequences as the last two, ending at row t_max: 16382
+    zero-input sequences of about 1024 tokens come first. The tail against the
+    oracle; the zero-input sequences give zero output and hand back their
+    initial states bit for bit."""
+    t_max, n_max = gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT
+    tail = workloads.make_custom([200, 77], 1, 1, seed=139, h0_sigma=0.02)
+    F = t_max - tail.n_tokens
+    nf = n_max - 2
+    cu = np.empty(n_max + 1, np.int64)
+    cu[:nf + 1] = np.arange(nf + 1, dtype=np.int64) * F // nf
+    cu[nf + 1], cu[nf + 2] = F + 200, t_max
+    log(f"token-serial at the capacity limits: t_max={t_max} n_max={n_max} filler={F}")
+    d = device_inputs(tail)
+    x = {}
+    for name in ("q", "k", "v", "g", "beta"):
+        src = d[name]
+        x[name] = torch.zeros((t_max,) + tuple(src.shape[1:]), dtype=src.dtype, device=DEV)
+        x[name][F:] = src
+    h0 = torch.full((n_max, 1, 128, 128), 0.25, dtype=torch.float32, device=DEV)
+    h0[nf:] = d["h0"]
+    cfg = gdn.make_config(t_max, n_max, 1, 1, tail.qkv_dtype)
+    o = torch.full((t_max, 1, 128), float("nan"), dtype=torch.float32, device=DEV)
+    hT = torch.full((n_max, 1, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+    gdn.gdn_recurrent_fwd(cfg, x["q"], x["k"], x["v"], x["g"], x["beta"], h0,
+                          torch.from_numpy(cu.astype(np.int32)).to(DEV), o, hT)
+    torch.cuda.synchronize()
+    ref = oracle_lanes(tail, [(0, 0), (1, 0)])
+    eo, es = lane_errors(tail, o[F:], hT[nf:], ref)
+    log(f"  tail: o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= SERIAL_TOL and es <= SERIAL_TOL
+    assert (o[:F] == 0).all() and torch.equal(hT[:nf], h0[:nf])
+    del x, o, hT, h0
+    torch.cuda.empty_cache()
