@@ -87,7 +87,11 @@ typedef struct {
 /* Token capacity from which the automatic choice considers two segments. */
 #define GDN_SEGMENT_MIN_TOKENS 2048
 
-/* Largest valid gdn_config.t_max / n_max. */
+/* Largest valid gdn_config.t_max / n_max. Each kernel takes at most
+ * 2^31 - 1 work-groups per launch; a valid config whose grid needs more (only
+ * near all three limits at once, e.g. two segments at t_max = 2^24, n_max =
+ * 16384 and hv = 4096) makes the call return GDN_ERR_HIP, with the outputs
+ * unspecified. */
 #define GDN_T_MAX_LIMIT (1 << 24)
 #define GDN_N_MAX_LIMIT 16384
 
