@@ -88,10 +88,12 @@ typedef struct {
 #define GDN_SEGMENT_MIN_TOKENS 2048
 
 /* Largest valid gdn_config.t_max / n_max. Each kernel takes at most
- * 2^31 - 1 work-groups per launch; a valid config whose grid needs more (only
- * near all three limits at once, e.g. two segments at t_max = 2^24, n_max =
- * 16384 and hv = 4096) makes the call return GDN_ERR_HIP, with the outputs
- * unspecified. */
+ * 2^31 - 1 work-groups per launch. Within these limits only the fix-up of the
+ * two-segment walk can need more: about n_max * hv * t_max / 256 work-groups,
+ * so with segments = 2 and n_max * hv * t_max above about 2^39 the call
+ * returns GDN_ERR_HIP, with the outputs unspecified. The automatic choice
+ * takes two segments only for grids that fill at most half of the device,
+ * far inside that bound. */
 #define GDN_T_MAX_LIMIT (1 << 24)
 #define GDN_N_MAX_LIMIT 16384
 
