@@ -49,18 +49,20 @@ SOLVE_FLOP = 83328           # 64x64 unit-lower inverse: 41,664 multiply-adds
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
-def algorithmic_work(wl, nt, qkv_bytes, fused_front=False):
+def algorithmic_work(wl, nt, qkv_bytes, fused_front=False, u_bytes=4):
     """Bytes and flops each stage must move / perform (counted once; partial
     chunks counted as whole 64-token chunks for flops). w crosses between the
-    stages in 2 bytes and u in 3 (24-bit floats) per value. With the front
-    fused into stage 1, that stage reads the pre-conv bf16 q|k|v channels
-    instead of k and v."""
+    stages in 2 bytes per value and u in `u_bytes`: 4 (fp32) is the model the
+    headline roofline uses; this library stores u in 3 (24-bit floats), which
+    gives the smaller, stored-byte figure. With the front fused into stage 1,
+    that stage reads the pre-conv bf16 q|k|v channels instead of k and v."""
     T, H, Hv, D = wl.n_tokens, wl.H, wl.Hv, 128
     HG = Hv // H
     n_state = len(wl.cu_seqlens) - 1
     stage1_in = (2 * H + Hv) * D * 2 if fused_front else H * D * qkv_bytes + Hv * D * qkv_bytes
-    stage1_bytes = T * (stage1_in + Hv * 4 + Hv * 4 + Hv * D * 2 + Hv * D * 3)
-    stage2_bytes = T * (2 * H * D * qkv_bytes + Hv * D * 2 + Hv * D * 3 + Hv * 4 + Hv * D * 4)
+    stage1_bytes = T * (stage1_in + Hv * 4 + Hv * 4 + Hv * D * 2 + Hv * D * u_bytes)
+    stage2_bytes = T * (2 * H * D * qkv_bytes + Hv * D * 2 + Hv * D * u_bytes + Hv * 4 +
+                        Hv * D * 4)
     stage2_bytes += n_state * Hv * D * D * 4 * (2 if wl.h0 is not None else 1)
     stage1_flop = nt * H * (2 * 64 * 64 * D + HG * (2 * 2 * 64 * 64 * D + SOLVE_FLOP))
     stage2_flop = nt * Hv * (3 * 2 * 64 * D * D + 2 * 2 * 64 * 64 * D)
@@ -140,42 +142,75 @@ class HipEvents:
         self.made = []
 
 
-def cpu_baseline(wl, max_seconds=20.0, min_seconds=10.0):
-    """The fp64 oracle on this host's cores: whole workload if it fits the
-    budget, else the first key-head groups' lanes, scaled to tokens/s. Short
-    samples are repeated until about min_seconds of CPU work (at least 3
-    runs); the median run is reported."""
+def cpu_baseline(wl, max_seconds=20.0, min_seconds=10.0, one_thread_seconds=4.0):
+    """The fp64 oracle on this host's cores, over whole value-head lanes of
+    the workload (as many key-head groups as fit the budget), scaled to
+    tokens/s. For a workload with a front, the sample is its first sequence:
+    the fp64 front over every channel of it (timed on its own, not scaled),
+    then the lanes. Short samples are repeated until about min_seconds of CPU
+    work (at least 3 runs); the median run is reported. The same is then timed
+    on one thread, over fewer lanes."""
+    import numpy as np
     from oracle import recurrent
 
     threads = recurrent.threads()
-    q, k, v = wl.f64("q"), wl.f64("k"), wl.f64("v")
-    g, b, h0 = wl.f64("g"), wl.f64("beta"), wl.f64("h0")
     HG = wl.Hv // wl.H
+    front = wl.qkv is not None
+    g, b, h0 = wl.f64("g"), wl.f64("beta"), wl.f64("h0")
+    if front:
+        tokens = int(wl.cu_seqlens[1])
+        cu = np.array([0, tokens], np.int32)
+        x, w = wl.f64("qkv")[:tokens], wl.f64("conv_w")
+        g, b = g[:tokens], b[:tokens]
+        h0 = None if h0 is None else h0[:1]
+        q, k, v = recurrent.gdn_front(x, w, cu, wl.H, wl.Hv, 128, 128)
+    else:
+        tokens = wl.n_tokens
+        cu = wl.cu_seqlens
+        q, k, v = wl.f64("q"), wl.f64("k"), wl.f64("v")
 
-    def run(n_groups):  # the first n_groups key heads and their value heads
+    def run_front():
+        t0 = time.perf_counter()
+        recurrent.gdn_front(x, w, cu, wl.H, wl.Hv, 128, 128)
+        return time.perf_counter() - t0
+
+    def run_lanes(n_groups):  # the first n_groups key heads and their value heads
         hv_hi = n_groups * HG
         t0 = time.perf_counter()
         recurrent.gdn_recurrent(q[:, :n_groups], k[:, :n_groups], v[:, :hv_hi], g[:, :hv_hi],
-                                b[:, :hv_hi], wl.cu_seqlens,
-                                h0=None if h0 is None else h0[:, :hv_hi])
+                                b[:, :hv_hi], cu, h0=None if h0 is None else h0[:, :hv_hi])
         return time.perf_counter() - t0
 
-    lane_s = run(1)  # HG lanes side by side: about one lane's time
-    groups_per_round = max(1, threads // HG)
-    fit = int(max_seconds / 3 / max(lane_s, 1e-3)) * groups_per_round
-    n_groups = max(1, min(wl.H, fit))
-    times = [run(n_groups) for _ in range(3)]
-    while sum(times) < min_seconds and len(times) < 1000:
-        times.append(run(n_groups))
-    med = statistics.median(times)
-    lanes = n_groups * HG
-    full = med * (wl.Hv / lanes)
-    sample = (f"{'all' if lanes == wl.Hv else lanes} of {wl.Hv} value-head lanes x "
-              f"{wl.n_tokens} tokens, median of {len(times)} runs ({med:.3f} s each, "
-              f"{sum(times):.1f} s in all)"
-              + ("" if lanes == wl.Hv else ", scaled to all lanes"))
-    return {"value": wl.n_tokens / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample}
+    def measure(budget, floor):
+        lane_s = run_lanes(1)  # HG lanes side by side (about one lane's time on many threads)
+        per_round = max(1, recurrent.threads() // HG)
+        fit = int(budget / 3 / max(lane_s, 1e-3)) * per_round
+        n_groups = max(1, min(wl.H, fit))
+        times = [run_lanes(n_groups) for _ in range(3)]
+        while sum(times) < floor and len(times) < 1000:
+            times.append(run_lanes(n_groups))
+        med = statistics.median(times)
+        lanes = n_groups * HG
+        full = med * (wl.Hv / lanes)
+        what = (f"{'all' if lanes == wl.Hv else lanes} of {wl.Hv} value-head lanes x "
+                f"{tokens} tokens, median of {len(times)} runs ({med:.3f} s each, "
+                f"{sum(times):.1f} s in all)" + ("" if lanes == wl.Hv else ", scaled to all lanes"))
+        if front:
+            tf = [run_front() for _ in range(3)]
+            full += statistics.median(tf)
+            what = (f"sequence 0 of {wl.n_seqs}: the fp64 front over its {tokens} tokens "
+                    f"(median of 3 runs, {statistics.median(tf):.3f} s), then " + what)
+        return tokens / full, what
+
+    value, sample = measure(max_seconds, min_seconds)
+    recurrent.set_threads(1)
+    try:
+        value1, sample1 = measure(one_thread_seconds, one_thread_seconds / 2)
+    finally:
+        recurrent.set_threads(threads)
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample,
+            "one_thread": {"value": value1, "unit": "tokens/s", "cores": 1, "sample": sample1}}
 
 
 def main():
@@ -190,6 +225,10 @@ def main():
     ap.add_argument("--workload", type=int, default=1,
                     help="named workload 0..6 (5 and 6 time the token-serial kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-samples", type=int, default=10, metavar="N",
+                    help="after the timed region, time N more steps each preceded by a 1 GiB "
+                         "device write that evicts the last-level cache (reported apart from "
+                         "the headline value; 0 to skip)")
     ap.add_argument("--unfused-front", action="store_true",
                     help="front workload: run the standalone front, then the forward "
                          "(default: the front fused into stage 1)")
@@ -290,32 +329,60 @@ def main():
 
     pair = {"index": (0, 1), "intra": (2, 3), "inter": (4, 5), "front": (6, 7),
             "recurrent": (0, 1)}
-    per_stage_ms = {name: statistics.fmean(hip.ms(ev[pair[name][0]], ev[pair[name][1]])
-                                           for ev in events)
-                    for name in stages}
+
+    def stage_ms(evs):
+        return {name: statistics.fmean(hip.ms(ev[pair[name][0]], ev[pair[name][1]]) for ev in evs)
+                for name in stages}
+
+    per_stage_ms = stage_ms(events)
+
+    # Cold last-level cache (outside the timed region and the headline value):
+    # a 1 GiB device write before each sampled step evicts the 256 MB MALL, so
+    # the step's inputs and intermediates come from HBM.
+    cold = None
+    if args.cold_samples > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold_events = [hip.create(8 if has_front else 6) for _ in range(args.cold_samples)]
+        for ev in cold_events:
+            flush.fill_(1.0)
+            step(ev)
+        torch.cuda.synchronize()
+        del flush
+        cold_ms = stage_ms(cold_events)
+        cold = {"samples": args.cold_samples, "flush_bytes": 1 << 30,
+                **{f"{name}_us": round(cold_ms[name] * 1e3, 2) for name in stages}}
     hip.close()
     chunks = int(sum(-(-int(x) // 64) for x in np.diff(wl.cu_seqlens)))
-    work = algorithmic_work(wl, chunks, 4 if qkv_dtype == torch.float32 else 2, fused_front)
+    qkv_bytes = 4 if qkv_dtype == torch.float32 else 2
+    work = algorithmic_work(wl, chunks, qkv_bytes, fused_front)               # u at 4 bytes
+    work_u24 = algorithmic_work(wl, chunks, qkv_bytes, fused_front, u_bytes=3)  # as stored
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = wl.n_tokens
     detail = {}
     for name in stages:
         t_s = per_stage_ms[name] * 1e-3
         b, f = work[name]
+        b3 = work_u24[name][0]
         detail[name] = {"us": round(per_stage_ms[name] * 1e3, 2),
                         "alg_bytes": b, "alg_flop": f,
                         "hbm_frac": round(b / t_s / (HBM_PEAK_GBS * 1e9), 4) if b else None,
+                        "hbm_frac_u24": round(b3 / t_s / (HBM_PEAK_GBS * 1e9), 4) if b3 else None,
                         "mfma_frac": round(f / t_s / (BF16_PEAK_TFLOPS * 1e12), 4) if f else None}
+        if cold:
+            detail[name]["cold_us"] = cold[f"{name}_us"]
     dom = "recurrent" if serial else max(("intra", "inter"), key=lambda n: per_stage_ms[n])
     b_dom = work[dom][0]
     t_dom = per_stage_ms[dom] * 1e-3
     ach = b_dom / t_dom / 1e9
+    ach3 = work_u24[dom][0] / t_dom / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": counter_traffic(dom, wl.name)}
+                "traffic": counter_traffic(dom, wl.name),
+                "alg_bytes": b_dom, "u_bytes": 4,
+                "frac_u24": round(ach3 / HBM_PEAK_GBS, 4), "alg_bytes_u24": work_u24[dom][0]}
 
     cpu = None
-    if not args.no_cpu_baseline and not has_front:
+    if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl)
 
     line = {
@@ -339,6 +406,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": detail,
+        "cold_cache": cold,
     }
     print(json.dumps(line), flush=True)
 

@@ -114,10 +114,18 @@ def load_library():
     return lib
 
 
+_TORCH_DTYPE = {torch.bfloat16: GDN_BF16, torch.float32: GDN_F32}
+_GDN_DTYPE = {GDN_BF16: torch.bfloat16, GDN_F32: torch.float32}
+
+
 def make_config(t_max, n_max, h, hv, qkv_dtype=GDN_BF16, scale=0.0, o_dtype=GDN_F32,
                 dk=128, dv=128, chunk=64, segments=0, tiles=0) -> gdn_config:
+    """A gdn_config; qkv_dtype is GDN_BF16 / GDN_F32 or torch.bfloat16 /
+    torch.float32 (any other torch dtype raises ValueError)."""
     if isinstance(qkv_dtype, torch.dtype):
-        qkv_dtype = GDN_F32 if qkv_dtype == torch.float32 else GDN_BF16
+        if qkv_dtype not in _TORCH_DTYPE:
+            raise ValueError(f"q/k/v dtype {qkv_dtype}: bfloat16 or float32 expected")
+        qkv_dtype = _TORCH_DTYPE[qkv_dtype]
     return gdn_config(int(t_max), int(n_max), int(h), int(hv), int(dk), int(dv), int(chunk),
                       int(qkv_dtype), int(o_dtype), float(scale), int(segments), int(tiles))
 
@@ -134,6 +142,52 @@ def _ptr(x) -> Optional[int]:
             raise ValueError("contiguous tensor expected")
         return x.data_ptr()
     raise TypeError(type(x))
+
+
+def _need(x, name, elems, dtype, last=None):
+    """A tensor argument must have `dtype`, hold at least `elems` elements (the
+    kernels index that many from its start) and, when `last` is given and the
+    tensor has more than one dimension, end in a dimension of that size. Raw
+    pointers (ints) and None are passed through unchecked."""
+    if not isinstance(x, torch.Tensor):
+        return
+    if x.dtype != dtype:
+        raise ValueError(f"{name}: dtype {x.dtype}, {dtype} expected")
+    if x.numel() < elems:
+        raise ValueError(f"{name}: {x.numel()} elements, at least {elems} expected")
+    if last is not None and x.dim() > 1 and x.shape[-1] != last:
+        raise ValueError(f"{name}: last dimension {x.shape[-1]}, {last} expected")
+
+
+def _check_tensors(cfg, q=None, k=None, v=None, g=None, beta=None, h0=None, cu=None,
+                   table=None, o=None, hT=None):
+    """Dtypes and sizes of the tensor arguments against `cfg` (include/gdn.h layouts)."""
+    T, n, h, hv, dk, dv = cfg.t_max, cfg.n_max, cfg.h, cfg.hv, cfg.dk, cfg.dv
+    qdt = _GDN_DTYPE.get(cfg.qkv_dtype, torch.bfloat16)
+    _need(q, "q", T * h * dk, qdt, dk)
+    _need(k, "k", T * h * dk, qdt, dk)
+    _need(v, "v", T * hv * dv, qdt, dv)
+    _need(g, "g", T * hv, torch.float32)
+    _need(beta, "beta", T * hv, torch.float32)
+    _need(h0, "h0", n * hv * dv * dk, torch.float32, dk)
+    _need(hT, "hT", n * hv * dv * dk, torch.float32, dk)
+    _need(cu, "cu_seqlens", n + 1, torch.int32)
+    if table is not None:
+        _need(table, "chunk_indices", 2 * max(gdn_nt_max(T, n, cfg.chunk), 0), torch.int32)
+    _need(o, "o", T * hv * dv, torch.float32, dv)
+
+
+def _check_front(cfg, qkv, conv_w, d_conv):
+    C = (2 * cfg.h * cfg.dk + cfg.hv * cfg.dv)
+    _need(qkv, "qkv", cfg.t_max * C, torch.bfloat16, C)
+    _need(conv_w, "conv_w", C * int(d_conv), torch.bfloat16)
+
+
+def _check_ws(workspace, ws_bytes):
+    if isinstance(workspace, torch.Tensor) and \
+            workspace.numel() * workspace.element_size() < int(ws_bytes):
+        raise ValueError(f"workspace: {workspace.numel() * workspace.element_size()} bytes, "
+                         f"ws_bytes = {int(ws_bytes)}")
 
 
 def _stream(stream) -> Optional[int]:
@@ -165,12 +219,16 @@ def gdn_workspace_size(cfg: gdn_config) -> int:
 
 
 def gdn_build_chunk_indices(cfg, cu_seqlens, chunk_indices, stream=None):
+    _check_tensors(cfg, cu=cu_seqlens, table=chunk_indices)
     _check(load_library().gdn_build_chunk_indices(ctypes.byref(cfg), _ptr(cu_seqlens),
                                                   _ptr(chunk_indices), _stream(stream)),
            "gdn_build_chunk_indices")
 
 
 def gdn_front_conv_silu_l2(cfg, qkv, conv_w, d_conv, cu_seqlens, q, k, v, stream=None):
+    _check_front(cfg, qkv, conv_w, d_conv)
+    _check_tensors(make_config(cfg.t_max, cfg.n_max, cfg.h, cfg.hv, GDN_F32), q=q, k=k, v=v,
+                   cu=cu_seqlens)
     _check(load_library().gdn_front_conv_silu_l2(ctypes.byref(cfg), _ptr(qkv), _ptr(conv_w),
                                                  int(d_conv), _ptr(cu_seqlens), _ptr(q), _ptr(k),
                                                  _ptr(v), _stream(stream)),
@@ -193,6 +251,8 @@ def _ws_bytes(workspace, ws_bytes):
 
 def gdn_chunk_fwd_intra(cfg, q, k, v, g, beta, cu_seqlens, chunk_indices, workspace,
                         ws_bytes=None, stream=None):
+    _check_tensors(cfg, q=q, k=k, v=v, g=g, beta=beta, cu=cu_seqlens, table=chunk_indices)
+    _check_ws(workspace, _ws_bytes(workspace, ws_bytes))
     _check(load_library().gdn_chunk_fwd_intra(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
                                               _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                               _ptr(chunk_indices), _ptr(workspace),
@@ -201,6 +261,8 @@ def gdn_chunk_fwd_intra(cfg, q, k, v, g, beta, cu_seqlens, chunk_indices, worksp
 
 
 def gdn_chunk_fwd_inter(cfg, h0, cu_seqlens, workspace, o, hT, ws_bytes=None, stream=None):
+    _check_tensors(cfg, h0=h0, cu=cu_seqlens, o=o, hT=hT)
+    _check_ws(workspace, _ws_bytes(workspace, ws_bytes))
     _check(load_library().gdn_chunk_fwd_inter(ctypes.byref(cfg), _ptr(h0), _ptr(cu_seqlens),
                                               _ptr(workspace), _ws_bytes(workspace, ws_bytes),
                                               _ptr(o), _ptr(hT), _stream(stream)),
@@ -210,6 +272,8 @@ def gdn_chunk_fwd_inter(cfg, h0, cu_seqlens, workspace, o, hT, ws_bytes=None, st
 def gdn_chunk_fwd(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT, workspace,
                   ws_bytes=None, stream=None):
     ws_bytes = _ws_bytes(workspace, ws_bytes)
+    _check_tensors(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT)
+    _check_ws(workspace, ws_bytes)
     _check(load_library().gdn_chunk_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                         _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
                                         _ptr(chunk_indices), _ptr(o), _ptr(hT), _ptr(workspace),
@@ -222,6 +286,8 @@ def gdn_chunk_fwd_timed(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o,
     """gdn_chunk_fwd whose kernels record `events` (six raw hipEvent_t handles,
     ints) at their own start and end: table, intra, inter."""
     ws_bytes = _ws_bytes(workspace, ws_bytes)
+    _check_tensors(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT)
+    _check_ws(workspace, ws_bytes)
     if len(events) != 6:
         raise ValueError("six events expected")
     arr = (ctypes.c_void_p * 6)(*[int(e) for e in events])
@@ -235,6 +301,9 @@ def gdn_chunk_fwd_timed(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o,
 
 def gdn_front_conv_silu_l2_timed(cfg, qkv, conv_w, d_conv, cu_seqlens, q, k, v, ev_start, ev_stop,
                                  stream=None):
+    _check_front(cfg, qkv, conv_w, d_conv)
+    _check_tensors(make_config(cfg.t_max, cfg.n_max, cfg.h, cfg.hv, GDN_F32), q=q, k=k, v=v,
+                   cu=cu_seqlens)
     _check(load_library().gdn_front_conv_silu_l2_timed(
         ctypes.byref(cfg), _ptr(qkv), _ptr(conv_w), int(d_conv), _ptr(cu_seqlens), _ptr(q),
         _ptr(k), _ptr(v), _stream(stream), int(ev_start), int(ev_stop)),
@@ -244,6 +313,9 @@ def gdn_front_conv_silu_l2_timed(cfg, qkv, conv_w, d_conv, cu_seqlens, q, k, v, 
 def gdn_chunk_fwd_conv(cfg, qkv, conv_w, d_conv, g, beta, h0, cu_seqlens, chunk_indices, o, hT,
                        workspace, ws_bytes=None, stream=None):
     ws_bytes = _ws_bytes(workspace, ws_bytes)
+    _check_front(cfg, qkv, conv_w, d_conv)
+    _check_tensors(cfg, g=g, beta=beta, h0=h0, cu=cu_seqlens, table=chunk_indices, o=o, hT=hT)
+    _check_ws(workspace, ws_bytes)
     _check(load_library().gdn_chunk_fwd_conv(ctypes.byref(cfg), _ptr(qkv), _ptr(conv_w),
                                              int(d_conv), _ptr(g), _ptr(beta), _ptr(h0),
                                              _ptr(cu_seqlens), _ptr(chunk_indices), _ptr(o),
@@ -257,6 +329,9 @@ def gdn_chunk_fwd_conv_timed(cfg, qkv, conv_w, d_conv, g, beta, h0, cu_seqlens, 
     """gdn_chunk_fwd_conv whose kernels record `events` (six raw hipEvent_t
     handles): table, intra (with the fused front), inter."""
     ws_bytes = _ws_bytes(workspace, ws_bytes)
+    _check_front(cfg, qkv, conv_w, d_conv)
+    _check_tensors(cfg, g=g, beta=beta, h0=h0, cu=cu_seqlens, table=chunk_indices, o=o, hT=hT)
+    _check_ws(workspace, ws_bytes)
     if len(events) != 6:
         raise ValueError("six events expected")
     arr = (ctypes.c_void_p * 6)(*[int(e) for e in events])
@@ -269,6 +344,7 @@ def gdn_chunk_fwd_conv_timed(cfg, qkv, conv_w, d_conv, g, beta, h0, cu_seqlens, 
 
 
 def gdn_recurrent_fwd(cfg, q, k, v, g, beta, h0, cu_seqlens, o, hT, stream=None):
+    _check_tensors(cfg, q, k, v, g, beta, h0, cu_seqlens, None, o, hT)
     _check(load_library().gdn_recurrent_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                             _ptr(beta), _ptr(h0), _ptr(cu_seqlens), _ptr(o),
                                             _ptr(hT), _stream(stream)),
@@ -278,16 +354,27 @@ def gdn_recurrent_fwd(cfg, q, k, v, g, beta, h0, cu_seqlens, o, hT, stream=None)
 def gdn_recurrent_fwd_timed(cfg, q, k, v, g, beta, h0, cu_seqlens, o, hT, ev_start, ev_stop,
                             stream=None):
     """gdn_recurrent_fwd whose kernel records raw hipEvent_t handles at its start and end."""
+    _check_tensors(cfg, q, k, v, g, beta, h0, cu_seqlens, None, o, hT)
     _check(load_library().gdn_recurrent_fwd_timed(
         ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
         _ptr(cu_seqlens), _ptr(o), _ptr(hT), _stream(stream), int(ev_start), int(ev_stop)),
         "gdn_recurrent_fwd_timed")
 
 
+def _same_qkv_dtype(q, k, v):
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _TORCH_DTYPE:
+        raise ValueError(f"q, k, v must share one dtype in (bfloat16, float32): "
+                         f"{q.dtype}, {k.dtype}, {v.dtype}")
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
+        raise ValueError(f"q, k [T, H, 128] and v [T, Hv, 128] expected: {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+
+
 def recurrent_gated_delta_rule(q, k, v, g, beta, cu_seqlens, initial_state=None,
                                output_final_state=True, scale=None, n_max=None):
     """Allocate outputs with torch and run gdn_recurrent_fwd (token-serial decode /
     verify) on the current stream. Arguments as chunk_gated_delta_rule."""
+    _same_qkv_dtype(q, k, v)
     T, H, _ = q.shape
     Hv = v.shape[1]
     n = cu_seqlens.numel() - 1 if n_max is None else n_max
@@ -309,6 +396,7 @@ def chunk_gated_delta_rule(q, k, v, g, beta, cu_seqlens, initial_state=None,
     [N, Hv, 128, 128] fp32 or None. Returns (o [T, Hv, 128] fp32, final state
     or None).
     """
+    _same_qkv_dtype(q, k, v)
     T, H, _ = q.shape
     Hv = v.shape[1]
     n = cu_seqlens.numel() - 1 if n_max is None else n_max

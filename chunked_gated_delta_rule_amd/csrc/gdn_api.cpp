@@ -124,7 +124,10 @@ gdn::StageBuffers stage_buffers(const gdn_config *cfg, const gdn_workspace_layou
   b.uimg = reinterpret_cast<uint32_t *>(ws + l.uimg);
   b.pimg = reinterpret_cast<__bf16 *>(ws + l.pimg);
   b.gimg = reinterpret_cast<float *>(ws + l.gimg);
-  b.order = ranks_sequences(cfg) ? reinterpret_cast<int32_t *>(ws + l.order) : nullptr;
+  // stage 1 writes the ranking; with t_max == 0 it does not run, so stage 2
+  // must not read the (unwritten) table
+  b.order = ranks_sequences(cfg) && cfg->t_max > 0 ? reinterpret_cast<int32_t *>(ws + l.order)
+                                                   : nullptr;
   return b;
 }
 
@@ -140,6 +143,15 @@ float scale_of(const gdn_config *cfg) {
 }
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+// Every stage-2 grid of a (validated) config fits one launch; checked before
+// anything is queued, so a config past the limits returns without side effects.
+gdn_status check_inter_grids(const gdn_config *cfg) {
+  return gdn::inter_grids_fit(cfg->n_max, cfg->h, cfg->hv, cfg->t_max, segments_of(cfg),
+                              tiles_of(cfg))
+             ? GDN_OK
+             : GDN_ERR_CAPACITY;
+}
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -181,6 +193,8 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
       (chunk_indices && !aligned16(chunk_indices)) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
       (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return GDN_ERR_INVALID_ARG;
+  const gdn_status grids = check_inter_grids(cfg);
+  if (grids != GDN_OK) return grids;
   hipStream_t s = as_stream(stream);
   int32_t *ws_table = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + l.table);
   if (!chunk_indices && cfg->n_max > GDN_FUSED_INDEX_MAX_SEQS) {
@@ -308,6 +322,8 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
   const gdn_workspace_layout_t l = layout_of(cfg);
   const gdn_status ws = check_workspace(l, workspace, ws_bytes);
   if (ws != GDN_OK) return ws;
+  const gdn_status grids = check_inter_grids(cfg);
+  if (grids != GDN_OK) return grids;
   return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, stage_buffers(cfg, l, workspace), h0,
                                     cu_seqlens, cfg->n_max, cfg->h, cfg->hv, cfg->t_max,
                                     nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream),

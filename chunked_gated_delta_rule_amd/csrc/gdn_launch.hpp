@@ -108,6 +108,10 @@ struct SegScratch {
 // Compute units of the current device (queried once per device).
 int cu_count();
 
+// Whether every grid stage 2 launches for this shape (the walk, and with two
+// segments the fix-up) fits flat_grid; checked on the host before any launch.
+bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int segments, int tiles);
+
 // Work-groups of the one-walk stage-2 grid (one per (sequence, value head,
 // 16-column slice), rounded to whole XCD rounds).
 int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv);

@@ -66,6 +66,7 @@
 // gives them (longest first) when it ranks the batch, so the longest walks
 // start first. o rows of the one-tile, one-piece walk are stored streaming
 // (non-temporal).
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -776,6 +777,11 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
   }
 }
 
+// Work-groups of 128 output rows over the at most floor(ceil(t_max / 64) / 2)
+// chunks of segment B, per (sequence, value head); the fix-up grid has one
+// more (the final state) per pair.
+int fix_row_blocks(int32_t t_max) { return ((t_max + kC - 1) / kC / 2 + 1) / 2; }
+
 template <bool kF32In, int kDepth, int kS, int kNV = 1>
 hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
                        int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
@@ -807,6 +813,11 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
     return launch_walk<kF32In, kDepthSingle, 1>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
                                                 stream, ev.start, ev.stop);
   }
+  // the fix-up grid was checked on the host before anything was queued
+  const int nbo = fix_row_blocks(t_max);
+  dim3 grid;
+  if (!flat_grid(static_cast<int64_t>(n_max) * hv * (nbo + 1), kFixThreads, grid))
+    return hipErrorInvalidValue;
   const hipError_t e =
       2 * one_walk <= cu_count()
           ? launch_walk<kF32In, kDepthSeg, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
@@ -814,13 +825,6 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
           : launch_walk<kF32In, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
                                       ev.start, nullptr);
   if (e != hipSuccess) return e;
-  // work-groups of 128 output rows over the at most floor(ceil(t_max / 64) / 2)
-  // chunks of segment B, plus one final-state work-group, per (sequence,
-  // value head)
-  const int nbo = ((t_max + kC - 1) / kC / 2 + 1) / 2;
-  dim3 grid;
-  if (!flat_grid(static_cast<int64_t>(n_max) * hv * (nbo + 1), kFixThreads, grid))
-    return hipErrorInvalidValue;
   hipExtLaunchKernelGGL(segfix_kernel, grid, dim3(kFixThreads), 0,
                         stream, nullptr, ev.stop, 0, cu, o, hT, seg, n_max, hv, t_max, nbo);
   return hipGetLastError();
@@ -828,18 +832,28 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
 
 }  // namespace
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; the cache
+// is atomic, so concurrent callers at worst query the device twice).
 int cu_count() {
-  static int counts[64] = {0};
+  static std::atomic<int> counts[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (counts[dev] == 0) {
-    int n = 0;
+  int n = counts[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    counts[dev] = n;
+    counts[dev].store(n, std::memory_order_relaxed);
   }
-  return counts[dev];
+  return n;
+}
+
+bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int segments, int tiles) {
+  const int64_t members = (hv / h) * (kSlices / (segments == 2 ? 1 : tiles));
+  const int64_t rounds = (static_cast<int64_t>(n_max) * h + kXcds - 1) / kXcds;
+  dim3 grid;
+  if (!flat_grid((segments == 2 ? 2 : 1) * rounds * kXcds * members, 320, grid)) return false;
+  if (segments != 2) return true;
+  return flat_grid(static_cast<int64_t>(n_max) * hv * (fix_row_blocks(t_max) + 1), kFixThreads, grid);
 }
 
 int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv) {

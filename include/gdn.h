@@ -32,8 +32,10 @@
  *  - Errors: every argument and capacity is checked on the host before any
  *    HIP call; a failed check returns a status and touches nothing. A launch
  *    failure returns GDN_ERR_HIP. No call ever aborts the process.
- *  - Thread safety: the functions keep no state; concurrent calls on different
- *    streams are safe when their output and workspace buffers are disjoint.
+ *  - Thread safety: the only state the library keeps is a per-device cache of
+ *    the compute-unit count (atomic; read by the automatic launch-shape
+ *    choices). Concurrent calls on different streams are safe when their
+ *    output and workspace buffers are disjoint.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -90,10 +92,10 @@ typedef struct {
 /* Largest valid gdn_config.t_max / n_max. Each kernel takes at most
  * 2^31 - 1 work-groups per launch. Within these limits only the fix-up of the
  * two-segment walk can need more: about n_max * hv * t_max / 256 work-groups,
- * so with segments = 2 and n_max * hv * t_max above about 2^39 the call
- * returns GDN_ERR_HIP, with the outputs unspecified. The automatic choice
- * takes two segments only for grids that fill at most half of the device,
- * far inside that bound. */
+ * so with segments = 2 and n_max * hv * t_max above about 2^39 the forward
+ * returns GDN_ERR_CAPACITY. That check runs on the host before anything is
+ * queued, like every other check. The automatic choice takes two segments
+ * only for grids that fill at most half of the device, far inside that bound. */
 #define GDN_T_MAX_LIMIT (1 << 24)
 #define GDN_N_MAX_LIMIT 16384
 
@@ -155,7 +157,10 @@ typedef struct {
 gdn_status gdn_workspace_layout(const gdn_config *cfg, gdn_workspace_layout_t *layout);
 
 /* Bytes of workspace gdn_chunk_fwd needs for `cfg` (layout.total). Writes
- * *bytes; returns a validation status. */
+ * *bytes; returns a validation status. The size depends on the capacities
+ * (t_max, n_max) only, never on a batch's lengths, so one buffer sized once
+ * serves every batch of a static shape (FLA issue 1155, "Core design": static
+ * buffers sized from the maxima, owned by the caller). */
 gdn_status gdn_workspace_size(const gdn_config *cfg, size_t *bytes);
 
 /* Chunk-index table built on the device (FLA issue 1155, "Core design": a
@@ -215,7 +220,11 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
 
 /* Whole forward: [chunk table if chunk_indices is NULL and n_max >
  * GDN_FUSED_INDEX_MAX_SEQS] -> intra -> inter, all on `stream`, no host
- * synchronisation. Arguments as above; workspace (device) of at least
+ * synchronisation. This is the AMX page's section 3 wrapper (q, k, v, g,
+ * beta, an optional initial state and cu_seqlens in; o and the final state
+ * out), with FLA issue 1155's capture rules ("Core design": an optional
+ * caller-built chunk table, caller-owned static workspace, no host read of
+ * cu_seqlens). Arguments as above; workspace (device) of at least
  * gdn_workspace_size bytes, 256-byte aligned, holds the intermediates and the
  * table between the stages (when chunk_indices is NULL the table is built in
  * it, by the table kernel or by stage 1) and may be reused once the stream

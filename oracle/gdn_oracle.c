@@ -45,6 +45,9 @@
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int gdn_oracle_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the number of OpenMP threads of later calls (n >= 1). */
+void gdn_oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* Token recurrence over every (sequence, value head) lane. h0 may be NULL
  * (zero initial state); hT may be NULL. Lanes are independent, so they run in
  * parallel under OpenMP; each lane's arithmetic order is fixed. */

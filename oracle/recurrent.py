@@ -46,6 +46,8 @@ def _load():
     lib.gdn_oracle_front.restype = None
     lib.gdn_oracle_threads.argtypes = []
     lib.gdn_oracle_threads.restype = ctypes.c_int
+    lib.gdn_oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.gdn_oracle_set_threads.restype = None
     _lib = lib
     return lib
 
@@ -53,6 +55,11 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle's lane loop runs on."""
     return int(_load().gdn_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run later oracle calls on n OpenMP threads."""
+    _load().gdn_oracle_set_threads(int(n))
 
 
 def _dptr(a):

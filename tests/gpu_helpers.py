@@ -1,7 +1,8 @@
 """Shared helpers of the GPU parity tests: move a seeded workload to the device,
-run the HIP path through the C ABI, and evaluate the CPU oracle on sampled
-(sequence, value head) lanes. Imports the product binding and the oracle side
-by side; neither of those imports the other."""
+run the HIP path through the C ABI, and evaluate the CPU oracle, either on
+every (sequence, value head) lane of a batch in one call (the C oracle runs
+its lanes in parallel) or on chosen lanes. Imports the product binding and
+the oracle side by side; neither of those imports the other."""
 
 from __future__ import annotations
 
@@ -117,6 +118,36 @@ def oracle_lanes(wl, lanes, qkv64=None, scale=None):
                                         np.array([0, e - a], np.int32), h0=s0, scale=scale)
         out[(s, hv)] = (o[:, 0], hT[0, 0])
     return out
+
+
+def oracle_full(wl, qkv64=None, scale=None):
+    """fp64 recurrence on every lane of the batch in one oracle call (lanes in
+    parallel under OpenMP). Returns (o [t_max, Hv, 128], hT [n_max, Hv, 128,
+    128]); rows past the batch are zero."""
+    if qkv64 is None:
+        q, k, v = wl.f64("q"), wl.f64("k"), wl.f64("v")
+    else:
+        q, k, v = qkv64
+    return recurrent.gdn_recurrent(q, k, v, wl.f64("g"), wl.f64("beta"), wl.cu_seqlens,
+                                   h0=wl.f64("h0"), scale=scale)
+
+
+def full_errors(wl, o_gpu, hT_gpu, o_ref, hT_ref):
+    """(max |do| / max |o_ref| over every valid (t, hv, d); relative Frobenius
+    error over the whole final-state tensor). Non-finite GPU values fail."""
+    T = wl.n_tokens
+    og = o_gpu[:T].detach().cpu().to(torch.float64).numpy()
+    assert np.all(np.isfinite(og)), "non-finite o"
+    num_o = float(np.max(np.abs(og - o_ref[:T]))) if T else 0.0
+    den_o = float(np.max(np.abs(o_ref[:T]))) if T else 0.0
+    del og
+    sg = hT_gpu.detach().cpu().to(torch.float64).numpy()
+    assert np.all(np.isfinite(sg)), "non-finite final state"
+    num_s = float(np.linalg.norm((sg - hT_ref).ravel()))
+    den_s = float(np.linalg.norm(hT_ref.ravel()))
+    eo = num_o / den_o if den_o > 0 else num_o
+    es = num_s / den_s if den_s > 0 else num_s
+    return eo, es
 
 
 def lane_errors(wl, o_gpu, hT_gpu, ref):

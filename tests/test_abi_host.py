@@ -271,3 +271,66 @@ def test_recurrent_entry_points_host_errors(lib):
     assert lib.gdn_recurrent_fwd_timed(c, F, F, F, F, F, None, F, F, None, None, None, 8) == INVALID
     assert lib.gdn_recurrent_fwd_timed(c, F, F, F, F, F, None, F, F, None, None, 8, None) == INVALID
     assert lib.gdn_recurrent_fwd_timed(c, None, F, F, F, F, None, F, F, None, None, 8, 8) == INVALID
+
+
+def test_two_segment_fixup_past_the_launch_limit_is_refused_on_the_host(lib):
+    """Both capacities at their limits with two segments forced and two value
+    heads: the fix-up would need 16384 * 2 * 65537 > 2^31 - 1 work-groups, so
+    the forward (and the inter stage alone) returns GDN_ERR_CAPACITY from the
+    host checks, before anything is queued (no device exists here)."""
+    cfg = gdn.make_config(gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT, 1, 2, segments=2)
+    need = gdn.gdn_workspace_size(cfg)
+    assert _fwd(lib, cfg, ws_bytes=need) == CAPACITY
+    assert lib.gdn_chunk_fwd_inter(ctypes.byref(cfg), None, FAKE, FAKE, need, FAKE, None,
+                                   None) == CAPACITY
+    one = gdn.make_config(gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT, 1, 1, segments=2)
+    assert lib.gdn_workspace_size(ctypes.byref(one), ctypes.byref(ctypes.c_size_t())) == OK
+
+
+def test_binding_rejects_wrong_dtypes_and_sizes():
+    """The Python binding checks tensor dtypes and sizes against the config
+    before any pointer reaches the library (CPU tensors suffice: the checks run
+    first)."""
+    import torch
+    with pytest.raises(ValueError, match="dtype"):
+        gdn.make_config(64, 1, 1, 1, torch.float16)
+    T, n, H, Hv = 64, 1, 1, 2
+    cfg = gdn.make_config(T, n, H, Hv, torch.bfloat16)
+    ok = dict(q=torch.zeros(T, H, 128, dtype=torch.bfloat16),
+              k=torch.zeros(T, H, 128, dtype=torch.bfloat16),
+              v=torch.zeros(T, Hv, 128, dtype=torch.bfloat16),
+              g=torch.zeros(T, Hv), beta=torch.zeros(T, Hv),
+              h0=torch.zeros(n, Hv, 128, 128), cu=torch.tensor([0, T], dtype=torch.int32),
+              o=torch.zeros(T, Hv, 128), hT=torch.zeros(n, Hv, 128, 128))
+    bad_cases = [
+        ("q", torch.zeros(T, H, 128, dtype=torch.float16), "dtype"),
+        ("k", torch.zeros(T, H, 128), "dtype"),                       # fp32 in a bf16 config
+        ("v", torch.zeros(T, Hv, 64, dtype=torch.bfloat16), "elements"),
+        ("q", torch.zeros(2 * T, H, 64, dtype=torch.bfloat16), "last dimension"),
+        ("g", torch.zeros(T, Hv, dtype=torch.bfloat16), "dtype"),
+        ("beta", torch.zeros(T, 1), "elements"),
+        ("h0", torch.zeros(n, Hv, 128, 64), "elements"),
+        ("cu", torch.tensor([0, T]), "dtype"),                         # int64
+        ("o", torch.zeros(T, Hv, 128, dtype=torch.bfloat16), "dtype"),
+        ("hT", torch.zeros(n, 1, 128, 128), "elements"),
+    ]
+    for name, t, what in bad_cases:
+        a = dict(ok, **{name: t})
+        with pytest.raises(ValueError, match=what):
+            gdn.gdn_chunk_fwd(cfg, a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
+                              None, a["o"], a["hT"], torch.zeros(16, dtype=torch.uint8),
+                              ws_bytes=16)
+        with pytest.raises(ValueError, match=what):
+            gdn.gdn_recurrent_fwd(cfg, a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
+                                  a["cu"], a["o"], a["hT"])
+    with pytest.raises(ValueError, match="one dtype"):
+        gdn.chunk_gated_delta_rule(ok["q"], ok["k"].float(), ok["v"], ok["g"], ok["beta"],
+                                   ok["cu"])
+    with pytest.raises(ValueError, match="workspace"):
+        gdn.gdn_chunk_fwd(cfg, ok["q"], ok["k"], ok["v"], ok["g"], ok["beta"], None, ok["cu"],
+                          None, ok["o"], None, torch.zeros(16, dtype=torch.uint8), ws_bytes=4096)
+    # every check passed: the CPU tensors are then refused as non-device memory
+    with pytest.raises(ValueError, match="device tensor"):
+        gdn.gdn_chunk_fwd(cfg, ok["q"], ok["k"], ok["v"], ok["g"], ok["beta"], ok["h0"],
+                          ok["cu"], None, ok["o"], ok["hT"], torch.zeros(16, dtype=torch.uint8),
+                          ws_bytes=16)

@@ -4,7 +4,8 @@ Bar (from the method's tolerance): max |o_gpu - o_ref| / max |o_ref| <= 2e-3
 and relative Frobenius error of the final states <= 1e-3 over every checked
 lane; the chunk-index table is bit-exact. Small cases are checked on every
 lane; the five full-size workloads are run whole on the GPU, in the launch
-configuration the benchmark times, and checked on sampled lanes.
+configuration the benchmark times, and checked on every lane as well, against
+one oracle call over the whole batch.
 """
 
 import numpy as np
@@ -16,8 +17,9 @@ import workloads
 from oracle import chunked, index_table, recurrent
 
 from gpu_helpers import (O_TOL, S_TOL, config_of, decode_kimg, decode_pimg, decode_rowfrag, decode_uimg,
-                         device_inputs, lane_errors, log, oracle_inputs_f64, oracle_lanes,
-                         run_forward, run_forward_conv, run_front, workspace_views)
+                         device_inputs, full_errors, lane_errors, log, oracle_full,
+                         oracle_inputs_f64, oracle_lanes, run_forward, run_forward_conv, run_front,
+                         workspace_views)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -238,17 +240,15 @@ def test_fused_front_small_every_lane():
 
 def test_fused_front_workload_full_size():
     """The front workload (4 x 8192 tokens) through the fused path, in the
-    launch configuration the benchmark times; sampled lanes against the
-    fp64 front + recurrence."""
+    launch configuration the benchmark times, against the fp64 front +
+    recurrence on every lane."""
     wl = workloads.make(4)
     log(f"fused front, workload 4 ({wl.name}) tokens={wl.n_tokens}")
     o, hT = run_forward_conv(wl)
-    lanes = [(0, 0), (1, 13), (3, 31)]
-    ref = oracle_lanes(wl, lanes, qkv64=_front_for(wl, sorted({s for s, _ in lanes})))
-    eo, es = lane_errors(wl, o, hT, ref)
-    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    o_ref, s_ref = oracle_full(wl, qkv64=oracle_inputs_f64(wl))
+    eo, es = full_errors(wl, o, hT, o_ref, s_ref)
+    log(f"  every lane: o err {eo:.3e}  S err {es:.3e}")
     assert eo <= O_TOL and es <= S_TOL
-    assert torch.isfinite(o[:wl.n_tokens]).all()
 
 
 # --------------------------------------------------------------------------- #
@@ -324,6 +324,37 @@ def test_zero_length_sequences_keep_state():
     assert torch.count_nonzero(hT[[0, 2, 3, 4]]) == 0
 
 
+@pytest.mark.parametrize("n_max", [1, 2, 256, 300])
+def test_no_token_capacity_hands_back_every_initial_state(n_max):
+    """t_max = 0 (a valid config: nothing to compute): stage 1 does not run,
+    and stage 2 must still write hT = h0 for every sequence, including the
+    batch sizes for which stage 1 would rank the sequences (2..256)."""
+    H, Hv = 1, 2
+    cfg = gdn.make_config(0, n_max, H, Hv, torch.bfloat16)
+    log(f"t_max = 0, n_max = {n_max}")
+    one = lambda *shape, dt=torch.float32: torch.zeros(shape, dtype=dt, device=DEV)
+    q, k, v = one(1, H, 128, dt=torch.bfloat16), one(1, H, 128, dt=torch.bfloat16), \
+        one(1, Hv, 128, dt=torch.bfloat16)
+    g, beta, o = one(1, Hv), one(1, Hv), one(1, Hv, 128)
+    cu = torch.zeros(n_max + 1, dtype=torch.int32, device=DEV)
+    h0 = torch.full((n_max, Hv, 128, 128), 0.25, dtype=torch.float32, device=DEV)
+    h0[-1] = -0.5
+    hT = torch.full_like(h0, float("nan"))
+    ws = torch.full((max(gdn.gdn_workspace_size(cfg), 256),), 0x7f, dtype=torch.uint8, device=DEV)
+    gdn.gdn_chunk_fwd(cfg, q, k, v, g, beta, h0, cu, None, o, hT, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(hT, h0)
+    hT.fill_(float("nan"))
+    gdn.gdn_chunk_fwd(cfg, q, k, v, g, beta, None, cu, None, o, hT, ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(hT) == 0
+    # the split entry points agree
+    hT.fill_(float("nan"))
+    gdn.gdn_chunk_fwd_inter(cfg, h0, cu, ws, o, hT)
+    torch.cuda.synchronize()
+    assert torch.equal(hT, h0)
+
+
 def test_untouched_rows_past_the_batch():
     wl = workloads.make_custom([70, 10], 1, 2, seed=47, t_max=200, n_max=2)
     o, _, _ = run_forward(wl)
@@ -339,54 +370,21 @@ def test_no_decay_no_write_keeps_state_bitwise():
 
 
 # --------------------------------------------------------------------------- #
-# the five named workloads at full size (sampled lanes)
+# the five named workloads at full size, every lane
 # --------------------------------------------------------------------------- #
-
-SAMPLED = {
-    0: None,  # every lane
-    1: [(0, 0), (0, 1), (0, 13), (0, 31)],
-    2: "pick",
-    3: [(0, 0), (0, 15)],
-    4: [(0, 0), (3, 31)],
-}
-
 
 @pytest.mark.parametrize("cfg_id", [0, 1, 2, 3, 4])
 def test_named_workload_full_size(cfg_id):
+    """Each named workload, whole, in the launch configuration the benchmark
+    times (the front workload here through the standalone front kernel), against
+    the fp64 oracle on every (t, hv, d) and the whole final-state tensor."""
     wl = workloads.make(cfg_id)
     log(f"workload {cfg_id} ({wl.name}) tokens={wl.n_tokens}")
     o, hT, _ = run_forward(wl)
-    lanes = SAMPLED[cfg_id]
-    if lanes is None:
-        lanes = _all_lanes(wl)
-    elif lanes == "pick":
-        lens = np.diff(wl.cu_seqlens)
-        order = np.argsort(lens)
-        lanes = [(int(order[-1]), 5), (int(order[0]), 30), (int(order[len(order) // 2]), 17)]
-    qkv64 = None
-    if wl.qkv is not None:
-        # the fp64 front of only the sampled sequences
-        qkv64 = _front_for(wl, sorted({s for s, _ in lanes}))
-    ref = oracle_lanes(wl, lanes, qkv64=qkv64)
-    eo, es = lane_errors(wl, o, hT, ref)
-    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    o_ref, s_ref = oracle_full(wl, qkv64=oracle_inputs_f64(wl) if wl.qkv is not None else None)
+    eo, es = full_errors(wl, o, hT, o_ref, s_ref)
+    log(f"  every lane: o err {eo:.3e}  S err {es:.3e}")
     assert eo <= O_TOL and es <= S_TOL
-    T = wl.n_tokens
-    assert torch.isfinite(o[:T]).all()
-
-
-def _front_for(wl, seqs):
-    cu = wl.cu_seqlens
-    T = wl.t_max
-    q = np.zeros((T, wl.H, 128)); k = np.zeros((T, wl.H, 128)); v = np.zeros((T, wl.Hv, 128))
-    w64 = wl.f64("conv_w")
-    for s in seqs:
-        a, e = int(cu[s]), int(cu[s + 1])
-        x = wl.qkv[a:e].to(torch.float64).numpy()
-        qs, ks, vs = recurrent.gdn_front(x, w64, np.array([0, e - a], np.int32), wl.H, wl.Hv,
-                                         128, 128)
-        q[a:e], k[a:e], v[a:e] = qs, ks, vs
-    return q, k, v
 
 
 @pytest.mark.parametrize("n", [40, 300])
@@ -484,20 +482,24 @@ def test_graph_capture_replay_with_varying_cu_seqlens(entry, segments):
 
 
 @pytest.mark.parametrize("H,Hv,dtype", [(2, 8, torch.bfloat16), (1, 8, torch.float32),
-                                        (4, 32, torch.bfloat16), (24, 24, torch.bfloat16)])
+                                        (4, 32, torch.bfloat16), (24, 24, torch.bfloat16),
+                                        (3, 9, torch.bfloat16), (12, 36, torch.bfloat16),
+                                        (12, 24, torch.float32), (5, 15, torch.float32)])
 def test_gqa_group_sizes_every_lane(H, Hv, dtype):
-    """Other key/value head ratios than the named workloads (groups of 4 and 8,
-    and many heads with a group of 1) through the chunked path (one and two
-    stage-2 segments) and the token-serial kernel, every lane against the
-    oracle."""
+    """Other key/value head ratios than the named workloads (groups of 3, 4
+    and 8, key-head counts that are not multiples of the 8 XCDs, and many
+    heads with a group of 1) through the chunked path (one and two stage-2
+    segments; one, two and four column tiles) and the token-serial kernel,
+    every lane against the oracle."""
     lengths = [130, 0, 64, 257]
     wl = workloads.make_custom(lengths, H, Hv, seed=31 + H + Hv, dtype=dtype, h0_sigma=0.02,
                                n_max=len(lengths) + 1, t_max=sum(lengths) + 3)
     d = device_inputs(wl)
     ref = oracle_lanes(wl, _all_lanes(wl))
-    for tag in ("one segment", "two segments", "token-serial"):
+    for tag in ("one segment", "two segments", "two tiles", "four tiles", "token-serial"):
         cfg = gdn.make_config(wl.t_max, wl.n_max, H, Hv, dtype,
-                              segments=2 if tag == "two segments" else 1)
+                              segments=2 if tag == "two segments" else 1,
+                              tiles={"two tiles": 2, "four tiles": 4}.get(tag, 0))
         o = torch.full((wl.t_max, Hv, 128), float("nan"), dtype=torch.float32, device=DEV)
         hT = torch.full((wl.n_max, Hv, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
         if tag == "token-serial":

@@ -5,7 +5,7 @@ Checked against the CPU oracle on every lane of small batches (sequence lengths
 around the chunk and segment boundaries, empty sequences, fp32 and bf16, with
 and without initial states), and on the long-context workload in the launch
 configuration the benchmark uses (automatic segments), against the oracle on
-sampled lanes and against the one-piece walk.
+every lane and against the one-piece walk.
 """
 
 import numpy as np
@@ -15,7 +15,8 @@ import torch
 import chunked_gated_delta_rule_amd as gdn
 import workloads
 
-from gpu_helpers import O_TOL, S_TOL, device_inputs, lane_errors, log, oracle_lanes
+from gpu_helpers import (O_TOL, S_TOL, device_inputs, full_errors, lane_errors, log, oracle_full,
+                         oracle_lanes)
 from oracle import recurrent
 
 pytestmark = pytest.mark.gpu
@@ -84,10 +85,9 @@ def test_long_context_automatic_segments_vs_one_piece():
     d = device_inputs(wl, DEV)
     o2, h2 = _forward(wl, 0, d)
     o1, h1 = _forward(wl, 1, d)
-    lanes = [(0, 0), (0, 9), (0, 15)]
-    ref = oracle_lanes(wl, lanes)
+    o_ref, s_ref = oracle_full(wl)
     for tag, (o, h) in (("two segments", (o2, h2)), ("one piece", (o1, h1))):
-        eo, es = lane_errors(wl, o, h, ref)
+        eo, es = full_errors(wl, o, h, o_ref, s_ref)
         log(f"  {tag}: o err {eo:.3e}  S err {es:.3e}")
         assert eo <= O_TOL and es <= S_TOL
     T = wl.n_tokens

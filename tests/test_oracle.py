@@ -106,7 +106,8 @@ def test_bruteforce_matches_recurrent(seed):
 
 def test_bruteforce_rejects_planted_mistakes():
     """Mistakes planted in a NumPy copy of the step form are caught by the
-    exact brute force: correction before decay, and reading before writing."""
+    exact brute force: correction before decay, reading before writing, a
+    flipped sign in the correction, and the state read transposed."""
     rng = np.random.Generator(np.random.PCG64(7))
     T, D = 6, 4
     ql, kl, vl, al, bl, S0 = _rational_lane(rng, T, D)
@@ -124,6 +125,12 @@ def test_bruteforce_rejects_planted_mistakes():
             elif order == "read_before_write":
                 S = a * S; outs.append(S.T @ q[t])
                 d = b * (v[t] - S.T @ k[t]); S = S + np.outer(k[t], d)
+            elif order == "flipped_sign":
+                S = a * S; d = b * (v[t] + S.T @ k[t]); S = S + np.outer(k[t], d)
+                outs.append(S.T @ q[t])
+            elif order == "transposed_read":
+                S = a * S; d = b * (v[t] - S.T @ k[t]); S = S + np.outer(k[t], d)
+                outs.append(S @ q[t])
             else:
                 S = a * S; d = b * (v[t] - S.T @ k[t]); S = S + np.outer(k[t], d)
                 outs.append(S.T @ q[t])
@@ -133,6 +140,8 @@ def test_bruteforce_rejects_planted_mistakes():
     assert _relmax(step_form("right"), exact) < 1e-13
     assert _relmax(step_form("correct_then_decay"), exact) > 1e-3
     assert _relmax(step_form("read_before_write"), exact) > 1e-3
+    assert _relmax(step_form("flipped_sign"), exact) > 1e-3
+    assert _relmax(step_form("transposed_read"), exact) > 1e-3
 
 
 # --------------------------------------------------------------------------- #
@@ -250,7 +259,8 @@ def test_chunked_form_weak_decay(rng):
     assert _relmax(o_c, o_r) < 1e-11 and _relmax(s_c, s_r) < 1e-11
 
 
-@pytest.mark.parametrize("mutation", ["no_diagonal", "exclusive_cumsum", "first_order_solve"])
+@pytest.mark.parametrize("mutation", ["no_diagonal", "exclusive_cumsum", "first_order_solve",
+                                      "flipped_solve_sign", "transposed_decay_mask"])
 def test_chunked_pins_reject_planted_mistakes(rng, monkeypatch, mutation):
     q, k, v, g, b, cu, h0 = _rand_inputs(rng, [100], 1, 1, 16, 16, h0_sigma=0.3)
     o_r, _ = recurrent.gdn_recurrent(q, k, v, g, b, cu, h0=h0)
@@ -261,8 +271,14 @@ def test_chunked_pins_reject_planted_mistakes(rng, monkeypatch, mutation):
     elif mutation == "exclusive_cumsum":
         monkeypatch.setattr(chunked, "chunk_local_cumsum",
                             lambda gc: np.concatenate([[0.0], np.cumsum(gc)[:-1]]))
-    else:
+    elif mutation == "first_order_solve":
         monkeypatch.setattr(chunked, "solve_unit_lower", lambda A: np.eye(A.shape[0]) - A)
+    elif mutation == "flipped_solve_sign":  # (I - A)^-1 instead of (I + A)^-1
+        orig = chunked.solve_unit_lower
+        monkeypatch.setattr(chunked, "solve_unit_lower", lambda A: orig(-A))
+    else:
+        orig = chunked.decay_mask
+        monkeypatch.setattr(chunked, "decay_mask", lambda gm: orig(gm).T)
     o_c, _ = chunked.gdn_chunked(q, k, v, g, b, cu, h0=h0, chunk=16)
     assert _relmax(o_c, o_r) > 1e-4
 
@@ -329,6 +345,35 @@ def test_front_identity_and_delay_taps(rng):
     _, _, v = recurrent.gdn_front(x, w_del, cu, H, Hv, D, D)
     assert np.array_equal(v[:3, 0], np.zeros((3, D)))
     assert _relmax(v[3:, 0], _silu(x[:-3, 2 * D:])) < 1e-15
+
+
+def test_front_silu_closed_forms(rng):
+    """SiLU inside the front, pinned without restating it: with the identity
+    tap the v channels are SiLU(x) exactly, so SiLU(0) = 0, SiLU(x) - SiLU(-x)
+    = x, SiLU(x) + SiLU(-x) = x tanh(x / 2), SiLU(1) = sigmoid(1) and
+    SiLU(-1) = -sigmoid(-1) (textbook values), and SiLU(x) -> x, SiLU(-x) -> 0
+    for large x."""
+    H, Hv, D = 1, 1, 8
+    C = 2 * H * D + Hv * D
+    w_id = np.zeros((C, 4)); w_id[:, 3] = 1.0
+
+    def silu_of(vals):  # the oracle front's v channels for inputs `vals`
+        x = np.zeros((len(vals), C))
+        x[:, 2 * D:] = np.asarray(vals, np.float64)[:, None]
+        cu = np.arange(len(vals) + 1, dtype=np.int32)  # one token per sequence
+        _, _, v = recurrent.gdn_front(x, w_id, cu, H, Hv, D, D)
+        return v[:, 0, 0]
+
+    xs = rng.standard_normal(64) * 3
+    pos, neg = silu_of(xs), silu_of(-xs)
+    assert silu_of([0.0])[0] == 0.0
+    assert np.max(np.abs((pos - neg) - xs)) < 4e-15 * np.max(np.abs(xs))
+    assert np.max(np.abs((pos + neg) - xs * np.tanh(xs / 2))) < 4e-15 * np.max(np.abs(xs))
+    one = silu_of([1.0, -1.0])
+    assert abs(one[0] - 0.7310585786300049) < 1e-15  # 1 / (1 + e^-1)
+    assert abs(one[1] + 0.2689414213699951) < 1e-15  # -1 / (1 + e)
+    big = silu_of([40.0, -40.0])
+    assert big[0] == 40.0 and 0.0 > big[1] > -1e-15
 
 
 def test_front_unit_norm_heads(rng):
