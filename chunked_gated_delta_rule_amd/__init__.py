@@ -30,7 +30,7 @@ __all__ = [
     "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "GDN_FUSED_INDEX_MAX_SEQS",
     "gdn_chunk_fwd_conv", "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd",
     "gdn_recurrent_fwd_timed", "recurrent_gated_delta_rule", "GDN_SEGMENT_MIN_TOKENS", "GDN_FOUR_TILE_MIN_TOKENS",
-    "GDN_T_MAX_LIMIT", "GDN_N_MAX_LIMIT",
+    "GDN_T_MAX_LIMIT", "GDN_N_MAX_LIMIT", "gdn_chunk_fwd_noalloc", "GDN_NOALLOC_SCRATCH_BYTES",
 ]
 
 GDN_BF16 = 0
@@ -40,13 +40,15 @@ GDN_SEGMENT_MIN_TOKENS = 2048  # include/gdn.h
 GDN_FOUR_TILE_MIN_TOKENS = 384  # include/gdn.h
 GDN_T_MAX_LIMIT = 1 << 24  # include/gdn.h
 GDN_N_MAX_LIMIT = 16384  # include/gdn.h
+GDN_NOALLOC_SCRATCH_BYTES = 256 << 20  # include/gdn.h
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
            3: "GDN_ERR_CAPACITY", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 EXPORTED_SYMBOLS = ("gdn_nt_max", "gdn_workspace_layout", "gdn_workspace_size",
                     "gdn_build_chunk_indices", "gdn_front_conv_silu_l2", "gdn_chunk_fwd_intra",
                     "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
                     "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "gdn_chunk_fwd_conv",
-                    "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd", "gdn_recurrent_fwd_timed")
+                    "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd", "gdn_recurrent_fwd_timed",
+                    "gdn_chunk_fwd_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libgdn.so")
@@ -102,11 +104,13 @@ def load_library():
     lib.gdn_chunk_fwd_conv_timed.argtypes = [cfgp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                              vp, ctypes.POINTER(vp)]
     lib.gdn_recurrent_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_noalloc.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_recurrent_fwd_timed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     for name in ("gdn_workspace_size", "gdn_workspace_layout", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
                  "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd",
                  "gdn_chunk_fwd_timed", "gdn_front_conv_silu_l2_timed", "gdn_chunk_fwd_conv",
-                 "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd", "gdn_recurrent_fwd_timed"):
+                 "gdn_chunk_fwd_conv_timed", "gdn_recurrent_fwd", "gdn_recurrent_fwd_timed",
+                 "gdn_chunk_fwd_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_status_str.restype = ctypes.c_char_p
@@ -279,6 +283,18 @@ def gdn_chunk_fwd(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT, w
                                         _ptr(chunk_indices), _ptr(o), _ptr(hT), _ptr(workspace),
                                         int(ws_bytes), _stream(stream)),
            "gdn_chunk_fwd")
+
+
+def gdn_chunk_fwd_noalloc(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT,
+                          stream=None):
+    """gdn_chunk_fwd with the intermediates in the library's fixed device
+    scratch (no workspace argument; nothing is allocated)."""
+    _check_tensors(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT)
+    _check(load_library().gdn_chunk_fwd_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+                                                _ptr(chunk_indices), _ptr(o), _ptr(hT),
+                                                _stream(stream)),
+           "gdn_chunk_fwd_noalloc")
 
 
 def gdn_chunk_fwd_timed(cfg, q, k, v, g, beta, h0, cu_seqlens, chunk_indices, o, hT, workspace,

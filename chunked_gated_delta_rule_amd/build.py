@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["chunk_index.hip", "front.hip", "intra.hip", "inter.hip", "recurrent.hip", "gdn_api.cpp"]
+SOURCES = ["chunk_index.hip", "front.hip", "intra.hip", "inter.hip", "recurrent.hip", "noalloc.hip",
+           "gdn_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 ALU forms are disabled: scalar and float2 code must not be

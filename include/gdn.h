@@ -234,6 +234,30 @@ gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, co
                          const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,
                          float *hT, void *workspace, size_t ws_bytes, void *stream);
 
+/* Bytes of the library's fixed device scratch used by gdn_chunk_fwd_noalloc
+ * (256 MiB; one copy per GPU the library runs that call on, held until the
+ * process ends). */
+#define GDN_NOALLOC_SCRATCH_BYTES (256 << 20)
+
+/* gdn_chunk_fwd without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation after start-up). The intermediates go to a fixed
+ * device array inside the library, GDN_NOALLOC_SCRATCH_BYTES per device,
+ * whose address is looked up once per device on the first call with that
+ * device current. The call allocates nothing and frees nothing.
+ *   Arguments, layouts and results as gdn_chunk_fwd (workspace omitted).
+ *   Returns GDN_ERR_WORKSPACE when gdn_workspace_size(cfg) exceeds
+ *   GDN_NOALLOC_SCRATCH_BYTES (for example T = 4096 tokens at h = 16, hv = 32
+ *   needs about 134 MiB; about 7,800 tokens fit at those head counts), before
+ *   anything is queued.
+ * All calls on one device share its array: calls that overlap in time on one
+ * device (different streams, or threads enqueueing concurrently) race, and
+ * the caller must order them. Nothing in the array has to start at zero. */
+gdn_status gdn_chunk_fwd_noalloc(const gdn_config *cfg, const void *q, const void *k,
+                                 const void *v, const float *g, const float *beta,
+                                 const float *h0, const int32_t *cu_seqlens,
+                                 const int32_t *chunk_indices, void *o, float *hT, void *stream);
+
 /* Whole forward with the front fused into the intra stage (the "next" step
  * after gdn_front_conv_silu_l2 + gdn_chunk_fwd): each stage-1 work-group
  * computes its chunk's q, k (conv, SiLU, per-head L2 norm) and v (conv,
