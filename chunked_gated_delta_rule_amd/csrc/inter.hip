@@ -90,6 +90,14 @@ constexpr int kL2Lead = 2;       // chunks between the L2 warm-up and the operan
 template <bool kF32In, int kDepth, int kS, int kNV>
 constexpr bool kWarmWave = kNV == 1 && !(kF32In && kDepth == 2) && (kS == 1 || kDepth == 1);
 constexpr int kDepthSeg = 1;  // prefetch depth of the two-state walk (keeps the warm-up wave)
+
+// Chunks of segment A (walked from h0 with one state) when a sequence of nc
+// chunks is walked in two segments: the first ceil(nc / 2). Segment B carries
+// two states, but segment A's walk is no faster per chunk where the operands
+// come from HBM (T = 32768: splits giving B 3/8, 2/5 or 7/16 of the chunks
+// took stage 2 from 508 to 556, 541 and 532 us).
+constexpr int kSegBNum = 1, kSegBDen = 2;
+__host__ __device__ constexpr int seg_split(int nc) { return nc - nc * kSegBNum / kSegBDen; }
 template <bool kF32In, int kDepth, int kS, int kNV>
 constexpr int kInterThreads = kWarmWave<kF32In, kDepth, kS, kNV> ? 320 : 256;
 // waves per SIMD the register allocation must leave room for
@@ -206,7 +214,8 @@ struct Walk {
 
 template <bool kF32In, int kDepth, int X, int kS, int kNV>
 __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const StageBuffers &in,
-                                           u32x4 (*xch)[kXchFrags * kS * kNV][64]) {
+                                           u32x4 (*xch)[kXchFrags * kS * kNV][64],
+                                           float (*decx)[64]) {
   static_assert(kS == 1 || kNV == 1, "the two-state walk covers one column tile");
   constexpr int kNKw = kF32In ? 16 : 8;  // K^T fragments this wave uses per chunk
   const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;  // 1 KB fragment blocks
@@ -227,7 +236,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   f16x8 w[kDepth][8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
   bf16x8 k[kDepth][kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
   u32x3 u[kDepth][kNV][4];  // wave 0: u tile R (24-bit), rows 16 R + 4 g + i, column v0 + 16 ct + c
-  float dec[kDepth];        // e^{gamma_last - gamma} of token L.lane (spread by lane permutes)
+  float dec[kDepth];        // e^{gamma_last - gamma} of token L.lane (shared through LDS)
   float el[kDepth];         // e^{gamma_last}
   auto load_w = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
@@ -317,17 +326,17 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
 #pragma unroll
         for (int tl = 0; tl < 4; ++tl) S[st][ct][tl] = S[st][ct][tl] * e_last;
       }
+    if constexpr (X == 0) decx[c & 1][L.lane] = dec[B];  // token L.lane's factor
     __builtin_amdgcn_sched_barrier(0);
     load_w(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // chunk c's states (fp16) and all partials are published
     // S += K^T (e^{gamma_last - gamma} v'): rows 16 R + 4 g + i of this lane
-    // take their factors from lanes 16 R + 4 g + i (ds_bpermute)
+    // take their factors from the chunk's gate factors that wave 0 put in LDS
+    // before the barrier (one broadcast 16-byte read per token tile)
     f32x4 dr[4];
 #pragma unroll
-    for (int R = 0; R < 4; ++R)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dr[R][i] = __shfl(dec[B], 16 * R + L.g4 + i, 64);
+    for (int R = 0; R < 4; ++R) dr[R] = *reinterpret_cast<const f32x4 *>(&decx[c & 1][16 * R + L.g4]);
     bf16x8 eh[kS][kNV][2], elo[kS][kNV][2];
 #pragma unroll
     for (int st = 0; st < kS; ++st)
@@ -589,7 +598,7 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
 }
 
 // With kS = 1 every work-group walks its whole sequence. With kS = 2 the grid
-// is twice the one-walk grid: the first half walks the first ceil(nc / 2)
+// is twice the one-walk grid: the first half walks the first seg_split(nc)
 // chunks of each sequence from h0 (its final slice goes to seg.sa), the
 // second half walks the rest carrying the zero-start state (outputs into o,
 // final slice to seg.z) and the identity-start homogeneous state (outputs to
@@ -602,6 +611,8 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
     SegScratch seg) {
   __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags * kS * kNV][64];
   __shared__ uint32_t l2_sink[64];
+  // per chunk (double-buffered) the gate factors e^{gamma_last - gamma} by token
+  __shared__ __attribute__((aligned(16))) float decx[2][64];
 
   // ---- XCD-aware work-group -> (sequence, value head, slice) --------------
   constexpr int kWgSlices = kSlices / kNV;  // work-groups per value head
@@ -637,15 +648,15 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   if (kS == 1) {
     W = Walk{0, L.nc, h0, {o, nullptr}, {hT, nullptr}};
   } else {
-    const int cm = (L.nc + 1) / 2;
+    const int cm = seg_split(L.nc);
     W = role == 0 ? Walk{0, cm, h0, {o, nullptr}, {seg.sa, nullptr}}
                   : Walk{cm, L.nc, nullptr, {o, seg.oh}, {seg.z, seg.phi}};
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0)
-    chain_wave<kF32In, kDepth, 0, kS, kNV>(L, W, in, xch);
+    chain_wave<kF32In, kDepth, 0, kS, kNV>(L, W, in, xch, decx);
   else if (wave == 1)
-    chain_wave<kF32In, kDepth, 1, kS, kNV>(L, W, in, xch);
+    chain_wave<kF32In, kDepth, 1, kS, kNV>(L, W, in, xch, decx);
   else if (wave == 2)
     helper_wave<kDepth, 0, kS, kNV>(L, W, in, xch);
   else if (wave == 3)
@@ -681,7 +692,7 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
   const int s = pair / Hv, hv = pair % Hv;
   if (s >= n_max) return;
   const int bos = cu_at(cu, s, t_max), eos = cu_end(cu, s, bos, t_max);
-  const int nc = (eos - bos + kC - 1) / kC, cm = (nc + 1) / 2;
+  const int nc = (eos - bos + kC - 1) / kC, cm = seg_split(nc);
   const int64_t st = ((int64_t)s * Hv + hv) * kD * kD;
   const bool fin = blk == nbo;
   const int t_begin = bos + kC * (cm + 2 * blk);  // 128 output rows per work-group
@@ -777,10 +788,13 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
   }
 }
 
-// Work-groups of 128 output rows over the at most floor(ceil(t_max / 64) / 2)
-// chunks of segment B, per (sequence, value head); the fix-up grid has one
-// more (the final state) per pair.
-int fix_row_blocks(int32_t t_max) { return ((t_max + kC - 1) / kC / 2 + 1) / 2; }
+// Work-groups of 128 output rows over the at most nc - seg_split(nc) chunks
+// of segment B (nc = ceil(t_max / 64) at most), per (sequence, value head);
+// the fix-up grid has one more (the final state) per pair.
+int fix_row_blocks(int32_t t_max) {
+  const int nc = (t_max + kC - 1) / kC;
+  return (nc - seg_split(nc) + 1) / 2;
+}
 
 template <bool kF32In, int kDepth, int kS, int kNV = 1>
 hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,

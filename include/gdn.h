@@ -69,8 +69,10 @@ typedef struct {
   gdn_dtype o_dtype;   /* dtype of o: GDN_F32 (the only one supported) */
   float scale;         /* output scale; <= 0 selects 1 / sqrt(dk) */
   int32_t segments;    /* stage-2 walk of each sequence: 1 = one piece; 2 = its two
-                          halves at once, then a fix-up (the recurrence is affine in
-                          the starting state); 0 = automatic: 2 when t_max >=
+                          halves at once (the first from the initial state, the
+                          second from zero and from the identity), then a fix-up
+                          (the recurrence is affine in the starting state);
+                          0 = automatic: 2 when t_max >=
                           GDN_SEGMENT_MIN_TOKENS and the one-piece stage-2 grid fills
                           at most half of the current device's compute units */
   int32_t tiles;       /* 16-column tiles of the state per stage-2 work-group in the

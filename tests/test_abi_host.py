@@ -274,16 +274,17 @@ def test_recurrent_entry_points_host_errors(lib):
 
 
 def test_two_segment_fixup_past_the_launch_limit_is_refused_on_the_host(lib):
-    """Both capacities at their limits with two segments forced and two value
-    heads: the fix-up would need 16384 * 2 * 65537 > 2^31 - 1 work-groups, so
-    the forward (and the inter stage alone) returns GDN_ERR_CAPACITY from the
-    host checks, before anything is queued (no device exists here)."""
-    cfg = gdn.make_config(gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT, 1, 2, segments=2)
+    """Both capacities at their limits with two segments forced and three
+    value heads: segment B holds half of the 2^18 chunks, so the fix-up would
+    need 16384 * 3 * (65536 + 1) > 2^31 - 1 work-groups, and the forward (and
+    the inter stage alone) returns GDN_ERR_CAPACITY from the host checks,
+    before anything is queued (no device exists here)."""
+    cfg = gdn.make_config(gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT, 1, 3, segments=2)
     need = gdn.gdn_workspace_size(cfg)
     assert _fwd(lib, cfg, ws_bytes=need) == CAPACITY
     assert lib.gdn_chunk_fwd_inter(ctypes.byref(cfg), None, FAKE, FAKE, need, FAKE, None,
                                    None) == CAPACITY
-    one = gdn.make_config(gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT, 1, 1, segments=2)
+    one = gdn.make_config(gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT, 1, 2, segments=2)
     assert lib.gdn_workspace_size(ctypes.byref(one), ctypes.byref(ctypes.c_size_t())) == OK
 
 
