@@ -122,7 +122,7 @@ gdn::StageBuffers stage_buffers(const gdn_config *cfg, const gdn_workspace_layou
   b.q16 = reinterpret_cast<_Float16 *>(ws + l.q16);
   b.kimg = reinterpret_cast<__bf16 *>(ws + l.kimg);
   b.uimg = reinterpret_cast<uint32_t *>(ws + l.uimg);
-  b.pimg = reinterpret_cast<__bf16 *>(ws + l.pimg);
+  b.pimg = reinterpret_cast<_Float16 *>(ws + l.pimg);
   b.gimg = reinterpret_cast<float *>(ws + l.gimg);
   // stage 1 writes the ranking; with t_max == 0 it does not run, so stage 2
   // must not read the (unwritten) table

@@ -13,19 +13,19 @@
 namespace gdn {
 
 // P = scale * tril(q k^T * Gamma) per (value head, chunk): six pairs of
-// 16 x 16 tiles of P^T, each a 16 x 32 MFMA fragment in a hi and a lo bf16
-// term. In pairs 0 and 3 (output tiles 0 and 2, against the token block that
-// starts with their own tile) the second half of every lane's contraction
-// slots lies above the diagonal and is always zero, so those pairs keep 8
-// bytes per lane and term (512-byte terms) and the others 16 (1 KB terms).
-constexpr int kPBytes = 10 * 1024;
+// 16 x 16 tiles of P^T, each a 16 x 32 MFMA fragment of fp16 values. In pairs
+// 0 and 3 (output tiles 0 and 2, against the token block that starts with
+// their own tile) the second half of every lane's contraction slots lies
+// above the diagonal and is always zero, so those pairs keep 8 bytes per lane
+// (512-byte blocks) and the others 16 (1 KB).
+constexpr int kPBytes = 5 * 1024;
 __host__ __device__ constexpr bool p_half(int pi) { return pi == 0 || pi == 3; }
 __host__ __device__ constexpr int p_term_bytes(int pi) { return p_half(pi) ? 512 : 1024; }
-// byte offset of pair pi's hi term in its block (the lo term follows it)
+// byte offset of pair pi's block
 __host__ __device__ constexpr int p_offset(int pi) {
-  return pi == 0 ? 0 : pi == 1 ? 1024 : pi == 2 ? 3072 : pi == 3 ? 5120 : pi == 4 ? 6144 : 8192;
+  return pi == 0 ? 0 : pi == 1 ? 512 : pi == 2 ? 1536 : pi == 3 ? 2560 : pi == 4 ? 3072 : 4096;
 }
-static_assert(p_offset(5) + 2 * p_term_bytes(5) == kPBytes, "P block layout");
+static_assert(p_offset(5) + p_term_bytes(5) == kPBytes, "P block layout");
 
 // Intermediates written by the intra stage and read by the inter stage (all
 // device memory inside the caller's workspace; layouts in intra.hip).
@@ -34,7 +34,7 @@ struct StageBuffers {
   _Float16 *q16;  // [h, nt_max, 16 fragments, 64 lanes, 8]
   __bf16 *kimg;   // [h, nt_max, 16 or 32 fragments, 64 lanes, 8]
   uint32_t *uimg; // [hv, nt_max, 8, 4, 64 lanes, 3 words]: four 24-bit floats per lane
-  __bf16 *pimg;   // [hv, nt_max, 6 pairs, 2 terms, 64 lanes, 8]
+  _Float16 *pimg; // [hv, nt_max, 5 KB]: P fragments (fp16)
   float *gimg;    // [hv, nt_max, 192]
   // [n_max]: sequence indices ranked by chunk count, longest first (ties by
   // index), written by stage 1 and read by stage 2 to start the longest walks

@@ -20,7 +20,7 @@
 //
 //   v'      = u + (-w) S          A = -w fragment, B = S (fp16)      C = v' tiles
 //   o^T     = S^T q^T             A = S (fp16),   B = q16 fragment   C = o^T tiles
-//   o^T    += v'^T P^T            A = v' (hi+lo), B = P fragment (hi+lo)
+//   o^T    += v'^T P^T            A = v' (fp16 hi+lo), B = P fragment (fp16)
 //   S       = e^{gamma_last} S + K^T v'_dec    A = K^T fragment, B = v'_dec (hi+lo)
 //
 // A 16x16 accumulator gives lane (g, c) = (l >> 4, l & 15) rows 4g .. 4g + 3 of
@@ -115,6 +115,25 @@ __device__ __forceinline__ void split8(const f32x4 &a, const f32x4 &b, bf16x8 &h
   split8_words(x, h, l);
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// Two stacked accumulators -> fp16 hi + lo fragments (x = hi + lo to about
+// 22 significant bits; hi rounded to nearest even).
+__device__ __forceinline__ void split8_f16(const f32x4 &a, const f32x4 &b, f16x8 &hi, f16x8 &lo) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  f16x8 h, l;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f16x2 p = __builtin_convertvector(f32x2{x[i], x[i + 1]}, f16x2);
+    const f32x2 back = __builtin_convertvector(p, f32x2);
+    const f16x2 r = __builtin_convertvector(f32x2{x[i] - back[0], x[i + 1] - back[1]}, f16x2);
+    h[i] = p[0];
+    h[i + 1] = p[1];
+    l[i] = r[0];
+    l[i + 1] = r[1];
+  }
+  hi = h;
+  lo = l;
 }
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -434,7 +453,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     return r;
   };
   f16x8 qf[kDepth][8];            // q16 fragment (token tile 2 Y + Rl, key block p) at [4 Rl + p]
-  bf16x8 pf[kDepth][2 * kPairs];  // P pair kPair0 + n, term t at [2 n + t]
+  f16x8 pf[kDepth][kPairs];      // P pair kPair0 + n at [n]
   u32x2 exs[kDepth];              // scale * e^{gamma_r} (fp32 bits), r = 16 (2 Y + Rl) + c
   auto load_q = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
@@ -445,13 +464,13 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
   auto load_p = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
 #pragma unroll
-    for (int i = 0; i < 2 * kPairs; ++i) {
-      const int pi = kPair0 + (i >> 1), off = p_offset(pi) + (i & 1) * p_term_bytes(pi);
+    for (int i = 0; i < kPairs; ++i) {
+      const int pi = kPair0 + i, off = p_offset(pi);
       if (p_half(pi)) {  // the upper half of the lane's slots is zero
         const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(r.p, L.lane * 8, off, 0);
-        pf[B][i] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], 0u, 0u});
+        pf[B][i] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], 0u, 0u});
       } else {
-        pf[B][i] = __builtin_bit_cast(bf16x8, ld16(r.p, vo_f, off));
+        pf[B][i] = __builtin_bit_cast(f16x8, ld16(r.p, vo_f, off));
       }
     }
     exs[B] = __builtin_amdgcn_raw_buffer_load_b64(r.g, 16 * L.c16 + 8 * Y, 256, 0);
@@ -469,7 +488,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     lds_barrier();  // chunk c handed over
     const u32x4 *xb = &xch[c & 1][0][L.lane];
     f32x4 ya[kS][kNV][2];
-    bf16x8 dh[kS][kNV][kNQ], dl[kS][kNV][kNQ];
+    f16x8 dh[kS][kNV][kNQ], dl[kS][kNV][kNQ];
 #pragma unroll
     for (int st = 0; st < kS; ++st)
 #pragma unroll
@@ -492,7 +511,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
           for (int Rl = 0; Rl < 2; ++Rl)
             ya[st][ct][Rl] = mfma(s16[p], qf[B][4 * Rl + p], ya[st][ct][Rl]);
 #pragma unroll
-        for (int q = 0; q < kNQ; ++q) split8(v[2 * q], v[2 * q + 1], dh[st][ct][q], dl[st][ct][q]);
+        for (int q = 0; q < kNQ; ++q) split8_f16(v[2 * q], v[2 * q + 1], dh[st][ct][q], dl[st][ct][q]);
       }
     __builtin_amdgcn_sched_barrier(0);
     load_q(Bc, rn);
@@ -511,9 +530,8 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
 #pragma unroll
           for (int q = 0; q <= (R >> 1); ++q) {
             const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
-            pa[Rl] = mfma(dh[st][ct][q], pf[B][2 * n], pa[Rl]);
-            pa[Rl] = mfma(dl[st][ct][q], pf[B][2 * n], pa[Rl]);
-            pa[Rl] = mfma(dh[st][ct][q], pf[B][2 * n + 1], pa[Rl]);
+            pa[Rl] = mfma(dh[st][ct][q], pf[B][n], pa[Rl]);
+            pa[Rl] = mfma(dl[st][ct][q], pf[B][n], pa[Rl]);
           }
         }
         // a state without an output destination gets an empty store range
@@ -545,13 +563,18 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
 // their first requests for a chunk would all wait on the same misses to the
 // last-level cache or HBM. Per chunk step this wave requests, one 128-byte
 // line per lane, this work-group's share of the lines of chunk c + kDepth +
-// kL2Lead: 1/members of the key head's K^T and q16 blocks, 1/8 of the value
-// head's w16, P and gate blocks, and its own u slice. The loads go to LDS
+// kL2Lead: 1/members of the key head's K^T and q16 blocks and, when
+// warm_values is set, 1/8 of the value head's w16, P and gate blocks and its
+// own u slice. The host sets warm_values when the intermediates outgrow the
+// last-level cache (they then come from HBM); when they fit, the second
+// request per lane cost more than it saved (T = 4096: stage 2 52.3 us with
+// the key head's lines only, 54.7 us with both). The loads go to LDS
 // (LDS-DMA: no register is written) and are never read, so nothing waits on
 // them until the wave ends. Requests past the last chunk repeat its lines.
 template <bool kF32In, int kDepth>
 __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const StageBuffers &in,
-                                             int member, int members, uint32_t *sink) {
+                                             int member, int members, uint32_t *sink,
+                                             bool warm_values) {
   constexpr int kKLines = (kF32In ? 32 : 16) * 8;
   constexpr int kHLines = kKLines + 128;             // K^T image, q16
   constexpr int kWLines = 128, kPLines = kPBytes / 128;
@@ -572,6 +595,13 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
     const uint64_t gb = reinterpret_cast<uint64_t>(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride);
     const uint64_t ub = reinterpret_cast<uint64_t>(
         in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 64 * 3);
+    if (!warm_values) {  // the key head's lines only: one request per lane
+      const int lh = min(member * nh + min(L.lane, nh - 1), kHLines - 1);
+      const uint64_t a = lh < kKLines ? kb + 128u * lh : qb + 128u * (lh - kKLines);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)a,
+                                       (__attribute__((address_space(3))) void *)sink, 4, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = L.lane + 64 * i;
@@ -608,7 +638,7 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
                              kInterWavesPerSimd<kNV>) void inter_kernel(
     StageBuffers in, const float *__restrict__ h0, const int32_t *__restrict__ cu,
     float *__restrict__ o, float *__restrict__ hT, int n_max, int H, int Hv, int t_max, int nt,
-    SegScratch seg) {
+    SegScratch seg, bool warm_values) {
   __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags * kS * kNV][64];
   __shared__ uint32_t l2_sink[64];
   // per chunk (double-buffered) the gate factors e^{gamma_last - gamma} by token
@@ -662,7 +692,7 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   else if (wave == 3)
     helper_wave<kDepth, 1, kS, kNV>(L, W, in, xch);
   else if constexpr (kWarmWave<kF32In, kDepth, kS, kNV>)
-    l2_warm_wave<kF32In, kDepth>(L, W, in, member, members, l2_sink);
+    l2_warm_wave<kF32In, kDepth>(L, W, in, member, members, l2_sink, warm_values);
 }
 
 // ---- two-segment fix-up ------------------------------------------------------
@@ -806,8 +836,15 @@ hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *c
   constexpr int kThr = kInterThreads<kF32In, kDepth, kS, kNV>;
   dim3 grid;
   if (!flat_grid(kS * rounds * kXcds * members, kThr, grid)) return hipErrorInvalidValue;
+  // warm the value heads' lines too when the intermediates exceed about 160
+  // MiB (the last-level cache is 256 MB and also holds the inputs and o)
+  const int64_t per_chunk = static_cast<int64_t>(hv) * (16 * 1024 + kD * kC * 3 + kPBytes +
+                                                        kGateStride * 4) +
+                            static_cast<int64_t>(h) * ((kF32In ? 32 : 16) * 1024 + 16 * 1024);
+  const bool warm_values = static_cast<int64_t>(nt) * per_chunk > (160ll << 20);
   hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS, kNV>), grid, dim3(kThr), 0, stream,
-                        start, stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt, seg);
+                        start, stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt, seg,
+                        warm_values);
   return hipGetLastError();
 }
 

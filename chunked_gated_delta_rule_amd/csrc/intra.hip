@@ -19,8 +19,8 @@
 //   kimg  bf16 per (h, chunk)   K^T fragments for the state update (hi[, lo])
 //   uimg  f24 per (hv, chunk)   u fragments rounded to 24-bit floats (fp32's top
 //                               three bytes), one 768-byte block per 16 x 16 tile
-//   pimg  bf16 per (hv, chunk)  P = scale * tril(q k^T * Gamma) as hi + lo, the
-//                               two half-zero pairs packed to 8 bytes per lane
+//   pimg  fp16 per (hv, chunk)  P = scale * tril(q k^T * Gamma), the two
+//                               half-zero pairs packed to 8 bytes per lane
 //   gimg  fp32 per (hv, chunk)  e^{gamma_last - gamma}, scale e^gamma (ordered
 //                               [c][R] for r = 16 R + c), e^{gamma_last}
 // P is the intra-chunk attention term of the output (AMX page, section 5); it
@@ -579,7 +579,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     }
     wave_lds_sync();
 
-    // ---- P = scale * tril(q k^T * Gamma), this wave's pairs, as hi + lo bf16
+    // ---- P = scale * tril(q k^T * Gamma), this wave's pairs, as fp16
     // pair lane (g, c): tile (2q, R) rows 4 g + i then tile (2q + 1, R).
 #pragma unroll
     for (int n2 = 0; n2 < 2; ++n2) {
@@ -598,16 +598,13 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
             x[4 * hf + i] = (j <= r && r < L) ? scale * pacc[2 * n2 + hf][i] * fast_exp2(gr - gj[i]) : 0.f;
           }
         }
-        u32x4 hi, lo;
-        split8_words(x, hi, lo);
         char *dst = reinterpret_cast<char *>(out.pimg) + ((int64_t)hv * nt + slot) * kPBytes +
                     p_offset(pi);
         if (p_half(pi)) {  // x[4..7] are above the diagonal: only the first 8 bytes
-          *reinterpret_cast<u32x2 *>(dst + lane * 8) = u32x2{hi[0], hi[1]};
-          *reinterpret_cast<u32x2 *>(dst + 512 + lane * 8) = u32x2{lo[0], lo[1]};
+          *reinterpret_cast<u32x2 *>(dst + lane * 8) = u32x2{pack_f16(x[0], x[1]), pack_f16(x[2], x[3])};
         } else {
-          *reinterpret_cast<u32x4 *>(dst + lane * 16) = hi;
-          *reinterpret_cast<u32x4 *>(dst + 1024 + lane * 16) = lo;
+          *reinterpret_cast<u32x4 *>(dst + lane * 16) =
+              u32x4{pack_f16(x[0], x[1]), pack_f16(x[2], x[3]), pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
         }
       }
     }

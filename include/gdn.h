@@ -127,11 +127,10 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
  *         16 x 16 tile per 768-byte block; each lane's four values are 24-bit
  *         floats (the upper three bytes of fp32, rounded to nearest even),
  *         value i in bytes 3 i .. 3 i + 2 of the lane's 12
- *   pimg  bf16 [hv, nt_max, 10 KB]: scale * tril(q k^T * Gamma) as hi + lo
- *         terms of six 16 x 32 fragments; pairs 0 and 3 keep the 8 bytes per
- *         lane below the diagonal (512-byte terms), the others 16 (1 KB);
- *         term offsets 0, 512 | 1024, 2048 | 3072, 4096 | 5120, 5632 |
- *         6144, 7168 | 8192, 9216
+ *   pimg  fp16 [hv, nt_max, 5 KB]: scale * tril(q k^T * Gamma) as six 16 x 32
+ *         fragments; pairs 0 and 3 keep the 8 bytes per lane below the
+ *         diagonal (512-byte blocks), the others 16 (1 KB); block offsets
+ *         0, 512, 1536, 2560, 3072, 4096
  *   gimg  fp32 [hv, nt_max, 192]: per token e^{gamma_last - gamma} [64],
  *         scale * e^gamma [64] with token 16 R + c at 4 c + R, then
  *         e^{gamma_last}

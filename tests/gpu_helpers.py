@@ -200,7 +200,7 @@ def workspace_views(cfg, ws):
         q16=view("q16", torch.float16, (cfg.h, nt, 16, 64, 8)),
         kimg=view("kimg", torch.bfloat16, (cfg.h, nt, nk, 64, 8)),
         uimg=view("uimg", torch.int32, (cfg.hv, nt, 8, 4, 64, 3)),
-        pimg=view("pimg", torch.bfloat16, (cfg.hv, nt, 10 * 512)),
+        pimg=view("pimg", torch.float16, (cfg.hv, nt, 5 * 512)),
         gimg=view("gimg", torch.float32, (cfg.hv, nt, 192)),
         nt=nt, nk=nk)
 
@@ -257,21 +257,20 @@ def decode_uimg(uimg_slot):
     return U
 
 
-P_OFFSET = (0, 1024, 3072, 5120, 6144, 8192)  # bytes of each pair's hi term
-P_HALF = (True, False, False, True, False, False)  # 8 bytes per lane and term
+P_OFFSET = (0, 512, 1536, 2560, 3072, 4096)  # bytes of each pair's block
+P_HALF = (True, False, False, True, False, False)  # 8 bytes per lane
 
 
 def decode_pimg(pimg_slot):
-    """[10 KB of bf16] hi/lo terms -> P [64 r, 64 j] (hi + lo), zero outside the
-    pairs and in the packed-out upper halves of pairs 0 and 3."""
+    """[5 KB of fp16] -> P [64 r, 64 j], zero outside the pairs and in the
+    packed-out upper halves of pairs 0 and 3."""
     x = pimg_slot.float().numpy().astype(np.float64)
     P = np.zeros((64, 64))
     for pi, (q, R) in enumerate(PAIRS):
-        per = 4 if P_HALF[pi] else 8  # bf16 values per lane and term
-        hi = x[P_OFFSET[pi] // 2:][:64 * per].reshape(64, per)
-        lo = x[P_OFFSET[pi] // 2 + 64 * per:][:64 * per].reshape(64, per)
+        per = 4 if P_HALF[pi] else 8  # fp16 values per lane
+        blk = x[P_OFFSET[pi] // 2:][:64 * per].reshape(64, per)
         for lane in range(64):
             g, c = lane // 16, lane % 16
             for j in range(per):
-                P[16 * R + c, frag_token(q, g, j)] = hi[lane, j] + lo[lane, j]
+                P[16 * R + c, frag_token(q, g, j)] = blk[lane, j]
     return P

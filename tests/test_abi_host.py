@@ -65,7 +65,7 @@ def test_workspace_layout(lib, dtype, nk):
     al = lambda x: (x + 255) // 256 * 256
     nt = index_table.nt_max(T, N)
     sizes = [("w16", Hv * nt * 16 * 1024), ("q16", H * nt * 16 * 1024), ("kimg", H * nt * nk * 1024),
-             ("uimg", Hv * nt * 64 * 128 * 3), ("pimg", Hv * nt * 10 * 1024),
+             ("uimg", Hv * nt * 64 * 128 * 3), ("pimg", Hv * nt * 5 * 1024),
              ("gimg", Hv * nt * 192 * 4), ("table", nt * 8), ("order", N * 4)]
     lay = gdn.gdn_workspace_layout(cfg)
     at = 0

@@ -162,7 +162,7 @@ def test_intra_stage_intermediates(dtype):
     log(f"  w err {ew:.3e}  u err {eu:.3e}  P err {ep:.3e}  gate err {eg:.3e}")
     assert ew < 1e-3   # fp16 storage of w: half an ulp is 2^-12 of the value
     assert eu < 1e-4
-    assert ep < 2e-5   # hi + lo bf16 carries ~16 significant bits
+    assert ep < 5e-4   # fp16 storage of P: half an ulp is 2^-12 of the value
     assert eg < 1e-5
 
 
