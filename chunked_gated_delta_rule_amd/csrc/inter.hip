@@ -92,11 +92,12 @@ constexpr bool kWarmWave = kNV == 1 && !(kF32In && kDepth == 2) && (kS == 1 || k
 constexpr int kDepthSeg = 1;  // prefetch depth of the two-state walk (keeps the warm-up wave)
 
 // Chunks of segment A (walked from h0 with one state) when a sequence of nc
-// chunks is walked in two segments: the first ceil(nc / 2). Segment B carries
-// two states, but segment A's walk is no faster per chunk where the operands
-// come from HBM (T = 32768: splits giving B 3/8, 2/5 or 7/16 of the chunks
-// took stage 2 from 508 to 556, 541 and 532 us).
-constexpr int kSegBNum = 1, kSegBDen = 2;
+// chunks is walked in two segments: all but floor(2 nc / 5). Segment B carries
+// two states (twice the products per chunk), segment A one; with the operands
+// coming from HBM both are bound mostly by their loads, so the balance point
+// is near the middle (T = 32768: B taking 1/2, 2/5, 3/8 and 1/3 of the chunks
+// gave stage 2 503, 488, 495 and 509 us).
+constexpr int kSegBNum = 2, kSegBDen = 5;
 __host__ __device__ constexpr int seg_split(int nc) { return nc - nc * kSegBNum / kSegBDen; }
 template <bool kF32In, int kDepth, int kS, int kNV>
 constexpr int kInterThreads = kWarmWave<kF32In, kDepth, kS, kNV> ? 320 : 256;
@@ -229,6 +230,7 @@ struct Walk {
   const float *init0;
   float *out[2];
   float *fin[2];
+  bool two;  // state 1 is carried (segment B of the two-segment walk)
 };
 
 template <bool kF32In, int kDepth, int X, int kS, int kNV>
@@ -325,6 +327,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
+        if (st == 1 && !W.two) continue;  // segment A carries state 0 only
         u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
         f16x8 s16[2];
 #pragma unroll
@@ -361,6 +364,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
+        if (st == 1 && !W.two) continue;  // segment A carries state 0 only
         const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
         f32x4 v[4];
 #pragma unroll
@@ -381,6 +385,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) {
+          if (st == 1 && !W.two) continue;
 #pragma unroll
           for (int tl = 0; tl < 4; ++tl)
             S[st][ct][tl] = mfma(k[B][2 * tl + q], eh[st][ct][q], S[st][ct][tl]);
@@ -493,6 +498,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
+        if (st == 1 && !W.two) continue;  // segment A carries state 0 only
         const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
         f16x8 s16[4];
 #pragma unroll
@@ -523,6 +529,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
+        if (st == 1 && !W.two) continue;  // segment A carries state 0 only
         f32x4 pa[2] = {zero4(), zero4()};
 #pragma unroll
         for (int Rl = 0; Rl < 2; ++Rl) {
@@ -676,11 +683,11 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   L.nt = nt;
   Walk W;
   if (kS == 1) {
-    W = Walk{0, L.nc, h0, {o, nullptr}, {hT, nullptr}};
+    W = Walk{0, L.nc, h0, {o, nullptr}, {hT, nullptr}, false};
   } else {
     const int cm = seg_split(L.nc);
-    W = role == 0 ? Walk{0, cm, h0, {o, nullptr}, {seg.sa, nullptr}}
-                  : Walk{cm, L.nc, nullptr, {o, seg.oh}, {seg.z, seg.phi}};
+    W = role == 0 ? Walk{0, cm, h0, {o, nullptr}, {seg.sa, nullptr}, false}
+                  : Walk{cm, L.nc, nullptr, {o, seg.oh}, {seg.z, seg.phi}, true};
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0)

@@ -68,10 +68,11 @@ typedef struct {
   gdn_dtype qkv_dtype; /* dtype of q, k, v: GDN_BF16 or GDN_F32 */
   gdn_dtype o_dtype;   /* dtype of o: GDN_F32 (the only one supported) */
   float scale;         /* output scale; <= 0 selects 1 / sqrt(dk) */
-  int32_t segments;    /* stage-2 walk of each sequence: 1 = one piece; 2 = its two
-                          halves at once (the first from the initial state, the
-                          second from zero and from the identity), then a fix-up
-                          (the recurrence is affine in the starting state);
+  int32_t segments;    /* stage-2 walk of each sequence: 1 = one piece; 2 = two
+                          segments at once (the first 3/5 of its chunks from the
+                          initial state, the rest from zero and from the
+                          identity), then a fix-up (the recurrence is affine in
+                          the starting state);
                           0 = automatic: 2 when t_max >=
                           GDN_SEGMENT_MIN_TOKENS and the one-piece stage-2 grid fills
                           at most half of the current device's compute units */
@@ -93,9 +94,9 @@ typedef struct {
 
 /* Largest valid gdn_config.t_max / n_max. Each kernel takes at most
  * 2^31 - 1 work-groups per launch. Within these limits only the fix-up of the
- * two-segment walk can need more: about n_max * hv * t_max / 256 work-groups,
- * so with segments = 2 and n_max * hv * t_max above about 2^39 the forward
- * returns GDN_ERR_CAPACITY. That check runs on the host before anything is
+ * two-segment walk can need more: about n_max * hv * t_max / 320
+ * work-groups, so with segments = 2 and n_max * hv * t_max above about
+ * 2^39.3 the forward returns GDN_ERR_CAPACITY. That check runs on the host before anything is
  * queued, like every other check. The automatic choice takes two segments
  * only for grids that fill at most half of the device, far inside that bound. */
 #define GDN_T_MAX_LIMIT (1 << 24)

@@ -275,8 +275,8 @@ def test_recurrent_entry_points_host_errors(lib):
 
 def test_two_segment_fixup_past_the_launch_limit_is_refused_on_the_host(lib):
     """Both capacities at their limits with two segments forced and three
-    value heads: segment B holds half of the 2^18 chunks, so the fix-up would
-    need 16384 * 3 * (65536 + 1) > 2^31 - 1 work-groups, and the forward (and
+    value heads: segment B holds 2/5 of the 2^18 chunks, so the fix-up would
+    need 16384 * 3 * (52429 + 1) > 2^31 - 1 work-groups, and the forward (and
     the inter stage alone) returns GDN_ERR_CAPACITY from the host checks,
     before anything is queued (no device exists here)."""
     cfg = gdn.make_config(gdn.GDN_T_MAX_LIMIT, gdn.GDN_N_MAX_LIMIT, 1, 3, segments=2)
