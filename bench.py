@@ -229,6 +229,10 @@ def main():
                     help="after the timed region, time N more steps each preceded by a 1 GiB "
                          "device write that evicts the last-level cache (reported apart from "
                          "the headline value; 0 to skip)")
+    ap.add_argument("--front-dtype", choices=("f16", "f32"), default="f16",
+                    help="front workload: precision the front's q, k, v enter the chunk "
+                         "forward in (fused path: GDN_F16 rounds them to fp16, GDN_F32 keeps "
+                         "fp32; the unfused path always hands fp32 to the forward)")
     ap.add_argument("--unfused-front", action="store_true",
                     help="front workload: run the standalone front, then the forward "
                          "(default: the front fused into stage 1)")
@@ -264,7 +268,9 @@ def main():
     has_front = wl.qkv is not None
     fused_front = has_front and not args.unfused_front
     serial = args.workload in RECURRENT_WORKLOADS
-    qkv_dtype = torch.float32 if has_front else wl.qkv_dtype
+    qkv_dtype = wl.qkv_dtype
+    if has_front:
+        qkv_dtype = torch.float16 if fused_front and args.front_dtype == "f16" else torch.float32
     cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype)
     ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=dev)
     o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
@@ -396,7 +402,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if qkv_dtype == torch.bfloat16 else "f32-split-bf16",
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "f16",
+                  torch.float32: "f32-split-bf16"}[qkv_dtype],
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": tokens, "sequences": wl.n_seqs, "H": wl.H,
                    "Hv": wl.Hv, "Dk": 128, "Dv": 128, "chunk": 64,

@@ -23,7 +23,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "GDNError", "gdn_config", "GDN_BF16", "GDN_F32", "load_library", "library_path",
+    "GDNError", "gdn_config", "GDN_BF16", "GDN_F32", "GDN_F16", "load_library", "library_path",
     "gdn_nt_max", "gdn_workspace_size", "gdn_build_chunk_indices", "gdn_front_conv_silu_l2",
     "gdn_chunk_fwd_intra", "gdn_chunk_fwd_inter", "gdn_chunk_fwd", "gdn_status_str",
     "gdn_workspace_layout", "make_config", "chunk_gated_delta_rule", "EXPORTED_SYMBOLS",
@@ -35,6 +35,7 @@ __all__ = [
 
 GDN_BF16 = 0
 GDN_F32 = 1
+GDN_F16 = 2
 GDN_FUSED_INDEX_MAX_SEQS = 256  # include/gdn.h
 GDN_SEGMENT_MIN_TOKENS = 2048  # include/gdn.h
 GDN_FOUR_TILE_MIN_TOKENS = 384  # include/gdn.h
@@ -118,17 +119,17 @@ def load_library():
     return lib
 
 
-_TORCH_DTYPE = {torch.bfloat16: GDN_BF16, torch.float32: GDN_F32}
-_GDN_DTYPE = {GDN_BF16: torch.bfloat16, GDN_F32: torch.float32}
+_TORCH_DTYPE = {torch.bfloat16: GDN_BF16, torch.float32: GDN_F32, torch.float16: GDN_F16}
+_GDN_DTYPE = {GDN_BF16: torch.bfloat16, GDN_F32: torch.float32, GDN_F16: torch.float16}
 
 
 def make_config(t_max, n_max, h, hv, qkv_dtype=GDN_BF16, scale=0.0, o_dtype=GDN_F32,
                 dk=128, dv=128, chunk=64, segments=0, tiles=0) -> gdn_config:
-    """A gdn_config; qkv_dtype is GDN_BF16 / GDN_F32 or torch.bfloat16 /
-    torch.float32 (any other torch dtype raises ValueError)."""
+    """A gdn_config; qkv_dtype is GDN_BF16 / GDN_F32 / GDN_F16 or the torch
+    dtype (bfloat16, float32, float16; any other raises ValueError)."""
     if isinstance(qkv_dtype, torch.dtype):
         if qkv_dtype not in _TORCH_DTYPE:
-            raise ValueError(f"q/k/v dtype {qkv_dtype}: bfloat16 or float32 expected")
+            raise ValueError(f"q/k/v dtype {qkv_dtype}: bfloat16, float32 or float16 expected")
         qkv_dtype = _TORCH_DTYPE[qkv_dtype]
     return gdn_config(int(t_max), int(n_max), int(h), int(hv), int(dk), int(dv), int(chunk),
                       int(qkv_dtype), int(o_dtype), float(scale), int(segments), int(tiles))
@@ -379,7 +380,7 @@ def gdn_recurrent_fwd_timed(cfg, q, k, v, g, beta, h0, cu_seqlens, o, hT, ev_sta
 
 def _same_qkv_dtype(q, k, v):
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _TORCH_DTYPE:
-        raise ValueError(f"q, k, v must share one dtype in (bfloat16, float32): "
+        raise ValueError(f"q, k, v must share one dtype in (bfloat16, float32, float16): "
                          f"{q.dtype}, {k.dtype}, {v.dtype}")
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
         raise ValueError(f"q, k [T, H, 128] and v [T, Hv, 128] expected: {tuple(q.shape)}, "

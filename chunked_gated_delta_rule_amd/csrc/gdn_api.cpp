@@ -27,7 +27,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 gdn_status check_config(const gdn_config *cfg) {
   if (!cfg) return GDN_ERR_INVALID_ARG;
   if (cfg->t_max < 0 || cfg->n_max < 1 || cfg->h < 1 || cfg->hv < 1) return GDN_ERR_INVALID_ARG;
-  if (cfg->qkv_dtype != GDN_BF16 && cfg->qkv_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
+  if (cfg->qkv_dtype != GDN_BF16 && cfg->qkv_dtype != GDN_F32 && cfg->qkv_dtype != GDN_F16)
+    return GDN_ERR_INVALID_ARG;
   if (cfg->o_dtype != GDN_BF16 && cfg->o_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
   if (std::isnan(cfg->scale) || std::isinf(cfg->scale)) return GDN_ERR_INVALID_ARG;
   if (cfg->segments < 0 || cfg->segments > 2) return GDN_ERR_INVALID_ARG;
@@ -79,7 +80,7 @@ bool ranks_sequences(const gdn_config *cfg) {
 gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   const size_t t = static_cast<size_t>(cfg->t_max), nt = static_cast<size_t>(nt_max_of(cfg));
   const size_t h = static_cast<size_t>(cfg->h), hv = static_cast<size_t>(cfg->hv);
-  const size_t nk = cfg->qkv_dtype == GDN_F32 ? 32 : 16;
+  const size_t nk = cfg->qkv_dtype == GDN_BF16 ? 16 : 32;  // K^T terms (hi[, lo])
   gdn_workspace_layout_t l;
   size_t at = 0;
   auto take = [&](size_t bytes) { const size_t here = at; at += align_up(bytes); return here; };
@@ -144,6 +145,15 @@ float scale_of(const gdn_config *cfg) {
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+// How stage 1 takes q, k, v; stage 2 reads bf16 input's intermediates in one
+// layout and fp32 / fp16 input's (K^T as bf16 hi + lo) in the other.
+gdn::InKind in_kind(const gdn_config *cfg) {
+  return cfg->qkv_dtype == GDN_F32 ? gdn::InKind::kF32
+         : cfg->qkv_dtype == GDN_F16 ? gdn::InKind::kF16
+                                     : gdn::InKind::kBf16;
+}
+bool split_k(const gdn_config *cfg) { return cfg->qkv_dtype != GDN_BF16; }
+
 // Every stage-2 grid of a (validated) config fits one launch; checked before
 // anything is queued, so a config past the limits returns without side effects.
 gdn_status check_inter_grids(const gdn_config *cfg) {
@@ -181,7 +191,7 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
     if (!conv.conv_w) return GDN_ERR_INVALID_ARG;
     if (!aligned16(conv.qkv) || (reinterpret_cast<uintptr_t>(conv.conv_w) & 1u))
       return GDN_ERR_INVALID_ARG;
-    if (conv.d_conv < 1 || conv.d_conv > 4 || cfg->qkv_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+    if (conv.d_conv < 1 || conv.d_conv > 4 || cfg->qkv_dtype == GDN_BF16) return GDN_ERR_UNSUPPORTED;
     q = k = v = conv.qkv;
   }
   if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
@@ -207,13 +217,13 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
   const gdn::StageBuffers b = stage_buffers(cfg, l, workspace);
   if (cfg->t_max > 0) {
     // without a table, stage 1 locates its chunks and fills ws_table itself
-    const hipError_t e = gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
+    const hipError_t e = gdn::launch_intra(in_kind(cfg), q, k, v, g, beta, cu_seqlens,
                                            chunk_indices, ws_table, cfg->n_max, nt_max_of(cfg),
                                            cfg->h, cfg->hv, cfg->t_max, scale_of(cfg), b, s, ev[1],
                                            conv);
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
-  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, b, h0, cu_seqlens, cfg->n_max,
+  return from_hip(gdn::launch_inter(split_k(cfg), b, h0, cu_seqlens, cfg->n_max,
                                     cfg->h, cfg->hv, cfg->t_max, nt_max_of(cfg),
                                     static_cast<float *>(o), hT, s, ev[2], segments_of(cfg),
                                     tiles_of(cfg),
@@ -231,6 +241,7 @@ gdn_status recurrent_impl(const gdn_config *cfg, const void *q, const void *k, c
       (h0 && !aligned16(h0)) || (hT && !aligned16(hT)) || (reinterpret_cast<uintptr_t>(g) & 3u) ||
       (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return GDN_ERR_INVALID_ARG;
+  if (cfg->qkv_dtype == GDN_F16) return GDN_ERR_UNSUPPORTED;
   return from_hip(gdn::launch_recurrent(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, h0,
                                         cu_seqlens, cfg->n_max, cfg->t_max, cfg->h, cfg->hv,
                                         scale_of(cfg),
@@ -304,7 +315,7 @@ gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *q, const void 
   const gdn_status ws = check_workspace(l, workspace, ws_bytes);
   if (ws != GDN_OK) return ws;
   if (cfg->t_max == 0) return GDN_OK;
-  return from_hip(gdn::launch_intra(cfg->qkv_dtype == GDN_F32, q, k, v, g, beta, cu_seqlens,
+  return from_hip(gdn::launch_intra(in_kind(cfg), q, k, v, g, beta, cu_seqlens,
                                     chunk_indices, nullptr, cfg->n_max, nt_max_of(cfg), cfg->h,
                                     cfg->hv, cfg->t_max, scale_of(cfg), stage_buffers(cfg, l, workspace),
                                     as_stream(stream)));
@@ -324,7 +335,7 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
   if (ws != GDN_OK) return ws;
   const gdn_status grids = check_inter_grids(cfg);
   if (grids != GDN_OK) return grids;
-  return from_hip(gdn::launch_inter(cfg->qkv_dtype == GDN_F32, stage_buffers(cfg, l, workspace), h0,
+  return from_hip(gdn::launch_inter(split_k(cfg), stage_buffers(cfg, l, workspace), h0,
                                     cu_seqlens, cfg->n_max, cfg->h, cfg->hv, cfg->t_max,
                                     nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream),
                                     {}, segments_of(cfg), tiles_of(cfg), seg_scratch(l, workspace)));

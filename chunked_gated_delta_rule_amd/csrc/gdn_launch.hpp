@@ -81,15 +81,21 @@ hipError_t launch_front(const void *qkv, const void *conv_w, int32_t d_conv,
                         int32_t hv, float *q, float *k, float *v, hipStream_t stream,
                         KernelEvents ev = {});
 
+// How stage 1 takes q, k, v: bf16 (one bf16 term), fp32 (split into bf16
+// hi + lo, three-term products) or fp16 (one fp16 term). fp32 and fp16 both
+// write the K^T image as bf16 hi + lo terms, so stage 2 reads them alike.
+enum class InKind { kBf16 = 0, kF32 = 1, kF16 = 2 };
+
 // table: the chunk-index table, or null to have each work-group locate its
 // chunk from cu_seqlens (n_max <= kFusedIndexMaxSeqs) and write the table into
 // table_out. With conv.qkv set, q, k, v are ignored and computed from the
-// pre-conv channels (f32_in must then be true).
-hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v, const float *g,
-                        const float *beta, const int32_t *cu_seqlens, const int32_t *table,
-                        int32_t *table_out, int32_t n_max, int32_t nt_max, int32_t h, int32_t hv,
-                        int32_t t_max, float scale, const StageBuffers &out, hipStream_t stream,
-                        KernelEvents ev = {}, ConvIn conv = {});
+// pre-conv channels, kept in fp32 (in_kind kF32) or rounded to fp16 (kF16).
+hipError_t launch_intra(InKind in_kind, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const int32_t *cu_seqlens,
+                        const int32_t *table, int32_t *table_out, int32_t n_max, int32_t nt_max,
+                        int32_t h, int32_t hv, int32_t t_max, float scale,
+                        const StageBuffers &out, hipStream_t stream, KernelEvents ev = {},
+                        ConvIn conv = {});
 
 hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const void *v,
                             const float *g, const float *beta, const float *h0,

@@ -218,7 +218,7 @@ __device__ __forceinline__ ConvRaw load_conv(const ConvIn &ci, int channels, int
 // Rows rr < valid of the thread's 4 x 8 block as fp32, split into bf16 hi + lo
 // (rows >= valid are zero, as rows past a sequence are for stored inputs).
 // kTaps = d_conv, a template parameter so that every register index is fixed.
-template <int kTaps>
+template <int kTaps, bool kHalf>
 __device__ __forceinline__ void conv_terms(const ConvRaw &r, bool l2, int valid,
                                            u32x4 (&hi)[4], u32x4 (&lo)[4]) {
   float x[7][8];
@@ -249,8 +249,43 @@ __device__ __forceinline__ void conv_terms(const ConvRaw &r, bool l2, int valid,
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[c] = 0.f;
     }
-    split8_words(y, hi[rr], lo[rr]);
+    if constexpr (kHalf) {  // rounded to fp16 (nearest even), one term
+      hi[rr] = u32x4{pack_f16(y[0], y[1]), pack_f16(y[2], y[3]), pack_f16(y[4], y[5]),
+                     pack_f16(y[6], y[7])};
+      lo[rr] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      split8_words(y, hi[rr], lo[rr]);
+    }
   }
+}
+
+// MFMA on two 16-bit operand fragments held as raw bits: bf16, or fp16 when
+// kHalf (fp16 inputs).
+template <bool kHalf>
+__device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  if constexpr (kHalf)
+    return mfma(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c);
+  else
+    return mfma(a, b, c);
+}
+
+// fp16 bits -> float.
+__device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+// Eight fp32 values split into fp16 hi and lo words (x = hi + lo to about 22
+// significant bits; hi rounded to nearest even).
+__device__ __forceinline__ void split8_words_f16(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_f16(x[2 * i], x[2 * i + 1]);
+    l[i] = pack_f16(x[2 * i] - f16_bits_to_float(h[i] & 0xffffu),
+                    x[2 * i + 1] - f16_bits_to_float(h[i] >> 16));
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 // P pairs (q, R): token block q (32 tokens) of column tile R (16 outputs);
@@ -315,8 +350,11 @@ __device__ __forceinline__ void write_walk_order(const int32_t *__restrict__ cu,
 }
 
 // kTaps: 0 reads q, k, v; 1..4 computes them from the pre-conv channels with a
-// kTaps-tap conv (the fused front).
-template <bool kF32In, int kTaps>
+// kTaps-tap conv (the fused front). kHalf: q, k, v are fp16 (read as fp16, or
+// from the fused front rounded to fp16); the row tiles and their MFMAs are then
+// fp16 instead of bf16, the T s items are split into fp16 hi + lo, and the K^T
+// image is written as exact bf16 hi + lo terms (the layout of fp32 input).
+template <bool kF32In, int kTaps, bool kHalf = false>
 __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     const void *__restrict__ qin, const void *__restrict__ kin, const void *__restrict__ vin,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
@@ -324,7 +362,8 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     StageBuffers out, int H, int Hv, int t_max, int nt, float scale, ConvIn ci,
     bool head_fastest) {
   constexpr bool kConv = kTaps > 0;
-  static_assert(!kConv || kF32In, "the fused front produces fp32 q, k, v");
+  static_assert(!kConv || kF32In || kHalf, "the fused front produces fp32 or fp16 q, k, v");
+  static_assert(!(kF32In && kHalf), "one input kind");
   using Smem = IntraSmem<kF32In>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Smem::kBytes];
   __bf16 *rk = reinterpret_cast<__bf16 *>(smem + Smem::kOffK);    // K rows (hi[, lo])
@@ -384,7 +423,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   }
   const int HG = Hv / H;
   const int slot = (t0 >> 6) + ent.x;
-  constexpr int kNK = kF32In ? 32 : 16;
+  constexpr int kNK = kF32In || kHalf ? 32 : 16;
 
   const int lrow = 4 * (tid >> 4);  // this thread's 4 rows and 8 columns of a tile
   const int lcol = 8 * (tid & 15);
@@ -404,7 +443,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   auto tile_terms = [&](const auto &raw, bool l2, u32x4 (&hi)[4], u32x4 (&lo)[4])
       __attribute__((always_inline)) {
     if constexpr (kConv)
-      conv_terms<kTaps>(raw, l2, L - lrow, hi, lo);
+      conv_terms<kTaps, kHalf>(raw, l2, L - lrow, hi, lo);
     else
       to_terms(raw, hi, lo);
   };
@@ -447,7 +486,22 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     const int tau = f >> 1, qq = f & 1;
     const int g4 = 4 * (lane >> 4);
     __bf16 *dst = out.kimg + ((((int64_t)h * nt + slot) * kNK + f) * 64 + lane) * 8;
-    *reinterpret_cast<bf16x8 *>(dst) = frag_tr2(rk, kLdRow, 32 * qq + g4, 32 * qq + 16 + g4, 16 * tau, lane);
+    const bf16x8 kt = frag_tr2(rk, kLdRow, 32 * qq + g4, 32 * qq + 16 + g4, 16 * tau, lane);
+    if constexpr (kHalf) {  // fp16 values as exact bf16 hi + lo terms
+      const u32x4 bits = __builtin_bit_cast(u32x4, kt);
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = f16_bits_to_float(bits[i] & 0xffffu);
+        x[2 * i + 1] = f16_bits_to_float(bits[i] >> 16);
+      }
+      u32x4 hi, lo;
+      split8_words(x, hi, lo);
+      *reinterpret_cast<u32x4 *>(dst) = hi;
+      *reinterpret_cast<u32x4 *>(dst + 16 * 64 * 8) = lo;
+    } else {
+      *reinterpret_cast<bf16x8 *>(dst) = kt;
+    }
     if constexpr (kF32In)
       *reinterpret_cast<bf16x8 *>(dst + 16 * 64 * 8) =
           frag_tr2(rk + 64 * kLdRow, kLdRow, 32 * qq + g4, 32 * qq + 16 + g4, 16 * tau, lane);
@@ -467,8 +521,13 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
       const u32x2 a = *reinterpret_cast<const u32x2 *>(rq + off + 16 * half);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        x[4 * half + 2 * i] = __uint_as_float(a[i] << 16);
-        x[4 * half + 2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+        if constexpr (kHalf) {
+          x[4 * half + 2 * i] = f16_bits_to_float(a[i] & 0xffffu);
+          x[4 * half + 2 * i + 1] = f16_bits_to_float(a[i] >> 16);
+        } else {
+          x[4 * half + 2 * i] = __uint_as_float(a[i] << 16);
+          x[4 * half + 2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+        }
       }
       if constexpr (kF32In) {
         const u32x2 b = *reinterpret_cast<const u32x2 *>(rq + 64 * kLdRow + off + 16 * half);
@@ -503,7 +562,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 a = frag_rows(rk, kLdRow, 16 * bi, 32 * ks, lane);
         const bf16x8 bb = frag_rows(rk, kLdRow, 16 * bj, 32 * ks, lane);
-        acc = mfma(a, bb, acc);
+        acc = mma<kHalf>(a, bb, acc);
         if constexpr (kF32In) {
           const __bf16 *rlo = rk + 64 * kLdRow;
           acc = mfma(frag_rows(rlo, kLdRow, 16 * bi, 32 * ks, lane), bb, acc);
@@ -529,7 +588,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 a = frag_rows(rk, kLdRow, 16 * tj, 32 * ks, lane);
         const bf16x8 bb = frag_rows(rq, kLdRow, 16 * tr, 32 * ks, lane);
-        acc = mfma(a, bb, acc);
+        acc = mma<kHalf>(a, bb, acc);
         if constexpr (kF32In) {
           acc = mfma(frag_rows(rk + 64 * kLdRow, kLdRow, 16 * tj, 32 * ks, lane), bb, acc);
           acc = mfma(a, frag_rows(rq + 64 * kLdRow, kLdRow, 16 * tr, 32 * ks, lane), acc);
@@ -719,8 +778,13 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
         xw8[4 + i] = xu8[4 + i] * fast_exp2(g_b[i]);
       }
       u32x4 *d = ts + it * 4 * 64 + lane;
-      split8_words(xw8, d[0], d[64]);
-      split8_words(xu8, d[128], d[192]);
+      if constexpr (kHalf) {
+        split8_words_f16(xw8, d[0], d[64]);
+        split8_words_f16(xu8, d[128], d[192]);
+      } else {
+        split8_words(xw8, d[0], d[64]);
+        split8_words(xu8, d[128], d[192]);
+      }
     }
     put_rows(rv, vh, vl);
     __syncthreads();
@@ -742,10 +806,10 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
           const bf16x8 ka = frag_tr(rk, kLdRow, 32 * ks, 16 * db, lane);
           const bf16x8 vb = frag_tr(rv, kLdRow, 32 * ks, 16 * db, lane);
           f32x4 aw = wacc[db2], au = uacc[db2];
-          aw = mfma(ka, as_bf16x8(wh), aw);
-          aw = mfma(ka, as_bf16x8(wl), aw);
-          au = mfma(as_bf16x8(uh), vb, au);
-          au = mfma(as_bf16x8(ul), vb, au);
+          aw = mma<kHalf>(ka, as_bf16x8(wh), aw);
+          aw = mma<kHalf>(ka, as_bf16x8(wl), aw);
+          au = mma<kHalf>(as_bf16x8(uh), vb, au);
+          au = mma<kHalf>(as_bf16x8(ul), vb, au);
           if constexpr (kF32In) {
             aw = mfma(frag_tr(rk + 64 * kLdRow, kLdRow, 32 * ks, 16 * db, lane), as_bf16x8(wh), aw);
             au = mfma(as_bf16x8(uh), frag_tr(rv + 64 * kLdRow, kLdRow, 32 * ks, 16 * db, lane), au);
@@ -778,14 +842,14 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
 
 }  // namespace
 
-hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v, const float *g,
-                        const float *beta, const int32_t *cu_seqlens, const int32_t *table,
-                        int32_t *table_out, int32_t n_max, int32_t nt_max, int32_t h, int32_t hv,
-                        int32_t t_max, float scale,
+hipError_t launch_intra(InKind in_kind, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const int32_t *cu_seqlens,
+                        const int32_t *table, int32_t *table_out, int32_t n_max, int32_t nt_max,
+                        int32_t h, int32_t hv, int32_t t_max, float scale,
                         const StageBuffers &out, hipStream_t stream, KernelEvents ev, ConvIn conv) {
   if (!table && (n_max > kFusedIndexMaxSeqs || !table_out)) return hipErrorInvalidValue;
   if (out.order && n_max > kThreads) return hipErrorInvalidValue;  // one thread per sequence
-  if (conv.qkv && (!f32_in || !conv.conv_w || conv.d_conv < 1 || conv.d_conv > 4))
+  if (conv.qkv && (in_kind == InKind::kBf16 || !conv.conv_w || conv.d_conv < 1 || conv.d_conv > 4))
     return hipErrorInvalidValue;
   if (nt_max <= 0) return hipSuccess;
   // work-group order (see the kernel): slot fastest for one sequence, key head
@@ -793,21 +857,30 @@ hipError_t launch_intra(bool f32_in, const void *q, const void *k, const void *v
   const bool head_fastest = n_max > 1;
   dim3 grid;
   if (!flat_grid(static_cast<int64_t>(nt_max) * h, kThreads, grid)) return hipErrorInvalidValue;
-#define GDN_LAUNCH_INTRA(F32, TAPS)                                                             \
-  hipExtLaunchKernelGGL((intra_kernel<F32, TAPS>), grid, dim3(kThreads), 0, stream, ev.start,   \
-                        ev.stop, 0, q, k, v, g, beta, cu_seqlens, table, table_out, n_max, out, h, \
-                        hv, t_max, nt_max, scale, conv, head_fastest)
-  if (conv.qkv) {
+#define GDN_LAUNCH_INTRA(F32, TAPS, HALF)                                                       \
+  hipExtLaunchKernelGGL((intra_kernel<F32, TAPS, HALF>), grid, dim3(kThreads), 0, stream,       \
+                        ev.start, ev.stop, 0, q, k, v, g, beta, cu_seqlens, table, table_out,   \
+                        n_max, out, h, hv, t_max, nt_max, scale, conv, head_fastest)
+  if (conv.qkv && in_kind == InKind::kF16) {
     switch (conv.d_conv) {
-      case 1: GDN_LAUNCH_INTRA(true, 1); break;
-      case 2: GDN_LAUNCH_INTRA(true, 2); break;
-      case 3: GDN_LAUNCH_INTRA(true, 3); break;
-      default: GDN_LAUNCH_INTRA(true, 4); break;
+      case 1: GDN_LAUNCH_INTRA(false, 1, true); break;
+      case 2: GDN_LAUNCH_INTRA(false, 2, true); break;
+      case 3: GDN_LAUNCH_INTRA(false, 3, true); break;
+      default: GDN_LAUNCH_INTRA(false, 4, true); break;
     }
-  } else if (f32_in) {
-    GDN_LAUNCH_INTRA(true, 0);
+  } else if (conv.qkv) {
+    switch (conv.d_conv) {
+      case 1: GDN_LAUNCH_INTRA(true, 1, false); break;
+      case 2: GDN_LAUNCH_INTRA(true, 2, false); break;
+      case 3: GDN_LAUNCH_INTRA(true, 3, false); break;
+      default: GDN_LAUNCH_INTRA(true, 4, false); break;
+    }
+  } else if (in_kind == InKind::kF32) {
+    GDN_LAUNCH_INTRA(true, 0, false);
+  } else if (in_kind == InKind::kF16) {
+    GDN_LAUNCH_INTRA(false, 0, true);
   } else {
-    GDN_LAUNCH_INTRA(false, 0);
+    GDN_LAUNCH_INTRA(false, 0, false);
   }
 #undef GDN_LAUNCH_INTRA
   return hipGetLastError();

@@ -56,7 +56,10 @@ typedef enum {
   GDN_ERR_HIP = 5          /* a kernel launch failed */
 } gdn_status;
 
-typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+/* Element types. GDN_F16 is accepted for q, k, v by the chunked forward
+ * (gdn_chunk_fwd and its stages) and selects fp16 intermediates for the fused
+ * front (gdn_chunk_fwd_conv); the token-serial kernel takes bf16 or fp32. */
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1, GDN_F16 = 2 } gdn_dtype;
 
 typedef struct {
   int32_t t_max;       /* token capacity (rows of q, k, v, g, beta, o) */
@@ -65,7 +68,7 @@ typedef struct {
   int32_t hv;          /* value heads, a multiple of h */
   int32_t dk, dv;      /* head dims; must both be 128 */
   int32_t chunk;       /* chunk length; must be 64 */
-  gdn_dtype qkv_dtype; /* dtype of q, k, v: GDN_BF16 or GDN_F32 */
+  gdn_dtype qkv_dtype; /* dtype of q, k, v: GDN_BF16, GDN_F32 or GDN_F16 */
   gdn_dtype o_dtype;   /* dtype of o: GDN_F32 (the only one supported) */
   float scale;         /* output scale; <= 0 selects 1 / sqrt(dk) */
   int32_t segments;    /* stage-2 walk of each sequence: 1 = one piece; 2 = two
@@ -123,7 +126,8 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
  *         fragment 4 R + p, lane (g, c) holds row 16 R + c, columns
  *         32 p + 4 g + j (j < 4) and 32 p + 16 + 4 g + j - 4 (j >= 4)
  *   q16   fp16 [h, nt_max, 16, 64, 8]: q rounded to fp16, same fragments
- *   kimg  bf16 [h, nt_max, 16 (32 for fp32 input), 64, 8]: K^T fragments
+ *   kimg  bf16 [h, nt_max, 16 (32 for fp32 or fp16 input), 64, 8]: K^T
+ *         fragments (bf16 input: the values; otherwise exact hi + lo terms)
  *   uimg  u32 [hv, nt_max, dv / 16, 4, 64, 3]: u (AMX page, section 4), one
  *         16 x 16 tile per 768-byte block; each lane's four values are 24-bit
  *         floats (the upper three bytes of fp32, rounded to nearest even),
@@ -266,12 +270,17 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_config *cfg, const void *q, const voi
  * SiLU) itself from the pre-conv channels, reading a (d_conv - 1)-token halo
  * before the chunk (zero before each sequence start), with the same fp32
  * arithmetic as gdn_front_conv_silu_l2 (llama.cpp PR 399, "How (exactness)";
- * AMX page, section 7). The fp32 q, k, v never reach HBM; the result equals
- * gdn_front_conv_silu_l2 followed by gdn_chunk_fwd on its fp32 outputs.
+ * AMX page, section 7). The q, k, v never reach HBM.
  *   qkv    (device) bf16 [t_max, 2*h*dk + hv*dv], channels q | k | v, head-major
  *   conv_w (device) bf16 [2*h*dk + hv*dv, d_conv], 1 <= d_conv <= 4
- *   cfg->qkv_dtype must be GDN_F32 (the workspace holds fp32-split q, k, v
- *   intermediates: size it with GDN_F32); other arguments as gdn_chunk_fwd. */
+ *   cfg->qkv_dtype selects the precision the front's q, k, v enter the chunk
+ *   forward in: GDN_F32 keeps them in fp32, and the result equals
+ *   gdn_front_conv_silu_l2 followed by gdn_chunk_fwd (GDN_F32) on its
+ *   outputs; GDN_F16 rounds them to fp16 (nearest even), and the result
+ *   equals gdn_front_conv_silu_l2, its outputs rounded to fp16, then
+ *   gdn_chunk_fwd (GDN_F16). fp16 runs stage 1 at twice the occupancy with
+ *   one-term products; the rounding adds about 3e-4 of max |o| to the error.
+ *   The workspace is sized with the same cfg; other arguments as gdn_chunk_fwd. */
 gdn_status gdn_chunk_fwd_conv(const gdn_config *cfg, const void *qkv, const void *conv_w,
                               int32_t d_conv, const float *g, const float *beta, const float *h0,
                               const int32_t *cu_seqlens, const int32_t *chunk_indices, void *o,

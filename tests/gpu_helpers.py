@@ -189,7 +189,7 @@ def frag_token(q, g, j):
 def workspace_views(cfg, ws):
     lay = gdn.gdn_workspace_layout(cfg)
     nt = gdn.gdn_nt_max(cfg.t_max, cfg.n_max)
-    nk = 32 if cfg.qkv_dtype == gdn.GDN_F32 else 16
+    nk = 16 if cfg.qkv_dtype == gdn.GDN_BF16 else 32  # K^T terms: hi (+ lo)
 
     def view(name, dtype, shape):
         n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()

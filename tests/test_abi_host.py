@@ -118,6 +118,7 @@ def test_workspace_layout_segments(lib):
     ("dk", 64, UNSUPPORTED), ("dv", 256, UNSUPPORTED), ("chunk", 32, UNSUPPORTED),
     ("hv", 24, UNSUPPORTED), ("o_dtype", gdn.GDN_BF16, UNSUPPORTED),
     ("t_max", -1, INVALID), ("n_max", 0, INVALID), ("h", 0, INVALID), ("qkv_dtype", 7, INVALID),
+    ("qkv_dtype", 2, OK),
     ("scale", float("nan"), INVALID), ("t_max", (1 << 24) + 1, CAPACITY), ("n_max", 16385, CAPACITY),
     ("segments", 3, INVALID), ("segments", -1, INVALID), ("tiles", 3, INVALID),
     ("tiles", -1, INVALID), ("tiles", 8, INVALID), ("tiles", 4, OK), ("tiles", 1, OK),
@@ -268,6 +269,9 @@ def test_recurrent_entry_points_host_errors(lib):
     bad = gdn.make_config(256, 2, 16, 24)
     assert lib.gdn_recurrent_fwd(ctypes.byref(bad), F, F, F, F, F, None, F, F, None,
                                  None) == UNSUPPORTED
+    f16 = gdn.make_config(256, 2, 16, 32, gdn.GDN_F16)  # fp16 input: chunked forward only
+    assert lib.gdn_recurrent_fwd(ctypes.byref(f16), F, F, F, F, F, None, F, F, None,
+                                 None) == UNSUPPORTED
     assert lib.gdn_recurrent_fwd_timed(c, F, F, F, F, F, None, F, F, None, None, None, 8) == INVALID
     assert lib.gdn_recurrent_fwd_timed(c, F, F, F, F, F, None, F, F, None, None, 8, None) == INVALID
     assert lib.gdn_recurrent_fwd_timed(c, None, F, F, F, F, None, F, F, None, None, 8, 8) == INVALID
@@ -294,7 +298,8 @@ def test_binding_rejects_wrong_dtypes_and_sizes():
     first)."""
     import torch
     with pytest.raises(ValueError, match="dtype"):
-        gdn.make_config(64, 1, 1, 1, torch.float16)
+        gdn.make_config(64, 1, 1, 1, torch.float64)
+    assert gdn.make_config(64, 1, 1, 1, torch.float16).qkv_dtype == gdn.GDN_F16
     T, n, H, Hv = 64, 1, 1, 2
     cfg = gdn.make_config(T, n, H, Hv, torch.bfloat16)
     ok = dict(q=torch.zeros(T, H, 128, dtype=torch.bfloat16),
@@ -304,7 +309,7 @@ def test_binding_rejects_wrong_dtypes_and_sizes():
               h0=torch.zeros(n, Hv, 128, 128), cu=torch.tensor([0, T], dtype=torch.int32),
               o=torch.zeros(T, Hv, 128), hT=torch.zeros(n, Hv, 128, 128))
     bad_cases = [
-        ("q", torch.zeros(T, H, 128, dtype=torch.float16), "dtype"),
+        ("q", torch.zeros(T, H, 128, dtype=torch.float16), "dtype"),  # fp16 in a bf16 config
         ("k", torch.zeros(T, H, 128), "dtype"),                       # fp32 in a bf16 config
         ("v", torch.zeros(T, Hv, 64, dtype=torch.bfloat16), "elements"),
         ("q", torch.zeros(2 * T, H, 64, dtype=torch.bfloat16), "last dimension"),

@@ -93,7 +93,7 @@ def test_front_small_varlen(d_conv):
 # stage 1 alone: every intermediate against the chunked-form oracle
 # --------------------------------------------------------------------------- #
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
 def test_intra_stage_intermediates(dtype):
     wl = workloads.make_custom([130, 70, 64, 1], 2, 4, seed=5, dtype=dtype, t_max=300, n_max=5)
     log(f"intra stage {dtype}")
@@ -129,7 +129,7 @@ def test_intra_stage_intermediates(dtype):
                 q16 = decode_rowfrag(V["q16"][h, slot])
                 qref = np.zeros((64, 128))
                 qref[:L] = wl.q[t0:t0 + L, h].double().numpy()
-                if dtype == torch.bfloat16:
+                if dtype != torch.float32:
                     want = torch.from_numpy(qref).float().half().double().numpy()
                     assert np.array_equal(q16, want), "q16 is not q rounded to fp16"
                 else:
@@ -138,7 +138,8 @@ def test_intra_stage_intermediates(dtype):
                 Kd = sum(terms)
                 ref = np.zeros((64, 128))
                 ref[:L] = k64[t0:t0 + L, h]
-                tol = 0.0 if dtype == torch.bfloat16 else 2e-5 * np.max(np.abs(k64))
+                # bf16 and fp16 inputs are held exactly (fp16 as bf16 hi + lo)
+                tol = 2e-5 * np.max(np.abs(k64)) if dtype == torch.float32 else 0.0
                 assert np.max(np.abs(Kd - ref)) <= tol
             for hv in range(wl.Hv):
                 gamma, la = stages[(hv, t0)]
@@ -249,6 +250,82 @@ def test_fused_front_workload_full_size():
     eo, es = full_errors(wl, o, hT, o_ref, s_ref)
     log(f"  every lane: o err {eo:.3e}  S err {es:.3e}")
     assert eo <= O_TOL and es <= S_TOL
+
+
+@pytest.mark.parametrize("d_conv", [1, 2, 3, 4])
+def test_fused_front_fp16_equals_front_rounded_then_forward_bitwise(d_conv):
+    """With GDN_F16 the fused front rounds its fp32 q, k, v to fp16 (nearest
+    even): bit for bit the standalone front, its outputs rounded to fp16 by
+    torch, then gdn_chunk_fwd on fp16 inputs (ragged chunks, a sequence
+    shorter than the halo, an empty one, h0)."""
+    wl = workloads.make_custom([100, 2, 0, 64, 130], 2, 4, seed=171 + d_conv, front=True,
+                               d_conv=d_conv, h0_sigma=0.02, n_max=6, t_max=330)
+    log(f"fused fp16 front vs front + fp16 forward, d_conv={d_conv}")
+    d = device_inputs(wl)
+    q, k, v = run_front(wl, d)
+    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, torch.float16)
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    out = []
+    for fused in (False, True):
+        o = torch.full((wl.t_max, wl.Hv, 128), float("nan"), dtype=torch.float32, device=DEV)
+        hT = torch.full((wl.n_max, wl.Hv, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+        if fused:
+            gdn.gdn_chunk_fwd_conv(cfg, d["qkv"], d["conv_w"], wl.d_conv, d["g"], d["beta"], d["h0"],
+                                   d["cu"], None, o, hT, ws)
+        else:
+            gdn.gdn_chunk_fwd(cfg, q.half(), k.half(), v.half(), d["g"], d["beta"], d["h0"], d["cu"],
+                              None, o, hT, ws)
+        torch.cuda.synchronize()
+        out.append((o, hT))
+    T = wl.n_tokens
+    assert torch.equal(out[0][0][:T], out[1][0][:T]) and torch.equal(out[0][1], out[1][1])
+
+
+def test_fused_front_fp16_workload_full_size():
+    """The front workload (4 x 8192 tokens) through the fused path with fp16
+    intermediates (the configuration the benchmark times), against the fp64
+    front + recurrence on every lane: the fp16 rounding of q, k, v stays well
+    inside the bar."""
+    wl = workloads.make(4)
+    log(f"fused front, fp16 intermediates, workload 4 ({wl.name})")
+    d = device_inputs(wl)
+    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, torch.float16)
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    o = torch.full((wl.t_max, wl.Hv, 128), float("nan"), dtype=torch.float32, device=DEV)
+    hT = torch.full((wl.n_max, wl.Hv, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+    gdn.gdn_chunk_fwd_conv(cfg, d["qkv"], d["conv_w"], wl.d_conv, d["g"], d["beta"], d["h0"],
+                           d["cu"], None, o, hT, ws)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_full(wl, qkv64=oracle_inputs_f64(wl))
+    eo, es = full_errors(wl, o, hT, o_ref, s_ref)
+    log(f"  every lane: o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+
+
+@pytest.mark.parametrize("H,Hv,segments,tiles", [(2, 4, 1, 0), (1, 4, 2, 0), (4, 8, 1, 2),
+                                                 (2, 2, 1, 4)])
+def test_fp16_inputs_every_lane(H, Hv, segments, tiles):
+    """fp16 q, k, v through the chunked forward (stage 1's fp16 path, stage 2
+    on the exact bf16 hi + lo K^T image), ragged batches with an empty
+    sequence and h0, one and two segments, one, two and four tiles, every lane
+    against the oracle on the same fp16 values."""
+    lengths = [300, 0, 65, 128, 777]
+    wl = workloads.make_custom(lengths, H, Hv, seed=181 + H + Hv, dtype=torch.float16,
+                               h0_sigma=0.02, n_max=len(lengths) + 1, t_max=sum(lengths) + 9)
+    log(f"fp16 inputs H={H} Hv={Hv} segments={segments} tiles={tiles}")
+    d = device_inputs(wl)
+    cfg = gdn.make_config(wl.t_max, wl.n_max, H, Hv, torch.float16, segments=segments, tiles=tiles)
+    ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=DEV)
+    o = torch.full((wl.t_max, Hv, 128), float("nan"), dtype=torch.float32, device=DEV)
+    hT = torch.full((wl.n_max, Hv, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+    gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], None, o,
+                      hT, ws)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_full(wl)
+    eo, es = full_errors(wl, o, hT, o_ref, s_ref)
+    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+    assert torch.isnan(o[wl.n_tokens:]).all()
 
 
 # --------------------------------------------------------------------------- #
