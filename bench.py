@@ -236,6 +236,10 @@ def main():
     ap.add_argument("--unfused-front", action="store_true",
                     help="front workload: run the standalone front, then the forward "
                          "(default: the front fused into stage 1)")
+    ap.add_argument("--gqa-share", type=int, default=0, choices=(0, 1, 2, 4),
+                    help="stage 2 in the GQA-shared shape: one 16-column slice of this many "
+                         "value heads of a key head per work-group (default 0: the "
+                         "automatic column-tile and segment choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
@@ -271,7 +275,7 @@ def main():
     qkv_dtype = wl.qkv_dtype
     if has_front:
         qkv_dtype = torch.float16 if fused_front and args.front_dtype == "f16" else torch.float32
-    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype)
+    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype, gqa_share=args.gqa_share)
     ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=dev)
     o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
     hT = torch.empty((wl.n_max, wl.Hv, 128, 128), dtype=torch.float32, device=dev)
@@ -408,6 +412,8 @@ def main():
         "config": {"workload": wl.name, "tokens": tokens, "sequences": wl.n_seqs, "H": wl.H,
                    "Hv": wl.Hv, "Dk": 128, "Dv": 128, "chunk": 64,
                    "parallelism": "single GPU",
+                   **({"stage2": f"GQA-shared, {args.gqa_share} value heads per work-group"}
+                      if args.gqa_share > 1 else {}),
                    **({"front": "fused into stage 1" if fused_front else "standalone kernel"}
                       if has_front else {})},
         "roofline": roofline,

@@ -60,7 +60,7 @@ class gdn_config(ctypes.Structure):
                 ("hv", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int), ("o_dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("segments", ctypes.c_int32),
-                ("tiles", ctypes.c_int32)]
+                ("tiles", ctypes.c_int32), ("gqa_share", ctypes.c_int32)]
 
 
 class gdn_workspace_layout_t(ctypes.Structure):
@@ -124,7 +124,7 @@ _GDN_DTYPE = {GDN_BF16: torch.bfloat16, GDN_F32: torch.float32, GDN_F16: torch.f
 
 
 def make_config(t_max, n_max, h, hv, qkv_dtype=GDN_BF16, scale=0.0, o_dtype=GDN_F32,
-                dk=128, dv=128, chunk=64, segments=0, tiles=0) -> gdn_config:
+                dk=128, dv=128, chunk=64, segments=0, tiles=0, gqa_share=0) -> gdn_config:
     """A gdn_config; qkv_dtype is GDN_BF16 / GDN_F32 / GDN_F16 or the torch
     dtype (bfloat16, float32, float16; any other raises ValueError)."""
     if isinstance(qkv_dtype, torch.dtype):
@@ -132,7 +132,8 @@ def make_config(t_max, n_max, h, hv, qkv_dtype=GDN_BF16, scale=0.0, o_dtype=GDN_
             raise ValueError(f"q/k/v dtype {qkv_dtype}: bfloat16, float32 or float16 expected")
         qkv_dtype = _TORCH_DTYPE[qkv_dtype]
     return gdn_config(int(t_max), int(n_max), int(h), int(hv), int(dk), int(dv), int(chunk),
-                      int(qkv_dtype), int(o_dtype), float(scale), int(segments), int(tiles))
+                      int(qkv_dtype), int(o_dtype), float(scale), int(segments), int(tiles),
+                      int(gqa_share))
 
 
 def _ptr(x) -> Optional[int]:

@@ -34,8 +34,13 @@ gdn_status check_config(const gdn_config *cfg) {
   if (cfg->segments < 0 || cfg->segments > 2) return GDN_ERR_INVALID_ARG;
   if (cfg->tiles != 0 && cfg->tiles != 1 && cfg->tiles != 2 && cfg->tiles != 4)
     return GDN_ERR_INVALID_ARG;
+  if (cfg->gqa_share != 0 && cfg->gqa_share != 1 && cfg->gqa_share != 2 && cfg->gqa_share != 4)
+    return GDN_ERR_INVALID_ARG;
   if (cfg->dk != kD || cfg->dv != kD || cfg->chunk != kChunk) return GDN_ERR_UNSUPPORTED;
   if (cfg->hv % cfg->h != 0) return GDN_ERR_UNSUPPORTED;
+  if (cfg->gqa_share > 1 && ((cfg->hv / cfg->h) % cfg->gqa_share != 0 || cfg->segments == 2 ||
+                             cfg->tiles > 1))
+    return GDN_ERR_UNSUPPORTED;
   if (cfg->o_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (cfg->t_max > GDN_T_MAX_LIMIT || cfg->n_max > GDN_N_MAX_LIMIT || cfg->hv > kMaxHeads)
     return GDN_ERR_CAPACITY;
@@ -51,6 +56,7 @@ int32_t nt_max_of(const gdn_config *cfg) {
 // long sequences and the one-piece grid fills at most half of the device.
 int segments_of(const gdn_config *cfg) {
   if (cfg->segments != 0) return cfg->segments;
+  if (cfg->gqa_share > 1) return 1;
   if (cfg->t_max < GDN_SEGMENT_MIN_TOKENS) return 1;
   return 2 * static_cast<int64_t>(gdn::inter_one_walk_grid(cfg->n_max, cfg->h, cfg->hv)) <=
                  gdn::cu_count()
@@ -62,6 +68,7 @@ int segments_of(const gdn_config *cfg) {
 // config).
 int tiles_of(const gdn_config *cfg) {
   if (cfg->tiles != 0) return cfg->tiles;
+  if (cfg->gqa_share > 1) return 1;
   const int64_t one = gdn::inter_one_walk_grid(cfg->n_max, cfg->h, cfg->hv);
   const int64_t cus = gdn::cu_count();
   if (one <= cus) return 1;
@@ -70,6 +77,10 @@ int tiles_of(const gdn_config *cfg) {
     return 4;
   return 2;
 }
+
+// Value heads per GQA-shared stage-2 work-group (validated config; 1 = the
+// column-tile shapes).
+int share_of(const gdn_config *cfg) { return cfg->gqa_share > 1 ? cfg->gqa_share : 1; }
 
 // Whether stage 1 ranks the sequences for stage 2 (longest walks first): with
 // more than one sequence, up to one per stage-1 thread.
@@ -158,7 +169,7 @@ bool split_k(const gdn_config *cfg) { return cfg->qkv_dtype != GDN_BF16; }
 // anything is queued, so a config past the limits returns without side effects.
 gdn_status check_inter_grids(const gdn_config *cfg) {
   return gdn::inter_grids_fit(cfg->n_max, cfg->h, cfg->hv, cfg->t_max, segments_of(cfg),
-                              tiles_of(cfg))
+                              tiles_of(cfg), share_of(cfg))
              ? GDN_OK
              : GDN_ERR_CAPACITY;
 }
@@ -226,8 +237,7 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
   return from_hip(gdn::launch_inter(split_k(cfg), b, h0, cu_seqlens, cfg->n_max,
                                     cfg->h, cfg->hv, cfg->t_max, nt_max_of(cfg),
                                     static_cast<float *>(o), hT, s, ev[2], segments_of(cfg),
-                                    tiles_of(cfg),
-                                    seg_scratch(l, workspace)));
+                                    tiles_of(cfg), share_of(cfg), seg_scratch(l, workspace)));
 }
 
 gdn_status recurrent_impl(const gdn_config *cfg, const void *q, const void *k, const void *v,
@@ -338,7 +348,8 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
   return from_hip(gdn::launch_inter(split_k(cfg), stage_buffers(cfg, l, workspace), h0,
                                     cu_seqlens, cfg->n_max, cfg->h, cfg->hv, cfg->t_max,
                                     nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream),
-                                    {}, segments_of(cfg), tiles_of(cfg), seg_scratch(l, workspace)));
+                                    {}, segments_of(cfg), tiles_of(cfg), share_of(cfg),
+                                    seg_scratch(l, workspace)));
 }
 
 gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,

@@ -116,7 +116,8 @@ int cu_count();
 
 // Whether every grid stage 2 launches for this shape (the walk, and with two
 // segments the fix-up) fits flat_grid; checked on the host before any launch.
-bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int segments, int tiles);
+bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int segments, int tiles,
+                     int share);
 
 // Work-groups of the one-walk stage-2 grid (one per (sequence, value head,
 // 16-column slice), rounded to whole XCD rounds).
@@ -124,11 +125,14 @@ int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv);
 
 // segments: 1 walks each sequence in one piece; 2 walks its two halves at once
 // (the second carrying the zero-start and the homogeneous state) and then
-// combines them with a fix-up kernel, using `seg`.
+// combines them with a fix-up kernel, using `seg`. tiles: 16-column slices of
+// one value head per work-group (1, 2, 4). share: 2 or 4 selects the
+// GQA-shared shape instead (one 16-column slice of `share` value heads of a
+// key head per work-group; one-piece walk only).
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
                         int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,
-                        KernelEvents ev = {}, int segments = 1, int tiles = 1,
+                        KernelEvents ev = {}, int segments = 1, int tiles = 1, int share = 1,
                         SegScratch seg = {});
 
 }  // namespace gdn

@@ -233,37 +233,48 @@ struct Walk {
   bool two;  // state 1 is carried (segment B of the two-segment walk)
 };
 
-template <bool kF32In, int kDepth, int X, int kS, int kNV>
+template <bool kF32In, int kDepth, int X, int kS, int kNV, bool kGq>
 __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const StageBuffers &in,
                                            u32x4 (*xch)[kXchFrags * kS * kNV][64],
-                                           float (*decx)[64]) {
+                                           float (*decx)[kGq ? kNV : 1][64]) {
   static_assert(kS == 1 || kNV == 1, "the two-state walk covers one column tile");
   constexpr int kNKw = kF32In ? 16 : 8;  // K^T fragments this wave uses per chunk
+  constexpr int kNW = kGq ? kNV : 1;     // value heads whose w, u and gates are loaded
+  // distance between tile ct's rows of a state (the next value head, or the
+  // next 16 columns of one)
+  constexpr int64_t kCtState = kGq ? kD * kD : 16 * kD;
   const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;  // 1 KB fragment blocks
   const int slice = L.v0 / 16;
-  struct Rsrc { rsrc_t w, k, u, g; };
+  struct Rsrc { rsrc_t w[kNW], k, u[kNW], g[kNW]; };
   auto rsrc_of = [&](int c) __attribute__((always_inline)) {
     const int slot = slot_of(L, c);
     const bool ok = c < W.c1;
     Rsrc r;
-    r.w = make_rsrc(in.w16 + ((int64_t)L.hv * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
+#pragma unroll
+    for (int j = 0; j < kNW; ++j) {
+      const int64_t hvj = L.hv + j;
+      r.w[j] = make_rsrc(in.w16 + (hvj * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
+      r.u[j] = make_rsrc(in.uimg + ((hvj * L.nt + slot) * kSlices + slice) * 4 * 64 * 3,
+                         ok && X == 0 ? 3072 * (kNV / kNW) : 0);
+      r.g[j] = make_rsrc(in.gimg + (hvj * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
+    }
     r.k = make_rsrc(in.kimg + ((int64_t)L.h * L.nt + slot) * (kF32In ? 32 : 16) * 512,
                     ok ? (kF32In ? 32 : 16) * 1024 : 0);
-    r.u = make_rsrc(in.uimg + (((int64_t)L.hv * L.nt + slot) * kSlices + slice) * 4 * 64 * 3,
-                    ok && X == 0 ? 3072 * kNV : 0);
-    r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     return r;
   };
-  f16x8 w[kDepth][8];       // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
+  f16x8 w[kDepth][kNW][8];  // (-w) fragment (token tile R, key block 2 X + pl) at [2 R + pl]
   bf16x8 k[kDepth][kNKw];   // K^T fragment (key tile 4 X + tl, token block q) at [2 tl + q] (+8: lo)
-  u32x3 u[kDepth][kNV][4];  // wave 0: u tile R (24-bit), rows 16 R + 4 g + i, column v0 + 16 ct + c
-  float dec[kDepth];        // e^{gamma_last - gamma} of token L.lane (shared through LDS)
-  float el[kDepth];         // e^{gamma_last}
+  u32x3 u[kDepth][kNV][4];  // wave 0: u tile R (24-bit), rows 16 R + 4 g + i, of tile ct
+  float dec[kDepth][kNW];   // e^{gamma_last - gamma} of token L.lane (shared through LDS)
+  float el[kDepth][kNW];    // e^{gamma_last}
   auto load_w = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w[B][i] = __builtin_bit_cast(f16x8, ld16(r.w, vo_f, (4 * (i >> 1) + 2 * X + (i & 1)) * 1024));
+    for (int j = 0; j < kNW; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[B][j][i] =
+            __builtin_bit_cast(f16x8, ld16(r.w[j], vo_f, (4 * (i >> 1) + 2 * X + (i & 1)) * 1024));
   };
   auto load_k = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
@@ -282,10 +293,14 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
       for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
         for (int R = 0; R < 4; ++R)
-          u[B][ct][R] = __builtin_amdgcn_raw_buffer_load_b96(r.u, L.lane * 12, (4 * ct + R) * 768, 0);
+          u[B][ct][R] = __builtin_amdgcn_raw_buffer_load_b96(r.u[kGq ? ct : 0], L.lane * 12,
+                                                             (kGq ? R : 4 * ct + R) * 768, 0);
     }
-    dec[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 4 * L.lane, 0, 0));
-    el[B] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g, 0, 512, 0));
+#pragma unroll
+    for (int j = 0; j < kNW; ++j) {
+      dec[B][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g[j], 4 * L.lane, 0, 0));
+      el[B][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.g[j], 0, 512, 0));
+    }
   };
   auto load_all = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
@@ -304,7 +319,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl)
-      S[0][ct][tl] = W.init0 ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + 16 * ct * kD + 16 * tl)
+      S[0][ct][tl] = W.init0 ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + ct * kCtState + 16 * tl)
                              : zero4();
   if constexpr (kS == 2) {
 #pragma unroll
@@ -320,7 +335,9 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   auto step = [&](const int c, auto Bc) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
     const Rsrc rn = rsrc_of(c + kDepth);
-    const float e_last = c < W.c1 ? el[B] : 1.f;
+    float e_last[kNW];
+#pragma unroll
+    for (int j = 0; j < kNW; ++j) e_last[j] = c < W.c1 ? el[B][j] : 1.f;
     u32x4 *xb = &xch[c & 1][0][L.lane];
     f32x4 pv[kS][kNV][4];
 #pragma unroll
@@ -328,6 +345,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
         if (st == 1 && !W.two) continue;  // segment A carries state 0 only
+        const int wj = kGq ? ct : 0;
         u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
         f16x8 s16[2];
 #pragma unroll
@@ -342,13 +360,16 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-          for (int R = 0; R < 4; ++R) pv[st][ct][R] = mfma(w[B][2 * R + pl], s16[pl], pv[st][ct][R]);
+          for (int R = 0; R < 4; ++R) pv[st][ct][R] = mfma(w[B][wj][2 * R + pl], s16[pl], pv[st][ct][R]);
 #pragma unroll
         for (int R = 0; R < 4; ++R) xs[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[st][ct][R]);
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl) S[st][ct][tl] = S[st][ct][tl] * e_last;
+        for (int tl = 0; tl < 4; ++tl) S[st][ct][tl] = S[st][ct][tl] * e_last[wj];
       }
-    if constexpr (X == 0) decx[c & 1][L.lane] = dec[B];  // token L.lane's factor
+    if constexpr (X == 0) {
+#pragma unroll
+      for (int j = 0; j < kNW; ++j) decx[c & 1][j][L.lane] = dec[B][j];  // token L.lane's factor
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_w(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
@@ -356,15 +377,19 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     // S += K^T (e^{gamma_last - gamma} v'): rows 16 R + 4 g + i of this lane
     // take their factors from the chunk's gate factors that wave 0 put in LDS
     // before the barrier (one broadcast 16-byte read per token tile)
-    f32x4 dr[4];
+    f32x4 dr[kNW][4];
 #pragma unroll
-    for (int R = 0; R < 4; ++R) dr[R] = *reinterpret_cast<const f32x4 *>(&decx[c & 1][16 * R + L.g4]);
+    for (int j = 0; j < kNW; ++j)
+#pragma unroll
+      for (int R = 0; R < 4; ++R)
+        dr[j][R] = *reinterpret_cast<const f32x4 *>(&decx[c & 1][j][16 * R + L.g4]);
     bf16x8 eh[kS][kNV][2], elo[kS][kNV][2];
 #pragma unroll
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
         if (st == 1 && !W.two) continue;  // segment A carries state 0 only
+        const int wj = kGq ? ct : 0;
         const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
         f32x4 v[4];
 #pragma unroll
@@ -373,8 +398,8 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
           // both waves: partial0 + partial1
           v[R] = X == 0 ? pv[st][ct][R] + other : other + pv[st][ct][R];
         }
-        split8(v[0] * dr[0], v[1] * dr[1], eh[st][ct][0], elo[st][ct][0]);
-        split8(v[2] * dr[2], v[3] * dr[3], eh[st][ct][1], elo[st][ct][1]);
+        split8(v[0] * dr[wj][0], v[1] * dr[wj][1], eh[st][ct][0], elo[st][ct][0]);
+        split8(v[2] * dr[wj][2], v[3] * dr[wj][3], eh[st][ct][1], elo[st][ct][1]);
       }
     __builtin_amdgcn_sched_barrier(0);
     load_u(Bc, rn);
@@ -415,7 +440,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
       for (int tl = 0; tl < 4; ++tl)
-        *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + 16 * ct * kD + 16 * tl) = S[0][ct][tl];
+        *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + ct * kCtState + 16 * tl) = S[0][ct][tl];
   }
   if constexpr (kS == 2) {
     if (W.fin[1]) {
@@ -431,10 +456,12 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
 
 // Helper wave Y: output token tiles R = 2 Y, 2 Y + 1 (rows 32 Y .. 32 Y + 31)
 // of every carried state.
-template <int kDepth, int Y, int kS, int kNV>
+template <int kDepth, int Y, int kS, int kNV, bool kGq>
 __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const StageBuffers &in,
                                             u32x4 (*xch)[kXchFrags * kS * kNV][64]) {
   constexpr int kNQ = Y + 1;                 // token blocks of v' this wave contracts over
+  constexpr int kNW = kGq ? kNV : 1;         // value heads whose P and gates are loaded
+  constexpr int kCtO = kGq ? kD : 16;        // o columns between tile ct and ct + 1
   // o rows stream past the caches in the one-tile, one-piece walk: at one
   // work-group per CU, o's dirty lines otherwise displace what the next
   // kernels read (T = 4096: the following stage 1 ran 53 -> 44 us). Not in the
@@ -446,20 +473,24 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
   const uint32_t vo_o = static_cast<uint32_t>(L.c16 * L.Hv * kD + L.g4) * 4;     // o rows
   const uint32_t vo_f = static_cast<uint32_t>(L.lane) * 16;
   const uint32_t row_o = static_cast<uint32_t>(16 * L.Hv * kD * 4);             // 16 o rows
-  struct Rsrc { rsrc_t q, p, g; };
+  struct Rsrc { rsrc_t q, p[kNW], g[kNW]; };
   auto rsrc_of = [&](int c) __attribute__((always_inline)) {
     const int slot = slot_of(L, c);
     const bool ok = c < W.c1;
     Rsrc r;
     r.q = make_rsrc(in.q16 + ((int64_t)L.h * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
-    r.p = make_rsrc(reinterpret_cast<const char *>(in.pimg) + ((int64_t)L.hv * L.nt + slot) * kPBytes,
-                    ok ? kPBytes : 0);
-    r.g = make_rsrc(in.gimg + ((int64_t)L.hv * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
+#pragma unroll
+    for (int j = 0; j < kNW; ++j) {
+      const int64_t hvj = L.hv + j;
+      r.p[j] = make_rsrc(reinterpret_cast<const char *>(in.pimg) + (hvj * L.nt + slot) * kPBytes,
+                         ok ? kPBytes : 0);
+      r.g[j] = make_rsrc(in.gimg + (hvj * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
+    }
     return r;
   };
   f16x8 qf[kDepth][8];            // q16 fragment (token tile 2 Y + Rl, key block p) at [4 Rl + p]
-  f16x8 pf[kDepth][kPairs];      // P pair kPair0 + n at [n]
-  u32x2 exs[kDepth];              // scale * e^{gamma_r} (fp32 bits), r = 16 (2 Y + Rl) + c
+  f16x8 pf[kDepth][kNW][kPairs];  // P pair kPair0 + n at [n]
+  u32x2 exs[kDepth][kNW];         // scale * e^{gamma_r} (fp32 bits), r = 16 (2 Y + Rl) + c
   auto load_q = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
 #pragma unroll
@@ -469,16 +500,19 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
   auto load_p = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
 #pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const int pi = kPair0 + i, off = p_offset(pi);
-      if (p_half(pi)) {  // the upper half of the lane's slots is zero
-        const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(r.p, L.lane * 8, off, 0);
-        pf[B][i] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], 0u, 0u});
-      } else {
-        pf[B][i] = __builtin_bit_cast(f16x8, ld16(r.p, vo_f, off));
+    for (int j = 0; j < kNW; ++j) {
+#pragma unroll
+      for (int i = 0; i < kPairs; ++i) {
+        const int pi = kPair0 + i, off = p_offset(pi);
+        if (p_half(pi)) {  // the upper half of the lane's slots is zero
+          const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(r.p[j], L.lane * 8, off, 0);
+          pf[B][j][i] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], 0u, 0u});
+        } else {
+          pf[B][j][i] = __builtin_bit_cast(f16x8, ld16(r.p[j], vo_f, off));
+        }
       }
+      exs[B][j] = __builtin_amdgcn_raw_buffer_load_b64(r.g[j], 16 * L.c16 + 8 * Y, 256, 0);
     }
-    exs[B] = __builtin_amdgcn_raw_buffer_load_b64(r.g, 16 * L.c16 + 8 * Y, 256, 0);
   };
   auto load_all = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
@@ -530,6 +564,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
         if (st == 1 && !W.two) continue;  // segment A carries state 0 only
+        const int wj = kGq ? ct : 0;
         f32x4 pa[2] = {zero4(), zero4()};
 #pragma unroll
         for (int Rl = 0; Rl < 2; ++Rl) {
@@ -537,19 +572,19 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
 #pragma unroll
           for (int q = 0; q <= (R >> 1); ++q) {
             const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
-            pa[Rl] = mfma(dh[st][ct][q], pf[B][n], pa[Rl]);
-            pa[Rl] = mfma(dl[st][ct][q], pf[B][n], pa[Rl]);
+            pa[Rl] = mfma(dh[st][ct][q], pf[B][wj][n], pa[Rl]);
+            pa[Rl] = mfma(dl[st][ct][q], pf[B][wj][n], pa[Rl]);
           }
         }
         // a state without an output destination gets an empty store range
         const uintptr_t ob = reinterpret_cast<uintptr_t>(W.out[st]) +
-                             (((uintptr_t)t0 * L.Hv + L.hv) * kD + L.v0 + 16 * ct) * 4;
+                             (((uintptr_t)t0 * L.Hv + L.hv) * kD + L.v0 + kCtO * ct) * 4;
         const i32x4 ro = rsrc_words(reinterpret_cast<const void *>(ob),
                                     W.out[st] ? lc * L.Hv * kD * 4 : 0u);
 #pragma unroll
         for (int Rl = 0; Rl < 2; ++Rl)
           store16<kStreamO>(ro, vo_o, (2 * Y + Rl) * row_o,
-                            pa[Rl] + __uint_as_float(exs[B][Rl]) * ya[st][ct][Rl]);
+                            pa[Rl] + __uint_as_float(exs[B][wj][Rl]) * ya[st][ct][Rl]);
       }
     __builtin_amdgcn_sched_barrier(0);
     load_p(Bc, rn);
@@ -640,7 +675,7 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
 // second half walks the rest carrying the zero-start state (outputs into o,
 // final slice to seg.z) and the identity-start homogeneous state (outputs to
 // seg.oh, final slice to seg.phi); segfix_kernel then combines them.
-template <bool kF32In, int kDepth, int kS, int kNV>
+template <bool kF32In, int kDepth, int kS, int kNV, bool kGq>
 __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
                              kInterWavesPerSimd<kNV>) void inter_kernel(
     StageBuffers in, const float *__restrict__ h0, const int32_t *__restrict__ cu,
@@ -649,12 +684,14 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags * kS * kNV][64];
   __shared__ uint32_t l2_sink[64];
   // per chunk (double-buffered) the gate factors e^{gamma_last - gamma} by token
-  __shared__ __attribute__((aligned(16))) float decx[2][64];
+  __shared__ __attribute__((aligned(16))) float decx[2][kGq ? kNV : 1][64];
 
   // ---- XCD-aware work-group -> (sequence, value head, slice) --------------
-  constexpr int kWgSlices = kSlices / kNV;  // work-groups per value head
+  // kGq: the kNV tiles are one 16-column slice of kNV consecutive value heads
+  // of the key head; otherwise kNV consecutive slices of one value head
+  constexpr int kWgSlices = kGq ? kSlices : kSlices / kNV;  // work-groups per value-head set
   const int HG = Hv / H;
-  const int members = HG * kWgSlices;
+  const int members = (kGq ? HG / kNV : HG) * kWgSlices;
   const int one_walk = (n_max * H + kXcds - 1) / kXcds * kXcds * members;
   const int wg = flat_block();
   const int role = kS == 2 && wg >= one_walk ? 1 : 0;
@@ -669,8 +706,8 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   L.s = in.order ? in.order[group / H] : group / H;
   if (L.s < 0 || L.s >= n_max) return;
   L.h = group % H;
-  L.hv = L.h * HG + member / kWgSlices;
-  L.v0 = 16 * kNV * (member % kWgSlices);
+  L.hv = L.h * HG + (member / kWgSlices) * (kGq ? kNV : 1);
+  L.v0 = 16 * (kGq ? 1 : kNV) * (member % kWgSlices);
   L.lane = threadIdx.x & 63;
   L.c16 = L.lane & 15;
   L.g4 = 4 * (L.lane >> 4);
@@ -691,13 +728,13 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0)
-    chain_wave<kF32In, kDepth, 0, kS, kNV>(L, W, in, xch, decx);
+    chain_wave<kF32In, kDepth, 0, kS, kNV, kGq>(L, W, in, xch, decx);
   else if (wave == 1)
-    chain_wave<kF32In, kDepth, 1, kS, kNV>(L, W, in, xch, decx);
+    chain_wave<kF32In, kDepth, 1, kS, kNV, kGq>(L, W, in, xch, decx);
   else if (wave == 2)
-    helper_wave<kDepth, 0, kS, kNV>(L, W, in, xch);
+    helper_wave<kDepth, 0, kS, kNV, kGq>(L, W, in, xch);
   else if (wave == 3)
-    helper_wave<kDepth, 1, kS, kNV>(L, W, in, xch);
+    helper_wave<kDepth, 1, kS, kNV, kGq>(L, W, in, xch);
   else if constexpr (kWarmWave<kF32In, kDepth, kS, kNV>)
     l2_warm_wave<kF32In, kDepth>(L, W, in, member, members, l2_sink, warm_values);
 }
@@ -833,12 +870,12 @@ int fix_row_blocks(int32_t t_max) {
   return (nc - seg_split(nc) + 1) / 2;
 }
 
-template <bool kF32In, int kDepth, int kS, int kNV = 1>
+template <bool kF32In, int kDepth, int kS, int kNV = 1, bool kGq = false>
 hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
                        int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
                        const SegScratch &seg, hipStream_t stream, hipEvent_t start,
                        hipEvent_t stop) {
-  const int64_t members = (hv / h) * (kSlices / kNV);
+  const int64_t members = kGq ? (hv / h / kNV) * kSlices : (hv / h) * (kSlices / kNV);
   const int64_t rounds = (static_cast<int64_t>(n_max) * h + kXcds - 1) / kXcds;
   constexpr int kThr = kInterThreads<kF32In, kDepth, kS, kNV>;
   dim3 grid;
@@ -849,7 +886,7 @@ hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *c
                                                         kGateStride * 4) +
                             static_cast<int64_t>(h) * ((kF32In ? 32 : 16) * 1024 + 16 * 1024);
   const bool warm_values = static_cast<int64_t>(nt) * per_chunk > (160ll << 20);
-  hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS, kNV>), grid, dim3(kThr), 0, stream,
+  hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS, kNV, kGq>), grid, dim3(kThr), 0, stream,
                         start, stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt, seg,
                         warm_values);
   return hipGetLastError();
@@ -858,9 +895,17 @@ hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *c
 template <bool kF32In>
 hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *cu, int32_t n_max,
                         int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
-                        hipStream_t stream, KernelEvents ev, int segments, int tiles,
+                        hipStream_t stream, KernelEvents ev, int segments, int tiles, int share,
                         const SegScratch &seg) {
   const int one_walk = inter_one_walk_grid(n_max, h, hv);
+  // the GQA-shared shape (one slice of `share` value heads per work-group);
+  // the host admits it only for the one-piece, one-tile walk
+  if (share == 4)
+    return launch_walk<kF32In, 1, 1, 4, true>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
+                                              stream, ev.start, ev.stop);
+  if (share == 2)
+    return launch_walk<kF32In, 1, 1, 2, true>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
+                                              stream, ev.start, ev.stop);
   if (segments != 2) {
     if (tiles == 4)
       return launch_walk<kF32In, 1, 1, 4>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
@@ -905,8 +950,9 @@ int cu_count() {
   return n;
 }
 
-bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int segments, int tiles) {
-  const int64_t members = (hv / h) * (kSlices / (segments == 2 ? 1 : tiles));
+bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int segments, int tiles,
+                     int share) {
+  const int64_t members = (hv / h / share) * (kSlices / (segments == 2 ? 1 : tiles));
   const int64_t rounds = (static_cast<int64_t>(n_max) * h + kXcds - 1) / kXcds;
   dim3 grid;
   if (!flat_grid((segments == 2 ? 2 : 1) * rounds * kXcds * members, 320, grid)) return false;
@@ -923,11 +969,11 @@ int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv) {
 hipError_t launch_inter(bool f32_in, const StageBuffers &in, const float *h0,
                         const int32_t *cu_seqlens, int32_t n_max, int32_t h, int32_t hv,
                         int32_t t_max, int32_t nt_max, float *o, float *hT, hipStream_t stream,
-                        KernelEvents ev, int segments, int tiles, SegScratch seg) {
+                        KernelEvents ev, int segments, int tiles, int share, SegScratch seg) {
   return f32_in ? launch_waves<true>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT, stream,
-                                     ev, segments, tiles, seg)
+                                     ev, segments, tiles, share, seg)
                 : launch_waves<false>(in, h0, cu_seqlens, n_max, h, hv, t_max, nt_max, o, hT,
-                                      stream, ev, segments, tiles, seg);
+                                      stream, ev, segments, tiles, share, seg);
 }
 
 }  // namespace gdn

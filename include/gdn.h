@@ -96,6 +96,19 @@ typedef struct {
                           when it is more than 2x the device and t_max >= n_max *
                           GDN_FOUR_TILE_MIN_TOKENS (long sequences), else 2. The
                           two-segment walk always uses 1. */
+  int32_t gqa_share;   /* GQA-shared stage 2 ("Optimizing GDN Chunk Prefill on
+                          Intel AMX CPU", sections 3 and 5: the inter stage run
+                          over key heads, reusing the key head's operands across
+                          its value heads): 2 or 4 = each stage-2 work-group
+                          carries one 16-column slice of that many value heads
+                          of one key head and loads the key head's K^T and q
+                          fragments once for all of them; it must divide hv / h,
+                          and needs segments != 2 and tiles <= 1 (automatic
+                          segments and tiles then resolve to 1). 0 or 1 = the
+                          column-tile shapes above. Results are bitwise those of
+                          tiles = 1. Never chosen automatically: at equal
+                          registers per work-group, two or four column tiles of
+                          one value head load fewer bytes per column. */
 } gdn_config;
 
 /* Token capacity per sequence from which the automatic choice considers

@@ -122,12 +122,39 @@ def test_workspace_layout_segments(lib):
     ("scale", float("nan"), INVALID), ("t_max", (1 << 24) + 1, CAPACITY), ("n_max", 16385, CAPACITY),
     ("segments", 3, INVALID), ("segments", -1, INVALID), ("tiles", 3, INVALID),
     ("tiles", -1, INVALID), ("tiles", 8, INVALID), ("tiles", 4, OK), ("tiles", 1, OK),
+    ("gqa_share", 3, INVALID), ("gqa_share", -1, INVALID), ("gqa_share", 8, INVALID),
+    ("gqa_share", 2, OK), ("gqa_share", 1, OK),
+    ("gqa_share", 4, UNSUPPORTED),  # 4 does not divide hv / h = 2
 ])
 def test_config_validation(lib, field, value, status):
     cfg = gdn.make_config(256, 2, 16, 32)
     setattr(cfg, field, value)
     out = ctypes.c_size_t(0)
     assert lib.gdn_workspace_size(ctypes.byref(cfg), ctypes.byref(out)) == status
+
+
+def test_gqa_share_needs_the_one_piece_one_tile_walk(lib):
+    """The GQA-shared stage 2 carries one column slice of 2 or 4 value heads
+    per work-group: it needs hv / h divisible by the share, one segment and
+    one tile; automatic segments and tiles then resolve to one (no segment
+    scratch in the workspace, even where two segments would be chosen)."""
+    out = ctypes.c_size_t(0)
+
+    def status(**kw):
+        cfg = gdn.make_config(32768, 1, 4, 16, **kw)  # HG = 4
+        return lib.gdn_workspace_size(ctypes.byref(cfg), ctypes.byref(out))
+
+    assert status(gqa_share=4) == OK and status(gqa_share=2) == OK
+    assert status(gqa_share=2, segments=2) == UNSUPPORTED
+    assert status(gqa_share=2, tiles=2) == UNSUPPORTED
+    assert status(gqa_share=2, tiles=4) == UNSUPPORTED
+    assert status(gqa_share=2, segments=1, tiles=1) == OK
+    cfg = gdn.make_config(64, 1, 3, 6, gqa_share=4)  # HG = 2
+    assert lib.gdn_workspace_size(ctypes.byref(cfg), ctypes.byref(out)) == UNSUPPORTED
+    auto = gdn.gdn_workspace_layout(gdn.make_config(32768, 1, 4, 8))  # 128 work-groups
+    shared = gdn.gdn_workspace_layout(gdn.make_config(32768, 1, 4, 8, gqa_share=2))
+    assert auto["seg_oh"] < auto["total"]  # automatic: two segments
+    assert shared["seg_oh"] == shared["total"]  # shared: one piece, no segment scratch
 
 
 def test_null_config_and_output(lib):
