@@ -224,6 +224,11 @@ def main():
                          "microseconds to the step they are on)")
     ap.add_argument("--workload", type=int, default=1,
                     help="named workload 0..6 (5 and 6 time the token-serial kernel)")
+    ap.add_argument("--settle-ms", type=float, default=1000.0, metavar="MS",
+                    help="before the W warm-up steps, run untimed steps for this many "
+                         "milliseconds of wall time, so that the GPU clocks and the host "
+                         "launch path reach steady state even when W is small (reported as "
+                         "settle_steps; 0 to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-samples", type=int, default=10, metavar="N",
                     help="after the timed region, time N more steps each preceded by a 1 GiB "
@@ -323,10 +328,28 @@ def main():
             gdn.gdn_chunk_fwd_timed(cfg, q, k, v, d["g"], d["beta"], d["h0"], cu, None, o, hT, ws,
                                     evs[:6])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # Untimed steps run the same launch path as the timed loop: every E-th
+    # step carries dispatch events (one reused set), so first-use costs of
+    # the event path are paid before timing.
     every = max(1, args.event_every)
+    warm_events = hip.create(8 if has_front else 6)
+
+    def untimed(i):
+        step(warm_events if i % every == every - 1 else None)
+
+    # settle: untimed steps for a fixed wall time (a fresh process on an idle
+    # GPU runs its first steps at lower clocks and with a slower host path)
+    settle_steps = 0
+    if args.settle_ms > 0:
+        t_settle = time.perf_counter()
+        while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+            for _ in range(16):
+                untimed(settle_steps)
+                settle_steps += 1
+            torch.cuda.synchronize()
+    for i in range(args.warmup):
+        untimed(i)
+    torch.cuda.synchronize()
     timed = [s_ % every == every - 1 or s_ == args.steps - 1 for s_ in range(args.steps)]
     events = [hip.create(8 if has_front else 6) if t else None for t in timed]
     torch.cuda.synchronize()
@@ -403,6 +426,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
