@@ -610,6 +610,13 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
 
   for (int gi = 0; gi < HG; ++gi) {
     const int hv = h * HG + gi;
+    // The lane index as the lane-dependent conditions of this loop (token
+    // validity, the causal masks of P and A, the solve's row and column
+    // tests) see it. The opaque copy keeps their compares inside the loop:
+    // hoisted out of it, the lane masks (64-bit scalar values each) outgrew
+    // the scalar registers and were spilled to vector-register lanes.
+    int ml = lane;
+    asm volatile("" : "+v"(ml));
     // ---- this value head's operands, next value head's requests (a request
     // past the group reads an empty range) ----------------------------------
     u32x4 vh[4], vl[4];
@@ -632,9 +639,9 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     bsh[lane] = bv;
     if (wv == 0) {
       float *gd = out.gimg + ((int64_t)hv * nt + slot) * kGateStride;
-      gd[lane] = tok_ok ? fast_exp2(gl2 - gam2) : 0.f;
-      gd[64 + 4 * (lane & 15) + (lane >> 4)] = tok_ok ? scale * eg : 0.f;  // [c][R], r = 16 R + c
-      gd[128 + lane] = lane == 0 ? fast_exp2(gl2) : 0.f;
+      gd[lane] = ml < L ? fast_exp2(gl2 - gam2) : 0.f;
+      gd[64 + 4 * (lane & 15) + (lane >> 4)] = ml < L ? scale * eg : 0.f;  // [c][R], r = 16 R + c
+      gd[128 + lane] = ml == 0 ? fast_exp2(gl2) : 0.f;
     }
     wave_lds_sync();
 
@@ -644,12 +651,12 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     for (int n2 = 0; n2 < 2; ++n2) {
       if (n2 < npair) {
         const int pi = pair0 + n2;
-        const int r = 16 * pair_r(pi) + (lane & 15);
+        const int r = 16 * pair_r(pi) + (ml & 15);
         const float gr = gsh[r];
         float x[8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int j0 = 32 * pair_q(pi) + 16 * hf + 4 * (lane >> 4);
+          const int j0 = 32 * pair_q(pi) + 16 * hf + 4 * (ml >> 4);
           const f32x4 gj = *reinterpret_cast<const f32x4 *>(gsh + j0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -672,8 +679,8 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
       if (n < nblk) {
-        const int j = 16 * gbj[n] + (lane & 15);
-        const int r0 = 16 * gbi[n] + 4 * (lane >> 4);
+        const int j = 16 * gbj[n] + (ml & 15);
+        const int r0 = 16 * gbi[n] + 4 * (ml >> 4);
         const float gj = gsh[j];
         const f32x4 gr = *reinterpret_cast<const f32x4 *>(gsh + r0);
         const f32x4 br = *reinterpret_cast<const f32x4 *>(bsh + r0);
@@ -693,7 +700,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     // it. A is strictly lower and unknown T entries are still zero, so the
     // quarters need no mask. The whole block is read before T is written.
     {
-      const int c = lane >> 2, q = lane & 3;
+      const int c = ml >> 2, q = ml & 3;
       float *ab = at + (16 * wv) * kLdAT + 16 * wv;
       f32x4 arow[16];
 #pragma unroll
