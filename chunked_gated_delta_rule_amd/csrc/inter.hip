@@ -374,6 +374,9 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     load_w(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // chunk c's states (fp16) and all partials are published
+    __builtin_amdgcn_sched_barrier(0);
+    load_u(Bc, rn);
+    __builtin_amdgcn_sched_barrier(0);
     // S += K^T (e^{gamma_last - gamma} v'): rows 16 R + 4 g + i of this lane
     // take their factors from the chunk's gate factors that wave 0 put in LDS
     // before the barrier (one broadcast 16-byte read per token tile)
@@ -383,46 +386,46 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
 #pragma unroll
       for (int R = 0; R < 4; ++R)
         dr[j][R] = *reinterpret_cast<const f32x4 *>(&decx[c & 1][j][16 * R + L.g4]);
-    bf16x8 eh[kS][kNV][2], elo[kS][kNV][2];
+    // per token block q: form dec v' of its two token tiles, then apply them
+    // (the per-accumulator order of the products is q = 0 then q = 1)
 #pragma unroll
-    for (int st = 0; st < kS; ++st)
+    for (int q = 0; q < 2; ++q) {
+      bf16x8 eh[kS][kNV], elo[kS][kNV];
 #pragma unroll
-      for (int ct = 0; ct < kNV; ++ct) {
-        if (st == 1 && !W.two) continue;  // segment A carries state 0 only
-        const int wj = kGq ? ct : 0;
-        const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
-        f32x4 v[4];
+      for (int st = 0; st < kS; ++st)
 #pragma unroll
-        for (int R = 0; R < 4; ++R) {
-          const f32x4 other = __builtin_bit_cast(f32x4, xs[64 * (4 + 4 * (1 - X) + R)]);
-          // both waves: partial0 + partial1
-          v[R] = X == 0 ? pv[st][ct][R] + other : other + pv[st][ct][R];
+        for (int ct = 0; ct < kNV; ++ct) {
+          if (st == 1 && !W.two) continue;  // segment A carries state 0 only
+          const int wj = kGq ? ct : 0;
+          const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
+          f32x4 v[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int R = 2 * q + h2;
+            const f32x4 other = __builtin_bit_cast(f32x4, xs[64 * (4 + 4 * (1 - X) + R)]);
+            // both waves: partial0 + partial1
+            v[h2] = X == 0 ? pv[st][ct][R] + other : other + pv[st][ct][R];
+          }
+          split8(v[0] * dr[wj][2 * q], v[1] * dr[wj][2 * q + 1], eh[st][ct], elo[st][ct]);
         }
-        split8(v[0] * dr[wj][0], v[1] * dr[wj][1], eh[st][ct][0], elo[st][ct][0]);
-        split8(v[2] * dr[wj][2], v[3] * dr[wj][3], eh[st][ct][1], elo[st][ct][1]);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    load_u(Bc, rn);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int st = 0; st < kS; ++st)
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int st = 0; st < kS; ++st)
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) {
           if (st == 1 && !W.two) continue;
 #pragma unroll
           for (int tl = 0; tl < 4; ++tl)
-            S[st][ct][tl] = mfma(k[B][2 * tl + q], eh[st][ct][q], S[st][ct][tl]);
+            S[st][ct][tl] = mfma(k[B][2 * tl + q], eh[st][ct], S[st][ct][tl]);
 #pragma unroll
           for (int tl = 0; tl < 4; ++tl)
-            S[st][ct][tl] = mfma(k[B][2 * tl + q], elo[st][ct][q], S[st][ct][tl]);
+            S[st][ct][tl] = mfma(k[B][2 * tl + q], elo[st][ct], S[st][ct][tl]);
           if constexpr (kF32In) {
 #pragma unroll
             for (int tl = 0; tl < 4; ++tl)
-              S[st][ct][tl] = mfma(k[B][8 + 2 * tl + q], eh[st][ct][q], S[st][ct][tl]);
+              S[st][ct][tl] = mfma(k[B][8 + 2 * tl + q], eh[st][ct], S[st][ct][tl]);
           }
         }
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_k(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
