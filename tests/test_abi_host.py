@@ -5,6 +5,7 @@ documented status before any HIP call. No test here launches a kernel."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -155,6 +156,34 @@ def test_gqa_share_needs_the_one_piece_one_tile_walk(lib):
     shared = gdn.gdn_workspace_layout(gdn.make_config(32768, 1, 4, 8, gqa_share=2))
     assert auto["seg_oh"] < auto["total"]  # automatic: two segments
     assert shared["seg_oh"] == shared["total"]  # shared: one piece, no segment scratch
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The ctypes mirrors of gdn_config and gdn_workspace_layout_t have the
+    C header's size and field offsets (compiled here with the host C
+    compiler, so a field added to one side only fails)."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"gdn_config": gdn.gdn_config, "gdn_workspace_layout_t": gdn.gdn_workspace_layout_t}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gdn.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in py._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "offsets.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "offsets"
+    subprocess.run([cc, "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out.splitlines()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for field, _ in py._fields_:
+            assert got[(cname, field)] == getattr(py, field).offset, (cname, field)
 
 
 def test_null_config_and_output(lib):
