@@ -271,6 +271,10 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": args.steps}))
         return
     wl = workloads.make(args.workload)
+    if args.gqa_share > 1 and (wl.Hv // wl.H) % args.gqa_share != 0:
+        print(f"--gqa-share {args.gqa_share}: workload {args.workload} has {wl.Hv // wl.H} value "
+              f"heads per key head, which the share must divide", file=sys.stderr)
+        sys.exit(2)
     d = {n: (getattr(wl, n).to(dev).contiguous() if getattr(wl, n) is not None else None)
          for n in ("q", "k", "v", "g", "beta", "h0", "qkv", "conv_w")}
     cu = torch.from_numpy(wl.cu_seqlens).to(dev)
