@@ -391,7 +391,8 @@ def _same_qkv_dtype(q, k, v):
 def recurrent_gated_delta_rule(q, k, v, g, beta, cu_seqlens, initial_state=None,
                                output_final_state=True, scale=None, n_max=None):
     """Allocate outputs with torch and run gdn_recurrent_fwd (token-serial decode /
-    verify) on the current stream. Arguments as chunk_gated_delta_rule."""
+    verify) on the current stream. Arguments as chunk_gated_delta_rule, with
+    q, k, v in bf16 or fp32 (the token-serial kernel takes no fp16)."""
     _same_qkv_dtype(q, k, v)
     T, H, _ = q.shape
     Hv = v.shape[1]
@@ -409,7 +410,7 @@ def chunk_gated_delta_rule(q, k, v, g, beta, cu_seqlens, initial_state=None,
                            workspace=None, n_max=None):
     """Allocate outputs with torch and run gdn_chunk_fwd on the current stream.
 
-    q, k [T, H, 128] and v [T, Hv, 128] (bf16 or fp32, same dtype); g, beta
+    q, k [T, H, 128] and v [T, Hv, 128] (bf16, fp16 or fp32, one dtype); g, beta
     [T, Hv] fp32; cu_seqlens int32 [N + 1] on the device; initial_state
     [N, Hv, 128, 128] fp32 or None. Returns (o [T, Hv, 128] fp32, final state
     or None).
