@@ -31,14 +31,14 @@ gdn_status check_config(const gdn_config *cfg) {
     return GDN_ERR_INVALID_ARG;
   if (cfg->o_dtype != GDN_BF16 && cfg->o_dtype != GDN_F32) return GDN_ERR_INVALID_ARG;
   if (std::isnan(cfg->scale) || std::isinf(cfg->scale)) return GDN_ERR_INVALID_ARG;
-  if (cfg->segments < 0 || cfg->segments > 2) return GDN_ERR_INVALID_ARG;
+  if (cfg->segments < 0 || cfg->segments > 4) return GDN_ERR_INVALID_ARG;
   if (cfg->tiles != 0 && cfg->tiles != 1 && cfg->tiles != 2 && cfg->tiles != 4)
     return GDN_ERR_INVALID_ARG;
   if (cfg->gqa_share != 0 && cfg->gqa_share != 1 && cfg->gqa_share != 2 && cfg->gqa_share != 4)
     return GDN_ERR_INVALID_ARG;
   if (cfg->dk != kD || cfg->dv != kD || cfg->chunk != kChunk) return GDN_ERR_UNSUPPORTED;
   if (cfg->hv % cfg->h != 0) return GDN_ERR_UNSUPPORTED;
-  if (cfg->gqa_share > 1 && ((cfg->hv / cfg->h) % cfg->gqa_share != 0 || cfg->segments == 2 ||
+  if (cfg->gqa_share > 1 && ((cfg->hv / cfg->h) % cfg->gqa_share != 0 || cfg->segments >= 2 ||
                              cfg->tiles > 1))
     return GDN_ERR_UNSUPPORTED;
   if (cfg->o_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
@@ -52,16 +52,18 @@ int32_t nt_max_of(const gdn_config *cfg) {
                               cfg->n_max - 1);
 }
 
-// Stage-2 segments of a (validated) config: automatic = two when t_max allows
-// long sequences and the one-piece grid fills at most half of the device.
+// Stage-2 segments of a (validated) config: automatic = when t_max allows long
+// sequences, the most segments (up to 4) whose walks together still fit the
+// device at one work-group per CU (segments beyond that measured slower).
 int segments_of(const gdn_config *cfg) {
   if (cfg->segments != 0) return cfg->segments;
   if (cfg->gqa_share > 1) return 1;
   if (cfg->t_max < GDN_SEGMENT_MIN_TOKENS) return 1;
-  return 2 * static_cast<int64_t>(gdn::inter_one_walk_grid(cfg->n_max, cfg->h, cfg->hv)) <=
-                 gdn::cu_count()
-             ? 2
-             : 1;
+  const int64_t one = gdn::inter_one_walk_grid(cfg->n_max, cfg->h, cfg->hv);
+  int parts = 1;
+  for (int p = 2; p <= 4; ++p)
+    if (p * one <= gdn::cu_count()) parts = p;
+  return parts;
 }
 
 // 16-column tiles per work-group of the one-piece stage-2 walk (validated
@@ -103,11 +105,12 @@ gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   l.gimg = take(hv * nt * 192 * 4);
   l.table = take(nt * 2 * 4);
   l.order = take(ranks_sequences(cfg) ? static_cast<size_t>(cfg->n_max) * 4 : 0);
-  if (segments_of(cfg) == 2) {
+  const int parts = segments_of(cfg);
+  if (parts >= 2) {
     const size_t state = static_cast<size_t>(cfg->n_max) * hv * kD * kD * 4;
     l.seg_sa = take(state);
-    l.seg_z = take(state);
-    l.seg_phi = take(state);
+    l.seg_z = take((parts - 1) * state);
+    l.seg_phi = take((parts - 1) * state);
     l.seg_oh = take(t * hv * kD * 4);
   } else {
     l.seg_sa = l.seg_z = l.seg_phi = l.seg_oh = at;
@@ -116,13 +119,16 @@ gdn_workspace_layout_t layout_of(const gdn_config *cfg) {
   return l;
 }
 
-gdn::SegScratch seg_scratch(const gdn_workspace_layout_t &l, const void *workspace) {
+gdn::SegScratch seg_scratch(const gdn_config *cfg, const gdn_workspace_layout_t &l,
+                            const void *workspace) {
   char *ws = static_cast<char *>(const_cast<void *>(workspace));
   gdn::SegScratch g;
   g.sa = reinterpret_cast<float *>(ws + l.seg_sa);
   g.z = reinterpret_cast<float *>(ws + l.seg_z);
   g.phi = reinterpret_cast<float *>(ws + l.seg_phi);
   g.oh = reinterpret_cast<float *>(ws + l.seg_oh);
+  g.state_elems = static_cast<int64_t>(cfg->n_max) * cfg->hv * kD * kD;
+  g.parts = segments_of(cfg);
   return g;
 }
 
@@ -237,7 +243,7 @@ gdn_status chunk_fwd_impl(const gdn_config *cfg, const void *q, const void *k, c
   return from_hip(gdn::launch_inter(split_k(cfg), b, h0, cu_seqlens, cfg->n_max,
                                     cfg->h, cfg->hv, cfg->t_max, nt_max_of(cfg),
                                     static_cast<float *>(o), hT, s, ev[2], segments_of(cfg),
-                                    tiles_of(cfg), share_of(cfg), seg_scratch(l, workspace)));
+                                    tiles_of(cfg), share_of(cfg), seg_scratch(cfg, l, workspace)));
 }
 
 gdn_status recurrent_impl(const gdn_config *cfg, const void *q, const void *k, const void *v,
@@ -349,7 +355,7 @@ gdn_status gdn_chunk_fwd_inter(const gdn_config *cfg, const float *h0, const int
                                     cu_seqlens, cfg->n_max, cfg->h, cfg->hv, cfg->t_max,
                                     nt_max_of(cfg), static_cast<float *>(o), hT, as_stream(stream),
                                     {}, segments_of(cfg), tiles_of(cfg), share_of(cfg),
-                                    seg_scratch(l, workspace)));
+                                    seg_scratch(cfg, l, workspace)));
 }
 
 gdn_status gdn_chunk_fwd(const gdn_config *cfg, const void *q, const void *k, const void *v,

@@ -107,8 +107,14 @@ hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const voi
 // after segment A and segment B's zero-start end state, value-major
 // [dv][dk]; segment B's homogeneous end state, key-major [dk][dv]; and the
 // homogeneous output rows [t_max, hv, dv]).
+// Scratch of the segmented stage-2 walk (P = parts segments): sa, segment
+// 0's final state; z and phi, the P - 1 later segments' final zero-start and
+// homogeneous states, one array of state_elems floats each, consecutive; oh,
+// the homogeneous output rows of every later segment's tokens.
 struct SegScratch {
   float *sa = nullptr, *z = nullptr, *phi = nullptr, *oh = nullptr;
+  int64_t state_elems = 0;
+  int parts = 1;
 };
 
 // Compute units of the current device (queried once per device).
@@ -123,9 +129,9 @@ bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int se
 // 16-column slice), rounded to whole XCD rounds).
 int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv);
 
-// segments: 1 walks each sequence in one piece; 2 walks its two halves at once
-// (the second carrying the zero-start and the homogeneous state) and then
-// combines them with a fix-up kernel, using `seg`. tiles: 16-column slices of
+// segments: 1 walks each sequence in one piece; 2 to 4 walk that many
+// segments of it at once (all but the first carrying the zero-start and the
+// homogeneous state) and then combine them with fix-up kernels, using `seg`. tiles: 16-column slices of
 // one value head per work-group (1, 2, 4). share: 2 or 4 selects the
 // GQA-shared shape instead (one 16-column slice of `share` value heads of a
 // key head per work-group; one-piece walk only).

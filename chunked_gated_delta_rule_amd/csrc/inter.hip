@@ -91,14 +91,17 @@ template <bool kF32In, int kDepth, int kS, int kNV>
 constexpr bool kWarmWave = kNV == 1 && !(kF32In && kDepth == 2) && (kS == 1 || kDepth == 1);
 constexpr int kDepthSeg = 1;  // prefetch depth of the two-state walk (keeps the warm-up wave)
 
-// Chunks of segment A (walked from h0 with one state) when a sequence of nc
-// chunks is walked in two segments: all but floor(2 nc / 5). Segment B carries
-// two states (twice the products per chunk), segment A one; with the operands
-// coming from HBM both are bound mostly by their loads, so the balance point
-// is near the middle (T = 32768: B taking 1/2, 2/5, 3/8 and 1/3 of the chunks
-// gave stage 2 503, 488, 495 and 509 us).
-constexpr int kSegBNum = 2, kSegBDen = 5;
-__host__ __device__ constexpr int seg_split(int nc) { return nc - nc * kSegBNum / kSegBDen; }
+// Segments of a sequence of nc chunks walked in P parts at once. Segment 0
+// (from h0, one state) takes the first nc - (P - 1) y chunks; each later
+// segment carries two states (twice the products per chunk) and takes
+// y = floor(2 nc / (2 P + 1)) chunks, so segment 0 gets about 1.5 times as
+// many (T = 32768, two parts: the later segment taking 1/2, 2/5, 3/8 and 1/3
+// of the chunks gave stage 2 503, 488, 495 and 509 us).
+__host__ __device__ constexpr int seg_len(int nc, int parts) { return nc * 2 / (2 * parts + 1); }
+// first chunk of segment r (r = parts: the end of the sequence)
+__host__ __device__ constexpr int seg_begin(int nc, int parts, int r) {
+  return r == 0 ? 0 : nc - (parts - r) * seg_len(nc, parts);
+}
 template <bool kF32In, int kDepth, int kS, int kNV>
 constexpr int kInterThreads = kWarmWave<kF32In, kDepth, kS, kNV> ? 320 : 256;
 // waves per SIMD the register allocation must leave room for
@@ -673,11 +676,12 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
 }
 
 // With kS = 1 every work-group walks its whole sequence. With kS = 2 the grid
-// is twice the one-walk grid: the first half walks the first seg_split(nc)
-// chunks of each sequence from h0 (its final slice goes to seg.sa), the
-// second half walks the rest carrying the zero-start state (outputs into o,
-// final slice to seg.z) and the identity-start homogeneous state (outputs to
-// seg.oh, final slice to seg.phi); segfix_kernel then combines them.
+// is seg.parts times the one-walk grid: copy 0 walks segment 0 of each
+// sequence from h0 (its final slice goes to seg.sa), copy r >= 1 walks
+// segment r carrying the zero-start state (outputs into o, final slice to
+// seg.z's array r - 1) and the identity-start homogeneous state (outputs to
+// seg.oh, final slice to seg.phi's array r - 1); the fix-up kernels then
+// combine them.
 template <bool kF32In, int kDepth, int kS, int kNV, bool kGq>
 __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
                              kInterWavesPerSimd<kNV>) void inter_kernel(
@@ -697,7 +701,8 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   const int members = (kGq ? HG / kNV : HG) * kWgSlices;
   const int one_walk = (n_max * H + kXcds - 1) / kXcds * kXcds * members;
   const int wg = flat_block();
-  const int role = kS == 2 && wg >= one_walk ? 1 : 0;
+  const int role = kS == 2 ? wg / one_walk : 0;  // the segment walked
+  if (role >= seg.parts) return;
   const int b = wg - role * one_walk;
   const int xcd = b % kXcds;
   const int wslot = b / kXcds;
@@ -725,9 +730,11 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   if (kS == 1) {
     W = Walk{0, L.nc, h0, {o, nullptr}, {hT, nullptr}, false};
   } else {
-    const int cm = seg_split(L.nc);
-    W = role == 0 ? Walk{0, cm, h0, {o, nullptr}, {seg.sa, nullptr}, false}
-                  : Walk{cm, L.nc, nullptr, {o, seg.oh}, {seg.z, seg.phi}, true};
+    const int c0 = seg_begin(L.nc, seg.parts, role);
+    const int c1 = seg_begin(L.nc, seg.parts, role + 1);
+    const int64_t at = static_cast<int64_t>(role - 1) * seg.state_elems;
+    W = role == 0 ? Walk{0, c1, h0, {o, nullptr}, {seg.sa, nullptr}, false}
+                  : Walk{c0, c1, nullptr, {o, seg.oh}, {seg.z + at, seg.phi + at}, true};
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0)
@@ -742,44 +749,33 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
     l2_warm_wave<kF32In, kDepth>(L, W, in, member, members, l2_sink, warm_values);
 }
 
-// ---- two-segment fix-up ------------------------------------------------------
-// The recurrence is affine in the state a segment starts from: with S_A the
-// state after segment A, segment B's true state is Z + Phi S_A and its true
-// output rows are o_zero + o_hom S_A (Z, o_zero: the walk from zero with u;
-// Phi, o_hom: the walk from the identity without u). In the stored layouts
-// (value-major St[v][d]; Phi key-major) both updates are C = A B^T products:
-//   o rows:  C[v][t] = sum_j SA_t[v][j] o_hom[t][j],   o[t][v] += C[v][t]
-//   state:   C[d][v] = sum_j Phi[d][j] SA_t[v][j],     hT[v][d] = Z_t[v][d] + C[d][v]
+// ---- segment fix-up ----------------------------------------------------------
+// The recurrence is affine in the state a segment starts from: with S_{k-1}
+// the state before segment k >= 1, segment k's true final state is
+// S_k = Z_k + Phi_k S_{k-1} and its true output rows are o_zero + o_hom
+// S_{k-1} (Z, o_zero: the walk from zero with u; Phi, o_hom: the walk from
+// the identity without u). In the stored layouts (value-major St[v][d]; Phi
+// key-major) both updates are C = A B^T products:
+//   o rows:  C[v][t] = sum_j S_t[v][j] o_hom[t][j],    o[t][v] += C[v][t]
+//   state:   C[d][v] = sum_j Phi[d][j] S_t[v][j],      S'_t[v][d] = Z_t[v][d] + C[d][v]
 // One 256-thread work-group computes one 128 x 128 C (128 output rows of a
-// (sequence, value head), or its final state) on v_mfma_f32_16x16x32_bf16,
-// both fp32 operands split into bf16 hi + lo and three product terms; A is
-// staged in LDS, each wave owns 32 columns of C, and the wave's B^T rows and
-// the output tile are requested before A is staged.
+// (sequence, value head), or a state) on v_mfma_f32_16x16x32_bf16, both fp32
+// operands split into bf16 hi + lo and three product terms; A is staged in
+// LDS, each wave owns 32 columns of C, and the wave's B^T rows and the output
+// tile are requested before A is staged. With two parts one launch does the
+// rows and the final state (S_1 from S_0); with more, one launch per state
+// S_1, ..., S_{P-1} in order (S_k over Z_k in place, the last into hT), then
+// one for the rows of every later segment.
 constexpr int kFixThreads = 256;
 constexpr int kLdFix = kD + 8;
 
-__global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__restrict__ cu,
-                                                             float *__restrict__ o,
-                                                             float *__restrict__ hT, SegScratch seg,
-                                                             int n_max, int Hv, int t_max, int nbo) {
-  __shared__ __attribute__((aligned(16))) __bf16 ahi[kD * kLdFix];
-  __shared__ __attribute__((aligned(16))) __bf16 alo[kD * kLdFix];
-  const int per = nbo + 1;
-  const int pair = flat_block() / per, blk = flat_block() % per;
-  const int s = pair / Hv, hv = pair % Hv;
-  if (s >= n_max) return;
-  const int bos = cu_at(cu, s, t_max), eos = cu_end(cu, s, bos, t_max);
-  const int nc = (eos - bos + kC - 1) / kC, cm = seg_split(nc);
-  const int64_t st = ((int64_t)s * Hv + hv) * kD * kD;
-  const bool fin = blk == nbo;
-  const int t_begin = bos + kC * (cm + 2 * blk);  // 128 output rows per work-group
-  if (fin ? hT == nullptr : t_begin >= eos) return;
-  const float *A = fin ? seg.phi + st : seg.sa + st;
-  const float *Bt = fin ? seg.sa + st : seg.oh + ((int64_t)t_begin * Hv + hv) * kD;
-  const uint32_t bt_row = fin ? kD * 4 : static_cast<uint32_t>(Hv) * kD * 4;
-  const int rows = fin ? kD : min(2 * kC, eos - t_begin);
+// dst[n][16 mt + 4 g + i] = base[n][..] + C: rows n < rows of B^T (row
+// stride bt_row bytes) and of base / dst (base_row bytes); A is 128 x 128
+// value-major or key-major as above (row stride 128 floats).
+__device__ __forceinline__ void fix_block(const float *A, const float *Bt, uint32_t bt_row,
+                                          const float *base, float *dst, uint32_t base_row,
+                                          int rows, __bf16 *ahi, __bf16 *alo) {
   const rsrc_t rb = make_rsrc(Bt, static_cast<uint32_t>(rows) * bt_row);
-
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   // requests first: this wave's B^T rows (32 wv + 16 nt + c, all k) and the
@@ -793,11 +789,8 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
       braw[ks][nt][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
       braw[ks][nt][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, off + 16, 0, 0);
     }
-  // C tile (mt, nt) element i: row 16 mt + 4 g + i, column n = 32 wv + 16 nt + c;
-  // its base: hT row n / Z row n (final state) or o row t_begin + n (rows past
-  // the sequence read as zero and are not written)
-  const float *base = fin ? seg.z + st : o + ((int64_t)t_begin * Hv + hv) * kD;
-  const uint32_t base_row = fin ? kD * 4 : static_cast<uint32_t>(Hv) * kD * 4;
+  // C tile (mt, nt) element i: row 16 mt + 4 g + i, column n = 32 wv + 16 nt + c
+  // (rows past the sequence read as zero and are not written)
   const rsrc_t rc = make_rsrc(base, static_cast<uint32_t>(rows) * base_row);
   f32x4 add[8][2];
 #pragma unroll
@@ -851,26 +844,83 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
       }
     }
   }
-  // hT[v = n][d = 16 mt + 4 g ..] = Z + C, or o[t_begin + n][hv][v = 16 mt + 4 g ..] += C
-  float *dst_base = fin ? hT + st : o + ((int64_t)t_begin * Hv + hv) * kD;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int n = 32 * wv + 16 * nt + c;
     if (n < rows) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<f32x4 *>(dst_base + (int64_t)n * (base_row / 4) + 16 * mt + 4 * g) =
+        *reinterpret_cast<f32x4 *>(dst + (int64_t)n * (base_row / 4) + 16 * mt + 4 * g) =
             add[mt][nt] + acc[mt][nt];
     }
   }
 }
 
-// Work-groups of 128 output rows over the at most nc - seg_split(nc) chunks
-// of segment B (nc = ceil(t_max / 64) at most), per (sequence, value head);
-// the fix-up grid has one more (the final state) per pair.
-int fix_row_blocks(int32_t t_max) {
+// Row blocks of 128 outputs of segments 1 .. P - 1 (nbo per segment), and
+// with two parts also the final state S_1 (one more block per pair).
+__global__ __launch_bounds__(kFixThreads, 2) void segfix_kernel(const int32_t *__restrict__ cu,
+                                                             float *__restrict__ o,
+                                                             float *__restrict__ hT, SegScratch seg,
+                                                             int n_max, int Hv, int t_max, int nbo) {
+  __shared__ __attribute__((aligned(16))) __bf16 ahi[kD * kLdFix];
+  __shared__ __attribute__((aligned(16))) __bf16 alo[kD * kLdFix];
+  const int parts = seg.parts;
+  // (at least one work-group per pair: with a capacity too short for the
+  // later segments there are no row blocks, and the launch does nothing)
+  const int per = max(1, (parts - 1) * nbo + (parts == 2 ? 1 : 0));
+  const int pair = flat_block() / per, r = flat_block() % per;
+  const int s = pair / Hv, hv = pair % Hv;
+  if (s >= n_max) return;
+  const int64_t st = ((int64_t)s * Hv + hv) * kD * kD;
+  if (parts == 2 && r == nbo) {  // S_1 = Z_1 + Phi_1 S_0, the final state
+    if (hT == nullptr) return;
+    fix_block(seg.phi + st, seg.sa + st, kD * 4, seg.z + st, hT + st, kD * 4, kD, ahi, alo);
+    return;
+  }
+  if (nbo == 0) return;
+  const int bos = cu_at(cu, s, t_max), eos = cu_end(cu, s, bos, t_max);
+  const int nc = (eos - bos + kC - 1) / kC;
+  const int k = 1 + r / nbo, blk = r % nbo;  // segment, 128-row block of it
+  const int t_begin = bos + kC * (seg_begin(nc, parts, k) + 2 * blk);
+  const int t_end = min(eos, bos + kC * seg_begin(nc, parts, k + 1));
+  if (t_begin >= t_end) return;
+  const float *A = k == 1 ? seg.sa + st : seg.z + (k - 2) * seg.state_elems + st;  // S_{k-1}
+  const int64_t row0 = ((int64_t)t_begin * Hv + hv) * kD;
+  const uint32_t row_bytes = static_cast<uint32_t>(Hv) * kD * 4;
+  fix_block(A, seg.oh + row0, row_bytes, o + row0, o + row0, row_bytes, min(2 * kC, t_end - t_begin),
+            ahi, alo);
+}
+
+// State k of a walk in more than two parts: S_k = Z_k + Phi_k S_{k-1}, over
+// Z_k in place, or into hT for the last (not written when hT is null).
+__global__ __launch_bounds__(kFixThreads, 2) void segstate_kernel(float *__restrict__ hT,
+                                                               SegScratch seg, int n_max, int Hv,
+                                                               int k) {
+  __shared__ __attribute__((aligned(16))) __bf16 ahi[kD * kLdFix];
+  __shared__ __attribute__((aligned(16))) __bf16 alo[kD * kLdFix];
+  const int pair = flat_block();
+  if (pair >= n_max * Hv) return;
+  const int64_t st = static_cast<int64_t>(pair) * kD * kD;
+  const int64_t E = seg.state_elems;
+  float *z = seg.z + (k - 1) * E + st;
+  float *dst = k == seg.parts - 1 ? (hT ? hT + st : nullptr) : z;
+  if (dst == nullptr) return;
+  const float *prev = (k == 1 ? seg.sa : seg.z + (k - 2) * E) + st;
+  fix_block(seg.phi + (k - 1) * E + st, prev, kD * 4, z, dst, kD * 4, kD, ahi, alo);
+}
+
+// Row blocks of 128 outputs per later segment: a segment has at most
+// seg_len(nc, parts) chunks, nc = ceil(t_max / 64) at most.
+int fix_row_blocks(int32_t t_max, int parts) {
   const int nc = (t_max + kC - 1) / kC;
-  return (nc - seg_split(nc) + 1) / 2;
+  return (seg_len(nc, parts) + 1) / 2;
+}
+
+// Work-groups of the row fix-up launch (at least one per pair).
+int64_t fix_grid(int32_t n_max, int32_t hv, int32_t t_max, int parts) {
+  const int64_t per =
+      (parts - 1) * static_cast<int64_t>(fix_row_blocks(t_max, parts)) + (parts == 2 ? 1 : 0);
+  return static_cast<int64_t>(n_max) * hv * std::max<int64_t>(1, per);
 }
 
 template <bool kF32In, int kDepth, int kS, int kNV = 1, bool kGq = false>
@@ -882,7 +932,8 @@ hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *c
   const int64_t rounds = (static_cast<int64_t>(n_max) * h + kXcds - 1) / kXcds;
   constexpr int kThr = kInterThreads<kF32In, kDepth, kS, kNV>;
   dim3 grid;
-  if (!flat_grid(kS * rounds * kXcds * members, kThr, grid)) return hipErrorInvalidValue;
+  if (!flat_grid((kS == 2 ? seg.parts : 1) * rounds * kXcds * members, kThr, grid))
+    return hipErrorInvalidValue;
   // warm the value heads' lines too when the intermediates exceed about 160
   // MiB (the last-level cache is 256 MB and also holds the inputs and o)
   const int64_t per_chunk = static_cast<int64_t>(hv) * (16 * 1024 + kD * kC * 3 + kPBytes +
@@ -900,7 +951,6 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
                         int32_t h, int32_t hv, int32_t t_max, int32_t nt, float *o, float *hT,
                         hipStream_t stream, KernelEvents ev, int segments, int tiles, int share,
                         const SegScratch &seg) {
-  const int one_walk = inter_one_walk_grid(n_max, h, hv);
   // the GQA-shared shape (one slice of `share` value heads per work-group);
   // the host admits it only for the one-piece, one-tile walk
   if (share == 4)
@@ -909,7 +959,7 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
   if (share == 2)
     return launch_walk<kF32In, 1, 1, 2, true>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
                                               stream, ev.start, ev.stop);
-  if (segments != 2) {
+  if (segments < 2) {
     if (tiles == 4)
       return launch_walk<kF32In, 1, 1, 4>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
                                           ev.start, ev.stop);
@@ -919,18 +969,22 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
     return launch_walk<kF32In, kDepthSingle, 1>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
                                                 stream, ev.start, ev.stop);
   }
-  // the fix-up grid was checked on the host before anything was queued
-  const int nbo = fix_row_blocks(t_max);
-  dim3 grid;
-  if (!flat_grid(static_cast<int64_t>(n_max) * hv * (nbo + 1), kFixThreads, grid))
+  // the fix-up grids were checked on the host before anything was queued
+  const int parts = seg.parts;
+  if (parts != segments || parts > 4) return hipErrorInvalidValue;
+  const int nbo = fix_row_blocks(t_max, parts);
+  dim3 grid, sgrid;
+  if (!flat_grid(fix_grid(n_max, hv, t_max, parts), kFixThreads, grid) ||
+      !flat_grid(static_cast<int64_t>(n_max) * hv, kFixThreads, sgrid))
     return hipErrorInvalidValue;
-  const hipError_t e =
-      2 * one_walk <= cu_count()
-          ? launch_walk<kF32In, kDepthSeg, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg,
-                                              stream, ev.start, nullptr)
-          : launch_walk<kF32In, 1, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o, hT, seg, stream,
-                                      ev.start, nullptr);
+  const hipError_t e = launch_walk<kF32In, kDepthSeg, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o,
+                                                         hT, seg, stream, ev.start, nullptr);
   if (e != hipSuccess) return e;
+  for (int k = 1; parts > 2 && k < parts; ++k) {  // S_1 .. S_{P-1} in order
+    hipLaunchKernelGGL(segstate_kernel, sgrid, dim3(kFixThreads), 0, stream, hT, seg, n_max, hv, k);
+    const hipError_t es = hipGetLastError();
+    if (es != hipSuccess) return es;
+  }
   hipExtLaunchKernelGGL(segfix_kernel, grid, dim3(kFixThreads), 0,
                         stream, nullptr, ev.stop, 0, cu, o, hT, seg, n_max, hv, t_max, nbo);
   return hipGetLastError();
@@ -955,12 +1009,13 @@ int cu_count() {
 
 bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int segments, int tiles,
                      int share) {
-  const int64_t members = (hv / h / share) * (kSlices / (segments == 2 ? 1 : tiles));
+  const int64_t members = (hv / h / share) * (kSlices / (segments >= 2 ? 1 : tiles));
   const int64_t rounds = (static_cast<int64_t>(n_max) * h + kXcds - 1) / kXcds;
   dim3 grid;
-  if (!flat_grid((segments == 2 ? 2 : 1) * rounds * kXcds * members, 320, grid)) return false;
-  if (segments != 2) return true;
-  return flat_grid(static_cast<int64_t>(n_max) * hv * (fix_row_blocks(t_max) + 1), kFixThreads, grid);
+  if (!flat_grid((segments >= 2 ? segments : 1) * rounds * kXcds * members, 320, grid)) return false;
+  if (segments < 2) return true;
+  return flat_grid(fix_grid(n_max, hv, t_max, segments), kFixThreads, grid) &&
+         flat_grid(static_cast<int64_t>(n_max) * hv, kFixThreads, grid);
 }
 
 int inter_one_walk_grid(int32_t n_max, int32_t h, int32_t hv) {

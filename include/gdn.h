@@ -82,14 +82,17 @@ typedef struct {
   gdn_dtype qkv_dtype; /* dtype of q, k, v: GDN_BF16, GDN_F32 or GDN_F16 */
   gdn_dtype o_dtype;   /* dtype of o: GDN_F32 (the only one supported) */
   float scale;         /* output scale; <= 0 selects 1 / sqrt(dk) */
-  int32_t segments;    /* stage-2 walk of each sequence: 1 = one piece; 2 = two
-                          segments at once (the first 3/5 of its chunks from the
-                          initial state, the rest from zero and from the
-                          identity), then a fix-up (the recurrence is affine in
-                          the starting state);
-                          0 = automatic: 2 when t_max >=
-                          GDN_SEGMENT_MIN_TOKENS and the one-piece stage-2 grid fills
-                          at most half of the current device's compute units */
+  int32_t segments;    /* stage-2 walk of each sequence: 1 = one piece; P = 2, 3
+                          or 4 = P segments at once (of a sequence of nc chunks,
+                          every later segment y = floor(2 nc / (2P + 1)) chunks,
+                          walked from zero and from the identity; the first
+                          segment the rest, from the initial state), then fix-ups
+                          that chain the segments' states and correct their
+                          outputs (the recurrence is affine in the starting
+                          state); 0 = automatic: when t_max >=
+                          GDN_SEGMENT_MIN_TOKENS, the largest P <= 4 for which P
+                          times the one-piece stage-2 grid fits the current
+                          device's compute units (1 if none) */
   int32_t tiles;       /* 16-column tiles of the state per stage-2 work-group in the
                           one-piece walk: 1, 2 or 4 (the results are bitwise the same);
                           0 = automatic: 1 when the one-tile grid fits the device, 4
@@ -103,7 +106,7 @@ typedef struct {
                           carries one 16-column slice of that many value heads
                           of one key head and loads the key head's K^T and q
                           fragments once for all of them; it must divide hv / h,
-                          and needs segments != 2 and tiles <= 1 (automatic
+                          and needs segments <= 1 and tiles <= 1 (automatic
                           segments and tiles then resolve to 1). 0 or 1 = the
                           column-tile shapes above. Results are bitwise those of
                           tiles = 1. Never chosen automatically: at equal
@@ -116,16 +119,18 @@ typedef struct {
  * start and end of each walk are not hidden behind another work-group). */
 #define GDN_FOUR_TILE_MIN_TOKENS 384
 
-/* Token capacity from which the automatic choice considers two segments. */
+/* Token capacity from which the automatic choice considers segments. */
 #define GDN_SEGMENT_MIN_TOKENS 2048
 
 /* Largest valid gdn_config.t_max / n_max. Each kernel takes at most
- * 2^31 - 1 work-groups per launch. Within these limits only the fix-up of the
- * two-segment walk can need more: about n_max * hv * t_max / 320
- * work-groups, so with segments = 2 and n_max * hv * t_max above about
- * 2^39.3 the forward returns GDN_ERR_CAPACITY. That check runs on the host before anything is
- * queued, like every other check. The automatic choice takes two segments
- * only for grids that fill at most half of the device, far inside that bound. */
+ * 2^31 - 1 work-groups per launch. Within these limits only the output fix-up
+ * of a segmented walk can need more: about n_max * hv * t_max / 320
+ * work-groups with two segments (/ 224 with three, / 192 with four), so with
+ * segments >= 2 and n_max * hv * t_max above about 2^38.6 (four segments) to
+ * 2^39.3 (two) the forward returns
+ * GDN_ERR_CAPACITY. That check runs on the host before anything is queued,
+ * like every other check. The automatic choice takes segments only for grids
+ * that fit the device several times over, far inside that bound. */
 #define GDN_T_MAX_LIMIT (1 << 24)
 #define GDN_N_MAX_LIMIT 16384
 
@@ -168,17 +173,20 @@ int64_t gdn_nt_max(int32_t t_max, int32_t n_max, int32_t chunk);
  *         empty: the sequence indices ranked by chunk count, longest first
  *         (ties by index). Stage 1 writes it and stage 2 starts the walks in
  *         that order, so that the longest sequences do not start last.
- *   seg_sa, seg_z fp32 [n_max, hv, dv, dk]: with two segments, the state after
- *         the first half, and the second half's end state from zero
- *   seg_phi fp32 [n_max, hv, dk, dk]: the second half's homogeneous end state
- *         (the product of its chunk transitions), key-major
- *   seg_oh fp32 [t_max, hv, dv]: the second half's homogeneous output rows
+ *   seg_sa fp32 [n_max, hv, dv, dk]: with P >= 2 segments, the state after
+ *         the first segment
+ *   seg_z fp32 [P - 1][n_max, hv, dv, dk]: each later segment's end state
+ *         from zero (then, for all but the last, its true end state)
+ *   seg_phi fp32 [P - 1][n_max, hv, dk, dk]: each later segment's
+ *         homogeneous end state (the product of its chunk transitions),
+ *         key-major
+ *   seg_oh fp32 [t_max, hv, dv]: the later segments' homogeneous output rows
  * Per-chunk blocks are indexed by slot floor(t0 / 64) + n for a chunk starting
  * at token t0 of sequence n (distinct per chunk, < nt_max). With automatic
  * segments the size depends on the current device (its compute units). */
 typedef struct {
   size_t w16, q16, kimg, uimg, pimg, gimg, table, order;
-  size_t seg_sa, seg_z, seg_phi, seg_oh; /* two-segment scratch (equal to total when the
+  size_t seg_sa, seg_z, seg_phi, seg_oh; /* segment scratch (equal to total when the
                                             config resolves to one segment) */
   size_t total; /* bytes of workspace gdn_chunk_fwd needs */
 } gdn_workspace_layout_t;
@@ -234,7 +242,7 @@ gdn_status gdn_chunk_fwd_intra(const gdn_config *cfg, const void *q, const void 
                                void *stream);
 
 /* Inter-chunk stage over [n_max, hv, dv / 16] (AMX page, section 5), or with
- * two segments over twice that grid plus a fix-up (cfg->segments): chunks in
+ * P segments over P times that grid plus fix-ups (cfg->segments): chunks in
  * order with S on chip: v' = u - w S; o = scale (diag(e^gamma) q S +
  * tril(q k^T * Gamma) v'); S = e^{gamma_last} S + (diag(e^{gamma_last - gamma}) k)^T v',
  * Gamma[r, i] = exp(gamma_r - gamma_i) for i <= r (diagonal kept). Reads only

@@ -113,6 +113,20 @@ def test_workspace_layout_segments(lib):
     wide = gdn.make_config(32768, 1, 16, 32)  # 256 work-groups: one segment
     lay = gdn.gdn_workspace_layout(wide)
     assert lay["seg_oh"] == lay["total"]
+    # automatic, fewer heads: the most segments (up to four) whose walks fit
+    # the device (H = Hv = 8: 64 work-groups, four segments)
+    lay = gdn.gdn_workspace_layout(gdn.make_config(32768, 1, 8, 8))
+    four = gdn.gdn_workspace_layout(gdn.make_config(32768, 1, 8, 8, segments=4))
+    assert lay == four and lay["seg_phi"] - lay["seg_z"] == 3 * 8 * 128 * 128 * 4
+    # P segments: segment 0's state, then P - 1 zero-start and P - 1
+    # homogeneous states, then the homogeneous output rows
+    for parts in (3, 4):
+        lay = gdn.gdn_workspace_layout(gdn.make_config(T, N, H, Hv, segments=parts))
+        assert lay["seg_sa"] == one["total"]
+        assert lay["seg_z"] == lay["seg_sa"] + state
+        assert lay["seg_phi"] == lay["seg_z"] + al((parts - 1) * N * Hv * 128 * 128 * 4)
+        assert lay["seg_oh"] == lay["seg_phi"] + al((parts - 1) * N * Hv * 128 * 128 * 4)
+        assert lay["total"] == lay["seg_oh"] + al(T * Hv * 128 * 4)
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -121,7 +135,8 @@ def test_workspace_layout_segments(lib):
     ("t_max", -1, INVALID), ("n_max", 0, INVALID), ("h", 0, INVALID), ("qkv_dtype", 7, INVALID),
     ("qkv_dtype", 2, OK),
     ("scale", float("nan"), INVALID), ("t_max", (1 << 24) + 1, CAPACITY), ("n_max", 16385, CAPACITY),
-    ("segments", 3, INVALID), ("segments", -1, INVALID), ("tiles", 3, INVALID),
+    ("segments", 5, INVALID), ("segments", -1, INVALID), ("segments", 3, OK), ("segments", 4, OK),
+    ("tiles", 3, INVALID),
     ("tiles", -1, INVALID), ("tiles", 8, INVALID), ("tiles", 4, OK), ("tiles", 1, OK),
     ("gqa_share", 3, INVALID), ("gqa_share", -1, INVALID), ("gqa_share", 8, INVALID),
     ("gqa_share", 2, OK), ("gqa_share", 1, OK),

@@ -1,11 +1,13 @@
-"""GPU parity of the two-segment stage 2 (gdn_config.segments = 2): each
-sequence's halves are walked at once, the second from the zero state and from
-the identity, and a fix-up combines them with the first half's final state.
-Checked against the CPU oracle on every lane of small batches (sequence lengths
-around the chunk and segment boundaries, empty sequences, fp32 and bf16, with
-and without initial states), and on the long-context workload in the launch
-configuration the benchmark uses (automatic segments), against the oracle on
-every lane and against the one-piece walk.
+"""GPU parity of the segmented stage 2 (gdn_config.segments = 2, 3 or 4): each
+sequence's segments are walked at once, every segment after the first from
+the zero state and from the identity, and fix-up kernels chain the segments'
+states and correct their outputs. Checked against the CPU oracle on every
+lane of small batches (sequence lengths around the chunk and segment
+boundaries, sequences too short to reach the later segments, empty
+sequences, fp32 and bf16, with and without initial states), with a weak decay
+that makes the corrections large terms, and on the long-context workload in
+the launch configuration the benchmark uses (automatic segments) and in four
+segments, against the oracle on every lane and against the one-piece walk.
 """
 
 import numpy as np
@@ -52,13 +54,14 @@ def _forward(wl, segments, d=None, with_hT=True):
 LENGTHS = [0, 1, 64, 65, 127, 128, 129, 300, 1000, 63, 0]
 
 
+@pytest.mark.parametrize("segments", [2, 3, 4])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("with_h0", [True, False])
-def test_two_segments_every_lane(dtype, with_h0):
+def test_segments_every_lane(segments, dtype, with_h0):
     wl = workloads.make_custom(LENGTHS, 2, 4, seed=21, dtype=dtype, t_max=sum(LENGTHS) + 70,
                                n_max=len(LENGTHS) + 1, h0_sigma=0.02 if with_h0 else 0.0)
-    log(f"two segments: lengths {LENGTHS} dtype={dtype} h0={with_h0}")
-    o, hT = _forward(wl, 2)
+    log(f"{segments} segments: lengths {LENGTHS} dtype={dtype} h0={with_h0}")
+    o, hT = _forward(wl, segments)
     ref = oracle_lanes(wl, _all_lanes(wl))
     eo, es = lane_errors(wl, o, hT, ref)
     log(f"  o err {eo:.3e}  S err {es:.3e}")
@@ -67,11 +70,29 @@ def test_two_segments_every_lane(dtype, with_h0):
     assert torch.isnan(o[T:]).all()  # rows past the batch untouched
 
 
-def test_two_segments_without_final_state():
+@pytest.mark.parametrize("segments", [3, 4])
+def test_segments_capacity_too_short_for_later_segments(segments):
+    """t_max of at most 64 x segments tokens: no sequence reaches a later
+    segment (they have no chunks), so segment 0 walks everything and the
+    chained states hand its final state through unchanged."""
+    lengths = [100, 0, 30, 60]
+    wl = workloads.make_custom(lengths, 1, 2, seed=24, t_max=sum(lengths), h0_sigma=0.05)
+    assert wl.t_max <= 64 * segments
+    log(f"{segments} segments, t_max {wl.t_max}")
+    o, hT = _forward(wl, segments)
+    eo, es = lane_errors(wl, o, hT, oracle_lanes(wl, _all_lanes(wl)))
+    log(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
+
+
+@pytest.mark.parametrize("segments", [2, 4])
+def test_segments_without_final_state(segments):
+    """Without hT the outputs are bitwise those with it (with more than two
+    segments the intermediate states are still chained for the outputs)."""
     wl = workloads.make_custom([700, 5, 190], 2, 4, seed=22, h0_sigma=0.02)
     d = device_inputs(wl, DEV)
-    o_ref, _ = _forward(wl, 2, d)
-    o, _ = _forward(wl, 2, d, with_hT=False)
+    o_ref, _ = _forward(wl, segments, d)
+    o, _ = _forward(wl, segments, d, with_hT=False)
     assert torch.equal(o[:wl.n_tokens], o_ref[:wl.n_tokens])
 
 
@@ -97,19 +118,22 @@ def test_long_context_automatic_segments_vs_one_piece():
     assert eo <= O_TOL and es <= S_TOL
 
 
+@pytest.mark.parametrize("segments", [2, 3, 4])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_two_segments_weak_decay(dtype):
+def test_segments_weak_decay(segments, dtype):
     """With g scaled down the state carries across the whole sequence, so the
-    second half's outputs and the final state depend strongly on the first
-    half: the fix-up's correction is a large term here, not a rounding one."""
+    later segments' outputs and the final state depend strongly on the first
+    segment: the fix-up's correction is a large term here, not a rounding one."""
     lengths = [2000, 129, 700]
     wl = workloads.make_custom(lengths, 2, 4, seed=23, dtype=dtype, h0_sigma=0.05, g_scale=0.002)
     d = device_inputs(wl, DEV)
-    o, hT = _forward(wl, 2, d)
+    o, hT = _forward(wl, segments, d)
     ref = oracle_lanes(wl, _all_lanes(wl))
     eo, es = lane_errors(wl, o, hT, ref)
-    log(f"  weak decay, two segments: o err {eo:.3e}  S err {es:.3e}")
+    log(f"  weak decay, {segments} segments: o err {eo:.3e}  S err {es:.3e}")
     assert eo <= O_TOL and es <= S_TOL
+    if segments != 2:
+        return
     # the first half matters: the second half walked from zero alone (what the
     # fix-up corrects) is far from the true outputs
     s, hv = 0, 1
@@ -123,3 +147,15 @@ def test_two_segments_weak_decay(dtype):
     gap = np.max(np.abs(o_zero[:, 0] - o_true)) / np.max(np.abs(o_true))
     log(f"  second half from zero vs true: {gap:.3e}")
     assert gap > 50 * O_TOL
+
+
+def test_long_context_four_segments():
+    """The long-context workload walked in four segments (three chained
+    states): every lane against the oracle."""
+    wl = workloads.make(3)
+    log(f"four segments, workload 3 ({wl.name})")
+    o, hT = _forward(wl, 4)
+    o_ref, s_ref = oracle_full(wl)
+    eo, es = full_errors(wl, o, hT, o_ref, s_ref)
+    log(f"  every lane: o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL
