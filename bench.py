@@ -223,7 +223,9 @@ def main():
                          "others run the plain entry point: per-dispatch events add a few "
                          "microseconds to the step they are on)")
     ap.add_argument("--workload", type=int, default=1,
-                    help="named workload 0..6 (5 and 6 time the token-serial kernel)")
+                    help="named workload 0..7 (5 and 6 time the token-serial kernel)")
+    ap.add_argument("--segments", type=int, default=0, choices=(0, 1, 2, 3, 4),
+                    help="stage-2 segments per sequence (default 0: the automatic choice)")
     ap.add_argument("--settle-ms", type=float, default=1000.0, metavar="MS",
                     help="before the W warm-up steps, run untimed steps for this many "
                          "milliseconds of wall time, so that the GPU clocks and the host "
@@ -284,7 +286,8 @@ def main():
     qkv_dtype = wl.qkv_dtype
     if has_front:
         qkv_dtype = torch.float16 if fused_front and args.front_dtype == "f16" else torch.float32
-    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype, gqa_share=args.gqa_share)
+    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, qkv_dtype, gqa_share=args.gqa_share,
+                          segments=args.segments)
     ws = torch.empty(gdn.gdn_workspace_size(cfg), dtype=torch.uint8, device=dev)
     o = torch.empty((wl.t_max, wl.Hv, 128), dtype=torch.float32, device=dev)
     hT = torch.empty((wl.n_max, wl.Hv, 128, 128), dtype=torch.float32, device=dev)
@@ -442,6 +445,7 @@ def main():
                    "parallelism": "single GPU",
                    **({"stage2": f"GQA-shared, {args.gqa_share} value heads per work-group"}
                       if args.gqa_share > 1 else {}),
+                   **({"segments": args.segments} if args.segments else {}),
                    **({"front": "fused into stage 1" if fused_front else "standalone kernel"}
                       if has_front else {})},
         "roofline": roofline,

@@ -159,3 +159,20 @@ def test_long_context_four_segments():
     eo, es = full_errors(wl, o, hT, o_ref, s_ref)
     log(f"  every lane: o err {eo:.3e}  S err {es:.3e}")
     assert eo <= O_TOL and es <= S_TOL
+
+
+def test_long_context_fewer_heads_automatic_segments():
+    """The long-context recipe with H = Hv = 8 (a one-piece walk of 64
+    work-groups): the automatic choice takes four segments on an MI355X, and
+    every lane meets the bar against the oracle."""
+    wl = workloads.make(7)
+    log(f"automatic segments, workload 7 ({wl.name})")
+    cfg = gdn.make_config(wl.t_max, wl.n_max, wl.H, wl.Hv, wl.qkv_dtype)
+    lay = gdn.gdn_workspace_layout(cfg)
+    state = wl.n_max * wl.Hv * 128 * 128 * 4
+    assert lay["seg_phi"] - lay["seg_z"] == 3 * state, "automatic segments should pick four here"
+    o, hT = _forward(wl, 0)
+    o_ref, s_ref = oracle_full(wl)
+    eo, es = full_errors(wl, o, hT, o_ref, s_ref)
+    log(f"  every lane: o err {eo:.3e}  S err {es:.3e}")
+    assert eo <= O_TOL and es <= S_TOL

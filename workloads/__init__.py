@@ -29,6 +29,9 @@ for the chunked prefill; 5 and 6 for the token-serial decode / verify kernel):
   5 verify         N=64 sequences x 8 tokens (a draft-verify width), H=16, Hv=32,
                    bf16, h0 ~ N(0, 0.02)
   6 decode         N=256 sequences x 1 token, H=16, Hv=32, bf16, h0 ~ N(0, 0.02)
+  7 long, 8 heads  N=1,  T=32768, H=Hv=8, bf16, g mean 2, h0 ~ N(0, 0.02): the
+                   long-context recipe with fewer heads, whose stage-2 walk
+                   fills a quarter of the device (the segmented walk's case)
 """
 
 from __future__ import annotations
@@ -153,6 +156,7 @@ NAMES = {
     4: "front-4x8192-H16-Hv32-dconv4",
     5: "verify-64x8-H16-Hv32-bf16-h0",
     6: "decode-256x1-H16-Hv32-bf16-h0",
+    7: "long-T32768-H8-Hv8-bf16-strong-decay-h0",
 }
 
 
@@ -178,4 +182,6 @@ def make(cfg: int, seed: Optional[int] = None) -> Workload:
         return make_custom([8] * 64, 16, 32, seed=s, h0_sigma=0.02, name=NAMES[5])
     if cfg == 6:
         return make_custom([1] * 256, 16, 32, seed=s, h0_sigma=0.02, name=NAMES[6])
+    if cfg == 7:
+        return make_custom([32768], 8, 8, seed=s, g_mu=2.0, h0_sigma=0.02, name=NAMES[7])
     raise ValueError(cfg)
