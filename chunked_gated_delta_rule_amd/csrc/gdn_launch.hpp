@@ -103,14 +103,12 @@ hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const voi
                             int32_t hv, float scale, float *o, float *hT, hipStream_t stream,
                             KernelEvents ev = {});
 
-// Scratch of the two-segment stage 2 (per (sequence, value head): the state
-// after segment A and segment B's zero-start end state, value-major
-// [dv][dk]; segment B's homogeneous end state, key-major [dk][dv]; and the
-// homogeneous output rows [t_max, hv, dv]).
 // Scratch of the segmented stage-2 walk (P = parts segments): sa, segment
-// 0's final state; z and phi, the P - 1 later segments' final zero-start and
-// homogeneous states, one array of state_elems floats each, consecutive; oh,
-// the homogeneous output rows of every later segment's tokens.
+// 0's final state; z and phi, the P - 1 later segments' final zero-start
+// states (value-major [dv][dk] per (sequence, value head)) and homogeneous
+// states (key-major [dk][dv]), one array of state_elems floats each,
+// consecutive; oh, the homogeneous output rows [t_max, hv, dv] of every later
+// segment's tokens.
 struct SegScratch {
   float *sa = nullptr, *z = nullptr, *phi = nullptr, *oh = nullptr;
   int64_t state_elems = 0;

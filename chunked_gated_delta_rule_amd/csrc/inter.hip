@@ -233,7 +233,7 @@ struct Walk {
   const float *init0;
   float *out[2];
   float *fin[2];
-  bool two;  // state 1 is carried (segment B of the two-segment walk)
+  bool two;  // state 1 is carried (a later segment of a segmented walk)
 };
 
 template <bool kF32In, int kDepth, int X, int kS, int kNV, bool kGq>
@@ -347,7 +347,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
-        if (st == 1 && !W.two) continue;  // segment A carries state 0 only
+        if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
         const int wj = kGq ? ct : 0;
         u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
         f16x8 s16[2];
@@ -398,7 +398,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
       for (int st = 0; st < kS; ++st)
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) {
-          if (st == 1 && !W.two) continue;  // segment A carries state 0 only
+          if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
           const int wj = kGq ? ct : 0;
           const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
           f32x4 v[2];
@@ -470,8 +470,8 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
   constexpr int kCtO = kGq ? kD : 16;        // o columns between tile ct and ct + 1
   // o rows stream past the caches in the one-tile, one-piece walk: at one
   // work-group per CU, o's dirty lines otherwise displace what the next
-  // kernels read (T = 4096: the following stage 1 ran 53 -> 44 us). Not in the
-  // two-segment walk (the fix-up reads o back) nor with two tiles (each store
+  // kernels read (T = 4096: the following stage 1 ran 53 -> 44 us). Not in a
+  // segmented walk (the fix-up reads o back) nor with two tiles (each store
   // covers half a 128-byte line, which then went out as partial writes).
   constexpr bool kStreamO = kS == 1 && kNV == 1;
   constexpr int kPairs = Y == 0 ? 2 : 4;     // P pairs of its tiles
@@ -538,7 +538,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
-        if (st == 1 && !W.two) continue;  // segment A carries state 0 only
+        if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
         const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
         f16x8 s16[4];
 #pragma unroll
@@ -569,7 +569,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
-        if (st == 1 && !W.two) continue;  // segment A carries state 0 only
+        if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
         const int wj = kGq ? ct : 0;
         f32x4 pa[2] = {zero4(), zero4()};
 #pragma unroll

@@ -98,7 +98,7 @@ typedef struct {
                           0 = automatic: 1 when the one-tile grid fits the device, 4
                           when it is more than 2x the device and t_max >= n_max *
                           GDN_FOUR_TILE_MIN_TOKENS (long sequences), else 2. The
-                          two-segment walk always uses 1. */
+                          segmented walk always uses 1. */
   int32_t gqa_share;   /* GQA-shared stage 2 ("Optimizing GDN Chunk Prefill on
                           Intel AMX CPU", sections 3 and 5: the inter stage run
                           over key heads, reusing the key head's operands across
