@@ -858,7 +858,7 @@ __device__ __forceinline__ void fix_block(const float *A, const float *Bt, uint3
 
 // Row blocks of 128 outputs of segments 1 .. P - 1 (nbo per segment), and
 // with two parts also the final state S_1 (one more block per pair).
-__global__ __launch_bounds__(kFixThreads, 2) void segfix_kernel(const int32_t *__restrict__ cu,
+__global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__restrict__ cu,
                                                              float *__restrict__ o,
                                                              float *__restrict__ hT, SegScratch seg,
                                                              int n_max, int Hv, int t_max, int nbo) {
@@ -872,28 +872,41 @@ __global__ __launch_bounds__(kFixThreads, 2) void segfix_kernel(const int32_t *_
   const int s = pair / Hv, hv = pair % Hv;
   if (s >= n_max) return;
   const int64_t st = ((int64_t)s * Hv + hv) * kD * kD;
+  // one block, so that its code is inlined once
+  const float *A, *Bt, *base;
+  float *dst;
+  uint32_t bt_row, base_row;
+  int rows;
   if (parts == 2 && r == nbo) {  // S_1 = Z_1 + Phi_1 S_0, the final state
     if (hT == nullptr) return;
-    fix_block(seg.phi + st, seg.sa + st, kD * 4, seg.z + st, hT + st, kD * 4, kD, ahi, alo);
-    return;
+    A = seg.phi + st;
+    Bt = seg.sa + st;
+    base = seg.z + st;
+    dst = hT + st;
+    bt_row = base_row = kD * 4;
+    rows = kD;
+  } else {
+    if (nbo == 0) return;
+    const int bos = cu_at(cu, s, t_max), eos = cu_end(cu, s, bos, t_max);
+    const int nc = (eos - bos + kC - 1) / kC;
+    const int k = 1 + r / nbo, blk = r % nbo;  // segment, 128-row block of it
+    const int t_begin = bos + kC * (seg_begin(nc, parts, k) + 2 * blk);
+    const int t_end = min(eos, bos + kC * seg_begin(nc, parts, k + 1));
+    if (t_begin >= t_end) return;
+    A = k == 1 ? seg.sa + st : seg.z + (k - 2) * seg.state_elems + st;  // S_{k-1}
+    const int64_t row0 = ((int64_t)t_begin * Hv + hv) * kD;
+    Bt = seg.oh + row0;
+    base = o + row0;
+    dst = o + row0;
+    bt_row = base_row = static_cast<uint32_t>(Hv) * kD * 4;
+    rows = min(2 * kC, t_end - t_begin);
   }
-  if (nbo == 0) return;
-  const int bos = cu_at(cu, s, t_max), eos = cu_end(cu, s, bos, t_max);
-  const int nc = (eos - bos + kC - 1) / kC;
-  const int k = 1 + r / nbo, blk = r % nbo;  // segment, 128-row block of it
-  const int t_begin = bos + kC * (seg_begin(nc, parts, k) + 2 * blk);
-  const int t_end = min(eos, bos + kC * seg_begin(nc, parts, k + 1));
-  if (t_begin >= t_end) return;
-  const float *A = k == 1 ? seg.sa + st : seg.z + (k - 2) * seg.state_elems + st;  // S_{k-1}
-  const int64_t row0 = ((int64_t)t_begin * Hv + hv) * kD;
-  const uint32_t row_bytes = static_cast<uint32_t>(Hv) * kD * 4;
-  fix_block(A, seg.oh + row0, row_bytes, o + row0, o + row0, row_bytes, min(2 * kC, t_end - t_begin),
-            ahi, alo);
+  fix_block(A, Bt, bt_row, base, dst, base_row, rows, ahi, alo);
 }
 
 // State k of a walk in more than two parts: S_k = Z_k + Phi_k S_{k-1}, over
 // Z_k in place, or into hT for the last (not written when hT is null).
-__global__ __launch_bounds__(kFixThreads, 2) void segstate_kernel(float *__restrict__ hT,
+__global__ __launch_bounds__(kFixThreads) void segstate_kernel(float *__restrict__ hT,
                                                                SegScratch seg, int n_max, int Hv,
                                                                int k) {
   __shared__ __attribute__((aligned(16))) __bf16 ahi[kD * kLdFix];
