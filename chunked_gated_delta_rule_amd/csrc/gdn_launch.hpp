@@ -103,6 +103,16 @@ hipError_t launch_recurrent(bool f32_in, const void *q, const void *k, const voi
                             int32_t hv, float scale, float *o, float *hT, hipStream_t stream,
                             KernelEvents ev = {});
 
+// Bytes of the stage-1 intermediates stage 2 reads, nt chunk slots (K^T as
+// hi + lo when split_k). Above kLlcResident (the last-level cache is 256 MB
+// and also holds the inputs and o) they come back from HBM.
+inline int64_t stage2_operand_bytes(int64_t nt, int64_t h, int64_t hv, bool split_k) {
+  const int64_t per_chunk = hv * (16 * 1024 + 128 * 64 * 3 + kPBytes + 192 * 4) +
+                            h * ((split_k ? 32 : 16) * 1024 + 16 * 1024);
+  return nt * per_chunk;
+}
+constexpr int64_t kLlcResident = 160ll << 20;
+
 // Scratch of the segmented stage-2 walk (P = parts segments): sa, segment
 // 0's final state; z and phi, the P - 1 later segments' final zero-start
 // states (value-major [dv][dk] per (sequence, value head)) and homogeneous

@@ -947,12 +947,8 @@ hipError_t launch_walk(const StageBuffers &in, const float *h0, const int32_t *c
   dim3 grid;
   if (!flat_grid((kS == 2 ? seg.parts : 1) * rounds * kXcds * members, kThr, grid))
     return hipErrorInvalidValue;
-  // warm the value heads' lines too when the intermediates exceed about 160
-  // MiB (the last-level cache is 256 MB and also holds the inputs and o)
-  const int64_t per_chunk = static_cast<int64_t>(hv) * (16 * 1024 + kD * kC * 3 + kPBytes +
-                                                        kGateStride * 4) +
-                            static_cast<int64_t>(h) * ((kF32In ? 32 : 16) * 1024 + 16 * 1024);
-  const bool warm_values = static_cast<int64_t>(nt) * per_chunk > (160ll << 20);
+  // warm the value heads' lines too when the intermediates come from HBM
+  const bool warm_values = stage2_operand_bytes(nt, h, hv, kF32In) > kLlcResident;
   hipExtLaunchKernelGGL((inter_kernel<kF32In, kDepth, kS, kNV, kGq>), grid, dim3(kThr), 0, stream,
                         start, stop, 0, in, h0, cu, o, hT, n_max, h, hv, t_max, nt, seg,
                         warm_values);

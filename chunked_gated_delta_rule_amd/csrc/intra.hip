@@ -63,6 +63,9 @@ static_assert(kFusedIndexMaxSeqs == GDN_FUSED_INDEX_MAX_SEQS, "fused index bound
 
 namespace {
 
+// stage-1 work-group orders (see intra_kernel)
+constexpr int kSlotFastest = 0, kHeadFastest = 1, kHeadFastestReversed = 2;
+
 constexpr int kLdRow = kD + 8;   // bf16 row-major tile [64][136]
 constexpr int kLdAT = kC + 4;    // fp32 A, then T in place [64][68]
 constexpr int kLdX = 16 + 4;     // fp32 per-wave 16x16 scratch
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ table, int32_t *__restrict__ table_out, int n_max,
     StageBuffers out, int H, int Hv, int t_max, int nt, float scale, ConvIn ci,
-    bool head_fastest) {
+    int order) {
   constexpr bool kConv = kTaps > 0;
   static_assert(!kConv || kF32In || kHalf, "the fused front produces fp32 or fp16 q, k, v");
   static_assert(!(kF32In && kHalf), "one input kind");
@@ -378,22 +381,26 @@ __global__ __launch_bounds__(kThreads, kF32In ? 1 : 2) void intra_kernel(
   const int wv = tid >> 6;
   float *gsh = reinterpret_cast<float *>(smem + Smem::kOffGates) + wv * 2 * 64;  // this wave's gates
   float *bsh = gsh + 64;
-  // work-group -> (item = table slot, key head). With several sequences the
-  // numbering is key head fastest, so the dispatch reaches the sentinel slots
-  // past the batch's last chunk only at the end (a varlen batch of 32
-  // sequences has more sentinel slots than chunks); with one sequence, which
-  // has no such slots, it is slot fastest, which keeps the work-groups in
-  // flight spread over the whole sequence.
+  // work-group -> (item = table slot, key head), in one of three orders:
+  //   kSlotFastest: one sequence whose stage-2 operands stay in the
+  //     last-level cache; keeps the work-groups in flight spread over the
+  //     whole sequence;
+  //   kHeadFastest: batches; the dispatch reaches the sentinel slots past the
+  //     batch's last chunk only at the end (a varlen batch of 32 sequences has
+  //     more sentinel slots than chunks);
+  //   kHeadFastestReversed: one sequence whose stage-2 operands outgrow the
+  //     last-level cache; the last chunks come first, so the intermediates
+  //     stage 2 reads first are the last written and still in that cache.
   // a one-dimensional grid of nt * H work-groups (for batches it measured
   // faster than a two-dimensional (H, nt) grid in the same order)
   const int wg = flat_block();
   if (wg >= nt * H) return;  // past the grid's count (last row)
   int item, h;
-  if (!head_fastest) {
+  if (order == kSlotFastest) {
     item = wg % nt;
     h = wg / nt;
   } else {
-    item = wg / H;
+    item = order == kHeadFastest ? wg / H : nt - 1 - wg / H;
     h = wg % H;
   }
   // this work-group's chunk: from the caller's table, or located from
@@ -859,15 +866,17 @@ hipError_t launch_intra(InKind in_kind, const void *q, const void *k, const void
   if (conv.qkv && (in_kind == InKind::kBf16 || !conv.conv_w || conv.d_conv < 1 || conv.d_conv > 4))
     return hipErrorInvalidValue;
   if (nt_max <= 0) return hipSuccess;
-  // work-group order (see the kernel): slot fastest for one sequence, key head
-  // fastest for batches
-  const bool head_fastest = n_max > 1;
+  // work-group order (see the kernel)
+  const int order = n_max > 1 ? kHeadFastest
+                    : stage2_operand_bytes(nt_max, h, hv, in_kind != InKind::kBf16) > kLlcResident
+                        ? kHeadFastestReversed
+                        : kSlotFastest;
   dim3 grid;
   if (!flat_grid(static_cast<int64_t>(nt_max) * h, kThreads, grid)) return hipErrorInvalidValue;
 #define GDN_LAUNCH_INTRA(F32, TAPS, HALF)                                                       \
   hipExtLaunchKernelGGL((intra_kernel<F32, TAPS, HALF>), grid, dim3(kThreads), 0, stream,       \
                         ev.start, ev.stop, 0, q, k, v, g, beta, cu_seqlens, table, table_out,   \
-                        n_max, out, h, hv, t_max, nt_max, scale, conv, head_fastest)
+                        n_max, out, h, hv, t_max, nt_max, scale, conv, order)
   if (conv.qkv && in_kind == InKind::kF16) {
     switch (conv.d_conv) {
       case 1: GDN_LAUNCH_INTRA(false, 1, true); break;
