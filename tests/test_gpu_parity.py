@@ -494,10 +494,13 @@ def test_forward_without_table_builds_it_in_the_workspace(n):
     assert eo <= O_TOL and es <= S_TOL
 
 
-@pytest.mark.parametrize("entry,segments", [("chunk", 1), ("chunk", 2), ("recurrent", 0)])
+@pytest.mark.parametrize("entry,segments", [("chunk", 1), ("chunk", 2), ("chunk", 4),
+                                            ("noalloc", 2), ("recurrent", 0)])
 def test_graph_capture_replay_with_varying_cu_seqlens(entry, segments):
-    """gdn_chunk_fwd (one-piece and two-segment stage 2) or gdn_recurrent_fwd
-    captured once into a HIP graph at static sizes (t_max, n_max) and static
+    """gdn_chunk_fwd (one-piece stage 2, two segments, four segments with their
+    chained-state launches), gdn_chunk_fwd_noalloc (the entry point for
+    callers that cannot allocate, its workspace the library's own) or
+    gdn_recurrent_fwd captured once into a HIP graph at static sizes (t_max, n_max) and static
     addresses, then replayed with different cu_seqlens contents written into
     the same buffer (FLA issue 1155, "Core design": static grids, the
     device-built table, a sentinel for unused slots). Every replay is checked
@@ -517,6 +520,9 @@ def test_graph_capture_replay_with_varying_cu_seqlens(entry, segments):
     def call(o_, h_, ws_):
         if entry == "recurrent":
             gdn.gdn_recurrent_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, o_, h_)
+        elif entry == "noalloc":
+            gdn.gdn_chunk_fwd_noalloc(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None,
+                                      o_, h_)
         else:
             gdn.gdn_chunk_fwd(cfg, d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, None, o_, h_,
                               ws_)
