@@ -89,21 +89,23 @@ constexpr int kL2Lead = 2;       // chunks between the L2 warm-up and the operan
 // four tiles (kNV = 4) run one per CU with four waves of up to 512 registers.
 template <bool kF32In, int kDepth, int kS, int kNV>
 constexpr bool kWarmWave = kNV == 1 && !(kF32In && kDepth == 2) && (kS == 1 || kDepth == 1);
-constexpr int kDepthSeg = 1;  // prefetch depth of the two-state walk (keeps the warm-up wave)
+constexpr int kDepthSeg = 1;  // prefetch depth of the two-state walk (keeps the warm-up wave;
+                              // depth 2 measured the same)
 
 // Segments of a sequence of nc chunks walked in P parts at once. Segment 0
 // (from h0, one state) takes the first nc - (P - 1) y chunks; each later
-// segment carries two states (twice the products per chunk) and takes
-// y = floor(2 nc / (2 P + 1)) chunks, so segment 0 gets about 1.5 times as
-// many (T = 32768, two parts: the later segment taking 1/2, 2/5, 3/8 and 1/3
-// of the chunks gave stage 2 503, 488, 495 and 509 us).
-__host__ __device__ constexpr int seg_len(int nc, int parts) { return nc * 2 / (2 * parts + 1); }
+// segment carries two states (a chunk step about 1.25 times as long, and
+// rows for the fix-up) and takes y = floor(4 nc / (4 P + 1)) chunks, so
+// segment 0 gets about 1.25 times as many (T = 32768, H = Hv = 16, two
+// parts: ratios 1, 1.25 and 1.5 gave stage 2 484, 438 and 444 us).
+__host__ __device__ constexpr int seg_len(int nc, int parts) { return nc * 4 / (4 * parts + 1); }
 // first chunk of segment r (r = parts: the end of the sequence)
 __host__ __device__ constexpr int seg_begin(int nc, int parts, int r) {
   return r == 0 ? 0 : nc - (parts - r) * seg_len(nc, parts);
 }
+// The two-state walk carries each state on its own pair of chain waves.
 template <bool kF32In, int kDepth, int kS, int kNV>
-constexpr int kInterThreads = kWarmWave<kF32In, kDepth, kS, kNV> ? 320 : 256;
+constexpr int kInterThreads = 64 * (2 * kS + 2 + (kWarmWave<kF32In, kDepth, kS, kNV> ? 1 : 0));
 // waves per SIMD the register allocation must leave room for
 template <int kNV>
 constexpr int kInterWavesPerSimd = kNV == 2 ? 2 : 1;
@@ -236,11 +238,28 @@ struct Walk {
   bool two;  // state 1 is carried (a later segment of a segmented walk)
 };
 
+// LDS copies the zero-start state's chain waves leave for the identity-start
+// state's in a two-state walk: w and K^T fragments of two chunks (by chunk
+// parity) and e^{gamma_last} of three (chunk modulo 3, like the gate factors).
+template <bool kF32In>
+struct HomShare {
+  u32x4 (*w)[16][64];
+  u32x4 (*k)[kF32In ? 32 : 16][64];
+  float *el;
+};
+
+// Chain wave X of the zero-start state (the one that takes u). In a two-state
+// walk (kS = 2) it also leaves each chunk's w and K^T fragments, gate factors
+// and e^{gamma_last} in LDS for the identity-start state's chain waves, which
+// run a chunk behind, and takes one step more than the chunks.
 template <bool kF32In, int kDepth, int X, int kS, int kNV, bool kGq>
 __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const StageBuffers &in,
                                            u32x4 (*xch)[kXchFrags * kS * kNV][64],
-                                           float (*decx)[kGq ? kNV : 1][64]) {
+                                           float (*decx)[kGq ? kNV : 1][64],
+                                           const HomShare<kF32In> &sh) {
   static_assert(kS == 1 || kNV == 1, "the two-state walk covers one column tile");
+  constexpr int kSt0 = 0, kSn = 1;  // carries state 0
+  constexpr bool kU = true;
   constexpr int kNKw = kF32In ? 16 : 8;  // K^T fragments this wave uses per chunk
   constexpr int kNW = kGq ? kNV : 1;     // value heads whose w, u and gates are loaded
   // distance between tile ct's rows of a state (the next value head, or the
@@ -258,7 +277,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
       const int64_t hvj = L.hv + j;
       r.w[j] = make_rsrc(in.w16 + (hvj * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
       r.u[j] = make_rsrc(in.uimg + ((hvj * L.nt + slot) * kSlices + slice) * 4 * 64 * 3,
-                         ok && X == 0 ? 3072 * (kNV / kNW) : 0);
+                         ok && X == 0 && kU ? 3072 * (kNV / kNW) : 0);
       r.g[j] = make_rsrc(in.gimg + (hvj * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     }
     r.k = make_rsrc(in.kimg + ((int64_t)L.h * L.nt + slot) * (kF32In ? 32 : 16) * 512,
@@ -291,7 +310,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   };
   auto load_u = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
-    if constexpr (X == 0) {
+    if constexpr (X == 0 && kU) {
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
@@ -316,20 +335,17 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   };
 
   // state rows: S[st][ct][tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + 16 ct + c]
-  f32x4 S[kS][kNV][4];
+  // S[n] is state kSt0 + n
+  f32x4 S[kSn][kNV][4];
   const int64_t sbase = (((int64_t)L.s * L.Hv + L.hv) * kD + L.v0 + L.c16) * kD + 64 * X + L.g4;
+  if constexpr (kU) {
 #pragma unroll
-  for (int ct = 0; ct < kNV; ++ct)
+    for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl)
-      S[0][ct][tl] = W.init0 ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + ct * kCtState + 16 * tl)
-                             : zero4();
-  if constexpr (kS == 2) {
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[1][0][tl][i] = 64 * X + 16 * tl + L.g4 + i == L.v0 + L.c16 ? 1.f : 0.f;
+      for (int tl = 0; tl < 4; ++tl)
+        S[0][ct][tl] = W.init0
+                           ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + ct * kCtState + 16 * tl)
+                           : zero4();
   }
 
   // One chunk step on set B, which is refilled with chunk c + kDepth. A step
@@ -342,36 +358,47 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
 #pragma unroll
     for (int j = 0; j < kNW; ++j) e_last[j] = c < W.c1 ? el[B][j] : 1.f;
     u32x4 *xb = &xch[c & 1][0][L.lane];
-    f32x4 pv[kS][kNV][4];
+    const int ds = kS == 2 ? c % 3 : c & 1;  // gate-factor buffer of chunk c
+    f32x4 pv[kSn][kNV][4];
 #pragma unroll
-    for (int st = 0; st < kS; ++st)
+    for (int n = 0; n < kSn; ++n)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
+        const int st = kSt0 + n;
         if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
         const int wj = kGq ? ct : 0;
         u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
         f16x8 s16[2];
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) {
-          s16[pl] = to_f16x8(S[st][ct][2 * pl], S[st][ct][2 * pl + 1]);
+          s16[pl] = to_f16x8(S[n][ct][2 * pl], S[n][ct][2 * pl + 1]);
           xs[64 * (2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
         }
         // partial v' over this wave's key rows (wave 0 starts state 0 from u)
 #pragma unroll
         for (int R = 0; R < 4; ++R)
-          pv[st][ct][R] = X == 0 && st == 0 ? unpack_f24x4(u[B][ct][R]) : zero4();
+          pv[n][ct][R] = X == 0 && st == 0 ? unpack_f24x4(u[B][ct][R]) : zero4();
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-          for (int R = 0; R < 4; ++R) pv[st][ct][R] = mfma(w[B][wj][2 * R + pl], s16[pl], pv[st][ct][R]);
+          for (int R = 0; R < 4; ++R) pv[n][ct][R] = mfma(w[B][wj][2 * R + pl], s16[pl], pv[n][ct][R]);
 #pragma unroll
-        for (int R = 0; R < 4; ++R) xs[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[st][ct][R]);
+        for (int R = 0; R < 4; ++R) xs[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[n][ct][R]);
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl) S[st][ct][tl] = S[st][ct][tl] * e_last[wj];
+        for (int tl = 0; tl < 4; ++tl) S[n][ct][tl] = S[n][ct][tl] * e_last[wj];
       }
-    if constexpr (X == 0) {
+    if constexpr (X == 0 && kU) {
 #pragma unroll
-      for (int j = 0; j < kNW; ++j) decx[c & 1][j][L.lane] = dec[B][j];  // token L.lane's factor
+      for (int j = 0; j < kNW; ++j) decx[ds][j][L.lane] = dec[B][j];  // token L.lane's factor
+      if constexpr (kS == 2) {
+        if (L.lane == 0) sh.el[ds] = el[B][0];
+      }
+    }
+    if constexpr (kS == 2) {
+      if (W.two) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sh.w[c & 1][8 * X + i][L.lane] = __builtin_bit_cast(u32x4, w[B][0][i]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_w(Bc, rn);
@@ -388,16 +415,17 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     for (int j = 0; j < kNW; ++j)
 #pragma unroll
       for (int R = 0; R < 4; ++R)
-        dr[j][R] = *reinterpret_cast<const f32x4 *>(&decx[c & 1][j][16 * R + L.g4]);
+        dr[j][R] = *reinterpret_cast<const f32x4 *>(&decx[ds][j][16 * R + L.g4]);
     // per token block q: form dec v' of its two token tiles, then apply them
     // (the per-accumulator order of the products is q = 0 then q = 1)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      bf16x8 eh[kS][kNV], elo[kS][kNV];
+      bf16x8 eh[kSn][kNV], elo[kSn][kNV];
 #pragma unroll
-      for (int st = 0; st < kS; ++st)
+      for (int n = 0; n < kSn; ++n)
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) {
+          const int st = kSt0 + n;
           if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
           const int wj = kGq ? ct : 0;
           const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
@@ -407,27 +435,33 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
             const int R = 2 * q + h2;
             const f32x4 other = __builtin_bit_cast(f32x4, xs[64 * (4 + 4 * (1 - X) + R)]);
             // both waves: partial0 + partial1
-            v[h2] = X == 0 ? pv[st][ct][R] + other : other + pv[st][ct][R];
+            v[h2] = X == 0 ? pv[n][ct][R] + other : other + pv[n][ct][R];
           }
-          split8(v[0] * dr[wj][2 * q], v[1] * dr[wj][2 * q + 1], eh[st][ct], elo[st][ct]);
+          split8(v[0] * dr[wj][2 * q], v[1] * dr[wj][2 * q + 1], eh[n][ct], elo[n][ct]);
         }
 #pragma unroll
-      for (int st = 0; st < kS; ++st)
+      for (int n = 0; n < kSn; ++n)
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) {
-          if (st == 1 && !W.two) continue;
+          if (kSt0 + n == 1 && !W.two) continue;
 #pragma unroll
           for (int tl = 0; tl < 4; ++tl)
-            S[st][ct][tl] = mfma(k[B][2 * tl + q], eh[st][ct], S[st][ct][tl]);
+            S[n][ct][tl] = mfma(k[B][2 * tl + q], eh[n][ct], S[n][ct][tl]);
 #pragma unroll
           for (int tl = 0; tl < 4; ++tl)
-            S[st][ct][tl] = mfma(k[B][2 * tl + q], elo[st][ct], S[st][ct][tl]);
+            S[n][ct][tl] = mfma(k[B][2 * tl + q], elo[n][ct], S[n][ct][tl]);
           if constexpr (kF32In) {
 #pragma unroll
             for (int tl = 0; tl < 4; ++tl)
-              S[st][ct][tl] = mfma(k[B][8 + 2 * tl + q], eh[st][ct], S[st][ct][tl]);
+              S[n][ct][tl] = mfma(k[B][8 + 2 * tl + q], eh[n][ct], S[n][ct][tl]);
           }
         }
+    }
+    if constexpr (kS == 2) {
+      if (W.two) {
+#pragma unroll
+        for (int i = 0; i < kNKw; ++i) sh.k[c & 1][kNKw * X + i][L.lane] = __builtin_bit_cast(u32x4, k[B][i]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_k(Bc, rn);
@@ -437,31 +471,125 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
     load_all(Bc, rsrc_of(W.c0 + decltype(Bc)::value));
   });
-  for (int c = W.c0; c < W.c1; c += kDepth)  // a step past the last chunk changes nothing
-    for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
-      step(c + decltype(Bc)::value, Bc);
-    });
-  if (W.fin[0]) {
-#pragma unroll
-    for (int ct = 0; ct < kNV; ++ct)
-#pragma unroll
-      for (int tl = 0; tl < 4; ++tl)
-        *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + ct * kCtState + 16 * tl) = S[0][ct][tl];
-  }
   if constexpr (kS == 2) {
-    if (W.fin[1]) {
-      // key-major: row d = 64 X + 16 tl + 4 g + i, column v0 + c
-      float *f = W.fin[1] + ((int64_t)L.s * L.Hv + L.hv) * kD * kD + L.v0 + L.c16;
+    // one step past the last chunk (it changes nothing here) closes the
+    // lagging chain's last chunk
+    const int c_end = W.c1 + (W.two ? 1 : 0);
+    for (int c = W.c0; c < c_end; c += kDepth)
+      for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+        step(c + decltype(Bc)::value, Bc);
+      });
+  } else {
+    for (int c = W.c0; c < W.c1; c += kDepth)  // a step past the last chunk changes nothing
+      for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+        step(c + decltype(Bc)::value, Bc);
+      });
+  }
+  if constexpr (kU) {
+    if (W.fin[0]) {
 #pragma unroll
-      for (int tl = 0; tl < 4; ++tl)
+      for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[(64 * X + 16 * tl + L.g4 + i) * kD] = S[1][0][tl][i];
+        for (int tl = 0; tl < 4; ++tl)
+          *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + ct * kCtState + 16 * tl) = S[0][ct][tl];
     }
   }
 }
 
+// Chain wave X of the identity-start (homogeneous) state of a later segment.
+// It runs one chunk behind the zero-start state's chain waves and takes w,
+// K^T, the gate factors and e^{gamma_last} of each chunk from the LDS copies
+// they leave, so the work-group loads every operand once. Per step c it forms
+// chunk c - 1's partial (-w) Phi over its key rows before the step's barrier
+// and applies chunk c - 1's update after it; the exchange is that of the
+// one-state chain (its own double-buffered block).
+template <bool kF32In, int X>
+__device__ __forceinline__ void hom_chain_wave(const Lane &L, const Walk &W,
+                                               u32x4 (*xch)[kXchFrags * 2][64],
+                                               float (*decx)[1][64], const HomShare<kF32In> &sh) {
+  constexpr int kNKw = kF32In ? 16 : 8;
+  if (!W.two) {  // segment 0 carries no homogeneous state: keep the barrier count
+    for (int c = W.c0; c < W.c1; ++c) lds_barrier();
+    return;
+  }
+  // rows d = 64 X + 16 tl + 4 g + i of the identity's columns v0 + c
+  f32x4 S[4];
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[tl][i] = 64 * X + 16 * tl + L.g4 + i == L.v0 + L.c16 ? 1.f : 0.f;
+  for (int c = W.c0; c <= W.c1; ++c) {
+    const int p = c - 1;  // the chunk of this step
+    const bool live = p >= W.c0;
+    u32x4 *xs = &xch[p & 1][kXchFrags][L.lane];
+    f32x4 pv[4];
+    if (live) {
+      f16x8 s16[2];
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        s16[pl] = to_f16x8(S[2 * pl], S[2 * pl + 1]);
+        xs[64 * (2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
+      }
+      const u32x4 *wf = &sh.w[p & 1][8 * X][L.lane];
+#pragma unroll
+      for (int R = 0; R < 4; ++R) pv[R] = zero4();
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+          pv[R] = mfma(__builtin_bit_cast(f16x8, wf[64 * (2 * R + pl)]), s16[pl], pv[R]);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) xs[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[R]);
+      const float e_last = sh.el[p % 3];
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) S[tl] = S[tl] * e_last;
+    }
+    lds_barrier();  // chunk p's Phi rows (fp16) and partials are published
+    if (live) {
+      f32x4 dr[4];
+#pragma unroll
+      for (int R = 0; R < 4; ++R) dr[R] = *reinterpret_cast<const f32x4 *>(&decx[p % 3][0][16 * R + L.g4]);
+      const u32x4 *kf = &sh.k[p & 1][kNKw * X][L.lane];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        f32x4 v[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int R = 2 * q + h2;
+          const f32x4 other = __builtin_bit_cast(f32x4, xs[64 * (4 + 4 * (1 - X) + R)]);
+          v[h2] = X == 0 ? pv[R] + other : other + pv[R];
+        }
+        bf16x8 eh, elo;
+        split8(v[0] * dr[2 * q], v[1] * dr[2 * q + 1], eh, elo);
+#pragma unroll
+        for (int tl = 0; tl < 4; ++tl)
+          S[tl] = mfma(__builtin_bit_cast(bf16x8, kf[64 * (2 * tl + q)]), eh, S[tl]);
+#pragma unroll
+        for (int tl = 0; tl < 4; ++tl)
+          S[tl] = mfma(__builtin_bit_cast(bf16x8, kf[64 * (2 * tl + q)]), elo, S[tl]);
+        if constexpr (kF32In) {
+#pragma unroll
+          for (int tl = 0; tl < 4; ++tl)
+            S[tl] = mfma(__builtin_bit_cast(bf16x8, kf[64 * (8 + 2 * tl + q)]), eh, S[tl]);
+        }
+      }
+    }
+  }
+  if (W.fin[1]) {
+    // key-major: row d = 64 X + 16 tl + 4 g + i, column v0 + c
+    float *f = W.fin[1] + ((int64_t)L.s * L.Hv + L.hv) * kD * kD + L.v0 + L.c16;
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[(64 * X + 16 * tl + L.g4 + i) * kD] = S[tl][i];
+  }
+}
+
 // Helper wave Y: output token tiles R = 2 Y, 2 Y + 1 (rows 32 Y .. 32 Y + 31)
-// of every carried state.
+// of every carried state. In a two-state walk step c writes chunk c of the
+// zero-start state and chunk c - 1 of the identity-start one (its chain runs a
+// chunk behind), with that chunk's q16, P and gate fragments kept from the
+// step before.
 template <int kDepth, int Y, int kS, int kNV, bool kGq>
 __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const StageBuffers &in,
                                             u32x4 (*xch)[kXchFrags * kS * kNV][64]) {
@@ -497,6 +625,8 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
   f16x8 qf[kDepth][8];            // q16 fragment (token tile 2 Y + Rl, key block p) at [4 Rl + p]
   f16x8 pf[kDepth][kNW][kPairs];  // P pair kPair0 + n at [n]
   u32x2 exs[kDepth][kNW];         // scale * e^{gamma_r} (fp32 bits), r = 16 (2 Y + Rl) + c
+  f16x8 qpv[8], ppv[kPairs];      // two states: the previous chunk's q16 and P fragments
+  u32x2 epv;                      // and gate factors
   auto load_q = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
 #pragma unroll
@@ -531,7 +661,6 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
     constexpr int B = decltype(Bc)::value;
     const Rsrc rn = rsrc_of(c + kDepth);
     lds_barrier();  // chunk c handed over
-    const u32x4 *xb = &xch[c & 1][0][L.lane];
     f32x4 ya[kS][kNV][2];
     f16x8 dh[kS][kNV][kNQ], dl[kS][kNV][kNQ];
 #pragma unroll
@@ -539,7 +668,8 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
         if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
-        const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
+        const int cs = st == 0 ? c : c - 1;  // the chunk of state st written this step
+        const u32x4 *xs = &xch[cs & 1][0][L.lane] + 64 * kXchFrags * (kNV * st + ct);
         f16x8 s16[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) s16[p] = __builtin_bit_cast(f16x8, xs[64 * p]);
@@ -555,21 +685,35 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
         for (int p = 0; p < 4; ++p)
 #pragma unroll
           for (int Rl = 0; Rl < 2; ++Rl)
-            ya[st][ct][Rl] = mfma(s16[p], qf[B][4 * Rl + p], ya[st][ct][Rl]);
+            ya[st][ct][Rl] = mfma(s16[p], st == 0 ? qf[B][4 * Rl + p] : qpv[4 * Rl + p], ya[st][ct][Rl]);
 #pragma unroll
         for (int q = 0; q < kNQ; ++q) split8_f16(v[2 * q], v[2 * q + 1], dh[st][ct][q], dl[st][ct][q]);
       }
+    if constexpr (kS == 2) {
+      if (W.two) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qpv[i] = qf[B][i];
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_q(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
     // o^T = v'^T P^T + scale e^gamma y^T
-    const int t0 = L.bos + kC * c;
-    const uint32_t lc = c < W.c1 ? static_cast<uint32_t>(min(kC, L.eos - t0)) : 0u;  // past the end: no store
+    const int t0c = L.bos + kC * c;
+    const uint32_t lcc = c < W.c1 ? static_cast<uint32_t>(min(kC, L.eos - t0c)) : 0u;  // past the end: no store
 #pragma unroll
     for (int st = 0; st < kS; ++st)
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct) {
         if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
+        int t0 = t0c;
+        uint32_t lc = lcc;
+        if constexpr (kS == 2) {
+          if (st == 1) {  // chunk c - 1: no store before the segment's start
+            t0 = t0c - kC;
+            lc = c - 1 >= W.c0 && c - 1 < W.c1 ? static_cast<uint32_t>(min(kC, L.eos - t0)) : 0u;
+          }
+        }
         const int wj = kGq ? ct : 0;
         f32x4 pa[2] = {zero4(), zero4()};
 #pragma unroll
@@ -578,8 +722,9 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
 #pragma unroll
           for (int q = 0; q <= (R >> 1); ++q) {
             const int n = (R < 2 ? R : 2 * R - 2 + q) - kPair0;
-            pa[Rl] = mfma(dh[st][ct][q], pf[B][wj][n], pa[Rl]);
-            pa[Rl] = mfma(dl[st][ct][q], pf[B][wj][n], pa[Rl]);
+            const f16x8 pn = st == 0 ? pf[B][wj][n] : ppv[n];
+            pa[Rl] = mfma(dh[st][ct][q], pn, pa[Rl]);
+            pa[Rl] = mfma(dl[st][ct][q], pn, pa[Rl]);
           }
         }
         // a state without an output destination gets an empty store range
@@ -590,8 +735,15 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
 #pragma unroll
         for (int Rl = 0; Rl < 2; ++Rl)
           store16<kStreamO>(ro, vo_o, (2 * Y + Rl) * row_o,
-                            pa[Rl] + __uint_as_float(exs[B][wj][Rl]) * ya[st][ct][Rl]);
+                            pa[Rl] + __uint_as_float(st == 0 ? exs[B][wj][Rl] : epv[Rl]) * ya[st][ct][Rl]);
       }
+    if constexpr (kS == 2) {
+      if (W.two) {
+#pragma unroll
+        for (int i = 0; i < kPairs; ++i) ppv[i] = pf[B][0][i];
+        epv = exs[B][0];
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_p(Bc, rn);
     __builtin_amdgcn_sched_barrier(0);
@@ -600,10 +752,18 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
   for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
     load_all(Bc, rsrc_of(W.c0 + decltype(Bc)::value));
   });
-  for (int c = W.c0; c < W.c1; c += kDepth)  // a step past the last chunk changes nothing
-    for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
-      step(c + decltype(Bc)::value, Bc);
-    });
+  if constexpr (kS == 2) {
+    const int c_end = W.c1 + (W.two ? 1 : 0);  // the lagging state's last chunk
+    for (int c = W.c0; c < c_end; c += kDepth)
+      for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+        step(c + decltype(Bc)::value, Bc);
+      });
+  } else {
+    for (int c = W.c0; c < W.c1; c += kDepth)  // a step past the last chunk changes nothing
+      for_sets<kDepth>([&](auto Bc) __attribute__((always_inline)) {
+        step(c + decltype(Bc)::value, Bc);
+      });
+  }
 }
 
 // L2 warm-up wave. The work-groups of one key head (and of one value head)
@@ -619,7 +779,7 @@ __device__ __forceinline__ void helper_wave(const Lane &L, const Walk &W, const 
 // the key head's lines only, 54.7 us with both). The loads go to LDS
 // (LDS-DMA: no register is written) and are never read, so nothing waits on
 // them until the wave ends. Requests past the last chunk repeat its lines.
-template <bool kF32In, int kDepth>
+template <bool kF32In, int kDepth, bool kTwo>
 __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const StageBuffers &in,
                                              int member, int members, uint32_t *sink,
                                              bool warm_values) {
@@ -629,7 +789,12 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
   constexpr int kVLines = kWLines + kPLines + kGateStride * 4 / 128;  // w16, P, gates
   constexpr int kULines = 24;  // one slice of u: 4 tiles x 768 bytes
   static_assert(kGateStride * 4 % 128 == 0, "gate block is whole lines");
-  if (W.c1 <= W.c0) return;
+  if (W.c1 <= W.c0) {  // nothing to warm; the other waves' barriers still count this wave
+    if constexpr (kTwo) {
+      if (W.two) lds_barrier();  // the lagging chain's closing step
+    }
+    return;
+  }
   const int slice = L.v0 / 16;
   const int nh = (kHLines + members - 1) / members;
   const int nv = (kVLines + kSlices - 1) / kSlices;
@@ -671,6 +836,9 @@ __device__ __forceinline__ void l2_warm_wave(const Lane &L, const Walk &W, const
       issue(c + decltype(Bc)::value + kDepth + kL2Lead);
       lds_barrier();
     });
+  if constexpr (kTwo) {
+    if (W.two) lds_barrier();  // a two-state walk's extra step (nothing left to warm)
+  }
   // the LDS-DMA writes must land before the work-group's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -691,7 +859,13 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
   __shared__ __attribute__((aligned(16))) u32x4 xch[2][kXchFrags * kS * kNV][64];
   __shared__ uint32_t l2_sink[64];
   // per chunk (double-buffered) the gate factors e^{gamma_last - gamma} by token
-  __shared__ __attribute__((aligned(16))) float decx[2][kGq ? kNV : 1][64];
+  // (three buffers with two states: the lagging chain reads chunk c - 1's
+  // while chunk c + 1's are written)
+  __shared__ __attribute__((aligned(16))) float decx[kS == 2 ? 3 : 2][kGq ? kNV : 1][64];
+  // two states: the LDS copies for the identity-start state's chain
+  __shared__ __attribute__((aligned(16))) u32x4 hom_w[kS == 2 ? 2 : 1][16][64];
+  __shared__ __attribute__((aligned(16))) u32x4 hom_k[kS == 2 ? 2 : 1][kF32In ? 32 : 16][64];
+  __shared__ float hom_el[kS == 2 ? 3 : 1];
 
   // ---- XCD-aware work-group -> (sequence, value head, slice) --------------
   // kGq: the kNV tiles are one 16-column slice of kNV consecutive value heads
@@ -737,16 +911,36 @@ __global__ __launch_bounds__((kInterThreads<kF32In, kDepth, kS, kNV>),
                   : Walk{c0, c1, nullptr, {o, seg.oh}, {seg.z + at, seg.phi + at}, true};
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave == 0)
-    chain_wave<kF32In, kDepth, 0, kS, kNV, kGq>(L, W, in, xch, decx);
-  else if (wave == 1)
-    chain_wave<kF32In, kDepth, 1, kS, kNV, kGq>(L, W, in, xch, decx);
-  else if (wave == 2)
-    helper_wave<kDepth, 0, kS, kNV, kGq>(L, W, in, xch);
-  else if (wave == 3)
-    helper_wave<kDepth, 1, kS, kNV, kGq>(L, W, in, xch);
-  else if constexpr (kWarmWave<kF32In, kDepth, kS, kNV>)
-    l2_warm_wave<kF32In, kDepth>(L, W, in, member, members, l2_sink, warm_values);
+  const HomShare<kF32In> sh{hom_w, hom_k, hom_el};
+  if constexpr (kS == 2) {
+    // waves 0, 1: the identity-start state, a chunk behind; 2, 3: the
+    // zero-start state; 4, 5: both states' outputs; 6: L2 warm-up
+    if (wave == 0)
+      hom_chain_wave<kF32In, 0>(L, W, xch, decx, sh);
+    else if (wave == 1)
+      hom_chain_wave<kF32In, 1>(L, W, xch, decx, sh);
+    else if (wave == 2)
+      chain_wave<kF32In, kDepth, 0, kS, kNV, kGq>(L, W, in, xch, decx, sh);
+    else if (wave == 3)
+      chain_wave<kF32In, kDepth, 1, kS, kNV, kGq>(L, W, in, xch, decx, sh);
+    else if (wave == 4)
+      helper_wave<kDepth, 0, kS, kNV, kGq>(L, W, in, xch);
+    else if (wave == 5)
+      helper_wave<kDepth, 1, kS, kNV, kGq>(L, W, in, xch);
+    else if constexpr (kWarmWave<kF32In, kDepth, kS, kNV>)
+      l2_warm_wave<kF32In, kDepth, true>(L, W, in, member, members, l2_sink, warm_values);
+  } else {
+    if (wave == 0)
+      chain_wave<kF32In, kDepth, 0, kS, kNV, kGq>(L, W, in, xch, decx, sh);
+    else if (wave == 1)
+      chain_wave<kF32In, kDepth, 1, kS, kNV, kGq>(L, W, in, xch, decx, sh);
+    else if (wave == 2)
+      helper_wave<kDepth, 0, kS, kNV, kGq>(L, W, in, xch);
+    else if (wave == 3)
+      helper_wave<kDepth, 1, kS, kNV, kGq>(L, W, in, xch);
+    else if constexpr (kWarmWave<kF32In, kDepth, kS, kNV>)
+      l2_warm_wave<kF32In, kDepth, false>(L, W, in, member, members, l2_sink, warm_values);
+  }
 }
 
 // ---- segment fix-up ----------------------------------------------------------
@@ -1021,7 +1215,9 @@ bool inter_grids_fit(int32_t n_max, int32_t h, int32_t hv, int32_t t_max, int se
   const int64_t members = (hv / h / share) * (kSlices / (segments >= 2 ? 1 : tiles));
   const int64_t rounds = (static_cast<int64_t>(n_max) * h + kXcds - 1) / kXcds;
   dim3 grid;
-  if (!flat_grid((segments >= 2 ? segments : 1) * rounds * kXcds * members, 320, grid)) return false;
+  const int threads = segments >= 2 ? kInterThreads<false, kDepthSeg, 2, 1> : 320;
+  if (!flat_grid((segments >= 2 ? segments : 1) * rounds * kXcds * members, threads, grid))
+    return false;
   if (segments < 2) return true;
   return flat_grid(fix_grid(n_max, hv, t_max, segments), kFixThreads, grid) &&
          flat_grid(static_cast<int64_t>(n_max) * hv, kFixThreads, grid);

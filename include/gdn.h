@@ -84,7 +84,7 @@ typedef struct {
   float scale;         /* output scale; <= 0 selects 1 / sqrt(dk) */
   int32_t segments;    /* stage-2 walk of each sequence: 1 = one piece; P = 2, 3
                           or 4 = P segments at once (of a sequence of nc chunks,
-                          every later segment y = floor(2 nc / (2P + 1)) chunks,
+                          every later segment y = floor(4 nc / (4P + 1)) chunks,
                           walked from zero and from the identity; the first
                           segment the rest, from the initial state), then fix-ups
                           that chain the segments' states and correct their
