@@ -48,6 +48,13 @@
 // loads return zero. Between them the four waves load each operand once per
 // chunk.
 //
+// A segmented walk (a later segment of a long sequence, carrying the state
+// from zero and the homogeneous state from the identity) adds a second pair
+// of chain waves for the homogeneous state. It runs one chunk behind and
+// takes w, K^T and the gate factors from LDS copies the first pair leaves,
+// so the work-group still loads each operand once; the helper waves write
+// both states' outputs.
+//
 // Three launch shapes (the caller's choice, or automatic by grid size and
 // tokens per sequence). When the grid of one-tile work-groups fits the device
 // (one per CU), fragments are prefetched two chunks ahead and a fifth wave
