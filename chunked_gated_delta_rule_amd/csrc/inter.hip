@@ -265,8 +265,6 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
                                            float (*decx)[kGq ? kNV : 1][64],
                                            const HomShare<kF32In> &sh) {
   static_assert(kS == 1 || kNV == 1, "the two-state walk covers one column tile");
-  constexpr int kSt0 = 0, kSn = 1;  // carries state 0
-  constexpr bool kU = true;
   constexpr int kNKw = kF32In ? 16 : 8;  // K^T fragments this wave uses per chunk
   constexpr int kNW = kGq ? kNV : 1;     // value heads whose w, u and gates are loaded
   // distance between tile ct's rows of a state (the next value head, or the
@@ -284,7 +282,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
       const int64_t hvj = L.hv + j;
       r.w[j] = make_rsrc(in.w16 + (hvj * L.nt + slot) * 16 * 512, ok ? 16 * 1024 : 0);
       r.u[j] = make_rsrc(in.uimg + ((hvj * L.nt + slot) * kSlices + slice) * 4 * 64 * 3,
-                         ok && X == 0 && kU ? 3072 * (kNV / kNW) : 0);
+                         ok && X == 0 ? 3072 * (kNV / kNW) : 0);
       r.g[j] = make_rsrc(in.gimg + (hvj * L.nt + slot) * kGateStride, ok ? kGateStride * 4 : 0);
     }
     r.k = make_rsrc(in.kimg + ((int64_t)L.h * L.nt + slot) * (kF32In ? 32 : 16) * 512,
@@ -317,7 +315,7 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   };
   auto load_u = [&](auto Bc, const Rsrc &r) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
-    if constexpr (X == 0 && kU) {
+    if constexpr (X == 0) {
 #pragma unroll
       for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
@@ -342,18 +340,15 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
   };
 
   // state rows: S[st][ct][tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + 16 ct + c]
-  // S[n] is state kSt0 + n
-  f32x4 S[kSn][kNV][4];
+  // state rows: S[ct][tl] holds S[d = 64 X + 16 tl + 4 g + i][v0 + 16 ct + c]
+  f32x4 S[kNV][4];
   const int64_t sbase = (((int64_t)L.s * L.Hv + L.hv) * kD + L.v0 + L.c16) * kD + 64 * X + L.g4;
-  if constexpr (kU) {
 #pragma unroll
-    for (int ct = 0; ct < kNV; ++ct)
+  for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
-      for (int tl = 0; tl < 4; ++tl)
-        S[0][ct][tl] = W.init0
-                           ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + ct * kCtState + 16 * tl)
-                           : zero4();
-  }
+    for (int tl = 0; tl < 4; ++tl)
+      S[ct][tl] = W.init0 ? *reinterpret_cast<const f32x4 *>(W.init0 + sbase + ct * kCtState + 16 * tl)
+                          : zero4();
 
   // One chunk step on set B, which is refilled with chunk c + kDepth. A step
   // past the last chunk (c >= c1) runs on zero fragments with a decay of 1
@@ -366,35 +361,30 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     for (int j = 0; j < kNW; ++j) e_last[j] = c < W.c1 ? el[B][j] : 1.f;
     u32x4 *xb = &xch[c & 1][0][L.lane];
     const int ds = kS == 2 ? c % 3 : c & 1;  // gate-factor buffer of chunk c
-    f32x4 pv[kSn][kNV][4];
+    f32x4 pv[kNV][4];
 #pragma unroll
-    for (int n = 0; n < kSn; ++n)
+    for (int ct = 0; ct < kNV; ++ct) {
+      const int wj = kGq ? ct : 0;
+      u32x4 *xs = xb + 64 * kXchFrags * ct;
+      f16x8 s16[2];
 #pragma unroll
-      for (int ct = 0; ct < kNV; ++ct) {
-        const int st = kSt0 + n;
-        if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
-        const int wj = kGq ? ct : 0;
-        u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
-        f16x8 s16[2];
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl) {
-          s16[pl] = to_f16x8(S[n][ct][2 * pl], S[n][ct][2 * pl + 1]);
-          xs[64 * (2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
-        }
-        // partial v' over this wave's key rows (wave 0 starts state 0 from u)
-#pragma unroll
-        for (int R = 0; R < 4; ++R)
-          pv[n][ct][R] = X == 0 && st == 0 ? unpack_f24x4(u[B][ct][R]) : zero4();
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-          for (int R = 0; R < 4; ++R) pv[n][ct][R] = mfma(w[B][wj][2 * R + pl], s16[pl], pv[n][ct][R]);
-#pragma unroll
-        for (int R = 0; R < 4; ++R) xs[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[n][ct][R]);
-#pragma unroll
-        for (int tl = 0; tl < 4; ++tl) S[n][ct][tl] = S[n][ct][tl] * e_last[wj];
+      for (int pl = 0; pl < 2; ++pl) {
+        s16[pl] = to_f16x8(S[ct][2 * pl], S[ct][2 * pl + 1]);
+        xs[64 * (2 * X + pl)] = __builtin_bit_cast(u32x4, s16[pl]);
       }
-    if constexpr (X == 0 && kU) {
+      // partial v' over this wave's key rows (wave 0 starts from u)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) pv[ct][R] = X == 0 ? unpack_f24x4(u[B][ct][R]) : zero4();
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int R = 0; R < 4; ++R) pv[ct][R] = mfma(w[B][wj][2 * R + pl], s16[pl], pv[ct][R]);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) xs[64 * (4 + 4 * X + R)] = __builtin_bit_cast(u32x4, pv[ct][R]);
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) S[ct][tl] = S[ct][tl] * e_last[wj];
+    }
+    if constexpr (X == 0) {
 #pragma unroll
       for (int j = 0; j < kNW; ++j) decx[ds][j][L.lane] = dec[B][j];  // token L.lane's factor
       if constexpr (kS == 2) {
@@ -427,42 +417,32 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
     // (the per-accumulator order of the products is q = 0 then q = 1)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      bf16x8 eh[kSn][kNV], elo[kSn][kNV];
+      bf16x8 eh[kNV], elo[kNV];
 #pragma unroll
-      for (int n = 0; n < kSn; ++n)
+      for (int ct = 0; ct < kNV; ++ct) {
+        const int wj = kGq ? ct : 0;
+        const u32x4 *xs = xb + 64 * kXchFrags * ct;
+        f32x4 v[2];
 #pragma unroll
-        for (int ct = 0; ct < kNV; ++ct) {
-          const int st = kSt0 + n;
-          if (st == 1 && !W.two) continue;  // segment 0 carries state 0 only
-          const int wj = kGq ? ct : 0;
-          const u32x4 *xs = xb + 64 * kXchFrags * (kNV * st + ct);
-          f32x4 v[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int R = 2 * q + h2;
-            const f32x4 other = __builtin_bit_cast(f32x4, xs[64 * (4 + 4 * (1 - X) + R)]);
-            // both waves: partial0 + partial1
-            v[h2] = X == 0 ? pv[n][ct][R] + other : other + pv[n][ct][R];
-          }
-          split8(v[0] * dr[wj][2 * q], v[1] * dr[wj][2 * q + 1], eh[n][ct], elo[n][ct]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int R = 2 * q + h2;
+          const f32x4 other = __builtin_bit_cast(f32x4, xs[64 * (4 + 4 * (1 - X) + R)]);
+          // both waves: partial0 + partial1
+          v[h2] = X == 0 ? pv[ct][R] + other : other + pv[ct][R];
         }
+        split8(v[0] * dr[wj][2 * q], v[1] * dr[wj][2 * q + 1], eh[ct], elo[ct]);
+      }
 #pragma unroll
-      for (int n = 0; n < kSn; ++n)
+      for (int ct = 0; ct < kNV; ++ct) {
 #pragma unroll
-        for (int ct = 0; ct < kNV; ++ct) {
-          if (kSt0 + n == 1 && !W.two) continue;
+        for (int tl = 0; tl < 4; ++tl) S[ct][tl] = mfma(k[B][2 * tl + q], eh[ct], S[ct][tl]);
 #pragma unroll
-          for (int tl = 0; tl < 4; ++tl)
-            S[n][ct][tl] = mfma(k[B][2 * tl + q], eh[n][ct], S[n][ct][tl]);
+        for (int tl = 0; tl < 4; ++tl) S[ct][tl] = mfma(k[B][2 * tl + q], elo[ct], S[ct][tl]);
+        if constexpr (kF32In) {
 #pragma unroll
-          for (int tl = 0; tl < 4; ++tl)
-            S[n][ct][tl] = mfma(k[B][2 * tl + q], elo[n][ct], S[n][ct][tl]);
-          if constexpr (kF32In) {
-#pragma unroll
-            for (int tl = 0; tl < 4; ++tl)
-              S[n][ct][tl] = mfma(k[B][8 + 2 * tl + q], eh[n][ct], S[n][ct][tl]);
-          }
+          for (int tl = 0; tl < 4; ++tl) S[ct][tl] = mfma(k[B][8 + 2 * tl + q], eh[ct], S[ct][tl]);
         }
+      }
     }
     if constexpr (kS == 2) {
       if (W.two) {
@@ -492,14 +472,12 @@ __device__ __forceinline__ void chain_wave(const Lane &L, const Walk &W, const S
         step(c + decltype(Bc)::value, Bc);
       });
   }
-  if constexpr (kU) {
-    if (W.fin[0]) {
+  if (W.fin[0]) {
 #pragma unroll
-      for (int ct = 0; ct < kNV; ++ct)
+    for (int ct = 0; ct < kNV; ++ct)
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl)
-          *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + ct * kCtState + 16 * tl) = S[0][ct][tl];
-    }
+      for (int tl = 0; tl < 4; ++tl)
+        *reinterpret_cast<f32x4 *>(W.fin[0] + sbase + ct * kCtState + 16 * tl) = S[ct][tl];
   }
 }
 
