@@ -951,10 +951,16 @@ constexpr int kLdFix = kD + 8;
 // dst[n][16 mt + 4 g + i] = base[n][..] + C: rows n < rows of B^T (row
 // stride bt_row bytes) and of base / dst (base_row bytes); A is 128 x 128
 // value-major or key-major as above (row stride 128 floats).
+// With kBtLds, B^T is a 128 x 128 fp32 block in LDS (row stride kLdS) instead
+// of global memory; with kOutLds the result rows are also written to `sout`
+// in LDS (same layout), where the next product of a chain reads them.
+constexpr int kLdS = kD + 4;
+template <bool kBtLds = false, bool kOutLds = false>
 __device__ __forceinline__ void fix_block(const float *A, const float *Bt, uint32_t bt_row,
                                           const float *base, float *dst, uint32_t base_row,
-                                          int rows, __bf16 *ahi, __bf16 *alo) {
-  const rsrc_t rb = make_rsrc(Bt, static_cast<uint32_t>(rows) * bt_row);
+                                          int rows, __bf16 *ahi, __bf16 *alo,
+                                          float *sout = nullptr) {
+  const rsrc_t rb = make_rsrc(kBtLds ? nullptr : Bt, kBtLds ? 0u : static_cast<uint32_t>(rows) * bt_row);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   // requests first: this wave's B^T rows (32 wv + 16 nt + c, all k) and the
@@ -964,9 +970,15 @@ __device__ __forceinline__ void fix_block(const float *A, const float *Bt, uint3
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const uint32_t off = (32 * wv + 16 * nt + c) * bt_row + (32 * ks + 8 * g) * 4;
-      braw[ks][nt][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-      braw[ks][nt][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, off + 16, 0, 0);
+      if constexpr (kBtLds) {
+        const float *r = Bt + (32 * wv + 16 * nt + c) * kLdS + 32 * ks + 8 * g;
+        braw[ks][nt][0] = *reinterpret_cast<const u32x4 *>(r);
+        braw[ks][nt][1] = *reinterpret_cast<const u32x4 *>(r + 4);
+      } else {
+        const uint32_t off = (32 * wv + 16 * nt + c) * bt_row + (32 * ks + 8 * g) * 4;
+        braw[ks][nt][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        braw[ks][nt][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, off + 16, 0, 0);
+      }
     }
   // C tile (mt, nt) element i: row 16 mt + 4 g + i, column n = 32 wv + 16 nt + c
   // (rows past the sequence read as zero and are not written)
@@ -1028,9 +1040,11 @@ __device__ __forceinline__ void fix_block(const float *A, const float *Bt, uint3
     const int n = 32 * wv + 16 * nt + c;
     if (n < rows) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<f32x4 *>(dst + (int64_t)n * (base_row / 4) + 16 * mt + 4 * g) =
-            add[mt][nt] + acc[mt][nt];
+      for (int mt = 0; mt < 8; ++mt) {
+        const f32x4 r = add[mt][nt] + acc[mt][nt];
+        *reinterpret_cast<f32x4 *>(dst + (int64_t)n * (base_row / 4) + 16 * mt + 4 * g) = r;
+        if constexpr (kOutLds) *reinterpret_cast<f32x4 *>(sout + n * kLdS + 16 * mt + 4 * g) = r;
+      }
     }
   }
 }
@@ -1083,22 +1097,31 @@ __global__ __launch_bounds__(kFixThreads) void segfix_kernel(const int32_t *__re
   fix_block(A, Bt, bt_row, base, dst, base_row, rows, ahi, alo);
 }
 
-// State k of a walk in more than two parts: S_k = Z_k + Phi_k S_{k-1}, over
-// Z_k in place, or into hT for the last (not written when hT is null).
-__global__ __launch_bounds__(kFixThreads) void segstate_kernel(float *__restrict__ hT,
-                                                               SegScratch seg, int n_max, int Hv,
-                                                               int k) {
+// States S_1 .. S_{P-1} of a walk in more than two parts, in order, by one
+// work-group per (sequence, value head): S_k = Z_k + Phi_k S_{k-1}, over Z_k
+// in place, or into hT for the last (left out when hT is null: the row fix-up
+// needs S_1 .. S_{P-2} only). Each S_k also stays in LDS as the operand of the
+// next product, so the chain needs no round trip through global memory and
+// one launch.
+__global__ __launch_bounds__(kFixThreads) void segchain_kernel(float *__restrict__ hT,
+                                                               SegScratch seg, int n_max, int Hv) {
   __shared__ __attribute__((aligned(16))) __bf16 ahi[kD * kLdFix];
   __shared__ __attribute__((aligned(16))) __bf16 alo[kD * kLdFix];
+  __shared__ __attribute__((aligned(16))) float sprev[kD * kLdS];
   const int pair = flat_block();
   if (pair >= n_max * Hv) return;
   const int64_t st = static_cast<int64_t>(pair) * kD * kD;
   const int64_t E = seg.state_elems;
-  float *z = seg.z + (k - 1) * E + st;
-  float *dst = k == seg.parts - 1 ? (hT ? hT + st : nullptr) : z;
-  if (dst == nullptr) return;
-  const float *prev = (k == 1 ? seg.sa : seg.z + (k - 2) * E) + st;
-  fix_block(seg.phi + (k - 1) * E + st, prev, kD * 4, z, dst, kD * 4, kD, ahi, alo);
+  const int last = hT ? seg.parts - 1 : seg.parts - 2;
+  for (int k = 1; k <= last; ++k) {
+    float *z = seg.z + (k - 1) * E + st;
+    float *dst = k == seg.parts - 1 ? hT + st : z;
+    if (k == 1)
+      fix_block<false, true>(seg.phi + st, seg.sa + st, kD * 4, z, dst, kD * 4, kD, ahi, alo, sprev);
+    else
+      fix_block<true, true>(seg.phi + (k - 1) * E + st, sprev, 0, z, dst, kD * 4, kD, ahi, alo, sprev);
+    __syncthreads();  // S_k complete in LDS; A's staging space free again
+  }
 }
 
 // Row blocks of 128 outputs per later segment: a segment has at most
@@ -1168,8 +1191,8 @@ hipError_t launch_waves(const StageBuffers &in, const float *h0, const int32_t *
   const hipError_t e = launch_walk<kF32In, kDepthSeg, 2>(in, h0, cu, n_max, h, hv, t_max, nt, o,
                                                          hT, seg, stream, ev.start, nullptr);
   if (e != hipSuccess) return e;
-  for (int k = 1; parts > 2 && k < parts; ++k) {  // S_1 .. S_{P-1} in order
-    hipLaunchKernelGGL(segstate_kernel, sgrid, dim3(kFixThreads), 0, stream, hT, seg, n_max, hv, k);
+  if (parts > 2) {  // S_1 .. S_{P-1} in order
+    hipLaunchKernelGGL(segchain_kernel, sgrid, dim3(kFixThreads), 0, stream, hT, seg, n_max, hv);
     const hipError_t es = hipGetLastError();
     if (es != hipSuccess) return es;
   }
