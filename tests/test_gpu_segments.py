@@ -85,10 +85,11 @@ def test_segments_capacity_too_short_for_later_segments(segments):
     assert eo <= O_TOL and es <= S_TOL
 
 
-@pytest.mark.parametrize("segments", [2, 4])
+@pytest.mark.parametrize("segments", [2, 3, 4])
 def test_segments_without_final_state(segments):
     """Without hT the outputs are bitwise those with it (with more than two
-    segments the intermediate states are still chained for the outputs)."""
+    segments the intermediate states are still chained for the outputs, and
+    the chain stops before the last state)."""
     wl = workloads.make_custom([700, 5, 190], 2, 4, seed=22, h0_sigma=0.02)
     d = device_inputs(wl, DEV)
     o_ref, _ = _forward(wl, segments, d)
